@@ -1,0 +1,589 @@
+/*
+ * qref.c — plain CPU oracle.  TEST INFRASTRUCTURE ONLY (see qref.h).
+ *
+ * Every function follows the definition it cites, in plain loops.  Build:
+ *   gcc -std=c11 -O2 -ffp-contract=off -fopenmp -fPIC -shared qref.c -lm
+ */
+#include "qref.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Format geometry                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Per-block scales: one scale per 64 or 128 weights, value = code x scale
+ * ([P4] §2.1).  Block sizes per format are this library's choice: 256 for
+ * ternary, 32 for the 2- and 4-bit levels, 128 for 1-bit signs, 64 for the
+ * trellis codes. */
+int qref_scale_block(int fmt) {
+  switch (fmt) {
+    case QREF_TERN_B3: return 256;
+    case QREF_INT2: return 32;
+    case QREF_SIGN1: return 128;
+    case QREF_INT4: return 32;
+    case QREF_TRELLIS2: return 64;
+    default: return 0;
+  }
+}
+
+/* Bytes per row.  Ternary: a 256-weight block is 48 bytes of 5 trits plus
+ * 4 bytes of 4 trits = 52 bytes, 1.625 bits per weight, just above the
+ * log2(3) = 1.585 floor ([P3] §1.2).  The others are 2, 1, 4 and 2 bits. */
+int64_t qref_packed_row_bytes(int fmt, int K) {
+  int blk = qref_scale_block(fmt);
+  if (blk == 0 || K <= 0 || K % blk != 0) return -1;
+  switch (fmt) {
+    case QREF_TERN_B3: return (int64_t)52 * (K / 256);
+    case QREF_INT2: return K / 4;
+    case QREF_SIGN1: return K / 8;
+    case QREF_INT4: return K / 2;
+    case QREF_TRELLIS2: return K / 4;
+  }
+  return -1;
+}
+
+int64_t qref_row_stride(int fmt, int K) {
+  int64_t b = qref_packed_row_bytes(fmt, K);
+  if (b < 0) return b;
+  return (b + 15) / 16 * 16;
+}
+
+/* ------------------------------------------------------------------------ */
+/* fp16 conversion (IEEE binary16, round to nearest even)                    */
+/* ------------------------------------------------------------------------ */
+
+uint16_t qref_f64_to_f16(double x) {
+  uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  if (isnan(x)) return (uint16_t)(sign | 0x7E00u);
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  /* Largest finite fp16 is 65504; values >= 65520 round to infinity. */
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+  int e;
+  (void)frexp(a, &e);      /* a = m * 2^e, m in [0.5, 1) */
+  int E = e - 1;           /* a in [2^E, 2^(E+1)) */
+  if (E < -14) {
+    /* Subnormal range: quantum 2^-24.  a / 2^-24 is exact in double. */
+    double n = rint(ldexp(a, 24)); /* nearest integer, ties to even */
+    /* n == 1024 encodes the smallest normal, which the bit pattern does. */
+    return (uint16_t)(sign | (uint16_t)n);
+  }
+  double n = rint(ldexp(a, 10 - E)); /* in [1024, 2048] */
+  if (n >= 2048.0) {
+    n = 1024.0;
+    E += 1;
+  }
+  if (E > 15) return (uint16_t)(sign | 0x7C00u);
+  return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)n - 1024));
+}
+
+double qref_f16_to_f64(uint16_t h) {
+  int s = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1F;
+  int m = h & 0x3FF;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activation Q8                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* int8 activations are what the pages' int8 dot-product GEMV and int8
+ * tensor-core paths consume ([P1] "porting a non-standard format into
+ * llama.cpp": decode via DP4A GEMV, batches via INT8 MMA, prefill via INT8
+ * GEMM).  One fp32 scale per block of n values:
+ *   amax = max |v|;  d = amax / 127 (fp32, IEEE division);
+ *   id = amax == 0 ? 0 : 1 / d (fp32);  q = clamp(rint(v * id), -127, 127)
+ * with rint rounding half to even.  -128 never occurs. */
+void qref_q8_block(const float* v, int n, int8_t* q, float* d, int32_t* qsum) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float a = fabsf(v[i]);
+    if (a > amax) amax = a;
+  }
+  float dd = amax / 127.0f;
+  float id = (amax == 0.0f) ? 0.0f : 1.0f / dd;
+  int32_t s = 0;
+  for (int i = 0; i < n; ++i) {
+    float prod = v[i] * id;
+    float r = rintf(prod);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    q[i] = (int8_t)r;
+    s += q[i];
+  }
+  *d = dd;
+  *qsum = s;
+}
+
+void qref_act_quant(const float* x, int B, int K, int qblock, int8_t* q, float* d, int32_t* qsum) {
+  int nb = K / qblock;
+  for (int b = 0; b < B; ++b)
+    for (int kb = 0; kb < nb; ++kb) {
+      size_t off = (size_t)b * K + (size_t)kb * qblock;
+      qref_q8_block(x + off, qblock, q + off, d + (size_t)b * nb + kb, qsum + (size_t)b * nb + kb);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Weight quantizers (host-side data preparation), fp64 decisions            */
+/* ------------------------------------------------------------------------ */
+
+/* Ternary quantizer of [P3] §5.1: scale = mean|W| + 1e-8, code =
+ * clamp(round(W / scale), -1, 1), dequantized value = code * scale.  The page
+ * applies it per tensor; here it runs per 256-weight block, matching the
+ * per-block scales of [P4] §2.1.  round = half to even.  The mean is summed in
+ * index order in fp64; the stored scale is fp16(scale). */
+void qref_quant_tern(const float* w, int N, int K, int8_t* t, uint16_t* s) {
+  int nb = K / 256;
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int kb = 0; kb < nb; ++kb) {
+      const float* wb = w + (size_t)n * K + (size_t)kb * 256;
+      double sum = 0.0;
+      for (int i = 0; i < 256; ++i) sum += fabs((double)wb[i]);
+      double sc = sum / 256.0 + 1e-8;
+      for (int i = 0; i < 256; ++i) {
+        double r = rint((double)wb[i] / sc);
+        if (r > 1.0) r = 1.0;
+        if (r < -1.0) r = -1.0;
+        t[(size_t)n * K + (size_t)kb * 256 + i] = (int8_t)r;
+      }
+      s[(size_t)n * nb + kb] = qref_f64_to_f16(sc);
+    }
+}
+
+/* Shared by the 2- and 4-bit quantizers: levels (c - (L-1)/2) * s for
+ * c = 0..L-1, i.e. the half-integers +-0.5 .. +-(L-1)/2 times s, with
+ * s = fp16(amax / ((L-1)/2)) from the block's absolute maximum.  The code is
+ * the nearest level to w / s (s as stored), ties toward the upper level:
+ * c = clamp(floor(w/s) + L/2, 0, L-1).  A block with s == 0 gets c = L/2. */
+static void quant_levels(const float* w, int N, int K, int L, int8_t* c, uint16_t* s) {
+  int nb = K / 32;
+  double half_span = (L - 1) / 2.0;
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int kb = 0; kb < nb; ++kb) {
+      const float* wb = w + (size_t)n * K + (size_t)kb * 32;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        double a = fabs((double)wb[i]);
+        if (a > amax) amax = a;
+      }
+      uint16_t sh = qref_f64_to_f16(amax / half_span);
+      double sc = qref_f16_to_f64(sh);
+      for (int i = 0; i < 32; ++i) {
+        int code;
+        if (sc == 0.0) {
+          code = L / 2;
+        } else {
+          double f = floor((double)wb[i] / sc) + L / 2;
+          if (f < 0.0) f = 0.0;
+          if (f > L - 1) f = L - 1;
+          code = (int)f;
+        }
+        c[(size_t)n * K + (size_t)kb * 32 + i] = (int8_t)code;
+      }
+      s[(size_t)n * nb + kb] = sh;
+    }
+}
+
+/* 2 bits hold 4 levels ([P1] "how big is 2.4 bits"): {-1.5,-0.5,0.5,1.5} x s. */
+void qref_quant_int2(const float* w, int N, int K, int8_t* c, uint16_t* s) {
+  quant_levels(w, N, K, 4, c, s);
+}
+
+/* 4 bits hold 16 levels ([P1] "how big is 2.4 bits"): {-7.5..7.5} x s.
+ * int4 weights are dequantized and multiplied ([P4] §2.2). */
+void qref_quant_int4(const float* w, int N, int K, int8_t* c, uint16_t* s) {
+  quant_levels(w, N, K, 16, c, s);
+}
+
+/* 1 bit keeps only the sign ([P1] "how big is 2.4 bits"; binarization as the
+ * step beyond ternary, [P4] §7).  b = (w >= 0); the scale per 128 weights is
+ * the mean |w| of the block (fp64, index order), stored as fp16. */
+void qref_quant_sign1(const float* w, int N, int K, int8_t* b, uint16_t* s) {
+  int nb = K / 128;
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int kb = 0; kb < nb; ++kb) {
+      const float* wb = w + (size_t)n * K + (size_t)kb * 128;
+      double sum = 0.0;
+      for (int i = 0; i < 128; ++i) sum += fabs((double)wb[i]);
+      for (int i = 0; i < 128; ++i) b[(size_t)n * K + (size_t)kb * 128 + i] = wb[i] >= 0.0f ? 1 : 0;
+      s[(size_t)n * nb + kb] = qref_f64_to_f16(sum / 128.0);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Packers / unpackers                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Ternary byte: 5 trits of one byte form the base-3 number
+ *   b = sum_{i=0..4} (t_i + 1) * 3^(4-i)        (digit 0 most significant)
+ * stored as the 8-bit fixed-point base-3 fraction q = ceil(256 * b / 243),
+ * so b = floor(243 * q / 256).  3 states per weight need log2 3 = 1.585 bits
+ * ([P3] §1.2, [P4] §2.1); 5 per byte is 1.6 bits.
+ * Within a 256-weight block (13 little-endian 32-bit words, 52 bytes):
+ *   word m < 12, byte p, digit i  <->  weight 20m + 4i + p
+ *   word 12,     byte p, digit i<4 <->  weight 240 + 4i + p; digit 4 = 1 (t = 0)
+ */
+static uint8_t tern_encode(const int t[5]) {
+  int b = 0;
+  for (int i = 0; i < 5; ++i) b = b * 3 + (t[i] + 1);
+  return (uint8_t)((256 * b + 242) / 243); /* ceil(256 b / 243) */
+}
+
+static void tern_decode(uint8_t q, int t[5]) {
+  int b = (243 * (int)q) >> 8; /* floor(243 q / 256) */
+  for (int i = 4; i >= 0; --i) {
+    t[i] = b % 3 - 1;
+    b /= 3;
+  }
+}
+
+/* Bit position of weight k (within its group) for the plane formats:
+ * weight 4j + lane (lane = 0..3) lives in byte `lane` of the 32-bit word at
+ * bit offset j * bits.  Words are little-endian. */
+static int plane_bitpos(int k_in_word, int bits) {
+  int j = k_in_word / 4, lane = k_in_word % 4;
+  return 8 * lane + j * bits;
+}
+
+int qref_pack(int fmt, const int8_t* codes, int N, int K, uint8_t* packed) {
+  int64_t stride = qref_row_stride(fmt, K);
+  if (stride < 0) return -1;
+  memset(packed, 0, (size_t)stride * N);
+  for (int n = 0; n < N; ++n) {
+    const int8_t* c = codes + (size_t)n * K;
+    uint8_t* row = packed + (size_t)n * stride;
+    switch (fmt) {
+      case QREF_TERN_B3:
+        for (int blk = 0; blk < K / 256; ++blk) {
+          uint8_t* bb = row + 52 * blk;
+          const int8_t* cb = c + 256 * blk;
+          for (int m = 0; m < 13; ++m)
+            for (int p = 0; p < 4; ++p) {
+              int t[5];
+              for (int i = 0; i < 5; ++i) {
+                if (m < 12) t[i] = cb[20 * m + 4 * i + p];
+                else t[i] = (i < 4) ? cb[240 + 4 * i + p] : 0;
+              }
+              bb[4 * m + p] = tern_encode(t);
+            }
+        }
+        break;
+      case QREF_INT2:
+      case QREF_SIGN1:
+      case QREF_INT4: {
+        int bits = fmt == QREF_INT2 ? 2 : fmt == QREF_SIGN1 ? 1 : 4;
+        int per_word = 32 / bits;
+        for (int w = 0; w < K / per_word; ++w) {
+          uint32_t word = 0;
+          for (int k = 0; k < per_word; ++k)
+            word |= (uint32_t)(c[w * per_word + k] & ((1 << bits) - 1)) << plane_bitpos(k, bits);
+          for (int by = 0; by < 4; ++by) row[4 * w + by] = (uint8_t)(word >> (8 * by));
+        }
+        break;
+      }
+      case QREF_TRELLIS2:
+        /* Byte g = c[4g]<<6 | c[4g+1]<<4 | c[4g+2]<<2 | c[4g+3] (first symbol
+         * in the top bits). */
+        for (int g = 0; g < K / 4; ++g)
+          row[g] = (uint8_t)(((c[4 * g] & 3) << 6) | ((c[4 * g + 1] & 3) << 4) |
+                             ((c[4 * g + 2] & 3) << 2) | (c[4 * g + 3] & 3));
+        break;
+      default:
+        return -1;
+    }
+  }
+  return 0;
+}
+
+int qref_unpack(int fmt, const uint8_t* packed, int N, int K, int8_t* codes) {
+  int64_t stride = qref_row_stride(fmt, K);
+  if (stride < 0) return -1;
+  for (int n = 0; n < N; ++n) {
+    int8_t* c = codes + (size_t)n * K;
+    const uint8_t* row = packed + (size_t)n * stride;
+    switch (fmt) {
+      case QREF_TERN_B3:
+        for (int blk = 0; blk < K / 256; ++blk) {
+          const uint8_t* bb = row + 52 * blk;
+          int8_t* cb = c + 256 * blk;
+          for (int m = 0; m < 13; ++m)
+            for (int p = 0; p < 4; ++p) {
+              int t[5];
+              tern_decode(bb[4 * m + p], t);
+              for (int i = 0; i < 5; ++i) {
+                if (m < 12) cb[20 * m + 4 * i + p] = (int8_t)t[i];
+                else if (i < 4) cb[240 + 4 * i + p] = (int8_t)t[i];
+              }
+            }
+        }
+        break;
+      case QREF_INT2:
+      case QREF_SIGN1:
+      case QREF_INT4: {
+        int bits = fmt == QREF_INT2 ? 2 : fmt == QREF_SIGN1 ? 1 : 4;
+        int per_word = 32 / bits;
+        for (int w = 0; w < K / per_word; ++w) {
+          uint32_t word = 0;
+          for (int by = 0; by < 4; ++by) word |= (uint32_t)row[4 * w + by] << (8 * by);
+          for (int k = 0; k < per_word; ++k)
+            c[w * per_word + k] = (int8_t)((word >> plane_bitpos(k, bits)) & ((1u << bits) - 1));
+        }
+        break;
+      }
+      case QREF_TRELLIS2:
+        for (int g = 0; g < K / 4; ++g)
+          for (int j = 0; j < 4; ++j) c[4 * g + j] = (int8_t)((row[g] >> (6 - 2 * j)) & 3);
+        break;
+      default:
+        return -1;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Trellis codes and the hash codebook                                       */
+/* ------------------------------------------------------------------------ */
+
+/* The trellis format carries 2-3 bits per weight with a codebook computed at
+ * run time from a hash ([P1] "how big is 2.4 bits"), coding each row in groups
+ * of 4 weights ([P2] "12 GB 装下 27B，靠的是什么取舍").  This library's
+ * variant: 2 bits per weight, a 16-bit state
+ *   st <- ((st << 2) | c) & 0xFFFF, starting from a stored per-row seed,
+ * the value index h = ((st * 0x9E37) ^ (st >> 7)) & 0xFF computed in uint32
+ * on the state after its own symbol is shifted in. */
+uint32_t qref_trellis_hash(uint32_t st) {
+  return ((st * 0x9E37u) ^ (st >> 7)) & 0xFFu;
+}
+
+/* Standard normal CDF through the complementary error function. */
+static double norm_cdf(double z) {
+  return 0.5 * erfc(-z / sqrt(2.0));
+}
+
+/* Inverse standard normal CDF by bisection on norm_cdf: 200 halvings of
+ * [-40, 40] reach the double-precision root. */
+double qref_norm_ppf(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 200; ++it) {
+    double mid = 0.5 * (lo + hi);
+    if (mid == lo || mid == hi) break;
+    if (norm_cdf(mid) < p) lo = mid;
+    else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+/* The 8-bit hash selects one of 256 N(0,1) quantiles at the cell midpoints
+ * (k + 0.5) / 256, stored as fp16. */
+void qref_codebook_v16(uint16_t v16[256]) {
+  for (int k = 0; k < 256; ++k) v16[k] = qref_f64_to_f16(qref_norm_ppf((k + 0.5) / 256.0));
+}
+
+/* int8 image of the codebook for the int8 dot-product GEMV:
+ * V8[k] = rint(V16[k] * 127 / V16[255]), gain g = V16[255] / 127. */
+void qref_codebook_v8(int8_t v8[256], double* g) {
+  uint16_t v16[256];
+  qref_codebook_v16(v16);
+  double top = qref_f16_to_f64(v16[255]);
+  for (int k = 0; k < 256; ++k) v8[k] = (int8_t)rint(qref_f16_to_f64(v16[k]) * 127.0 / top);
+  if (g) *g = top / 127.0;
+}
+
+void qref_trellis_states(const uint8_t* packed, const uint16_t* seeds, int N, int K, uint16_t* st) {
+  int64_t stride = qref_row_stride(QREF_TRELLIS2, K);
+  for (int n = 0; n < N; ++n) {
+    const uint8_t* row = packed + (size_t)n * stride;
+    uint32_t s = seeds[n];
+    for (int i = 0; i < K; ++i) {
+      uint32_t c = (row[i / 4] >> (6 - 2 * (i % 4))) & 3u;
+      s = ((s << 2) | c) & 0xFFFFu;
+      st[(size_t)n * K + i] = (uint16_t)s;
+    }
+  }
+}
+
+/* Weight value = fp32(s64) * fp32(V16[h]); both factors have 11-bit
+ * significands, so the fp32 product is exact. */
+void qref_trellis_decode_f32(const uint8_t* packed, const uint16_t* seeds, const uint16_t* scales,
+                             int N, int K, float* w) {
+  uint16_t v16[256];
+  qref_codebook_v16(v16);
+  int64_t stride = qref_row_stride(QREF_TRELLIS2, K);
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n) {
+    const uint8_t* row = packed + (size_t)n * stride;
+    uint32_t s = seeds[n];
+    for (int i = 0; i < K; ++i) {
+      uint32_t c = (row[i / 4] >> (6 - 2 * (i % 4))) & 3u;
+      s = ((s << 2) | c) & 0xFFFFu;
+      float v = (float)qref_f16_to_f64(v16[qref_trellis_hash(s)]);
+      float sc = (float)qref_f16_to_f64(scales[(size_t)n * (K / 64) + i / 64]);
+      w[(size_t)n * K + i] = sc * v;
+    }
+  }
+}
+
+/* Decode-time Q8 of the exact fp32 weights per (row, oblock) so that an int8
+ * GEMM can consume trellis weights (the pages' prefill is an INT8 GEMM,
+ * [P1] "porting a non-standard format into llama.cpp"). */
+void qref_trellis_decode_i8(const uint8_t* packed, const uint16_t* seeds, const uint16_t* scales,
+                            int N, int K, int oblock, int8_t* wq, float* dw) {
+  float* w = (float*)malloc(sizeof(float) * (size_t)N * K);
+  qref_trellis_decode_f32(packed, seeds, scales, N, K, w);
+  int nb = K / oblock;
+  for (int n = 0; n < N; ++n)
+    for (int kb = 0; kb < nb; ++kb) {
+      int32_t qs;
+      size_t off = (size_t)n * K + (size_t)kb * oblock;
+      qref_q8_block(w + off, oblock, wq + off, dw + (size_t)n * nb + kb, &qs);
+    }
+  free(w);
+}
+
+/* ------------------------------------------------------------------------ */
+/* GEMV                                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* Integer level of each weight and the fp64 factor that turns the integer
+ * block dot into weight units:
+ *   TERN_B3  level t            factor s(256-block)
+ *   INT2     level 2c - 3       factor s(32-block) / 2
+ *   SIGN1    level 2b - 1       factor s(128-block)
+ *   INT4     level 2c - 15      factor s(32-block) / 2
+ *   TRELLIS2 level V8[h]        factor s(64-block) * g
+ * Ternary products reduce to add, subtract or skip ([P3] §1.2, [P4] §2.2);
+ * the integer dot below is that sum. */
+int qref_gemv(int fmt, const uint8_t* packed, const uint16_t* scales, const uint16_t* seeds,
+              int N, int K, const int8_t* q, const float* d, int B,
+              int64_t* I, double* y, double* absT) {
+  int blk = qref_scale_block(fmt);
+  if (blk == 0 || K % blk != 0 || K % 32 != 0) return -1;
+  int64_t stride = qref_row_stride(fmt, K);
+  int nsb = K / blk, nkb = K / 32;
+  int8_t v8[256];
+  double g = 0.0;
+  if (fmt == QREF_TRELLIS2) qref_codebook_v8(v8, &g);
+  int rc = 0;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int n = 0; n < N; ++n) {
+    int8_t* lev = (int8_t*)malloc((size_t)K);
+    int8_t* codes = (int8_t*)malloc((size_t)K);
+    const uint8_t* row = packed + (size_t)n * stride;
+    if (fmt == QREF_TRELLIS2) {
+      uint32_t st = seeds[n];
+      for (int i = 0; i < K; ++i) {
+        uint32_t c = (row[i / 4] >> (6 - 2 * (i % 4))) & 3u;
+        st = ((st << 2) | c) & 0xFFFFu;
+        lev[i] = v8[qref_trellis_hash(st)];
+      }
+    } else {
+      qref_unpack(fmt, row, 1, K, codes);
+      for (int i = 0; i < K; ++i) {
+        int c = codes[i];
+        lev[i] = (int8_t)(fmt == QREF_TERN_B3 ? c : fmt == QREF_INT2 ? 2 * c - 3
+                          : fmt == QREF_SIGN1 ? 2 * c - 1 : 2 * c - 15);
+      }
+    }
+    for (int b = 0; b < B; ++b) {
+      const int8_t* qb = q + (size_t)b * K;
+      double acc = 0.0, aacc = 0.0;
+      for (int kb = 0; kb < nkb; ++kb) {
+        int64_t dot = 0;
+        for (int i = 0; i < 32; ++i) dot += (int64_t)lev[kb * 32 + i] * qb[kb * 32 + i];
+        double s = qref_f16_to_f64(scales[(size_t)n * nsb + (kb * 32) / blk]);
+        double f = (fmt == QREF_INT2 || fmt == QREF_INT4) ? 0.5 * s : fmt == QREF_TRELLIS2 ? s * g : s;
+        double T = f * (double)d[(size_t)b * nkb + kb] * (double)dot;
+        acc += T;
+        aacc += fabs(T);
+        if (I) I[((size_t)b * N + n) * nkb + kb] = dot;
+      }
+      if (y) y[(size_t)b * N + n] = acc;
+      if (absT) absT[(size_t)b * N + n] = aacc;
+    }
+    free(lev);
+    free(codes);
+  }
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block-randomized Walsh-Hadamard rotation                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Random Hadamard rotation of the QuIP / QuIP# / QTIP line ([P2] "12 GB 装下
+ * 27B"): here applied to activations in 256-blocks.  Sylvester (natural)
+ * order; stage h = 1, 2, ..., 128 maps (u_i, u_{i+h}) to (u_i + u_{i+h},
+ * u_i - u_{i+h}) for every i with (i & h) == 0; then scale by 1/16 so the
+ * transform is orthonormal.  fp32, this exact order. */
+void qref_fwht256(float* u) {
+  for (int h = 1; h < 256; h <<= 1)
+    for (int i = 0; i < 256; ++i)
+      if ((i & h) == 0) {
+        float a = u[i], b = u[i + h];
+        u[i] = a + b;
+        u[i + h] = a - b;
+      }
+  for (int i = 0; i < 256; ++i) u[i] = u[i] * 0.0625f;
+}
+
+void qref_hadamard_quant(const float* x, int B, int K, const uint32_t* sign_bits, int qblock,
+                         int8_t* q, float* d, int32_t* qsum) {
+  int nq = K / qblock;
+  float u[256];
+  for (int b = 0; b < B; ++b) {
+    float* rot = (float*)malloc(sizeof(float) * (size_t)K);
+    for (int blk = 0; blk < K / 256; ++blk) {
+      for (int i = 0; i < 256; ++i) {
+        int k = blk * 256 + i;
+        float v = x[(size_t)b * K + k];
+        u[i] = ((sign_bits[k / 32] >> (k % 32)) & 1u) ? -v : v;
+      }
+      qref_fwht256(u);
+      memcpy(rot + blk * 256, u, sizeof(u));
+    }
+    for (int kb = 0; kb < nq; ++kb)
+      qref_q8_block(rot + kb * qblock, qblock, q + (size_t)b * K + kb * qblock,
+                    d + (size_t)b * nq + kb, qsum + (size_t)b * nq + kb);
+    free(rot);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* GEMM                                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* Prefill as an int8 GEMM with per-block scales on both operands ([P1]
+ * "porting a non-standard format into llama.cpp"). */
+void qref_gemm_i8(const int8_t* xq, const float* dx, int M, const int8_t* wq, const float* dw,
+                  int N, int K, int kblock, double* y, double* absT) {
+  int nb = K / kblock;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0, aacc = 0.0;
+      for (int kb = 0; kb < nb; ++kb) {
+        int64_t dot = 0;
+        for (int i = 0; i < kblock; ++i)
+          dot += (int64_t)xq[(size_t)m * K + kb * kblock + i] * wq[(size_t)n * K + kb * kblock + i];
+        double T = (double)dx[(size_t)m * nb + kb] * (double)dw[(size_t)n * nb + kb] * (double)dot;
+        acc += T;
+        aacc += fabs(T);
+      }
+      y[(size_t)m * N + n] = acc;
+      if (absT) absT[(size_t)m * N + n] = aacc;
+    }
+}
