@@ -1,0 +1,154 @@
+// act.hip — activation quantization to int8 (per 32 or 256 values) and the
+// block-randomized Walsh-Hadamard rotation that precedes it for prefill.
+//
+// Both kernels are bit-exact against their definitions: every float op below
+// is one IEEE fp32 op in the definition's order (contraction off), division
+// and reciprocal correctly rounded, rint rounds half to even.
+#include "internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace qk {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Butterfly reduction over the `width` lanes of a group (width a power of 2).
+__device__ __forceinline__ float group_max(float v, int width) {
+  for (int m = 1; m < width; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ int group_sum(int v, int width) {
+  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Q8 of four values held by this lane, whose block spans `width` lanes.
+// Writes the 4 int8 codes to q4 and, from the block's first lane, d and qsum.
+__device__ __forceinline__ void q8_lane4(f32x4 v, int width, bool first, uint32_t* q4, float* d, int32_t* qsum) {
+  float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  am = group_max(am, width);
+  const float dd = am / 127.0f;
+  const float id = am == 0.0f ? 0.0f : 1.0f / dd;
+  const float e[4] = {v.x, v.y, v.z, v.w};
+  uint32_t packed = 0;
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float r = rintf(e[i] * id);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    const int qi = (int)r;
+    s += qi;
+    packed |= ((uint32_t)(qi & 0xFF)) << (8 * i);
+  }
+  s = group_sum(s, width);
+  *q4 = packed;
+  if (first) {
+    *d = dd;
+    *qsum = s;
+  }
+}
+
+// One thread per 4 consecutive values; qblock/4 lanes per block.
+__global__ __launch_bounds__(256) void k_act_quant(const float* __restrict__ x, int64_t n4, int qblock,
+                                                   int8_t* __restrict__ q, float* __restrict__ d,
+                                                   int32_t* __restrict__ qsum) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int width = qblock / 4;
+  // Every lane of a block takes part in the shuffles, so out-of-range lanes
+  // (only possible in the last workgroup) use zeros and store nothing.
+  const bool ok = i < n4;
+  const f32x4 v = ok ? *(const f32x4*)(x + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  uint32_t q4;
+  float dd;
+  int32_t s;
+  const int64_t blk = (4 * i) / qblock;
+  const bool first = (threadIdx.x % width) == 0;
+  q8_lane4(v, width, first, &q4, &dd, &s);
+  if (ok) {
+    *(uint32_t*)(q + 4 * i) = q4;
+    if (first) {
+      d[blk] = dd;
+      qsum[blk] = s;
+    }
+  }
+}
+
+hipError_t launch_act_quant(const float* x, int B, int K, int qblock, int8_t* q, float* d, int32_t* qsum,
+                            hipStream_t s) {
+  const int64_t n4 = (int64_t)B * K / 4;
+  const int64_t grid = (n4 + 255) / 256;
+  hipLaunchKernelGGL(k_act_quant, dim3((unsigned)grid), dim3(256), 0, s, x, n4, qblock, q, d, qsum);
+  return hipGetLastError();
+}
+
+// One wave per (token, 256-block): lane l holds values 4l .. 4l+3.
+__global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict__ x, int K, int64_t nblocks,
+                                                        const uint32_t* __restrict__ sign_bits, int qblock,
+                                                        int8_t* __restrict__ q, float* __restrict__ d,
+                                                        int32_t* __restrict__ qsum) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nblocks) return;  // whole wave leaves together
+  const int nkb = K / 256;
+  const int64_t tok = blk / nkb;
+  const int kb = (int)(blk % nkb);
+  const int64_t off = tok * K + (int64_t)kb * 256 + 4 * lane;
+  const f32x4 v = *(const f32x4*)(x + off);
+  const int k0 = kb * 256 + 4 * lane;
+  const uint32_t sw = sign_bits[k0 >> 5] >> (k0 & 31);
+  float u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if ((sw >> i) & 1u) u[i] = -u[i];
+  // stage h = 1: pairs (0,1), (2,3); stage h = 2: pairs (0,2), (1,3)
+  {
+    const float a0 = u[0], a1 = u[1], a2 = u[2], a3 = u[3];
+    u[0] = a0 + a1;
+    u[1] = a0 - a1;
+    u[2] = a2 + a3;
+    u[3] = a2 - a3;
+  }
+  {
+    const float a0 = u[0], a1 = u[1], a2 = u[2], a3 = u[3];
+    u[0] = a0 + a2;
+    u[2] = a0 - a2;
+    u[1] = a1 + a3;
+    u[3] = a1 - a3;
+  }
+  // stages h = 4 .. 128 pair lane l with lane l ^ (h/4)
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float other = __shfl_xor(u[i], m);
+      // lower element: u_i + u_{i+h}; upper element: u_i - u_{i+h}
+      u[i] = upper ? other - u[i] : u[i] + other;
+    }
+  }
+  const f32x4 r = {u[0] * 0.0625f, u[1] * 0.0625f, u[2] * 0.0625f, u[3] * 0.0625f};
+  const int width = qblock / 4;
+  uint32_t q4;
+  float dd;
+  int32_t s;
+  const bool first = (lane % width) == 0;
+  q8_lane4(r, width, first, &q4, &dd, &s);
+  *(uint32_t*)(q + off) = q4;
+  if (first) {
+    const int64_t nq = K / qblock;
+    const int64_t qi = tok * nq + ((int64_t)kb * 256 + 4 * lane) / qblock;
+    d[qi] = dd;
+    qsum[qi] = s;
+  }
+}
+
+hipError_t launch_hadamard_quant(const float* x, int B, int K, const uint32_t* sign_bits, int qblock, int8_t* q,
+                                 float* d, int32_t* qsum, hipStream_t s) {
+  const int64_t nblocks = (int64_t)B * (K / 256);
+  const int64_t grid = (nblocks + 3) / 4;
+  hipLaunchKernelGGL(k_hadamard_quant, dim3((unsigned)grid), dim3(256), 0, s, x, K, nblocks, sign_bits, qblock, q, d,
+                     qsum);
+  return hipGetLastError();
+}
+
+}  // namespace qk

@@ -1,0 +1,313 @@
+// api.hip — the C ABI of libqgemv: host-side validation, then dispatch.
+// Every check runs before any HIP call, so rejected calls never touch the GPU.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "internal.hpp"
+
+using namespace qk;
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline hipStream_t S(void* s) { return (hipStream_t)s; }
+inline int hip_rc(hipError_t e) { return e == hipSuccess ? QERR_OK : QERR_HIP; }
+
+int check_weight(const qweight_t* w) {
+  if (!w) return QERR_INVALID_ARG;
+  const int32_t blk = scale_block(w->fmt);
+  if (blk == 0) return QERR_UNSUPPORTED_FMT;
+  if (w->rows < 0 || w->cols < 0) return QERR_INVALID_ARG;
+  if (w->block != blk) return QERR_SHAPE;
+  if (w->cols == 0 || w->cols % blk != 0 || w->cols % 32 != 0) return QERR_SHAPE;
+  if (w->rows == 0) return QERR_OK;
+  if (!w->codes || !w->scales) return QERR_INVALID_ARG;
+  if (w->fmt == QFMT_TRELLIS2 && !w->seeds) return QERR_INVALID_ARG;
+  const int64_t packed = packed_row_bytes(w->fmt, w->cols);
+  if (w->row_bytes < packed || w->row_bytes % 16 != 0) return QERR_SHAPE;
+  if (w->row_bytes >= ((int64_t)1 << 26)) return QERR_SHAPE;  // 64-row tile offsets fit 32 bits
+  if (!aligned(w->codes, 16) || !aligned(w->scales, 2) || (w->seeds && !aligned(w->seeds, 2)))
+    return QERR_ALIGNMENT;
+  return QERR_OK;
+}
+
+GemvItem make_item(const qweight_t* w, const int8_t* q, const float* d, const int32_t* qsum, float* y) {
+  GemvItem it{};
+  it.codes = (const uint8_t*)w->codes;
+  it.scales = w->scales;
+  it.seeds = w->seeds;
+  it.q = q;
+  it.d = d;
+  it.qsum = qsum;
+  it.y = y;
+  it.row_bytes = w->row_bytes;
+  it.fmt = w->fmt;
+  it.rows = w->rows;
+  it.cols = w->cols;
+  return it;
+}
+
+int check_act(const int8_t* q, const float* d, const int32_t* qsum) {
+  if (!q || !d || !qsum) return QERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(d, 4) || !aligned(qsum, 4)) return QERR_ALIGNMENT;
+  return QERR_OK;
+}
+
+int check_item(const qgemv_item_t& it, int32_t B) {
+  int rc = check_weight(&it.w);
+  if (rc) return rc;
+  if (it.w.rows == 0) return QERR_OK;
+  rc = check_act(it.q, it.d, it.qsum);
+  if (rc) return rc;
+  if (!it.y) return QERR_INVALID_ARG;
+  if (!aligned(it.y, 4)) return QERR_ALIGNMENT;
+  (void)B;
+  return QERR_OK;
+}
+
+using GemvLaunch = hipError_t (*)(const GemvItem&, hipStream_t);
+using GroupedLaunch = hipError_t (*)(const PlanHeader&, const void*, void*, hipStream_t);
+const GemvLaunch kGemv[9] = {nullptr, launch_gemv_b1, launch_gemv_b2, launch_gemv_b3, launch_gemv_b4,
+                             launch_gemv_b5, launch_gemv_b6, launch_gemv_b7, launch_gemv_b8};
+const GroupedLaunch kGrouped[9] = {nullptr, launch_grouped_b1, launch_grouped_b2, launch_grouped_b3,
+                                   launch_grouped_b4, launch_grouped_b5, launch_grouped_b6, launch_grouped_b7,
+                                   launch_grouped_b8};
+
+int64_t align16(int64_t x) { return (x + 15) / 16 * 16; }
+
+int64_t count_tiles(const qgemv_item_t* items, int32_t n) {
+  int64_t t = 0;
+  for (int32_t i = 0; i < n; ++i) t += (items[i].w.rows + 63) / 64;
+  return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qstrerror(int err) {
+  switch (err) {
+    case QERR_OK: return "ok";
+    case QERR_INVALID_ARG: return "invalid argument (null pointer, negative size or bad enum)";
+    case QERR_UNSUPPORTED_FMT: return "unsupported weight format for this call";
+    case QERR_SHAPE: return "shape violates the format's block rules";
+    case QERR_ALIGNMENT: return "pointer or stride misaligned";
+    case QERR_HIP: return "HIP launch or query failed";
+    case QERR_BUFFER: return "caller buffer too small or corrupt";
+  }
+  return "unknown error";
+}
+
+int32_t qfmt_scale_block(int32_t fmt) { return scale_block(fmt); }
+
+int64_t qfmt_packed_row_bytes(int32_t fmt, int32_t cols) {
+  const int32_t blk = scale_block(fmt);
+  if (blk == 0) return QERR_UNSUPPORTED_FMT;
+  if (cols <= 0 || cols % blk != 0 || cols % 32 != 0) return QERR_SHAPE;
+  return packed_row_bytes(fmt, cols);
+}
+
+int64_t qfmt_row_bytes(int32_t fmt, int32_t cols) {
+  const int64_t b = qfmt_packed_row_bytes(fmt, cols);
+  return b < 0 ? b : (b + 15) / 16 * 16;
+}
+
+int qweight_check(const qweight_t* w) { return check_weight(w); }
+
+int qweight_quantize(int32_t fmt, const float* w, int32_t rows, int32_t cols, void* codes, int64_t row_bytes,
+                     uint16_t* scales, void* stream) {
+  if (fmt == QFMT_TRELLIS2) return QERR_UNSUPPORTED_FMT;
+  qweight_t d{fmt, rows, cols, scale_block(fmt), codes, row_bytes, scales, nullptr};
+  const int rc = check_weight(&d);
+  if (rc) return rc;
+  if (rows == 0) return QERR_OK;
+  if (!w) return QERR_INVALID_ARG;
+  if (!aligned(w, 4)) return QERR_ALIGNMENT;
+  return hip_rc(launch_quantize(fmt, w, rows, cols, (uint8_t*)codes, row_bytes, scales, S(stream)));
+}
+
+int qweight_pack(int32_t fmt, const int8_t* levels, int32_t rows, int32_t cols, void* codes, int64_t row_bytes,
+                 void* stream) {
+  const int32_t blk = scale_block(fmt);
+  if (blk == 0) return QERR_UNSUPPORTED_FMT;
+  if (rows < 0 || cols < 0) return QERR_INVALID_ARG;
+  if (cols == 0 || cols % blk != 0 || cols % 32 != 0) return QERR_SHAPE;
+  if (rows == 0) return QERR_OK;
+  if (!levels || !codes) return QERR_INVALID_ARG;
+  if (row_bytes < packed_row_bytes(fmt, cols) || row_bytes % 16 != 0) return QERR_SHAPE;
+  if (!aligned(codes, 16)) return QERR_ALIGNMENT;
+  return hip_rc(launch_pack(fmt, levels, rows, cols, (uint8_t*)codes, row_bytes, S(stream)));
+}
+
+int qact_quant_i8(const float* x, int32_t B, int32_t K, int32_t qblock, int8_t* q, float* d, int32_t* qsum,
+                  void* stream) {
+  if (B < 0 || K < 0) return QERR_INVALID_ARG;
+  if (qblock != 32 && qblock != 256) return QERR_INVALID_ARG;
+  if (B == 0) return QERR_OK;
+  if (K == 0 || K % qblock != 0) return QERR_SHAPE;
+  if (!x || !q || !d || !qsum) return QERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(d, 4) || !aligned(qsum, 4)) return QERR_ALIGNMENT;
+  if ((int64_t)B * K >= ((int64_t)1 << 40)) return QERR_SHAPE;
+  return hip_rc(launch_act_quant(x, B, K, qblock, q, d, qsum, S(stream)));
+}
+
+int qact_hadamard_quant_i8(const float* x, int32_t B, int32_t K, const uint32_t* sign_bits, int32_t qblock,
+                           int8_t* q, float* d, int32_t* qsum, void* stream) {
+  if (B < 0 || K < 0) return QERR_INVALID_ARG;
+  if (qblock != 32 && qblock != 256) return QERR_INVALID_ARG;
+  if (B == 0) return QERR_OK;
+  if (K == 0 || K % 256 != 0) return QERR_SHAPE;
+  if (!x || !q || !d || !qsum || !sign_bits) return QERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(d, 4) || !aligned(qsum, 4) || !aligned(sign_bits, 4))
+    return QERR_ALIGNMENT;
+  if ((int64_t)B * (K / 256) >= ((int64_t)1 << 33)) return QERR_SHAPE;
+  return hip_rc(launch_hadamard_quant(x, B, K, sign_bits, qblock, q, d, qsum, S(stream)));
+}
+
+int qgemv(const qweight_t* w, const int8_t* q, const float* d, const int32_t* qsum, int32_t B, float* y,
+          void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (B < 0 || B > 8) return QERR_INVALID_ARG;
+  if (B == 0 || w->rows == 0) return QERR_OK;
+  rc = check_act(q, d, qsum);
+  if (rc) return rc;
+  if (!y) return QERR_INVALID_ARG;
+  if (!aligned(y, 4)) return QERR_ALIGNMENT;
+  return hip_rc(kGemv[B](make_item(w, q, d, qsum, y), S(stream)));
+}
+
+int qgemv_blockdots(const qweight_t* w, const int8_t* q, const int32_t* qsum, int32_t* out, void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (w->rows == 0) return QERR_OK;
+  if (!q || !qsum || !out) return QERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(qsum, 4) || !aligned(out, 4)) return QERR_ALIGNMENT;
+  // the scale path is unused by the hook; pass qsum for d so no pointer is null
+  return hip_rc(launch_blockdots(make_item(w, q, (const float*)qsum, qsum, nullptr), out, S(stream)));
+}
+
+int64_t qgemv_grouped_plan_bytes(const qgemv_item_t* items, int32_t n, int32_t B) {
+  if (!items || n <= 0 || B < 1 || B > 8) return QERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    const int rc = check_item(items[i], B);
+    if (rc) return rc;
+  }
+  return align16(sizeof(PlanHeader)) + align16((int64_t)sizeof(GemvItem) * n) +
+         align16((int64_t)sizeof(GemvTile) * count_tiles(items, n));
+}
+
+int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B, void* host_plan, int64_t plan_bytes) {
+  const int64_t need = qgemv_grouped_plan_bytes(items, n, B);
+  if (need < 0) return (int)need;
+  if (!host_plan) return QERR_INVALID_ARG;
+  if (plan_bytes < need) return QERR_BUFFER;
+  if (!aligned(host_plan, 16)) return QERR_ALIGNMENT;
+  const int64_t ntiles = count_tiles(items, n);
+  if (ntiles >= ((int64_t)1 << 31)) return QERR_SHAPE;
+  uint8_t* base = (uint8_t*)host_plan;
+  std::memset(base, 0, (size_t)need);
+  PlanHeader h{};
+  h.magic = kPlanMagic;
+  h.version = 1;
+  h.n_items = n;
+  h.n_tiles = (int32_t)ntiles;
+  h.B = B;
+  h.items_off = align16(sizeof(PlanHeader));
+  h.tiles_off = h.items_off + align16((int64_t)sizeof(GemvItem) * n);
+  h.total_bytes = need;
+  GemvItem* it = (GemvItem*)(base + h.items_off);
+  for (int32_t i = 0; i < n; ++i) {
+    it[i] = make_item(&items[i].w, items[i].q, items[i].d, items[i].qsum, items[i].y);
+    if (items[i].w.rows > 0) h.fmt_mask |= 1 << items[i].w.fmt;
+  }
+  // Tiles: longest first inside each format; formats interleaved in
+  // proportion to their total bytes so VALU-heavy and byte-heavy work overlap.
+  struct T { int64_t cost; uint32_t item, row0; };
+  std::vector<std::vector<T>> q(6);
+  std::vector<int64_t> total(6, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const qweight_t& w = items[i].w;
+    for (int32_t r = 0; r < w.rows; r += 64) {
+      const int64_t rows = std::min(64, w.rows - r);
+      const int64_t c = rows * (w.row_bytes + (int64_t)(w.cols / w.block) * 2);
+      q[w.fmt].push_back({c, (uint32_t)i, (uint32_t)r});
+      total[w.fmt] += c;
+    }
+  }
+  for (auto& v : q)
+    std::stable_sort(v.begin(), v.end(), [](const T& a, const T& b) { return a.cost > b.cost; });
+  std::vector<size_t> pos(6, 0);
+  std::vector<int64_t> used(6, 0);
+  GemvTile* tiles = (GemvTile*)(base + h.tiles_off);
+  for (int64_t k = 0; k < ntiles; ++k) {
+    int best = -1;
+    double bf = 2.0;
+    for (int f = 1; f <= 5; ++f) {
+      if (pos[f] >= q[f].size()) continue;
+      const double frac = (double)used[f] / (double)total[f];
+      if (frac < bf) {
+        bf = frac;
+        best = f;
+      }
+    }
+    const T& t = q[best][pos[best]++];
+    used[best] += t.cost;
+    tiles[k].item = t.item;
+    tiles[k].row0 = t.row0;
+  }
+  std::memcpy(base, &h, sizeof(h));
+  return QERR_OK;
+}
+
+int64_t qgemv_grouped_scratch_bytes(void) { return kGroupedScratch; }
+
+int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* dev_scratch, int64_t scratch_bytes,
+                      void* stream) {
+  if (!host_plan || !dev_plan || !dev_scratch) return QERR_INVALID_ARG;
+  if (!aligned(host_plan, 16) || !aligned(dev_plan, 16) || !aligned(dev_scratch, 4)) return QERR_ALIGNMENT;
+  if (scratch_bytes < kGroupedScratch) return QERR_BUFFER;
+  PlanHeader h;
+  std::memcpy(&h, host_plan, sizeof(h));
+  if (h.magic != kPlanMagic || h.version != 1 || h.B < 1 || h.B > 8 || h.n_items < 1 || h.n_tiles < 0)
+    return QERR_BUFFER;
+  if (h.n_tiles == 0) return QERR_OK;
+  return hip_rc(kGrouped[h.B](h, dev_plan, dev_scratch, S(stream)));
+}
+
+int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw, void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (w->fmt != QFMT_TRELLIS2) return QERR_UNSUPPORTED_FMT;
+  if (oblock != 32 && oblock != 256) return QERR_INVALID_ARG;
+  if (w->cols % 256 != 0) return QERR_SHAPE;
+  if (w->rows == 0) return QERR_OK;
+  if (!wq || !dw) return QERR_INVALID_ARG;
+  if (!aligned(wq, 4) || !aligned(dw, 4)) return QERR_ALIGNMENT;
+  return hip_rc(launch_trellis_decode(make_item(w, nullptr, nullptr, nullptr, nullptr), oblock, wq, dw, S(stream)));
+}
+
+int qweight_unpack_i8(const qweight_t* w, int8_t* wq, float* dw, void* stream) {
+  int rc = check_weight(w);
+  if (rc) return rc;
+  if (w->fmt == QFMT_TRELLIS2) return QERR_UNSUPPORTED_FMT;
+  if (w->rows == 0) return QERR_OK;
+  if (!wq || !dw) return QERR_INVALID_ARG;
+  if (!aligned(dw, 4)) return QERR_ALIGNMENT;
+  return hip_rc(launch_unpack_i8(make_item(w, nullptr, nullptr, nullptr, nullptr), wq, dw, S(stream)));
+}
+
+int qgemm_i8(const int8_t* xq, const float* dx, int32_t M, const int8_t* wq, const float* dw, int32_t N, int32_t K,
+             int32_t kblock, float* y, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return QERR_INVALID_ARG;
+  if (kblock != 32 && kblock != 256) return QERR_INVALID_ARG;
+  if (M == 0 || N == 0) return QERR_OK;
+  if (K == 0 || K % kblock != 0 || K % 64 != 0) return QERR_SHAPE;
+  if (!xq || !dx || !wq || !dw || !y) return QERR_INVALID_ARG;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(dx, 4) || !aligned(dw, 4) || !aligned(y, 4))
+    return QERR_ALIGNMENT;
+  return hip_rc(launch_gemm(xq, dx, M, wq, dw, N, K, kblock, y, S(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// gemv_inst.hip — instantiates the GEMV kernels for one batch size.  Built once
+// per batch size B = 1..8 with -DQGEMV_NB=B (separate objects, parallel build).
+#include "gemv_impl.hpp"
+
+#ifndef QGEMV_NB
+#error "QGEMV_NB must be defined"
+#endif
+
+#define QK_CAT2(a, b) a##b
+#define QK_CAT(a, b) QK_CAT2(a, b)
+
+namespace qk {
+
+namespace {
+int grouped_grid(const void* kernel, int lds_bytes) {
+  static int cached_dev = -1, cached_grid = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev == cached_dev) return cached_grid;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  (void)lds_bytes;
+  cached_dev = dev;
+  cached_grid = cus * per_cu;
+  return cached_grid;
+}
+}  // namespace
+
+hipError_t QK_CAT(launch_gemv_b, QGEMV_NB)(const GemvItem& it, hipStream_t s) {
+  constexpr int NB = QGEMV_NB;
+  V16Table v16;
+  V8Table v8;
+  float gain = 0.0f;
+  if (it.fmt == QFMT_TRELLIS2) trellis_tables(&v16, &v8, &gain);
+  const dim3 grid((it.rows + 63) / 64), block(256);
+  switch (it.fmt) {
+    case QFMT_SIGN1: hipLaunchKernelGGL((k_gemv<QFMT_SIGN1, NB, false>), grid, block, 0, s, it, v8, gain, nullptr); break;
+    case QFMT_INT2: hipLaunchKernelGGL((k_gemv<QFMT_INT2, NB, false>), grid, block, 0, s, it, v8, gain, nullptr); break;
+    case QFMT_INT4: hipLaunchKernelGGL((k_gemv<QFMT_INT4, NB, false>), grid, block, 0, s, it, v8, gain, nullptr); break;
+    case QFMT_TERN_B3: hipLaunchKernelGGL((k_gemv<QFMT_TERN_B3, NB, false>), grid, block, 0, s, it, v8, gain, nullptr); break;
+    case QFMT_TRELLIS2: hipLaunchKernelGGL((k_gemv<QFMT_TRELLIS2, NB, false>), grid, block, 0, s, it, v8, gain, nullptr); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t QK_CAT(launch_grouped_b, QGEMV_NB)(const PlanHeader& h, const void* plan, void* scratch, hipStream_t s) {
+  constexpr int NB = QGEMV_NB;
+  V16Table v16;
+  V8Table v8;
+  float gain = 0.0f;
+  if (h.fmt_mask & (1 << QFMT_TRELLIS2)) trellis_tables(&v16, &v8, &gain);
+  const int grid = grouped_grid((const void*)k_gemv_grouped<NB>, 0);
+  if (grid <= 0) return hipErrorInvalidDevice;
+  hipLaunchKernelGGL((k_gemv_grouped<NB>), dim3(grid), dim3(256), 0, s, (const uint8_t*)plan, (uint32_t*)scratch,
+                     v8, gain);
+  return hipGetLastError();
+}
+
+#if QGEMV_NB == 1
+hipError_t launch_blockdots(const GemvItem& it, int32_t* out, hipStream_t s) {
+  V16Table v16;
+  V8Table v8;
+  float gain = 0.0f;
+  if (it.fmt == QFMT_TRELLIS2) trellis_tables(&v16, &v8, &gain);
+  const dim3 grid((it.rows + 63) / 64), block(256);
+  switch (it.fmt) {
+    case QFMT_SIGN1: hipLaunchKernelGGL((k_gemv<QFMT_SIGN1, 1, true>), grid, block, 0, s, it, v8, gain, out); break;
+    case QFMT_INT2: hipLaunchKernelGGL((k_gemv<QFMT_INT2, 1, true>), grid, block, 0, s, it, v8, gain, out); break;
+    case QFMT_INT4: hipLaunchKernelGGL((k_gemv<QFMT_INT4, 1, true>), grid, block, 0, s, it, v8, gain, out); break;
+    case QFMT_TERN_B3: hipLaunchKernelGGL((k_gemv<QFMT_TERN_B3, 1, true>), grid, block, 0, s, it, v8, gain, out); break;
+    case QFMT_TRELLIS2: hipLaunchKernelGGL((k_gemv<QFMT_TRELLIS2, 1, true>), grid, block, 0, s, it, v8, gain, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+#endif
+
+}  // namespace qk

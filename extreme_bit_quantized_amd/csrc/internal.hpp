@@ -1,0 +1,137 @@
+// internal.hpp — shared declarations of libqgemv's translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qgemv.h"
+
+namespace qk {
+
+// ---- format geometry ---------------------------------------------------------------
+__host__ __device__ inline int32_t scale_block(int32_t fmt) {
+  switch (fmt) {
+    case QFMT_TERN_B3: return 256;
+    case QFMT_INT2: return 32;
+    case QFMT_SIGN1: return 128;
+    case QFMT_INT4: return 32;
+    case QFMT_TRELLIS2: return 64;
+  }
+  return 0;
+}
+
+// Packed bytes per row: bits per weight x cols / 8, ternary 52 bytes per 256.
+__host__ __device__ inline int64_t packed_row_bytes(int32_t fmt, int64_t cols) {
+  switch (fmt) {
+    case QFMT_TERN_B3: return cols / 256 * 52;
+    case QFMT_INT2: return cols / 4;
+    case QFMT_SIGN1: return cols / 8;
+    case QFMT_INT4: return cols / 2;
+    case QFMT_TRELLIS2: return cols / 4;
+  }
+  return -1;
+}
+
+// fp64 -> IEEE fp16 bits, round to nearest even, from the double's fields.
+__host__ __device__ inline uint16_t f64_to_f16_bits(double x) {
+  const uint64_t bits = __builtin_bit_cast(uint64_t, x);
+  const uint32_t sign = (uint32_t)(bits >> 48) & 0x8000u;
+  const int ex = (int)((bits >> 52) & 0x7FF);
+  const uint64_t frac = bits & 0xFFFFFFFFFFFFFull;
+  if (ex == 0x7FF) return (uint16_t)(sign | 0x7C00u | (frac ? 0x200u : 0u));
+  if (ex == 0) return (uint16_t)sign;  // double subnormals are far below fp16's range
+  const int e = ex - 1023;
+  const uint64_t m = frac | (1ull << 52);  // value = m * 2^(e - 52)
+  int shift;      // low bits of m dropped
+  uint32_t base;  // exponent field before rounding carries
+  if (e >= -14) {
+    if (e > 15) return (uint16_t)(sign | 0x7C00u);
+    shift = 42;
+    base = (uint32_t)(e + 14);  // biased exponent - 1; the implicit bit of n adds the 1
+  } else {
+    shift = 28 - e;  // subnormal quantum 2^-24
+    base = 0;
+    if (shift > 63) return (uint16_t)sign;
+  }
+  uint64_t n = m >> shift;
+  const uint64_t rem = m & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (n & 1))) ++n;
+  // normal: n in [1024, 2048] and base<<10 + n carries into the exponent by
+  // itself; subnormal: bits = n (n = 1024 is the smallest normal).
+  const uint32_t out = (base << 10) + (uint32_t)n;
+  if (out >= 0x7C00u) return (uint16_t)(sign | 0x7C00u);
+  return (uint16_t)(sign | out);
+}
+
+// ---- GEMV work description -------------------------------------------------------------
+// One matrix of a grouped launch (or the single matrix of qgemv).  80 bytes.
+struct alignas(16) GemvItem {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* seeds;
+  const int8_t* q;
+  const float* d;
+  const int32_t* qsum;
+  float* y;
+  int64_t row_bytes;
+  int32_t fmt, rows, cols, pad;
+};
+static_assert(sizeof(GemvItem) == 80, "item layout");
+
+struct alignas(8) GemvTile {
+  uint32_t item;
+  uint32_t row0;
+};
+
+// Plan blob: header, items, tiles (16-byte aligned sections).
+struct alignas(16) PlanHeader {
+  uint32_t magic;   // 'QGVP'
+  uint32_t version;
+  int32_t n_items;
+  int32_t n_tiles;
+  int32_t B;
+  int32_t fmt_mask;  // bit f set if some item has format f
+  int64_t items_off;
+  int64_t tiles_off;
+  int64_t total_bytes;
+  int64_t pad;
+};
+constexpr uint32_t kPlanMagic = 0x50564751u;  // "QGVP"
+constexpr int64_t kGroupedScratch = 256;
+
+// Codebook tables passed by value to the kernels that need them.
+struct V8Table { int8_t v[256]; };
+struct V16Table { uint16_t v[256]; };
+// Host-side codebook (built once, thread-safe): V16, V8 and the gain V16[255]/127.
+void trellis_tables(V16Table* v16, V8Table* v8, float* gain);
+
+// ---- launchers (each returns a hipError_t) --------------------------------------------
+hipError_t launch_act_quant(const float* x, int B, int K, int qblock, int8_t* q, float* d,
+                            int32_t* qsum, hipStream_t s);
+hipError_t launch_hadamard_quant(const float* x, int B, int K, const uint32_t* sign_bits, int qblock,
+                                 int8_t* q, float* d, int32_t* qsum, hipStream_t s);
+hipError_t launch_quantize(int fmt, const float* w, int rows, int cols, uint8_t* codes,
+                           int64_t row_bytes, uint16_t* scales, hipStream_t s);
+hipError_t launch_pack(int fmt, const int8_t* levels, int rows, int cols, uint8_t* codes,
+                       int64_t row_bytes, hipStream_t s);
+hipError_t launch_unpack_i8(const GemvItem& it, int8_t* wq, float* dw, hipStream_t s);
+hipError_t launch_blockdots(const GemvItem& it, int32_t* out, hipStream_t s);
+#define QK_DECL_NB(n)                                                    \
+  hipError_t launch_gemv_b##n(const GemvItem& it, hipStream_t s);        \
+  hipError_t launch_grouped_b##n(const PlanHeader& h, const void* plan, \
+                                 void* scratch, hipStream_t s);
+QK_DECL_NB(1)
+QK_DECL_NB(2)
+QK_DECL_NB(3)
+QK_DECL_NB(4)
+QK_DECL_NB(5)
+QK_DECL_NB(6)
+QK_DECL_NB(7)
+QK_DECL_NB(8)
+#undef QK_DECL_NB
+hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, float* dw, hipStream_t s);
+hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* wq, const float* dw,
+                       int N, int K, int kblock, float* y, hipStream_t s);
+
+}  // namespace qk

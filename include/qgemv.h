@@ -1,0 +1,227 @@
+/*
+ * qgemv.h — C ABI of libqgemv, extreme low-bit GEMV/GEMM for AMD MI355X (gfx950).
+ *
+ * What it computes.  Matrix-vector and small-batch products y = W x for LLM
+ * weights stored in extreme low-bit packed form, multiplied against int8
+ * activations; an int8 GEMM for prefill.  The pages this follows:
+ *   [P1] "A 27B model at 2.4 bits on a 12 GB RTX 3090" (61893.com)
+ *   [P2] "27B 模型压进 12GB 显存的量化实践" (feinterview.poetries.top)
+ *   [P3] "为什么'8G显卡跑27B'…" ternary portable pack (pptc.cn)
+ *   [P4] "一个 27B 模型被塞进 5.9 GB" (mhpq.cn)
+ *   [P5] "升到 4 比特慢了 29%、1 比特快了三倍…" (neodrop.ai)
+ *
+ * Conventions for every call below.
+ *   - Pointers marked (device) are device memory owned by the caller; the
+ *     library never allocates, frees or keeps them.  (host) pointers are read
+ *     during the call only.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every device call
+ *     is asynchronous on that stream; nothing synchronises the host.
+ *   - Return value: 0 on success or a negative QERR_* code.  All argument checks
+ *     run on the host before any HIP call, so a rejected call has no effect on
+ *     the GPU.  QERR_HIP means a launch failed.  No exception crosses the ABI.
+ *   - Calls are reentrant and keep no state between calls.
+ *   - Formats are dense row-major: weight row n is `row_bytes` bytes at
+ *     codes + n*row_bytes; scales are fp16 bit patterns [rows][cols/block].
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ------------------------------------------------------------- */
+#define QERR_OK 0
+#define QERR_INVALID_ARG (-1)     /* null pointer, negative size, bad enum value */
+#define QERR_UNSUPPORTED_FMT (-2) /* unknown format, or format not valid for the call */
+#define QERR_SHAPE (-3)           /* sizes violate the format's block rules */
+#define QERR_ALIGNMENT (-4)       /* pointer or stride misaligned */
+#define QERR_HIP (-5)             /* a HIP launch or query failed */
+#define QERR_BUFFER (-6)          /* caller buffer (plan, scratch) too small */
+
+/* Human-readable text for a QERR_* code (static storage, never NULL). */
+const char* qstrerror(int err);
+
+/* ---- weight formats ----------------------------------------------------------- *
+ * Level counts: 4 bits hold 16 levels, 2 bits 4, 1 bit only the sign ([P1]
+ * "2.4bit 是个什么量级").  Every format carries one fp16 scale per block of
+ * `block` weights along a row ([P4] §2.1: value = code x block scale).
+ *
+ *  QFMT_TERN_B3 (block 256): ternary {-1,0,1}.  Products become add, subtract or
+ *    skip ([P3] §1.2, [P4] §2.2).  5 trits per byte in base 3: the trits'
+ *    digits d_i = t_i + 1 form b = sum_i d_i 3^(4-i) (digit 0 most significant),
+ *    stored as the fixed-point base-3 fraction byte = ceil(256 b / 243).  A
+ *    256-weight block is 13 little-endian 32-bit words (52 bytes, 1.625 bits per
+ *    weight; log2 3 = 1.585 is the floor, [P3] §1.2): word m < 12, byte p, digit
+ *    i holds weight 20m + 4i + p; word 12, byte p, digit i < 4 holds weight
+ *    240 + 4i + p and its digit 4 is 1.  Row bytes 52*cols/256.
+ *  QFMT_INT2 (block 32): four levels (2c - 3)/2 * s, c = 0..3.  One 32-bit
+ *    word per 16 weights; weight 4j + b (j, b = 0..3) is bits 8b+2j .. 8b+2j+1.
+ *  QFMT_SIGN1 (block 128): levels (2b - 1) * s.  One 32-bit word per 32 weights;
+ *    weight 4j + b (j = 0..7, b = 0..3) is bit 8b + j.
+ *  QFMT_INT4 (block 32): sixteen levels (2c - 15)/2 * s.  One 32-bit word per 8
+ *    weights; weight 4j + b (j = 0..1) is bits 8b+4j .. 8b+4j+3.
+ *  QFMT_TRELLIS2 (block 64): 2-bit bit-shift trellis codes with a codebook
+ *    computed at run time from a hash ([P1] "2.4bit 是个什么量级"), each row coded
+ *    in groups of 4 weights from a stored seed ([P2] "12 GB 装下 27B，靠的是什么
+ *    取舍").  Byte g of a row = c[4g]<<6 | c[4g+1]<<4 | c[4g+2]<<2 | c[4g+3].
+ *    State st <- ((st << 2) | c) & 0xFFFF starting at the row's uint16 seed;
+ *    h = ((st * 0x9E37) ^ (st >> 7)) & 0xFF; value = s * V16[h] where V16[k] is
+ *    the fp16 nearest to the N(0,1) quantile at (k + 0.5)/256.
+ */
+#define QFMT_TERN_B3 1
+#define QFMT_INT2 2
+#define QFMT_SIGN1 3
+#define QFMT_INT4 4
+#define QFMT_TRELLIS2 5
+
+/* Scale block along K for a format, 0 if unknown. */
+int32_t qfmt_scale_block(int32_t fmt);
+/* Packed bytes of one row (no padding); <0 (QERR_*) on bad arguments.
+ * cols must be a positive multiple of the scale block. */
+int64_t qfmt_packed_row_bytes(int32_t fmt, int32_t cols);
+/* Minimum legal row stride: packed bytes rounded up to 16. */
+int64_t qfmt_row_bytes(int32_t fmt, int32_t cols);
+
+/* Packed-weight descriptor.  All pointers (device). */
+typedef struct qweight {
+  int32_t fmt;            /* QFMT_* */
+  int32_t rows;           /* N >= 1 (output features) */
+  int32_t cols;           /* K >= 1 (input features), multiple of block, and of 256 for TERN_B3 */
+  int32_t block;          /* must equal qfmt_scale_block(fmt) */
+  const void* codes;      /* [rows][row_bytes] bytes, 16-byte aligned */
+  int64_t row_bytes;      /* stride, a multiple of 16, >= qfmt_packed_row_bytes */
+  const uint16_t* scales; /* [rows][cols/block] fp16, 4-byte aligned */
+  const uint16_t* seeds;  /* [rows] uint16 trellis seeds; TRELLIS2 only, else NULL */
+} qweight_t;
+
+/* Host-only validation of a descriptor (no HIP call).  0 or QERR_*. */
+int qweight_check(const qweight_t* w);
+
+/* ---- weight preparation (device) ------------------------------------------------ */
+
+/* Quantize fp32 weights w [rows][cols] (device) and pack them.  Quantizer per
+ * format, decisions taken in fp64:
+ *   TERN_B3: per 256-block s = mean|w| + 1e-8, t = clamp(round(w / s), -1, 1)
+ *            with round half to even ([P3] §5.1, there per tensor);
+ *   INT2 / INT4: s = fp16(amax / 1.5) resp. fp16(amax / 7.5) per 32-block,
+ *            code = nearest level to w / s, ties to the upper level;
+ *   SIGN1:   bit = (w >= 0), s = mean |w| per 128-block.
+ * Sums run in index order; stored scale = fp16 (round to nearest even).
+ * Output codes [rows][row_bytes] (16-byte aligned, padding zeroed) and
+ * scales [rows][cols/block].  TRELLIS2 is not a quantizer target
+ * (QERR_UNSUPPORTED_FMT). */
+int qweight_quantize(int32_t fmt, const float* w, int32_t rows, int32_t cols,
+                     void* codes, int64_t row_bytes, uint16_t* scales, void* stream);
+
+/* Pack per-weight integer codes levels [rows][cols] int8 (device) into the
+ * format's bytes: TERN_B3 trits -1..1; INT2 0..3; SIGN1 0..1; INT4 0..15;
+ * TRELLIS2 symbols 0..3.  Out-of-range codes are masked to the field width
+ * (ternary values other than -1..1 give undefined bytes).  Padding zeroed. */
+int qweight_pack(int32_t fmt, const int8_t* levels, int32_t rows, int32_t cols,
+                 void* codes, int64_t row_bytes, void* stream);
+
+/* ---- activation quantization (device) --------------------------------------------- */
+
+/* Q8 per block of `qblock` (32 or 256) values of x [B][K] fp32:
+ *   amax = max|x|; d = amax / 127 (fp32, IEEE division); id = amax ? 1/d : 0;
+ *   q = clamp(rint(x * id), -127, 127) (ties to even); qsum = sum q.
+ * int8 activations are what the pages' int8 dot-product GEMV and int8 MMA /
+ * GEMM paths consume ([P1] "把非标准格式塞进 llama.cpp，难在哪").
+ * Outputs q [B][K] int8, d [B][K/qblock] fp32, qsum [B][K/qblock] int32.
+ * Bit-exact: the same fp32 operations as the definition. */
+int qact_quant_i8(const float* x, int32_t B, int32_t K, int32_t qblock,
+                  int8_t* q, float* d, int32_t* qsum, void* stream);
+
+/* Block-randomized Walsh-Hadamard rotation then Q8 (the random Hadamard
+ * rotation of [P2] "12 GB 装下 27B", applied to activations): per token and
+ * 256-block, u = sigma * x with sigma_k = -1 where bit k%32 of sign_bits[k/32]
+ * is set; stages h = 1, 2, ..., 128 map (u_i, u_{i+h}) to (u_i + u_{i+h},
+ * u_i - u_{i+h}) for (i & h) == 0 (Sylvester order); times 1/16; then Q8 per
+ * qblock (32 or 256) as in qact_quant_i8.  fp32, bit-exact.
+ * K multiple of 256; sign_bits [K/32] (device). */
+int qact_hadamard_quant_i8(const float* x, int32_t B, int32_t K, const uint32_t* sign_bits,
+                           int32_t qblock, int8_t* q, float* d, int32_t* qsum, void* stream);
+
+/* ---- GEMV ----------------------------------------------------------------------- */
+
+/* y[b][n] = sum_kb T[b][n][kb], T = f * s_w * d[b][kb] * I[b][n][kb], where I is
+ * the exact integer dot of the weight levels with q over the 32-block kb:
+ *   TERN_B3 level t, f = 1;  INT2 level 2c-3, f = 1/2;  SIGN1 level 2b-1, f = 1;
+ *   INT4 level 2c-15, f = 1/2;  TRELLIS2 level V8[h] = rint(V16[h]*127/V16[255]),
+ *   f = V16[255]/127.
+ * The decode-time GEMV of the pages runs over int8 activations with 4-way int8
+ * dot products ([P1] "把非标准格式塞进 llama.cpp，难在哪"); with batch B the
+ * weights are decoded once for all tokens ([P5] §五: checking 16 tokens costs
+ * about as much as 1 when the product is bandwidth-bound).
+ * Inputs (device): q [B][K] int8 (16-byte aligned), d [B][K/32] fp32,
+ * qsum [B][K/32] int32 (block sums of q, as written by qact_quant_i8).
+ * Output y [B][rows] fp32 (device), overwritten.  1 <= B <= 8.
+ * Accuracy: I exact; |y - y_exact| <= 1e-4 * sum|T| (fp32 accumulation). */
+int qgemv(const qweight_t* w, const int8_t* q, const float* d, const int32_t* qsum,
+          int32_t B, float* y, void* stream);
+
+/* Test hook: the exact integer block dots I [rows][cols/32] int32 (device) of
+ * the GEMV above for a single token (B = 1), written by the same decode. */
+int qgemv_blockdots(const qweight_t* w, const int8_t* q, const int32_t* qsum,
+                    int32_t* out, void* stream);
+
+/* ---- grouped GEMV: many matrices in one persistent launch --------------------------
+ * Fusing many small single-token kernels was part of the 3x decode gain of the
+ * pages' 1-bit kernel ([P5] §二).  Use: build a plan on the host, copy the
+ * plan bytes to device memory, then run it as often as wanted.  The plan
+ * stores the device pointers of every item; it stays valid while they do. */
+typedef struct qgemv_item {
+  qweight_t w;
+  const int8_t* q;      /* [B][w.cols] (device) */
+  const float* d;       /* [B][w.cols/32] (device) */
+  const int32_t* qsum;  /* [B][w.cols/32] (device) */
+  float* y;             /* [B][w.rows] (device), must not overlap another item's y */
+} qgemv_item_t;
+
+/* Bytes of the plan for these items (host); <0 on invalid items. */
+int64_t qgemv_grouped_plan_bytes(const qgemv_item_t* items, int32_t n, int32_t B);
+/* Validate the items and write the plan to host_plan [plan_bytes] (host).
+ * The work is cut into 64-row tiles, ordered longest first. */
+int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B,
+                       void* host_plan, int64_t plan_bytes);
+/* Scratch needed by a run (a tile counter and an exit counter). */
+int64_t qgemv_grouped_scratch_bytes(void);
+/* Run a plan: host_plan (host) is the plan as written by qgemv_grouped_plan,
+ * dev_plan (device, 16-byte aligned) a byte copy of it.  dev_scratch (device,
+ * >= qgemv_grouped_scratch_bytes) must be zero before the first run; every
+ * run leaves it zero again.  Runs sharing a scratch buffer must not overlap. */
+int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* dev_scratch,
+                      int64_t scratch_bytes, void* stream);
+
+/* ---- prefill: trellis decode to int8 and the int8 MFMA GEMM --------------------------- */
+
+/* Decode TRELLIS2 weights to int8 for the GEMM: per row the exact fp32 values
+ * s * V16[h] (both fp16, so the product is exact), then Q8 per (row, oblock)
+ * as in qact_quant_i8.  Output wq [rows][cols] int8, dw [rows][cols/oblock]
+ * fp32 (device).  oblock 256 or 32. */
+int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw, void* stream);
+
+/* Unpack TERN_B3 / INT2 / SIGN1 / INT4 weights to int8 levels for the GEMM:
+ * wq [rows][cols] = the format's integer level, dw [rows][cols/32] = the
+ * fp32 factor f * s of each 32-block (so W = dw * wq exactly). */
+int qweight_unpack_i8(const qweight_t* w, int8_t* wq, float* dw, void* stream);
+
+/* Block-scaled int8 GEMM on the matrix cores (the pages' prefill is an INT8 GEMM
+ * and large batches run on INT8 tensor-core MMA, [P1] "把非标准格式塞进
+ * llama.cpp，难在哪"):
+ *   y[m][n] = sum_kb dx[m][kb] * dw[n][kb] * I[m][n][kb],
+ *   I = exact int32 dot of xq[m] and wq[n] over K-block kb (size kblock).
+ * xq [M][K] int8, dx [M][K/kblock], wq [N][K] int8, dw [N][K/kblock],
+ * y [M][N] fp32 (all device; xq, wq 16-byte aligned).  kblock 256 or 32;
+ * K a multiple of kblock and of 64. */
+int qgemm_i8(const int8_t* xq, const float* dx, int32_t M, const int8_t* wq, const float* dw,
+             int32_t N, int32_t K, int32_t kblock, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGEMV_H */

@@ -1,0 +1,138 @@
+"""Host-only checks of the C ABI: the library loads, exports what the header
+declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+
+@pytest.fixture(scope="module")
+def ebq():
+    import extreme_bit_quantized_amd as ebq
+
+    if not os.path.exists(ebq.LIB_PATH):
+        from extreme_bit_quantized_amd import build
+
+        build.build()
+    ebq.load()
+    return ebq
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(ebq):
+    names = _declared_functions()
+    assert len(names) >= 17, names
+    lib = ctypes.CDLL(ebq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_geometry_agrees_with_oracle(ebq, qref):
+    for fmt in qref.FORMATS:
+        assert ebq.qfmt_scale_block(fmt) == qref.scale_block(fmt)
+        blk = qref.scale_block(fmt)
+        for K in (blk, 2 * blk, 256, 1024, 1280, 5120, 6144, 17408):
+            if K % blk or K % 32:
+                continue
+            assert ebq.qfmt_packed_row_bytes(fmt, K) == qref.packed_row_bytes(fmt, K)
+            assert ebq.qfmt_row_bytes(fmt, K) == qref.row_stride(fmt, K)
+    assert ebq.load().qfmt_row_bytes(9, 256) == -2
+    assert ebq.load().qfmt_row_bytes(ebq.QFMT_INT2, 48) == -3
+
+
+def _desc(ebq, fmt=3, rows=64, cols=1024, block=None, codes=4096, row_bytes=None, scales=8192, seeds=None):
+    if block is None:
+        block = ebq.qfmt_scale_block(fmt) if fmt in (1, 2, 3, 4, 5) else 32
+    if row_bytes is None:
+        row_bytes = ebq.load().qfmt_row_bytes(fmt, cols) if fmt in (1, 2, 3, 4, 5) else 16
+    return ebq.qweight_t(fmt, rows, cols, block, codes, row_bytes, scales, seeds)
+
+
+def test_weight_validation(ebq):
+    L = ebq.load()
+    chk = lambda d: L.qweight_check(ctypes.byref(d))
+    assert chk(_desc(ebq)) == 0
+    assert chk(_desc(ebq, fmt=7)) == -2
+    assert chk(_desc(ebq, block=64)) == -3
+    assert chk(_desc(ebq, cols=1000)) == -3
+    assert chk(_desc(ebq, rows=-1)) == -1
+    assert chk(_desc(ebq, codes=4104)) == -4
+    assert chk(_desc(ebq, scales=8193)) == -4
+    assert chk(_desc(ebq, codes=None)) == -1
+    assert chk(_desc(ebq, row_bytes=64)) == -3          # below the packed size
+    assert chk(_desc(ebq, row_bytes=136)) == -3         # not a multiple of 16
+    assert chk(_desc(ebq, fmt=5, cols=512)) == -1       # trellis without seeds
+    assert chk(_desc(ebq, fmt=5, cols=512, seeds=12288)) == 0
+    assert chk(_desc(ebq, rows=0, codes=None, scales=None)) == 0  # empty matrix
+
+
+def test_call_validation_without_gpu(ebq):
+    L = ebq.load()
+    d = _desc(ebq)
+    w = ctypes.byref(d)
+    A = 1 << 20  # fake, aligned "device" addresses: every call below is rejected before launch
+    assert L.qgemv(w, A, A, A, 9, A, None) == -1
+    assert L.qgemv(w, A, A, A, 0, A, None) == 0            # empty batch: no-op
+    assert L.qgemv(w, A + 4, A, A, 1, A, None) == -4
+    assert L.qgemv(w, None, A, A, 1, A, None) == -1
+    assert L.qgemv(w, A, A, A, 1, A + 2, None) == -4
+    assert L.qact_quant_i8(A, 1, 1024, 64, A, A, A, None) == -1
+    assert L.qact_quant_i8(A, 1, 48, 32, A, A, A, None) == -3
+    assert L.qact_quant_i8(A, 0, 1024, 32, A, A, A, None) == 0
+    assert L.qact_quant_i8(A + 4, 1, 1024, 32, A, A, A, None) == -4
+    assert L.qact_hadamard_quant_i8(A, 1, 1000, A, 256, A, A, A, None) == -3
+    assert L.qact_hadamard_quant_i8(A, 1, 1024, None, 256, A, A, A, None) == -1
+    assert L.qgemm_i8(A, A, 16, A, A, 16, 96, 32, A, None) == -3
+    assert L.qgemm_i8(A, A, 16, A, A, 16, 256, 64, A, None) == -1
+    assert L.qgemm_i8(A, A, 0, A, A, 16, 256, 256, A, None) == 0
+    assert L.qtrellis_decode_i8(w, 256, A, A, None) == -2   # not a trellis matrix
+    assert L.qweight_quantize(5, A, 4, 256, A, 64, A, None) == -2
+    assert L.qweight_pack(2, A, 4, 48, A, 16, None) == -3
+    assert L.qgemv_grouped_run(None, A, A, 256, None) == -1
+    assert ebq.load().qstrerror(-4).decode().startswith("pointer")
+
+
+def test_grouped_plan_on_host(ebq):
+    import torch
+
+    A = 1 << 20
+    shapes = [(3, 5120, 1024), (1, 1024, 5120), (3, 100, 1024), (4, 17408, 512)]
+    descs = [_desc(ebq, fmt=f, rows=n, cols=k, codes=A, scales=A) for f, n, k in shapes]
+    items = (ebq.qgemv_item_t * len(descs))()
+    for i, d in enumerate(descs):
+        items[i] = ebq.qgemv_item_t(d, A, A, A, A)
+    nb = ebq.qgemv_grouped_plan_bytes(items, 2)
+    raw = torch.zeros(nb + 16, dtype=torch.uint8)
+    off = (-raw.data_ptr()) % 16
+    host = raw[off:off + nb]
+    ebq.qgemv_grouped_plan(items, 2, host)
+    h = host.numpy()
+    hdr = np.frombuffer(h[:64].tobytes(), dtype=np.int32)
+    assert hdr[0] == 0x50564751 and hdr[2] == 4 and hdr[4] == 2
+    ntiles = sum((n + 63) // 64 for _, n, _ in shapes)
+    assert hdr[3] == ntiles
+    tiles_off = int(np.frombuffer(h[32:40].tobytes(), dtype=np.int64)[0])
+    tiles = np.frombuffer(h[tiles_off:tiles_off + 8 * ntiles].tobytes(), dtype=np.uint32).reshape(-1, 2)
+    got = sorted(map(tuple, tiles.tolist()))
+    want = sorted((i, r) for i, (_, n, _) in enumerate(shapes) for r in range(0, n, 64))
+    assert got == want
+    # within one format, tiles come longest first
+    fmt_of = [s[0] for s in shapes]
+    for f in set(fmt_of):
+        costs = [min(64, shapes[i][1] - r) * (descs[i].row_bytes + shapes[i][2] // descs[i].block * 2)
+                 for i, r in tiles.tolist() if fmt_of[i] == f]
+        assert costs == sorted(costs, reverse=True)
+    # too small a buffer is refused
+    assert ebq.load().qgemv_grouped_plan(items, 4, 2, host.data_ptr(), nb - 16) == -6

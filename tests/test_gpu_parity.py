@@ -1,0 +1,307 @@
+"""GPU parity of every kernel against the CPU oracle, at sizes the oracle runs
+in seconds (several 64-row tiles, ragged row counts, K with and without a tail
+segment) and on edge cases.  All calls go through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import (INT2, INT4, NAMES, SIGN1, TERN, TRELLIS, assert_close_terms, dev, gpu_act, gpu_weight,
+                        host, oracle_weight, raw_weight)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import extreme_bit_quantized_amd as ebq  # noqa: E402
+
+ebq.load()
+ALL = [TERN, INT2, SIGN1, INT4, TRELLIS]
+SHAPES = [(1, 1024), (70, 1280), (200, 1024), (130, 5120), (64, 2304)]
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------------------------
+# activation quantization and the Hadamard rotation (bit-exact)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,K,qblock", [(1, 32, 32), (3, 1024, 32), (5, 5120, 32), (64, 17408, 32),
+                                        (2, 512, 256), (7, 6144, 256)])
+def test_act_quant_bit_exact(B, K, qblock):
+    x = synth.gauss([100, B, K], (B, K)) * synth.uniform([101, B], (B, 1), 1e-3, 1e3)
+    x[0, :qblock] = 0.0                                   # zero block
+    if K >= 2 * qblock:
+        x[0, qblock:2 * qblock] = np.linspace(-127, 127, qblock, dtype=np.float32) / 2   # half-way ties
+    q, d, s = gpu_act(x, qblock)
+    _sync()
+    rq, rd, rs = oracle.act_quant(x, qblock)
+    assert (host(q) == rq).all()
+    assert (host(d).view(np.uint32) == rd.view(np.uint32)).all()
+    assert (host(s) == rs).all()
+
+
+def test_act_quant_empty_batch():
+    x = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
+    q = torch.zeros((0, 64), dtype=torch.int8, device="cuda")
+    d = torch.zeros((0, 2), dtype=torch.float32, device="cuda")
+    ebq.qact_quant_i8(x, 32, q, d, d)                     # no-op, no error
+
+
+@pytest.mark.parametrize("B,K,qblock", [(1, 256, 256), (3, 5120, 256), (4, 17408, 256), (2, 1024, 32)])
+def test_hadamard_quant_bit_exact(B, K, qblock):
+    x = synth.with_outliers(synth.gauss([110, B, K], (B, K)), [111, B, K])
+    sb = synth.sign_bits([112, K], K)
+    xt = dev(x)
+    q = torch.empty((B, K), dtype=torch.int8, device="cuda")
+    d = torch.empty((B, K // qblock), dtype=torch.float32, device="cuda")
+    s = torch.empty((B, K // qblock), dtype=torch.int32, device="cuda")
+    ebq.qact_hadamard_quant_i8(xt, dev(sb), qblock, q, d, s)
+    _sync()
+    rq, rd, rs = oracle.hadamard_quant(x, sb, qblock)
+    assert (host(q) == rq).all()
+    assert (host(d).view(np.uint32) == rd.view(np.uint32)).all()
+    assert (host(s) == rs).all()
+
+
+# ---------------------------------------------------------------------------------------------
+# weight preparation (bit-exact bytes and scales)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", [TERN, INT2, SIGN1, INT4])
+@pytest.mark.parametrize("N,K", [(1, 256), (37, 1024), (100, 5120)])
+def test_quantize_pack_bit_exact(fmt, N, K):
+    raw = raw_weight(fmt, N, K, 120 + fmt)
+    raw["w"][0, :32] = 0.0                               # an all-zero block
+    pw = gpu_weight(fmt, raw, N, K)
+    _sync()
+    rp, rs, _ = oracle_weight(fmt, raw)
+    assert (host(pw.codes) == rp).all(), NAMES[fmt]
+    assert (host(pw.scales).view(np.uint16) == rs).all(), NAMES[fmt]
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_pack_levels_bit_exact(fmt):
+    N, K = 45, 1280 if fmt != TERN else 1536
+    lo, n = {TERN: (-1, 3), INT2: (0, 4), SIGN1: (0, 2), INT4: (0, 16), TRELLIS: (0, 4)}[fmt]
+    codes = (synth.symbols([130, fmt], (N, K), n) + lo).astype(np.int8)
+    pw = ebq.PackedWeight.empty(fmt, N, K)
+    ebq.qweight_pack(fmt, dev(codes), pw)
+    _sync()
+    assert (host(pw.codes) == oracle.pack(fmt, codes)).all()
+
+
+# ---------------------------------------------------------------------------------------------
+# GEMV: exact block dots, fp32 outputs within tolerance, batches 1..8
+# ---------------------------------------------------------------------------------------------
+
+def _prep(fmt, N, K, seed, B=1):
+    raw = raw_weight(fmt, N, K, seed)
+    pw = gpu_weight(fmt, raw, N, K)
+    rp, rs, rseeds = oracle_weight(fmt, raw)
+    x = synth.gauss([seed, 9], (B, K))
+    return raw, pw, (rp, rs, rseeds), x
+
+
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_blockdots_bit_exact(fmt, N, K):
+    raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 140 + fmt)
+    q, d, s = gpu_act(x)
+    out = torch.full((N, K // 32), -7, dtype=torch.int32, device="cuda")
+    ebq.qgemv_blockdots(pw, q, s, out)
+    _sync()
+    rq, rd, _ = oracle.act_quant(x)
+    _, _, I = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd, want_I=True)
+    assert (host(out) == I[0]).all(), NAMES[fmt]
+
+
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_gemv_parity(fmt, N, K, B):
+    raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 150 + fmt + B, B)
+    q, d, s = gpu_act(x)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    ebq.qgemv(pw, q, d, s, B, y)
+    _sync()
+    rq, rd, _ = oracle.act_quant(x)
+    yr, absT, _ = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd)
+    assert_close_terms(host(y), yr, absT, what="%s N=%d K=%d B=%d" % (NAMES[fmt], N, K, B))
+
+
+@pytest.mark.parametrize("B", [2, 4, 5, 6, 7])
+def test_gemv_every_batch_size(B):
+    fmt, N, K = SIGN1, 96, 2048
+    raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 160 + B, B)
+    q, d, s = gpu_act(x)
+    y = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    ebq.qgemv(pw, q, d, s, B, y)
+    _sync()
+    rq, rd, _ = oracle.act_quant(x)
+    yr, absT, _ = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd)
+    assert_close_terms(host(y), yr, absT, what="B=%d" % B)
+
+
+def test_gemv_deterministic():
+    fmt, N, K = TERN, 300, 5120
+    raw, pw, _, x = _prep(fmt, N, K, 170)
+    q, d, s = gpu_act(x)
+    y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y1)
+    ebq.qgemv(pw, q, d, s, 1, y1)
+    ebq.qgemv(pw, q, d, s, 1, y2)
+    _sync()
+    assert (host(y1).view(np.uint32) == host(y2).view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("fmt", [TERN, INT2, SIGN1, INT4])
+def test_gemv_edge_cases(fmt):
+    """All-max / all-min codes, zero activations, and exact zeros where every
+    term is zero."""
+    N, K = 66, 1024
+    lo, hi = {TERN: (-1, 1), INT2: (0, 3), SIGN1: (0, 1), INT4: (0, 15)}[fmt]
+    codes = np.zeros((N, K), np.int8)
+    codes[0::3] = hi
+    codes[1::3] = lo
+    codes[2::3] = synth.symbols([180, fmt], (N // 3, K), hi - lo + 1) + lo
+    scales = synth.uniform_f16([181, fmt], (N, K // oracle.scale_block(fmt)), 0.01, 0.1)
+    scales[5] = 0                                           # a row with zero scales
+    raw = {"codes": codes, "scales": scales}
+    pw = gpu_weight(fmt, raw, N, K)
+    rp, rs, _ = oracle_weight(fmt, raw)
+    x = synth.gauss([182], (3, K))
+    x[1] = 0.0                                              # zero activations
+    x[2, :] = 127.0                                         # every q = 127
+    q, d, s = gpu_act(x)
+    y = torch.empty((3, N), dtype=torch.float32, device="cuda")
+    ebq.qgemv(pw, q, d, s, 3, y)
+    _sync()
+    rq, rd, _ = oracle.act_quant(x)
+    yr, absT, _ = oracle.gemv(fmt, rp, rs, None, K, rq, rd)
+    assert_close_terms(host(y), yr, absT, what=NAMES[fmt])
+    assert not host(y)[1].any() and not host(y)[:, 5].any()
+
+
+def test_sign_balanced_rows_give_exact_zero():
+    """1-bit rows with as many +1 as -1 against constant activations: every
+    block dot is 0, so y must be exactly 0."""
+    N, K = 64, 512
+    codes = np.zeros((N, K), np.int8)
+    codes[:, 0::2] = 1
+    scales = synth.uniform_f16([183], (N, K // 128), 0.5, 1.0)
+    pw = gpu_weight(SIGN1, {"codes": codes, "scales": scales}, N, K)
+    x = np.full((1, K), 3.0, np.float32)
+    q, d, s = gpu_act(x)
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    ebq.qgemv(pw, q, d, s, 1, y)
+    _sync()
+    assert (host(y) == 0).all()
+
+
+# ---------------------------------------------------------------------------------------------
+# grouped launch
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_grouped_parity_and_reuse(B):
+    specs = [(SIGN1, 130, 5120), (TERN, 64, 1024), (INT4, 200, 1280), (INT2, 1, 2048), (TRELLIS, 70, 1280),
+             (TERN, 300, 2304), (SIGN1, 65, 17408)]
+    entries, refs = [], []
+    for i, (fmt, N, K) in enumerate(specs):
+        raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 190 + i, B)
+        q, d, s = gpu_act(x)
+        y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+        entries.append((pw, q, d, s, y))
+        rq, rd, _ = oracle.act_quant(x)
+        refs.append(oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd))
+    plan = ebq.GroupedPlan(entries, B)
+    for rep in range(3):                                      # the scratch resets itself
+        for e in entries:
+            e[4].fill_(float("nan"))
+        plan.run()
+        _sync()
+        assert (host(plan.scratch) == 0).all()
+        for (fmt, N, K), e, (yr, absT, _) in zip(specs, entries, refs):
+            assert_close_terms(host(e[4]), yr, absT, what="grouped %s rep %d" % (NAMES[fmt], rep))
+
+
+# ---------------------------------------------------------------------------------------------
+# trellis decode, unpack, GEMM
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("oblock", [256, 32])
+@pytest.mark.parametrize("N,K", [(1, 256), (33, 1024), (17, 5120)])
+def test_trellis_decode_bit_exact(oblock, N, K):
+    raw = raw_weight(TRELLIS, N, K, 200)
+    pw = gpu_weight(TRELLIS, raw, N, K)
+    wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    dw = torch.empty((N, K // oblock), dtype=torch.float32, device="cuda")
+    ebq.qtrellis_decode_i8(pw, oblock, wq, dw)
+    _sync()
+    rp, rs, rseeds = oracle_weight(TRELLIS, raw)
+    rwq, rdw = oracle.trellis_decode_i8(rp, rseeds, rs, K, oblock)
+    assert (host(wq) == rwq).all()
+    assert (host(dw).view(np.uint32) == rdw.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("fmt", [TERN, INT2, SIGN1, INT4])
+def test_unpack_i8(fmt):
+    N, K = 40, 1024
+    raw = raw_weight(fmt, N, K, 210 + fmt)
+    pw = gpu_weight(fmt, raw, N, K)
+    wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    dw = torch.empty((N, K // 32), dtype=torch.float32, device="cuda")
+    ebq.qweight_unpack_i8(pw, wq, dw)
+    _sync()
+    rp, rs, _ = oracle_weight(fmt, raw)
+    c = oracle.unpack(fmt, rp, K).astype(np.int32)
+    lev = {TERN: c, INT2: 2 * c - 3, SIGN1: 2 * c - 1, INT4: 2 * c - 15}[fmt]
+    assert (host(wq) == lev).all()
+    blk = oracle.scale_block(fmt)
+    f = np.repeat(rs.view(np.float16).astype(np.float32), blk // 32, axis=1)
+    if fmt in (INT2, INT4):
+        f = f * np.float32(0.5)
+    assert (host(dw) == f).all()
+
+
+@pytest.mark.parametrize("kblock", [256, 32])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (17, 130, 512), (200, 64, 1024), (128, 257, 2048)])
+def test_gemm_parity(kblock, M, N, K):
+    xq = synth.integers([220, M, K], (M, K), -127, 127).astype(np.int8)
+    wq = synth.integers([221, N, K], (N, K), -127, 127).astype(np.int8)
+    dx = synth.uniform([222], (M, K // kblock), 1e-3, 0.1)
+    dw = synth.uniform([223], (N, K // kblock), 1e-3, 0.1)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ebq.qgemm_i8(dev(xq), dev(dx), dev(wq), dev(dw), kblock, y)
+    _sync()
+    yr, absT = oracle.gemm_i8(xq, dx, wq, dw, kblock)
+    assert_close_terms(host(y), yr, absT, what="gemm %dx%dx%d/%d" % (M, N, K, kblock))
+
+
+def test_prefill_pipeline_small():
+    """Rotation + Q8, trellis decode, GEMM chained as in prefill."""
+    M, K, N = 96, 1024, 160
+    x = synth.with_outliers(synth.gauss([230], (M, K)), [231])
+    sb = synth.sign_bits([232], K)
+    raw = raw_weight(TRELLIS, N, K, 233)
+    pw = gpu_weight(TRELLIS, raw, N, K)
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    dx = torch.empty((M, K // 256), dtype=torch.float32, device="cuda")
+    sx = torch.empty((M, K // 256), dtype=torch.int32, device="cuda")
+    ebq.qact_hadamard_quant_i8(dev(x), dev(sb), 256, xq, dx, sx)
+    wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    dw = torch.empty((N, K // 256), dtype=torch.float32, device="cuda")
+    ebq.qtrellis_decode_i8(pw, 256, wq, dw)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ebq.qgemm_i8(xq, dx, wq, dw, 256, y)
+    _sync()
+    rxq, rdx, _ = oracle.hadamard_quant(x, sb, 256)
+    rp, rs, rseeds = oracle_weight(TRELLIS, raw)
+    rwq, rdw = oracle.trellis_decode_i8(rp, rseeds, rs, K, 256)
+    yr, absT = oracle.gemm_i8(rxq, rdx, rwq, rdw, 256)
+    assert_close_terms(host(y), yr, absT, what="prefill")
