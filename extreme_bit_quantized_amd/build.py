@@ -24,7 +24,7 @@ ARCH = "gfx950"
 MAX_B = 8
 
 FLAGS = [
-    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC",
     # packed fp32 VALU ops stay off: plain fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-ffp-contract=fast-honor-pragmas",

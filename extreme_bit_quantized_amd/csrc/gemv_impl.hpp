@@ -26,15 +26,23 @@
 
 #include <hip/hip_fp16.h>
 
+#include <utility>
+
 #include "internal.hpp"
 
 namespace qk {
 
-typedef const int32_t __attribute__((address_space(4))) c_i32;
-typedef const float __attribute__((address_space(4))) c_f32;
-typedef const uint8_t __attribute__((address_space(4))) c_u8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// Global-address-space views: loads become global_load with an SGPR base and a
+// 32-bit VGPR offset instead of flat loads (which also count against lgkmcnt).
+typedef const uint8_t __attribute__((address_space(1))) g_u8;
+typedef const uint16_t __attribute__((address_space(1))) g_u16;
+typedef const uint32_t __attribute__((address_space(1))) g_u32;
+typedef const u32x4 __attribute__((address_space(1))) g_u32x4;
+typedef const u32x2 __attribute__((address_space(1))) g_u32x2;
+typedef float __attribute__((address_space(1))) g_f32;
+template <typename T> __device__ __forceinline__ T gptr(const void* p) { return (T)p; }
 
 __device__ __forceinline__ int dot4(uint32_t w, int32_t a, int acc) {
   return __builtin_amdgcn_sdot4((int)w, a, acc, false);
@@ -62,200 +70,302 @@ template <> struct Seg<QFMT_TRELLIS2> {
 template <int CH> struct Pitch { static constexpr int value = (CH % 2 ? CH : CH + 1) * 16; };
 constexpr int kMaxWaveLds = 64 * 208;  // largest per-wave tile region (ternary)
 
-// Wave-uniform view of the activations of NB tokens (scalar address space).
-struct Act {
-  c_i32* q;   // token b, act block kb, dword j at q[b*kq + kb*8 + j]
-  c_f32* d;   // d[b*kb_stride + kb]
-  c_i32* qs;  // qs[b*kb_stride + kb]
-  int kq;     // K / 4
-  int kbs;    // K / 32
+// ---- activation sub-chunks and DPP-broadcast block dots ----------------------------------------
+// Activations reach the dot products as the DPP operand of v_dot4c: the 256
+// int8 values of one 256-weight sub-chunk sit in four VGPRs, lane i of every
+// 16-lane row holding bytes 16i .. 16i+15, and `row_newbcast:i` hands lane i's
+// dword to the whole row inside the dot instruction itself.  d and the qsum
+// term of the sub-chunk's 8 activation blocks sit in lanes 0..7 of two more
+// VGPRs and are broadcast the same way.  Each block is one asm statement that
+// starts with s_nop 1: a VALU write to a DPP source needs two wait states;
+// and a v_dot4c result needs three wait states (s_nop 2) before any other VALU
+// instruction reads it (dependent v_dot4c chains forward without waits).
+// Only non-reversed ops take a DPP operand here: for the reversed forms
+// (v_subrev_*) the broadcast lands on the other source, so the qsum term is
+// stored negated and added with v_add_u32_dpp.
+struct ActSub {
+  int32_t a[4];  // q dwords 4i .. 4i+3 of the sub-chunk in row lane i
+  float d;       // lane kb (0..7): scale of activation block kb
+  int32_t Q;     // lane kb (0..7): minus the format multiple of the block's qsum
 };
 
-// ---- per-format segment compute ------------------------------------------------------------
-// T: the lane's row codes for the segment (dwords), S: its fp16 scales as
-// packed pairs, kb0: act block index of the segment start, nkb: valid act
-// blocks (FULL: all).  y accumulates the per-format scaled result.
+// Global views of one token's activations (token b at offset b * K).
+struct ActG {
+  g_u8* q;
+  const float __attribute__((address_space(1)))* d;
+  const int32_t __attribute__((address_space(1)))* qs;
+  int K, kbs;
+};
 
-template <int NB, bool FULL, bool WI>
-__device__ __forceinline__ void seg_sign1(const uint32_t (&T)[32], const uint32_t (&S)[4], const Act& A,
-                                          int kb0, int nkb, float (&y)[NB], int32_t* Iout) {
+template <int QMUL>
+__device__ __forceinline__ void load_act(ActSub& s, const ActG& A, int b, int kb_base) {
+  const int i = threadIdx.x & 15;
+  // bytes 16i.. of the sub-chunk; a partial last sub-chunk re-reads valid bytes
+  const int off = min(kb_base * 32 + 16 * i, A.K - 16);
+  const u32x4 v = *(g_u32x4*)(A.q + (int64_t)b * A.K + off);
+  s.a[0] = (int32_t)v.x;
+  s.a[1] = (int32_t)v.y;
+  s.a[2] = (int32_t)v.z;
+  s.a[3] = (int32_t)v.w;
+  const int kb = min(kb_base + (i & 7), A.kbs - 1);
+  s.d = A.d[(int64_t)b * A.kbs + kb];
+  s.Q = A.qs[(int64_t)b * A.kbs + kb] * -QMUL;
+}
+
+#define QK_DOT(ACC, A, P, L) "v_dot4c_i32_i8_dpp " ACC ", " A ", " P " row_newbcast:" L " row_mask:0xf bank_mask:0xf\n\t"
+
+// Two dot chains (16x weight plane in the second): R = 16*x + z + Q[KB] (Q holds -mult*qsum);
+// acc += d[KB] * R.  Dword j of the block is a[j % 4] at row lane 2KB + j/4.
+// SIGN1: chain z = dwords 4..7.   INT2: chain z = dwords 2, 3, 6, 7.
+template <int KB, bool INT2>
+__device__ __forceinline__ int blk_two_chain_fmac(float& acc, const ActSub& s, const uint32_t (&p)[8]) {
+  int x, z;
+  if constexpr (!INT2) {
+    asm("s_nop 1\n\t"
+        "v_mov_b32 %1, 0\n\t"
+        "v_mov_b32 %2, 0\n\t"
+        QK_DOT("%1", "%3", "%7", "%c17") QK_DOT("%2", "%3", "%11", "%c18")
+        QK_DOT("%1", "%4", "%8", "%c17") QK_DOT("%2", "%4", "%12", "%c18")
+        QK_DOT("%1", "%5", "%9", "%c17") QK_DOT("%2", "%5", "%13", "%c18")
+        QK_DOT("%1", "%6", "%10", "%c17") QK_DOT("%2", "%6", "%14", "%c18")
+        "s_nop 2\n\t"
+        "v_lshl_add_u32 %1, %1, 4, %2\n\t"
+        "v_add_u32_dpp %1, %16, %1 row_newbcast:%c19 row_mask:0xf bank_mask:0xf\n\t"
+        "v_cvt_f32_i32 %2, %1\n\t"
+        "v_fmac_f32_dpp %0, %15, %2 row_newbcast:%c19 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc), "=&v"(x), "=&v"(z)
+        : "v"(s.a[0]), "v"(s.a[1]), "v"(s.a[2]), "v"(s.a[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]),
+          "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(s.d), "v"(s.Q), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
+  } else {
+    asm("s_nop 1\n\t"
+        "v_mov_b32 %1, 0\n\t"
+        "v_mov_b32 %2, 0\n\t"
+        QK_DOT("%1", "%3", "%7", "%c17") QK_DOT("%1", "%4", "%8", "%c17")
+        QK_DOT("%2", "%5", "%9", "%c17") QK_DOT("%2", "%6", "%10", "%c17")
+        QK_DOT("%1", "%3", "%11", "%c18") QK_DOT("%1", "%4", "%12", "%c18")
+        QK_DOT("%2", "%5", "%13", "%c18") QK_DOT("%2", "%6", "%14", "%c18")
+        "s_nop 2\n\t"
+        "v_lshl_add_u32 %1, %1, 4, %2\n\t"
+        "v_add_u32_dpp %1, %16, %1 row_newbcast:%c19 row_mask:0xf bank_mask:0xf\n\t"
+        "v_cvt_f32_i32 %2, %1\n\t"
+        "v_mul_f32_dpp %0, %15, %2 row_newbcast:%c19 row_mask:0xf bank_mask:0xf"
+        : "=v"(acc), "=&v"(x), "=&v"(z)
+        : "v"(s.a[0]), "v"(s.a[1]), "v"(s.a[2]), "v"(s.a[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]),
+          "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(s.d), "v"(s.Q), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
+  }
+  return x;  // R (8 * I)
+}
+
+// One dot chain.  INT4: R = 2x + Q[KB] (Q = -15 qsum), out = d[KB] * R.
+template <int KB>
+__device__ __forceinline__ int blk_one_chain_mul2(float& out, const ActSub& s, const uint32_t (&p)[8]) {
+  int x, t;
+  asm("s_nop 1\n\t"
+      "v_mov_b32 %1, 0\n\t"
+      QK_DOT("%1", "%3", "%7", "%c17") QK_DOT("%1", "%4", "%8", "%c17")
+      QK_DOT("%1", "%5", "%9", "%c17") QK_DOT("%1", "%6", "%10", "%c17")
+      QK_DOT("%1", "%3", "%11", "%c18") QK_DOT("%1", "%4", "%12", "%c18")
+      QK_DOT("%1", "%5", "%13", "%c18") QK_DOT("%1", "%6", "%14", "%c18")
+      "s_nop 2\n\t"
+      "v_lshlrev_b32 %1, 1, %1\n\t"
+      "v_add_u32_dpp %1, %16, %1 row_newbcast:%c19 row_mask:0xf bank_mask:0xf\n\t"
+      "v_cvt_f32_i32 %2, %1\n\t"
+      "v_mul_f32_dpp %0, %15, %2 row_newbcast:%c19 row_mask:0xf bank_mask:0xf"
+      : "=v"(out), "=&v"(x), "=&v"(t)
+      : "v"(s.a[0]), "v"(s.a[1]), "v"(s.a[2]), "v"(s.a[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]),
+        "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(s.d), "v"(s.Q), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
+  return x;
+}
+
+// One dot chain.  TERN: R = x + Q[KB] (Q = -qsum, digits are t + 1); TRELLIS:
+// Q = 0.  acc += d[KB] * R.
+template <int KB>
+__device__ __forceinline__ int blk_one_chain_fmac(float& acc, const ActSub& s, const uint32_t (&p)[8]) {
+  int x, t;
+  asm("s_nop 1\n\t"
+      "v_mov_b32 %1, 0\n\t"
+      QK_DOT("%1", "%3", "%7", "%c17") QK_DOT("%1", "%4", "%8", "%c17")
+      QK_DOT("%1", "%5", "%9", "%c17") QK_DOT("%1", "%6", "%10", "%c17")
+      QK_DOT("%1", "%3", "%11", "%c18") QK_DOT("%1", "%4", "%12", "%c18")
+      QK_DOT("%1", "%5", "%13", "%c18") QK_DOT("%1", "%6", "%14", "%c18")
+      "s_nop 2\n\t"
+      "v_add_u32_dpp %1, %16, %1 row_newbcast:%c19 row_mask:0xf bank_mask:0xf\n\t"
+      "v_cvt_f32_i32 %2, %1\n\t"
+      "v_fmac_f32_dpp %0, %15, %2 row_newbcast:%c19 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc), "=&v"(x), "=&v"(t)
+      : "v"(s.a[0]), "v"(s.a[1]), "v"(s.a[2]), "v"(s.a[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]),
+        "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(s.d), "v"(s.Q), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
+  return x;
+}
+
+__device__ __forceinline__ float scale_half(uint32_t pair, int hi) {
+  return __half2float(__ushort_as_half((unsigned short)(hi ? (pair >> 16) : (pair & 0xFFFFu))));
+}
+
+// ---- per-format compute of one 256-weight sub-chunk --------------------------------------------------
+// T: the lane's row codes of the whole segment (dwords), SUB: sub-chunk index
+// in the segment, S: the segment's fp16 scales (pairs).  AS[b]: activations of
+// token b.  y accumulates (final per-format factor applied by the caller).
+template <int NB, int SUB, bool WI>
+__device__ __forceinline__ void sub_sign1(const uint32_t (&T)[32], const uint32_t (&S)[4], const ActSub (&AS)[NB],
+                                          float (&y)[NB], int32_t* Iout) {
 #pragma unroll
-  for (int sb = 0; sb < 8; ++sb) {
-    if (!(FULL || sb * 4 < nkb)) continue;
+  for (int h = 0; h < 2; ++h) {  // two 128-weight scale blocks
     float acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
-      const int kb = sb * 4 + j4;
-      const uint32_t W = T[kb];
-      uint32_t P[8];
+      const int kb = h * 4 + j4;  // activation block within the sub-chunk
+      const uint32_t W = T[SUB * 8 + kb];
+      uint32_t p[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t t = W >> j;
-        P[j] = t & 0x01010101u;
-        P[j + 4] = t & 0x10101010u;
+        p[j] = t & 0x01010101u;
+        p[j + 4] = t & 0x10101010u;
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        c_i32* a = A.q + b * A.kq + (kb0 + kb) * 8;
-        int x = 0, z = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x = dot4(P[j], a[j], x);
-          z = dot4(P[j + 4], a[j + 4], z);
+        int R;
+        switch (kb) {
+          case 0: R = blk_two_chain_fmac<0, false>(acc[b], AS[b], p); break;
+          case 1: R = blk_two_chain_fmac<1, false>(acc[b], AS[b], p); break;
+          case 2: R = blk_two_chain_fmac<2, false>(acc[b], AS[b], p); break;
+          case 3: R = blk_two_chain_fmac<3, false>(acc[b], AS[b], p); break;
+          case 4: R = blk_two_chain_fmac<4, false>(acc[b], AS[b], p); break;
+          case 5: R = blk_two_chain_fmac<5, false>(acc[b], AS[b], p); break;
+          case 6: R = blk_two_chain_fmac<6, false>(acc[b], AS[b], p); break;
+          default: R = blk_two_chain_fmac<7, false>(acc[b], AS[b], p); break;
         }
-        // 16*S1 - 8*qsum = 8*I with I = 2*S1 - qsum = sum (2b-1) q
-        const int i8 = (x << 4) + z - (A.qs[b * A.kbs + kb0 + kb] << 3);
-        if (WI && b == 0 && Iout) Iout[kb0 + kb] = i8 >> 3;
-        acc[b] = __builtin_fmaf(A.d[b * A.kbs + kb0 + kb], (float)i8, acc[b]);
+        if (WI && b == 0 && Iout) Iout[SUB * 8 + kb] = R >> 3;
       }
     }
-    const uint32_t sp = S[sb >> 1];
-    const float s = __half2float(__ushort_as_half((unsigned short)((sb & 1) ? (sp >> 16) : (sp & 0xFFFF))));
+    const float s = scale_half(S[SUB], h);
 #pragma unroll
     for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, acc[b], y[b]);
   }
 }
 
-template <int NB, bool FULL, bool WI>
-__device__ __forceinline__ void seg_int2(const uint32_t (&T)[32], const uint32_t (&S)[8], const Act& A,
-                                         int kb0, int nkb, float (&y)[NB], int32_t* Iout) {
+template <int KB, int NB, bool WI, int MODE>
+__device__ __forceinline__ void blk_dispatch(float (&out)[NB], const ActSub (&AS)[NB], const uint32_t (&p)[8],
+                                             int32_t* Iout, int idx) {
 #pragma unroll
-  for (int kb = 0; kb < 16; ++kb) {
-    if (!(FULL || kb < nkb)) continue;
-    const uint32_t W0 = T[2 * kb], W1 = T[2 * kb + 1];
-    const uint32_t V0 = W0 >> 2, V1 = W1 >> 2;
-    const uint32_t p0 = W0 & 0x03030303u, p1 = V0 & 0x03030303u, p4 = W1 & 0x03030303u, p5 = V1 & 0x03030303u;
-    const uint32_t p2 = W0 & 0x30303030u, p3 = V0 & 0x30303030u, p6 = W1 & 0x30303030u, p7 = V1 & 0x30303030u;
-    const uint32_t sp = S[kb >> 1];
-    const float s = __half2float(__ushort_as_half((unsigned short)((kb & 1) ? (sp >> 16) : (sp & 0xFFFF))));
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      c_i32* a = A.q + b * A.kq + (kb0 + kb) * 8;
-      int x = dot4(p0, a[0], 0);
-      x = dot4(p1, a[1], x);
-      x = dot4(p4, a[4], x);
-      x = dot4(p5, a[5], x);
-      int z = dot4(p2, a[2], 0);
-      z = dot4(p3, a[3], z);
-      z = dot4(p6, a[6], z);
-      z = dot4(p7, a[7], z);
-      // 16*sum(c q) - 24*qsum = 8*I with I = sum (2c-3) q
-      const int i8 = (x << 4) + z - A.qs[b * A.kbs + kb0 + kb] * 24;
-      if (WI && b == 0 && Iout) Iout[kb0 + kb] = i8 >> 3;
-      y[b] = __builtin_fmaf(s, A.d[b * A.kbs + kb0 + kb] * (float)i8, y[b]);
-    }
+  for (int b = 0; b < NB; ++b) {
+    int R;
+    if constexpr (MODE == 0) R = blk_two_chain_fmac<KB, true>(out[b], AS[b], p) >> 3;   // INT2: R = 8 I
+    else if constexpr (MODE == 1) R = blk_one_chain_mul2<KB>(out[b], AS[b], p);          // INT4
+    else R = blk_one_chain_fmac<KB>(out[b], AS[b], p);                                   // TERN, TRELLIS
+    if (WI && b == 0 && Iout) Iout[idx] = R;
   }
 }
 
-template <int NB, bool FULL, bool WI>
-__device__ __forceinline__ void seg_int4(const uint32_t (&T)[32], const uint32_t (&S)[4], const Act& A,
-                                         int kb0, int nkb, float (&y)[NB], int32_t* Iout) {
+template <int NB, bool WI, int MODE>
+__device__ __forceinline__ void blk_any(int kb, float (&out)[NB], const ActSub (&AS)[NB], const uint32_t (&p)[8],
+                                        int32_t* Iout, int idx) {
+  switch (kb) {
+    case 0: blk_dispatch<0, NB, WI, MODE>(out, AS, p, Iout, idx); break;
+    case 1: blk_dispatch<1, NB, WI, MODE>(out, AS, p, Iout, idx); break;
+    case 2: blk_dispatch<2, NB, WI, MODE>(out, AS, p, Iout, idx); break;
+    case 3: blk_dispatch<3, NB, WI, MODE>(out, AS, p, Iout, idx); break;
+    case 4: blk_dispatch<4, NB, WI, MODE>(out, AS, p, Iout, idx); break;
+    case 5: blk_dispatch<5, NB, WI, MODE>(out, AS, p, Iout, idx); break;
+    case 6: blk_dispatch<6, NB, WI, MODE>(out, AS, p, Iout, idx); break;
+    default: blk_dispatch<7, NB, WI, MODE>(out, AS, p, Iout, idx); break;
+  }
+}
+
+template <int NB, int SUB, bool WI>
+__device__ __forceinline__ void sub_int2(const uint32_t (&T)[32], const uint32_t (&S)[8], const ActSub (&AS)[NB],
+                                         float (&y)[NB], int32_t* Iout) {
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) {
-    if (!(FULL || kb < nkb)) continue;
-    uint32_t P[8];
+    const uint32_t W0 = T[SUB * 16 + 2 * kb], W1 = T[SUB * 16 + 2 * kb + 1];
+    const uint32_t V0 = W0 >> 2, V1 = W1 >> 2;
+    // levels of activation dwords 0..7 (dwords 2, 3, 6, 7 carry 16x)
+    const uint32_t p[8] = {W0 & 0x03030303u, V0 & 0x03030303u, W0 & 0x30303030u, V0 & 0x30303030u,
+                           W1 & 0x03030303u, V1 & 0x03030303u, W1 & 0x30303030u, V1 & 0x30303030u};
+    float t[NB];
+    blk_any<NB, WI, 0>(kb, t, AS, p, Iout, SUB * 8 + kb);
+    const int si = SUB * 8 + kb;  // scale index within the segment
+    const float s = scale_half(S[si >> 1], si & 1);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, t[b], y[b]);
+  }
+}
+
+template <int NB, bool WI>
+__device__ __forceinline__ void sub_int4(const uint32_t (&T)[32], const uint32_t (&S)[4], const ActSub (&AS)[NB],
+                                         float (&y)[NB], int32_t* Iout) {
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    uint32_t p[8];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const uint32_t W = T[4 * kb + m];
-      P[2 * m] = W & 0x0F0F0F0Fu;
-      P[2 * m + 1] = (W >> 4) & 0x0F0F0F0Fu;
+      p[2 * m] = W & 0x0F0F0F0Fu;
+      p[2 * m + 1] = (W >> 4) & 0x0F0F0F0Fu;
     }
-    const uint32_t sp = S[kb >> 1];
-    const float s = __half2float(__ushort_as_half((unsigned short)((kb & 1) ? (sp >> 16) : (sp & 0xFFFF))));
+    float t[NB];
+    blk_any<NB, WI, 1>(kb, t, AS, p, Iout, kb);
+    const float s = scale_half(S[kb >> 1], kb & 1);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      c_i32* a = A.q + b * A.kq + (kb0 + kb) * 8;
-      int x = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x = dot4(P[j], a[j], x);
-      // I = sum (2c-15) q = 2*sum(c q) - 15*qsum
-      const int I = (x << 1) - A.qs[b * A.kbs + kb0 + kb] * 15;
-      if (WI && b == 0 && Iout) Iout[kb0 + kb] = I;
-      y[b] = __builtin_fmaf(s, A.d[b * A.kbs + kb0 + kb] * (float)I, y[b]);
-    }
+    for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, t[b], y[b]);
   }
 }
 
-template <int NB, bool FULL, bool WI>
-__device__ __forceinline__ void seg_tern(const uint32_t (&T)[52], const uint32_t (&S)[2], const Act& A,
-                                         int kb0, int nkb, float (&y)[NB], int32_t* Iout) {
+// Ternary: 13 words of one 256-weight block; digit dwords come out in
+// activation-dword order g = 0..63 (word m < 12: g = 5m + i; word 12: 60 + i).
+template <int NB, int SUB, bool WI>
+__device__ __forceinline__ void sub_tern(const uint32_t (&T)[52], const uint32_t (&S)[2], const ActSub (&AS)[NB],
+                                         float (&y)[NB], int32_t* Iout) {
+  float acc[NB];
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
-    if (!(FULL || sb * 8 < nkb)) continue;
-    float acc[NB];
-    int blk[NB];
+  for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+  uint32_t p[8];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      acc[b] = 0.0f;
-      blk[b] = 0;
-    }
+  for (int m = 0; m < 13; ++m) {
+    const uint32_t W = T[13 * SUB + m];
+    uint32_t xl = W & 0x00FF00FFu;         // bytes 0, 2 in 16-bit lanes
+    uint32_t xh = (W >> 8) & 0x00FF00FFu;  // bytes 1, 3
+    const int ndig = m < 12 ? 5 : 4;
 #pragma unroll
-    for (int m = 0; m < 13; ++m) {
-      const uint32_t W = T[13 * sb + m];
-      uint32_t xl = W & 0x00FF00FFu;         // bytes 0, 2 in 16-bit lanes
-      uint32_t xh = (W >> 8) & 0x00FF00FFu;  // bytes 1, 3
-      const int ndig = m < 12 ? 5 : 4;
-#pragma unroll
-      for (int i = 0; i < ndig; ++i) {
-        const uint32_t yl = xl * 3u, yh = xh * 3u;
-        // digits sit in bits 8..9 of every 16-bit lane; gather bytes 1, 5, 3, 7
-        const uint32_t D = __builtin_amdgcn_perm(yh, yl, 0x07030501u);
-        if (i + 1 < ndig) {
-          xl = yl & 0x00FF00FFu;
-          xh = yh & 0x00FF00FFu;
-        }
-        const int g = m < 12 ? 5 * m + i : 60 + i;  // activation dword within the 256-block
-        const int kbl = sb * 8 + (g >> 3);
-        const int j = g & 7;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          c_i32* a = A.q + b * A.kq + (kb0 + kbl) * 8;
-          blk[b] = dot4(D, a[j], blk[b]);
-        }
-        if (j == 7) {
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            // digits are t + 1: sum d q - qsum = sum t q
-            const int I = blk[b] - A.qs[b * A.kbs + kb0 + kbl];
-            if (WI && b == 0 && Iout) Iout[kb0 + kbl] = I;
-            acc[b] = __builtin_fmaf(A.d[b * A.kbs + kb0 + kbl], (float)I, acc[b]);
-            blk[b] = 0;
-          }
-        }
+    for (int i = 0; i < ndig; ++i) {
+      const uint32_t yl = xl * 3u, yh = xh * 3u;
+      const int g = m < 12 ? 5 * m + i : 60 + i;
+      // the next digit of every byte sits in bits 8..9 of its 16-bit lane
+      p[g & 7] = __builtin_amdgcn_perm(yh, yl, 0x07030501u);
+      if (i + 1 < ndig) {
+        xl = yl & 0x00FF00FFu;
+        xh = yh & 0x00FF00FFu;
       }
+      if ((g & 7) == 7) blk_any<NB, WI, 2>(g >> 3, acc, AS, p, Iout, SUB * 8 + (g >> 3));
     }
-    const uint32_t sp = S[sb >> 1];
-    const float s = __half2float(__ushort_as_half((unsigned short)((sb & 1) ? (sp >> 16) : (sp & 0xFFFF))));
-#pragma unroll
-    for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, acc[b], y[b]);
   }
+  const float s = scale_half(S[SUB >> 1], SUB & 1);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, acc[b], y[b]);
 }
 
-// Trellis: `prev` holds the last 16 bits of seed||bytes before the segment.
-template <int NB, bool FULL, bool WI>
-__device__ __forceinline__ void seg_trellis(const uint32_t (&T)[32], const uint32_t (&S)[4], const Act& A,
-                                            int kb0, int nkb, uint32_t prev, const int8_t* v8,
-                                            float (&y)[NB], int32_t* Iout) {
+// Trellis: `prev` holds the last 16 bits of seed||bytes before the sub-chunk.
+template <int NB, int SUB, bool WI>
+__device__ __forceinline__ void sub_trellis(const uint32_t (&T)[32], const uint32_t (&S)[4], const ActSub (&AS)[NB],
+                                            uint32_t& prev, const int8_t* v8, float (&y)[NB], int32_t* Iout) {
 #pragma unroll
-  for (int sb = 0; sb < 8; ++sb) {  // 64-weight scale blocks = 2 act blocks = 4 dwords
-    if (!(FULL || sb * 2 < nkb)) continue;
+  for (int sb = 0; sb < 4; ++sb) {  // 64-weight scale blocks
     float acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int kb = sb * 2 + h2;
-      int blk[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) blk[b] = 0;
+      uint32_t p[8];
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        const uint32_t W = T[kb * 2 + w];
+        const uint32_t W = T[SUB * 16 + kb * 2 + w];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t w24 = (prev << 8) | ((W >> (8 * p)) & 0xFFu);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint32_t w24 = (prev << 8) | ((W >> (8 * q4)) & 0xFFu);
           uint32_t L = 0;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
@@ -264,22 +374,13 @@ __device__ __forceinline__ void seg_trellis(const uint32_t (&T)[32], const uint3
             L |= ((uint32_t)(uint8_t)v8[h]) << (8 * jj);
           }
           prev = w24 & 0xFFFFu;
-          const int j = w * 4 + p;
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            c_i32* a = A.q + b * A.kq + (kb0 + kb) * 8;
-            blk[b] = dot4(L, a[j], blk[b]);
-          }
+          p[w * 4 + q4] = L;
         }
       }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (WI && b == 0 && Iout) Iout[kb0 + kb] = blk[b];
-        acc[b] = __builtin_fmaf(A.d[b * A.kbs + kb0 + kb], (float)blk[b], acc[b]);
-      }
+      blk_any<NB, WI, 2>(kb, acc, AS, p, Iout, SUB * 8 + kb);
     }
-    const uint32_t sp = S[sb >> 1];
-    const float s = __half2float(__ushort_as_half((unsigned short)((sb & 1) ? (sp >> 16) : (sp & 0xFFFF))));
+    const int si = SUB * 4 + sb;
+    const float s = scale_half(S[si >> 1], si & 1);
 #pragma unroll
     for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, acc[b], y[b]);
   }
@@ -288,19 +389,19 @@ __device__ __forceinline__ void seg_trellis(const uint32_t (&T)[32], const uint3
 // ---- scale loads ---------------------------------------------------------------------------------
 // SPS fp16 scales of one lane's row for one segment, as SPS/2 packed pairs.
 template <int SPS>
-__device__ __forceinline__ void load_scales(const uint16_t* p, bool vec_ok, uint32_t (&S)[SPS / 2]) {
+__device__ __forceinline__ void load_scales(g_u16* p, bool vec_ok, uint32_t (&S)[SPS / 2]) {
   if (vec_ok) {
     if constexpr (SPS >= 8) {
 #pragma unroll
       for (int i = 0; i < SPS / 8; ++i) {
-        const u32x4 v = *(const u32x4*)(p + 8 * i);
+        const u32x4 v = *(g_u32x4*)(p + 8 * i);
         S[4 * i] = v.x;
         S[4 * i + 1] = v.y;
         S[4 * i + 2] = v.z;
         S[4 * i + 3] = v.w;
       }
     } else {
-      const u32x2 v = *(const u32x2*)p;
+      const u32x2 v = *(g_u32x2*)p;
       S[0] = v.x;
       S[1] = v.y;
     }
@@ -312,7 +413,7 @@ __device__ __forceinline__ void load_scales(const uint16_t* p, bool vec_ok, uint
 
 // Tail segment scales: only nsc of them are valid.
 template <int SPS>
-__device__ __forceinline__ void load_scales_tail(const uint16_t* p, int nsc, uint32_t (&S)[SPS / 2]) {
+__device__ __forceinline__ void load_scales_tail(g_u16* p, int nsc, uint32_t (&S)[SPS / 2]) {
 #pragma unroll
   for (int i = 0; i < SPS / 2; ++i) {
     const uint32_t lo = 2 * i < nsc ? p[2 * i] : 0u;
@@ -321,15 +422,42 @@ __device__ __forceinline__ void load_scales_tail(const uint16_t* p, int nsc, uin
   }
 }
 
-template <int FMT, int NB, bool FULL, bool WI>
-__device__ __forceinline__ void seg_compute(const uint32_t (&T)[Seg<FMT>::CH * 4], const uint32_t (&S)[Seg<FMT>::SPS / 2],
-                                            const Act& A, int kb0, int nkb, uint32_t prev, const int8_t* v8,
-                                            float (&y)[NB], int32_t* Iout) {
-  if constexpr (FMT == QFMT_SIGN1) seg_sign1<NB, FULL, WI>(T, S, A, kb0, nkb, y, Iout);
-  else if constexpr (FMT == QFMT_INT2) seg_int2<NB, FULL, WI>(T, S, A, kb0, nkb, y, Iout);
-  else if constexpr (FMT == QFMT_INT4) seg_int4<NB, FULL, WI>(T, S, A, kb0, nkb, y, Iout);
-  else if constexpr (FMT == QFMT_TERN_B3) seg_tern<NB, FULL, WI>(T, S, A, kb0, nkb, y, Iout);
-  else seg_trellis<NB, FULL, WI>(T, S, A, kb0, nkb, prev, v8, y, Iout);
+template <int... I, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// Multiple of qsum each format's block result subtracts (see the asm blocks).
+template <int FMT> struct QMul;
+template <> struct QMul<QFMT_SIGN1> { static constexpr int v = 8; };
+template <> struct QMul<QFMT_INT2> { static constexpr int v = 24; };
+template <> struct QMul<QFMT_INT4> { static constexpr int v = 15; };
+template <> struct QMul<QFMT_TERN_B3> { static constexpr int v = 1; };
+template <> struct QMul<QFMT_TRELLIS2> { static constexpr int v = 0; };
+
+template <int FMT, int NB>
+__device__ __forceinline__ void load_act_all(ActSub (&dst)[NB], const ActG& AG, int kb_base, int kbv) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    load_act<QMul<FMT>::v>(dst[b], AG, b, kb_base);
+    if (kbv < 8 && (int)(threadIdx.x & 7) >= kbv) {  // blocks past the end of K contribute nothing
+      dst[b].d = 0.0f;
+      dst[b].Q = 0;
+    }
+  }
+}
+
+// One sub-chunk of a segment; Ib: test-hook row output at the sub-chunk's
+// first activation block (entries below ivalid are written).
+template <int FMT, int NB, int SUB, bool WI>
+__device__ __forceinline__ void sub_compute(const uint32_t (&T)[Seg<FMT>::CH * 4], const uint32_t (&S)[Seg<FMT>::SPS / 2],
+                                            const ActSub (&AS)[NB], uint32_t& prev, const int8_t* v8, float (&y)[NB],
+                                            int32_t* Iseg) {
+  if constexpr (FMT == QFMT_SIGN1) sub_sign1<NB, SUB, WI>(T, S, AS, y, Iseg);
+  else if constexpr (FMT == QFMT_INT2) sub_int2<NB, SUB, WI>(T, S, AS, y, Iseg);
+  else if constexpr (FMT == QFMT_INT4) sub_int4<NB, WI>(T, S, AS, y, Iseg);
+  else if constexpr (FMT == QFMT_TERN_B3) sub_tern<NB, SUB, WI>(T, S, AS, y, Iseg);
+  else sub_trellis<NB, SUB, WI>(T, S, AS, prev, v8, y, Iseg);
 }
 
 // Result scale applied once per row after accumulation.
@@ -353,6 +481,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   constexpr int SPS = Seg<FMT>::SPS;
   constexpr int PITCH = Pitch<CH>::value;
   constexpr int SEGB = CH * 16;
+  constexpr int NSUB = SEGK / 256;
   const int lane = threadIdx.x & 63;
   const int K = it.cols;
   const int N = it.rows;
@@ -362,42 +491,43 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   const int64_t rb = it.row_bytes;
   const int nsb = K / Seg<FMT>::WBLK;
 
-  Act A;
-  A.q = (c_i32*)(const void*)it.q;
-  A.d = (c_f32*)(const void*)it.d;
-  A.qs = (c_i32*)(const void*)it.qsum;
-  A.kq = K >> 2;
-  A.kbs = K >> 5;
+  ActG AG;
+  AG.q = gptr<g_u8*>(it.q);
+  AG.d = gptr<const float __attribute__((address_space(1)))*>(it.d);
+  AG.qs = gptr<const int32_t __attribute__((address_space(1)))*>(it.qsum);
+  AG.K = K;
+  AG.kbs = K >> 5;
 
-  const uint16_t* srow = it.scales + (int64_t)row * nsb;
+  g_u16* srow = gptr<g_u16*>(it.scales) + (int64_t)row * nsb;
   constexpr int SALIGN = SPS * 2 >= 16 ? 16 : SPS * 2;  // bytes per vector scale load
   const bool svec = ((((uintptr_t)it.scales) | (uintptr_t)(nsb * 2)) & (SALIGN - 1)) == 0;
   // Only lanes that own a row write the test-hook output.
-  int32_t* Iout = (WI && lane < nvalid) ? Ibase + (int64_t)row * (K >> 5) : nullptr;
-  const uint8_t* tile = it.codes + (int64_t)row0 * rb;
+  int32_t* Irow = (WI && lane < nvalid) ? Ibase + (int64_t)row * (K >> 5) : nullptr;
+  g_u8* tile = gptr<g_u8*>(it.codes) + (int64_t)row0 * rb;
 
-  // Per-lane offsets of the coalesced tile load and its LDS slot.
+  // Per-lane offsets of the coalesced tile load and its LDS slot.  Rows past
+  // the end of the matrix re-read the last valid row (no branch per load);
+  // the lanes that would own them compute on it and store nothing.
   uint32_t goff[CH], loff[CH];
-  uint32_t vmask = 0;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int f = i * 64 + lane;
     const int r = f / CH, c = f % CH;
-    goff[i] = (uint32_t)(r * rb + c * 16);
+    goff[i] = (uint32_t)(min(r, nvalid - 1) * rb + c * 16);
     loff[i] = (uint32_t)(r * PITCH + c * 16);
-    if (r < nvalid) vmask |= 1u << i;
   }
   uint8_t* myrow = lds + lane * PITCH;
 
   u32x4 L[CH];
   uint32_t S[SPS / 2], Sn[SPS / 2];
+  ActSub cur[NB], nxt[NB];
   int seg = wk;
   if (seg < nseg) {
+    g_u8* tseg = tile + (int64_t)seg * SEGB;
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
-      L[i] = (vmask >> i) & 1 ? __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)seg * SEGB + goff[i]))
-                              : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < CH; ++i) L[i] = __builtin_nontemporal_load((g_u32x4*)(tseg + goff[i]));
     load_scales<SPS>(srow + seg * SPS, svec, Sn);
+    load_act_all<FMT, NB>(cur, AG, seg * (SEGK / 32), 8);
   }
   for (; seg < nseg; seg += nwk) {
     // transpose through LDS: write the tile, read back this lane's row
@@ -418,25 +548,35 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     __builtin_amdgcn_wave_barrier();
     const int nx = seg + nwk;
     if (nx < nseg) {
+      g_u8* tseg = tile + (int64_t)nx * SEGB;
 #pragma unroll
-      for (int i = 0; i < CH; ++i)
-        L[i] = (vmask >> i) & 1 ? __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)nx * SEGB + goff[i]))
-                                : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < CH; ++i) L[i] = __builtin_nontemporal_load((g_u32x4*)(tseg + goff[i]));
       load_scales<SPS>(srow + nx * SPS, svec, Sn);
     }
     uint32_t prev = 0;
     if constexpr (FMT == QFMT_TRELLIS2) {
-      const uint8_t* rp = it.codes + (int64_t)row * rb + (int64_t)seg * SEGB;
-      prev = seg == 0 ? (uint32_t)it.seeds[row] : (((uint32_t)rp[-2] << 8) | rp[-1]);
+      g_u8* rp = gptr<g_u8*>(it.codes) + (int64_t)row * rb + (int64_t)seg * SEGB;
+      prev = seg == 0 ? (uint32_t)gptr<g_u16*>(it.seeds)[row] : (((uint32_t)rp[-2] << 8) | rp[-1]);
     }
-    seg_compute<FMT, NB, true, WI>(T, S, A, seg * (SEGK / 32), SEGK / 32, prev, v8, y, Iout);
+    static_for(std::make_integer_sequence<int, NSUB>{}, [&](auto sc) {
+      constexpr int SUB = decltype(sc)::value;
+      // prefetch the next sub-chunk's activations (the next segment's first one last)
+      const bool more = (SUB + 1 < NSUB) || (nx < nseg);
+      const int nkb = (SUB + 1 < NSUB) ? seg * (SEGK / 32) + (SUB + 1) * 8 : nx * (SEGK / 32);
+      if (more) load_act_all<FMT, NB>(nxt, AG, nkb, 8);
+      sub_compute<FMT, NB, SUB, WI>(T, S, cur, prev, v8, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
+      if (more) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) cur[b] = nxt[b];
+      }
+    });
   }
 
   // Tail: fewer than SEGK weights left; this lane loads its own row directly.
   const int tailK = K - nseg * SEGK;
   if (tailK > 0 && (nseg % nwk) == wk) {
     const int64_t tb = packed_row_bytes(FMT, tailK);
-    const uint32_t* rp = (const uint32_t*)(it.codes + (int64_t)row * rb + (int64_t)nseg * SEGB);
+    g_u32* rp = (g_u32*)(gptr<g_u8*>(it.codes) + (int64_t)row * rb + (int64_t)nseg * SEGB);
     uint32_t T[CH * 4];
 #pragma unroll
     for (int i = 0; i < CH * 4; ++i) T[i] = 4 * i < tb ? rp[i] : 0u;
@@ -444,10 +584,32 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     load_scales_tail<SPS>(srow + nseg * SPS, tailK / Seg<FMT>::WBLK, St);
     uint32_t prev = 0;
     if constexpr (FMT == QFMT_TRELLIS2) {
-      const uint8_t* rb8 = (const uint8_t*)rp;
-      prev = nseg == 0 ? (uint32_t)it.seeds[row] : (((uint32_t)rb8[-2] << 8) | rb8[-1]);
+      g_u8* rb8 = (g_u8*)rp;
+      prev = nseg == 0 ? (uint32_t)gptr<g_u16*>(it.seeds)[row] : (((uint32_t)rb8[-2] << 8) | rb8[-1]);
     }
-    seg_compute<FMT, NB, false, WI>(T, St, A, nseg * (SEGK / 32), tailK / 32, prev, v8, y, Iout);
+    const int kb0 = nseg * (SEGK / 32);
+    const int nkb_tail = tailK / 32;
+    int32_t Ib[NSUB * 8];  // test-hook values of the tail segment, copied out below
+    static_for(std::make_integer_sequence<int, NSUB>{}, [&](auto sc) {
+      constexpr int SUB = decltype(sc)::value;
+      const int kbv = nkb_tail - SUB * 8;  // valid activation blocks in this sub-chunk
+      if (kbv > 0) {
+        ActSub at[NB];
+        load_act_all<FMT, NB>(at, AG, kb0 + SUB * 8, kbv);
+        float yt[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) yt[b] = 0.0f;
+        // the test hook must not write past the row's last block: bounded copy
+        sub_compute<FMT, NB, SUB, WI>(T, St, at, prev, v8, yt, WI && Irow ? Ib : nullptr);
+        if (WI && Irow) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (j < kbv) Irow[kb0 + SUB * 8 + j] = Ib[SUB * 8 + j];
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) y[b] += yt[b];
+      }
+    });
   }
 }
 
@@ -461,7 +623,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float ga
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * 64 * Pitch<Seg<FMT>::CH>::value];
   __shared__ float red[4][NB][64];
   __shared__ int8_t v8[256];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform: lets the compiler keep everything derived from it in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if constexpr (FMT == QFMT_TRELLIS2) {
     v8[threadIdx.x] = v8t.v[threadIdx.x];
     __syncthreads();
@@ -480,7 +643,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float ga
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const float v = ((red[0][b][lane] + red[1][b][lane]) + red[2][b][lane]) + red[3][b][lane];
-      it.y[(int64_t)b * it.rows + row0 + lane] = v * fs;
+      gptr<g_f32*>(it.y)[(int64_t)b * it.rows + row0 + lane] = v * fs;
     }
   }
 }
@@ -529,7 +692,7 @@ __global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict_
     }
     if (row0 + lane < it.rows) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) it.y[(int64_t)b * it.rows + row0 + lane] = y[b] * fs;
+      for (int b = 0; b < NB; ++b) gptr<g_f32*>(it.y)[(int64_t)b * it.rows + row0 + lane] = y[b] * fs;
     }
     t = tn;
   }
