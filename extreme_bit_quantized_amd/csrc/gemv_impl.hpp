@@ -67,8 +67,13 @@ template <> struct Seg<QFMT_TRELLIS2> {
 };
 // LDS row pitch of the transposed tile: an odd number of 16-byte chunks so
 // that the 8 lanes of a ds_read_b128 phase hit 8 different bank groups.
+// Per-wave LDS tile region of a format (0: the largest over all formats).
+template <int FMT> constexpr int wave_lds_bytes() {
+  if constexpr (FMT == 0) return 13 * 1024;
+  else return Seg<FMT>::CH * 1024;
+}
 template <int CH> struct Pitch { static constexpr int value = (CH % 2 ? CH : CH + 1) * 16; };
-constexpr int kMaxWaveLds = 64 * 208;  // largest per-wave tile region (ternary)
+constexpr int kMaxWaveLds = 13 * 1024;  // largest per-wave tile region (ternary)
 
 // ---- activation sub-chunks and DPP-broadcast block dots ----------------------------------------
 // Activations reach the dot products as the DPP operand of v_dot4c: the 256
@@ -470,6 +475,16 @@ __device__ __forceinline__ float final_scale(float trellis_gain) {
   else return trellis_gain;
 }
 
+// Waits for every vector-memory load of this wave, LDS-DMA tile loads
+// included, and keeps the compiler from moving memory accesses across the
+// wait.  The compiler's own LDS-DMA tracking is not relied on: it can leave out
+// the wait before an LDS read of a DMA'd region.
+__device__ __forceinline__ void wait_vm_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---- one 64-row tile ----------------------------------------------------------------------------------
 // Accumulates (unscaled by final_scale) into y for segments wk, wk + nwk, ...
 // and the tail segment if (nseg % nwk) == wk.  lds: this wave's region.
@@ -508,68 +523,142 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   // Per-lane offsets of the coalesced tile load and its LDS slot.  Rows past
   // the end of the matrix re-read the last valid row (no branch per load);
   // the lanes that would own them compute on it and store nothing.
-  uint32_t goff[CH], loff[CH];
+  // Tile loads go straight to LDS (global_load_lds_dwordx4): load i puts lane
+  // l's 16 bytes at slot 64 i + l of this wave's region.  For 8-chunk segments
+  // slot s holds row s / 8, chunk (s % 8) ^ (row % 8), so lane r reading its
+  // chunk k from slot 8 r + (k ^ (r % 8)) never has two lanes of a read phase
+  // in one bank group; 13-chunk segments are plain row-major (an odd pitch is
+  // conflict free).  Each load instruction still covers whole 128-byte lines.
+  uint32_t goff[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int f = i * 64 + lane;
-    const int r = f / CH, c = f % CH;
+    const int r = f / CH, pos = f % CH;
+    const int c = CH == 8 ? (pos ^ (r & 7)) : pos;
     goff[i] = (uint32_t)(min(r, nvalid - 1) * rb + c * 16);
-    loff[i] = (uint32_t)(r * PITCH + c * 16);
   }
-  uint8_t* myrow = lds + lane * PITCH;
+  // real == false: every lane re-reads the tile's first 16 bytes (one cached
+  // line) so that each iteration issues the same loads, which keeps the
+  // compiler's wait counts exact across the loop.
+  auto issue_tile = [&](int sg, bool real) {
+    g_u8* tseg = tile + (real ? (int64_t)sg * SEGB : 0);
+    const uint32_t keep = real ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tseg + (goff[i] & keep)),
+                                       (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0, 0);
+  };
 
-  u32x4 L[CH];
   uint32_t S[SPS / 2], Sn[SPS / 2];
-  ActSub cur[NB], nxt[NB];
   int seg = wk;
-  if (seg < nseg) {
-    g_u8* tseg = tile + (int64_t)seg * SEGB;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) L[i] = __builtin_nontemporal_load((g_u32x4*)(tseg + goff[i]));
-    load_scales<SPS>(srow + seg * SPS, svec, Sn);
-    load_act_all<FMT, NB>(cur, AG, seg * (SEGK / 32), 8);
-  }
-  for (; seg < nseg; seg += nwk) {
-    // transpose through LDS: write the tile, read back this lane's row
-#pragma unroll
-    for (int i = 0; i < CH; ++i) *(u32x4*)(lds + loff[i]) = L[i];
-    __builtin_amdgcn_wave_barrier();
-    uint32_t T[CH * 4];
+  auto read_row = [&](uint32_t (&T)[CH * 4]) {
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const u32x4 v = *(const u32x4*)(myrow + 16 * k);
+      const int off = CH == 8 ? lane * 128 + ((k ^ (lane & 7)) << 4) : lane * (CH * 16) + 16 * k;
+      const u32x4 v = *(const u32x4*)(lds + off);
       T[4 * k] = v.x;
       T[4 * k + 1] = v.y;
       T[4 * k + 2] = v.z;
       T[4 * k + 3] = v.w;
     }
-#pragma unroll
-    for (int i = 0; i < SPS / 2; ++i) S[i] = Sn[i];
-    __builtin_amdgcn_wave_barrier();
-    const int nx = seg + nwk;
-    if (nx < nseg) {
-      g_u8* tseg = tile + (int64_t)nx * SEGB;
-#pragma unroll
-      for (int i = 0; i < CH; ++i) L[i] = __builtin_nontemporal_load((g_u32x4*)(tseg + goff[i]));
-      load_scales<SPS>(srow + nx * SPS, svec, Sn);
-    }
-    uint32_t prev = 0;
+  };
+  // Trellis state carried into segment sg: the row seed for the first segment,
+  // else the last two code bytes before it (big-endian).  Split into the load
+  // (issued ahead) and the byte order fix (applied after the segment-top wait),
+  // so no wait is needed between the two.
+  auto trellis_prev_raw = [&](int sg) -> uint32_t {
     if constexpr (FMT == QFMT_TRELLIS2) {
-      g_u8* rp = gptr<g_u8*>(it.codes) + (int64_t)row * rb + (int64_t)seg * SEGB;
-      prev = seg == 0 ? (uint32_t)gptr<g_u16*>(it.seeds)[row] : (((uint32_t)rp[-2] << 8) | rp[-1]);
+      if (sg == 0) return (uint32_t)gptr<g_u16*>(it.seeds)[row];
+      g_u8* rp = gptr<g_u8*>(it.codes) + (int64_t)row * rb + (int64_t)sg * SEGB;
+      return (uint32_t)((g_u16*)rp)[-1];  // rp is 16-byte aligned
+    } else {
+      return 0u;
     }
-    static_for(std::make_integer_sequence<int, NSUB>{}, [&](auto sc) {
-      constexpr int SUB = decltype(sc)::value;
-      // prefetch the next sub-chunk's activations (the next segment's first one last)
-      const bool more = (SUB + 1 < NSUB) || (nx < nseg);
-      const int nkb = (SUB + 1 < NSUB) ? seg * (SEGK / 32) + (SUB + 1) * 8 : nx * (SEGK / 32);
-      if (more) load_act_all<FMT, NB>(nxt, AG, nkb, 8);
-      sub_compute<FMT, NB, SUB, WI>(T, S, cur, prev, v8, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
-      if (more) {
+  };
+  auto trellis_prev_fix = [&](int sg, uint32_t raw) -> uint32_t {
+    if constexpr (FMT == QFMT_TRELLIS2) return sg == 0 ? raw : (((raw & 0xFFu) << 8) | (raw >> 8));
+    else return 0u;
+  };
+  if constexpr (NB <= 2) {
+    // Whole-segment pipeline: at the top of a segment everything in flight is
+    // waited for once; then the next segment's activations, scales and tile DMA
+    // are issued (activations first) and the current segment is computed from
+    // registers with no further waits.  (LDS-DMA loads and ordinary loads in
+    // flight together make any later wait a full drain, so no ordinary load may
+    // be waited for between a DMA issue and the next segment top.)
+    ActSub acur[NSUB][NB], anxt[NSUB][NB];
+    uint32_t prevn = 0;
+    if (seg < nseg) {
+#pragma unroll
+      for (int sc = 0; sc < NSUB; ++sc) load_act_all<FMT, NB>(anxt[sc], AG, seg * (SEGK / 32) + sc * 8, 8);
+      load_scales<SPS>(srow + seg * SPS, svec, Sn);
+      prevn = trellis_prev_raw(seg);
+      issue_tile(seg, true);
+    }
+    for (; seg < nseg; seg += nwk) {
+      wait_vm_all();
+      uint32_t T[CH * 4];
+      read_row(T);
+#pragma unroll
+      for (int i = 0; i < SPS / 2; ++i) S[i] = Sn[i];
+#pragma unroll
+      for (int sc = 0; sc < NSUB; ++sc)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acur[sc][b] = anxt[sc][b];
+      uint32_t prev = trellis_prev_fix(seg, prevn);
+      // the tile reads must be complete before the next DMA overwrites the region
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const int nx = seg + nwk;
+      const bool more_seg = nx < nseg;
+      const int nsg = more_seg ? nx : seg;  // a last iteration re-reads valid data
+#pragma unroll
+      for (int sc = 0; sc < NSUB; ++sc) load_act_all<FMT, NB>(anxt[sc], AG, nsg * (SEGK / 32) + sc * 8, 8);
+      load_scales<SPS>(srow + nsg * SPS, svec, Sn);
+      prevn = trellis_prev_raw(nsg);
+      issue_tile(nx, more_seg);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for(std::make_integer_sequence<int, NSUB>{}, [&](auto scc) {
+        constexpr int SUB = decltype(scc)::value;
+        sub_compute<FMT, NB, SUB, WI>(T, S, acur[SUB], prev, v8, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
+      });
+    }
+  } else {
+    // Larger batches: activations prefetched one sub-chunk ahead.
+    ActSub cur[NB], nxt[NB];
+    uint32_t prevn = 0;
+    if (seg < nseg) {
+      prevn = trellis_prev_raw(seg);
+      issue_tile(seg, true);
+      load_scales<SPS>(srow + seg * SPS, svec, Sn);
+      load_act_all<FMT, NB>(cur, AG, seg * (SEGK / 32), 8);
+    }
+    for (; seg < nseg; seg += nwk) {
+      wait_vm_all();
+      uint32_t T[CH * 4];
+      read_row(T);
+#pragma unroll
+      for (int i = 0; i < SPS / 2; ++i) S[i] = Sn[i];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads done before the next DMA
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const int nx = seg + nwk;
+      const bool more_seg = nx < nseg;
+      uint32_t prev = trellis_prev_fix(seg, prevn);
+      prevn = trellis_prev_raw(more_seg ? nx : seg);
+      issue_tile(nx, more_seg);
+      load_scales<SPS>(srow + (more_seg ? nx : seg) * SPS, svec, Sn);
+      static_for(std::make_integer_sequence<int, NSUB>{}, [&](auto scc) {
+        constexpr int SUB = decltype(scc)::value;
+        const int nkb = (SUB + 1 < NSUB) ? seg * (SEGK / 32) + (SUB + 1) * 8
+                                         : (more_seg ? nx : seg) * (SEGK / 32);
+        load_act_all<FMT, NB>(nxt, AG, nkb, 8);
+        sub_compute<FMT, NB, SUB, WI>(T, S, cur, prev, v8, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
 #pragma unroll
         for (int b = 0; b < NB; ++b) cur[b] = nxt[b];
-      }
-    });
+      });
+    }
   }
 
   // Tail: fewer than SEGK weights left; this lane loads its own row directly.
@@ -620,7 +709,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
 // order, so results are deterministic.
 template <int FMT, int NB, bool WI>
 __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float gain, int32_t* Iout) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * 64 * Pitch<Seg<FMT>::CH>::value];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * Seg<FMT>::CH * 1024];
   __shared__ float red[4][NB][64];
   __shared__ int8_t v8[256];
   // wave-uniform: lets the compiler keep everything derived from it in SGPRs
@@ -633,7 +722,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float ga
   float y[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) y[b] = 0.0f;
-  gemv_tile<FMT, NB, WI>(it, row0, wave, 4, lds + wave * 64 * Pitch<Seg<FMT>::CH>::value, v8, y, Iout);
+  gemv_tile<FMT, NB, WI>(it, row0, wave, 4, lds + wave * Seg<FMT>::CH * 1024, v8, y, Iout);
+  wait_vm_all();  // no tile DMA may still be landing in LDS when the wave ends
   if (WI) return;
 #pragma unroll
   for (int b = 0; b < NB; ++b) red[wave][b][lane] = y[b];
@@ -650,10 +740,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float ga
 
 // Grouped: persistent waves pull 64-row tiles from an atomic counter.  The
 // last wave to leave resets the counters so the scratch is zero again.
-template <int NB>
+// ONLY = 0 serves plans of any format mix; ONLY = f serves plans whose items all
+// have format f (the other formats' code is compiled out, which frees registers).
+template <int NB, int ONLY>
 __global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict__ plan, uint32_t* scratch,
                                                       V8Table v8t, float gain) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kMaxWaveLds];
+  constexpr int WAVE_LDS = wave_lds_bytes<ONLY>();
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * WAVE_LDS];
   __shared__ int8_t v8[256];
   const PlanHeader* hp = (const PlanHeader*)plan;
   const int n_tiles = __builtin_amdgcn_readfirstlane(hp->n_tiles);
@@ -665,7 +758,7 @@ __global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict_
     __syncthreads();
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint8_t* my = lds + wave * kMaxWaveLds;
+  uint8_t* my = lds + wave * WAVE_LDS;
   auto grab = [&]() -> int {
     uint32_t t = 0;
     if (lane == 0) t = atomicAdd(&scratch[0], 1u);
@@ -678,7 +771,7 @@ __global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict_
     const int ii = __builtin_amdgcn_readfirstlane((int)tl.item);
     const int row0 = __builtin_amdgcn_readfirstlane((int)tl.row0);
     const GemvItem it = items[ii];
-    const int fmt = __builtin_amdgcn_readfirstlane(it.fmt);
+    const int fmt = ONLY ? ONLY : __builtin_amdgcn_readfirstlane(it.fmt);
     float y[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) y[b] = 0.0f;
@@ -696,6 +789,7 @@ __global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict_
     }
     t = tn;
   }
+  wait_vm_all();  // no tile DMA may still be landing in LDS when the wave ends
   if (lane == 0) {
     __threadfence();
     const uint32_t done = atomicAdd(&scratch[1], 1u);

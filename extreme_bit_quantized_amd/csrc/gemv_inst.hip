@@ -12,18 +12,28 @@
 namespace qk {
 
 namespace {
-int grouped_grid(const void* kernel, int lds_bytes) {
-  static int cached_dev = -1, cached_grid = 0;
+// Grid of a persistent grouped launch: every CU filled to the kernel's occupancy.
+// Cached per variant and device (one device per process in practice).
+int grouped_grid(const void* kernel, int variant) {
+  static int cached_dev[6] = {-1, -1, -1, -1, -1, -1}, cached_grid[6] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev == cached_dev) return cached_grid;
+  if (dev == cached_dev[variant]) return cached_grid[variant];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
-  (void)lds_bytes;
-  cached_dev = dev;
-  cached_grid = cus * per_cu;
-  return cached_grid;
+  cached_dev[variant] = dev;
+  cached_grid[variant] = cus * per_cu;
+  return cached_grid[variant];
+}
+
+template <int NB, int ONLY>
+hipError_t launch_grouped_variant(const void* plan, void* scratch, const V8Table& v8, float gain, hipStream_t s) {
+  const int grid = grouped_grid((const void*)k_gemv_grouped<NB, ONLY>, ONLY);
+  if (grid <= 0) return hipErrorInvalidDevice;
+  hipLaunchKernelGGL((k_gemv_grouped<NB, ONLY>), dim3(grid), dim3(256), 0, s, (const uint8_t*)plan,
+                     (uint32_t*)scratch, v8, gain);
+  return hipGetLastError();
 }
 }  // namespace
 
@@ -51,11 +61,14 @@ hipError_t QK_CAT(launch_grouped_b, QGEMV_NB)(const PlanHeader& h, const void* p
   V8Table v8;
   float gain = 0.0f;
   if (h.fmt_mask & (1 << QFMT_TRELLIS2)) trellis_tables(&v16, &v8, &gain);
-  const int grid = grouped_grid((const void*)k_gemv_grouped<NB>, 0);
-  if (grid <= 0) return hipErrorInvalidDevice;
-  hipLaunchKernelGGL((k_gemv_grouped<NB>), dim3(grid), dim3(256), 0, s, (const uint8_t*)plan, (uint32_t*)scratch,
-                     v8, gain);
-  return hipGetLastError();
+  switch (h.fmt_mask) {
+    case 1 << QFMT_SIGN1: return launch_grouped_variant<NB, QFMT_SIGN1>(plan, scratch, v8, gain, s);
+    case 1 << QFMT_INT2: return launch_grouped_variant<NB, QFMT_INT2>(plan, scratch, v8, gain, s);
+    case 1 << QFMT_INT4: return launch_grouped_variant<NB, QFMT_INT4>(plan, scratch, v8, gain, s);
+    case 1 << QFMT_TERN_B3: return launch_grouped_variant<NB, QFMT_TERN_B3>(plan, scratch, v8, gain, s);
+    case 1 << QFMT_TRELLIS2: return launch_grouped_variant<NB, QFMT_TRELLIS2>(plan, scratch, v8, gain, s);
+    default: return launch_grouped_variant<NB, 0>(plan, scratch, v8, gain, s);
+  }
 }
 
 #if QGEMV_NB == 1
