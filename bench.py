@@ -436,7 +436,7 @@ def main():
         "equiv_tok_s": round(1.0 / t_step, 1),
         "parity": {"sampled_rows": "ok" if ok else "FAIL", "worst_err_over_sum_abs_terms": worst},
         "roofline": {
-            "kernel": "qk::k_gemv_grouped<1>",
+            "kernel": "qk::k_gemv_grouped<1, QFMT_SIGN1>",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -67,8 +67,7 @@ def load(path: str = LIB_PATH):
         "qgemv_blockdots": (ctypes.c_int, [W, P, P, P, P]),
         "qgemv_grouped_plan_bytes": (i64, [ctypes.POINTER(qgemv_item_t), i32, i32]),
         "qgemv_grouped_plan": (ctypes.c_int, [ctypes.POINTER(qgemv_item_t), i32, i32, P, i64]),
-        "qgemv_grouped_scratch_bytes": (i64, []),
-        "qgemv_grouped_run": (ctypes.c_int, [P, P, P, i64, P]),
+        "qgemv_grouped_run": (ctypes.c_int, [P, P, P]),
         "qtrellis_decode_i8": (ctypes.c_int, [W, i32, P, P, P]),
         "qweight_unpack_i8": (ctypes.c_int, [W, P, P, P]),
         "qgemm_i8": (ctypes.c_int, [P, P, i32, P, P, i32, i32, i32, P, P]),
@@ -205,17 +204,12 @@ def qgemv_grouped_plan(items, B: int, host_plan) -> None:
            "qgemv_grouped_plan")
 
 
-def qgemv_grouped_scratch_bytes() -> int:
-    return load().qgemv_grouped_scratch_bytes()
-
-
-def qgemv_grouped_run(host_plan, dev_plan, dev_scratch, stream=None):
-    _check(load().qgemv_grouped_run(_ptr(host_plan), _ptr(dev_plan), _ptr(dev_scratch), dev_scratch.numel() *
-                                    dev_scratch.element_size(), _stream(stream)), "qgemv_grouped_run")
+def qgemv_grouped_run(host_plan, dev_plan, stream=None):
+    _check(load().qgemv_grouped_run(_ptr(host_plan), _ptr(dev_plan), _stream(stream)), "qgemv_grouped_run")
 
 
 class GroupedPlan:
-    """A plan built on the host and copied to the device, plus its scratch."""
+    """A plan built on the host and copied to the device."""
 
     def __init__(self, entries, B: int, device="cuda"):
         import torch
@@ -230,10 +224,9 @@ class GroupedPlan:
         self._raw = raw
         qgemv_grouped_plan(self.items, B, self.host)
         self.dev = self.host.to(device)
-        self.scratch = torch.zeros(qgemv_grouped_scratch_bytes() // 4, dtype=torch.int32, device=device)
 
     def run(self, stream=None):
-        qgemv_grouped_run(self.host, self.dev, self.scratch, stream)
+        qgemv_grouped_run(self.host, self.dev, stream)
 
 
 def qtrellis_decode_i8(w: PackedWeight, oblock: int, wq, dw, stream=None):

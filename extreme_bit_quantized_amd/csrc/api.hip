@@ -67,7 +67,7 @@ int check_item(const qgemv_item_t& it, int32_t B) {
 }
 
 using GemvLaunch = hipError_t (*)(const GemvItem&, hipStream_t);
-using GroupedLaunch = hipError_t (*)(const PlanHeader&, const void*, void*, hipStream_t);
+using GroupedLaunch = hipError_t (*)(const PlanHeader&, const void*, hipStream_t);
 const GemvLaunch kGemv[9] = {nullptr, launch_gemv_b1, launch_gemv_b2, launch_gemv_b3, launch_gemv_b4,
                              launch_gemv_b5, launch_gemv_b6, launch_gemv_b7, launch_gemv_b8};
 const GroupedLaunch kGrouped[9] = {nullptr, launch_grouped_b1, launch_grouped_b2, launch_grouped_b3,
@@ -261,19 +261,15 @@ int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B, void* ho
   return QERR_OK;
 }
 
-int64_t qgemv_grouped_scratch_bytes(void) { return kGroupedScratch; }
-
-int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* dev_scratch, int64_t scratch_bytes,
-                      void* stream) {
-  if (!host_plan || !dev_plan || !dev_scratch) return QERR_INVALID_ARG;
-  if (!aligned(host_plan, 16) || !aligned(dev_plan, 16) || !aligned(dev_scratch, 4)) return QERR_ALIGNMENT;
-  if (scratch_bytes < kGroupedScratch) return QERR_BUFFER;
+int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* stream) {
+  if (!host_plan || !dev_plan) return QERR_INVALID_ARG;
+  if (!aligned(host_plan, 16) || !aligned(dev_plan, 16)) return QERR_ALIGNMENT;
   PlanHeader h;
   std::memcpy(&h, host_plan, sizeof(h));
   if (h.magic != kPlanMagic || h.version != 1 || h.B < 1 || h.B > 8 || h.n_items < 1 || h.n_tiles < 0)
     return QERR_BUFFER;
   if (h.n_tiles == 0) return QERR_OK;
-  return hip_rc(kGrouped[h.B](h, dev_plan, dev_scratch, S(stream)));
+  return hip_rc(kGrouped[h.B](h, dev_plan, S(stream)));
 }
 
 int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw, void* stream) {

@@ -738,13 +738,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float ga
   }
 }
 
-// Grouped: persistent waves pull 64-row tiles from an atomic counter.  The
-// last wave to leave resets the counters so the scratch is zero again.
+// Grouped: persistent waves walk the plan's tile list in a fixed snake order:
+// in round r, wave w of W takes tile r W + w (r even) or r W + W - 1 - w (r odd).
+// The list is ordered longest first, so the snake balances the waves' totals.
+// No counter is shared: a single device-wide atomic per tile caps streaming
+// throughput well below what the HBM delivers.
 // ONLY = 0 serves plans of any format mix; ONLY = f serves plans whose items all
 // have format f (the other formats' code is compiled out, which frees registers).
 template <int NB, int ONLY>
-__global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict__ plan, uint32_t* scratch,
-                                                      V8Table v8t, float gain) {
+__global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict__ plan, V8Table v8t, float gain) {
   constexpr int WAVE_LDS = wave_lds_bytes<ONLY>();
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * WAVE_LDS];
   __shared__ int8_t v8[256];
@@ -757,16 +759,12 @@ __global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict_
     v8[threadIdx.x] = v8t.v[threadIdx.x];
     __syncthreads();
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint8_t* my = lds + wave * WAVE_LDS;
-  auto grab = [&]() -> int {
-    uint32_t t = 0;
-    if (lane == 0) t = atomicAdd(&scratch[0], 1u);
-    return __builtin_amdgcn_readfirstlane((int)t);
-  };
-  int t = grab();
-  while (t < n_tiles) {
-    const int tn = grab();
+  const int nw = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
+  for (int base = 0, r = 0; base < n_tiles; base += nw, ++r) {
+    const int t = base + ((r & 1) ? nw - 1 - gw : gw);
+    if (t >= n_tiles) break;  // the last, partial round
     const GemvTile tl = tiles[t];
     const int ii = __builtin_amdgcn_readfirstlane((int)tl.item);
     const int row0 = __builtin_amdgcn_readfirstlane((int)tl.row0);
@@ -787,17 +785,8 @@ __global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict_
 #pragma unroll
       for (int b = 0; b < NB; ++b) gptr<g_f32*>(it.y)[(int64_t)b * it.rows + row0 + lane] = y[b] * fs;
     }
-    t = tn;
   }
   wait_vm_all();  // no tile DMA may still be landing in LDS when the wave ends
-  if (lane == 0) {
-    __threadfence();
-    const uint32_t done = atomicAdd(&scratch[1], 1u);
-    if (done == gridDim.x * 4 - 1) {
-      atomicExch(&scratch[0], 0u);
-      atomicExch(&scratch[1], 0u);
-    }
-  }
 }
 
 }  // namespace qk

@@ -28,11 +28,10 @@ int grouped_grid(const void* kernel, int variant) {
 }
 
 template <int NB, int ONLY>
-hipError_t launch_grouped_variant(const void* plan, void* scratch, const V8Table& v8, float gain, hipStream_t s) {
+hipError_t launch_grouped_variant(const void* plan, const V8Table& v8, float gain, hipStream_t s) {
   const int grid = grouped_grid((const void*)k_gemv_grouped<NB, ONLY>, ONLY);
   if (grid <= 0) return hipErrorInvalidDevice;
-  hipLaunchKernelGGL((k_gemv_grouped<NB, ONLY>), dim3(grid), dim3(256), 0, s, (const uint8_t*)plan,
-                     (uint32_t*)scratch, v8, gain);
+  hipLaunchKernelGGL((k_gemv_grouped<NB, ONLY>), dim3(grid), dim3(256), 0, s, (const uint8_t*)plan, v8, gain);
   return hipGetLastError();
 }
 }  // namespace
@@ -55,19 +54,19 @@ hipError_t QK_CAT(launch_gemv_b, QGEMV_NB)(const GemvItem& it, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t QK_CAT(launch_grouped_b, QGEMV_NB)(const PlanHeader& h, const void* plan, void* scratch, hipStream_t s) {
+hipError_t QK_CAT(launch_grouped_b, QGEMV_NB)(const PlanHeader& h, const void* plan, hipStream_t s) {
   constexpr int NB = QGEMV_NB;
   V16Table v16;
   V8Table v8;
   float gain = 0.0f;
   if (h.fmt_mask & (1 << QFMT_TRELLIS2)) trellis_tables(&v16, &v8, &gain);
   switch (h.fmt_mask) {
-    case 1 << QFMT_SIGN1: return launch_grouped_variant<NB, QFMT_SIGN1>(plan, scratch, v8, gain, s);
-    case 1 << QFMT_INT2: return launch_grouped_variant<NB, QFMT_INT2>(plan, scratch, v8, gain, s);
-    case 1 << QFMT_INT4: return launch_grouped_variant<NB, QFMT_INT4>(plan, scratch, v8, gain, s);
-    case 1 << QFMT_TERN_B3: return launch_grouped_variant<NB, QFMT_TERN_B3>(plan, scratch, v8, gain, s);
-    case 1 << QFMT_TRELLIS2: return launch_grouped_variant<NB, QFMT_TRELLIS2>(plan, scratch, v8, gain, s);
-    default: return launch_grouped_variant<NB, 0>(plan, scratch, v8, gain, s);
+    case 1 << QFMT_SIGN1: return launch_grouped_variant<NB, QFMT_SIGN1>(plan, v8, gain, s);
+    case 1 << QFMT_INT2: return launch_grouped_variant<NB, QFMT_INT2>(plan, v8, gain, s);
+    case 1 << QFMT_INT4: return launch_grouped_variant<NB, QFMT_INT4>(plan, v8, gain, s);
+    case 1 << QFMT_TERN_B3: return launch_grouped_variant<NB, QFMT_TERN_B3>(plan, v8, gain, s);
+    case 1 << QFMT_TRELLIS2: return launch_grouped_variant<NB, QFMT_TRELLIS2>(plan, v8, gain, s);
+    default: return launch_grouped_variant<NB, 0>(plan, v8, gain, s);
   }
 }
 

@@ -98,7 +98,6 @@ struct alignas(16) PlanHeader {
   int64_t pad;
 };
 constexpr uint32_t kPlanMagic = 0x50564751u;  // "QGVP"
-constexpr int64_t kGroupedScratch = 256;
 
 // Codebook tables passed by value to the kernels that need them.
 struct V8Table { int8_t v[256]; };
@@ -119,8 +118,7 @@ hipError_t launch_unpack_i8(const GemvItem& it, int8_t* wq, float* dw, hipStream
 hipError_t launch_blockdots(const GemvItem& it, int32_t* out, hipStream_t s);
 #define QK_DECL_NB(n)                                                    \
   hipError_t launch_gemv_b##n(const GemvItem& it, hipStream_t s);        \
-  hipError_t launch_grouped_b##n(const PlanHeader& h, const void* plan, \
-                                 void* scratch, hipStream_t s);
+  hipError_t launch_grouped_b##n(const PlanHeader& h, const void* plan, hipStream_t s);
 QK_DECL_NB(1)
 QK_DECL_NB(2)
 QK_DECL_NB(3)

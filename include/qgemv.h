@@ -40,7 +40,7 @@ extern "C" {
 #define QERR_SHAPE (-3)           /* sizes violate the format's block rules */
 #define QERR_ALIGNMENT (-4)       /* pointer or stride misaligned */
 #define QERR_HIP (-5)             /* a HIP launch or query failed */
-#define QERR_BUFFER (-6)          /* caller buffer (plan, scratch) too small */
+#define QERR_BUFFER (-6)          /* caller buffer too small, or not a plan */
 
 /* Human-readable text for a QERR_* code (static storage, never NULL). */
 const char* qstrerror(int err);
@@ -188,14 +188,12 @@ int64_t qgemv_grouped_plan_bytes(const qgemv_item_t* items, int32_t n, int32_t B
  * The work is cut into 64-row tiles, ordered longest first. */
 int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B,
                        void* host_plan, int64_t plan_bytes);
-/* Scratch needed by a run (a tile counter and an exit counter). */
-int64_t qgemv_grouped_scratch_bytes(void);
 /* Run a plan: host_plan (host) is the plan as written by qgemv_grouped_plan,
- * dev_plan (device, 16-byte aligned) a byte copy of it.  dev_scratch (device,
- * >= qgemv_grouped_scratch_bytes) must be zero before the first run; every
- * run leaves it zero again.  Runs sharing a scratch buffer must not overlap. */
-int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* dev_scratch,
-                      int64_t scratch_bytes, void* stream);
+ * dev_plan (device, 16-byte aligned) a byte copy of it.  The launch needs no
+ * scratch memory: every wave takes its tiles in a fixed order, so runs are
+ * deterministic and independent of one another.  QERR_BUFFER if host_plan is
+ * not a plan. */
+int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* stream);
 
 /* ---- prefill: trellis decode to int8 and the int8 MFMA GEMM --------------------------- */
 

@@ -39,6 +39,33 @@ def test_exports_every_declared_symbol(ebq):
         assert hasattr(lib, n), n
 
 
+def _declared_arity():
+    """name -> number of parameters, from the prototypes in the header."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    out = {}
+    for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z][a-z0-9_]*)\s*\(([^)]*)\)\s*;",
+                         src, flags=re.M):
+        params = " ".join(m.group(2).split())
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_header(ebq):
+    """Every ctypes prototype the binding sets has the header's parameter count."""
+    arity = _declared_arity()
+    lib = ebq.load()
+    checked = 0
+    for name, n in arity.items():
+        f = getattr(lib, name)
+        if f.argtypes is None:
+            continue
+        assert len(f.argtypes) == n, (name, len(f.argtypes), n)
+        checked += 1
+    assert checked >= 15, checked
+
+
 def test_geometry_agrees_with_oracle(ebq, qref):
     for fmt in qref.FORMATS:
         assert ebq.qfmt_scale_block(fmt) == qref.scale_block(fmt)

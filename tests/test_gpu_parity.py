@@ -220,14 +220,20 @@ def test_grouped_parity_and_reuse(B):
         rq, rd, _ = oracle.act_quant(x)
         refs.append(oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd))
     plan = ebq.GroupedPlan(entries, B)
-    for rep in range(3):                                      # the scratch resets itself
+    first = None
+    for rep in range(3):                                      # a plan runs any number of times
         for e in entries:
             e[4].fill_(float("nan"))
         plan.run()
         _sync()
-        assert (host(plan.scratch) == 0).all()
-        for (fmt, N, K), e, (yr, absT, _) in zip(specs, entries, refs):
-            assert_close_terms(host(e[4]), yr, absT, what="grouped %s rep %d" % (NAMES[fmt], rep))
+        outs = [host(e[4]).copy() for e in entries]
+        for (fmt, N, K), o, (yr, absT, _) in zip(specs, outs, refs):
+            assert_close_terms(o, yr, absT, what="grouped %s rep %d" % (NAMES[fmt], rep))
+        if first is None:
+            first = outs
+        else:                                                 # fixed tile order: bit-identical runs
+            for a, b in zip(first, outs):
+                assert (a.view(np.uint32) == b.view(np.uint32)).all()
 
 
 # ---------------------------------------------------------------------------------------------
