@@ -304,7 +304,8 @@ def bench_prefill(ebq, reps):
         pw = ebq.PackedWeight.empty(TRELLIS, Nout, Kin)
         ebq.qweight_pack(TRELLIS, codes, pw)
         del codes
-        pw.scales.copy_(torch.from_numpy(synth.uniform_f16([5, 3, Kin], (Nout, Kin // 64), 0.01, 0.03).view(np.int16)).cuda())
+        ebq.qweight_set_scales(pw, torch.from_numpy(
+            synth.uniform_f16([5, 3, Kin], (Nout, Kin // 64), 0.01, 0.03).view(np.int16)).cuda())
         pw.seeds.copy_(torch.from_numpy(synth.u16([5, 4, Kin], Nout).view(np.int16)).cuda())
         wq = torch.empty((Nout, Kin), dtype=torch.int8, device="cuda")
         dw = torch.empty((Nout, Kin // 256), dtype=torch.float32, device="cuda")
@@ -335,7 +336,7 @@ def bench_small_ternary(ebq, reps):
     trits = torch.from_numpy(synth.trits([1], (N, K))).cuda()
     pw = ebq.PackedWeight.empty(TERN, N, K)
     ebq.qweight_pack(TERN, trits, pw)
-    pw.scales.copy_(torch.from_numpy(synth.uniform_f16([1, 1], (N, K // 256), 0.01, 0.1).view(np.int16)).cuda())
+    ebq.qweight_set_scales(pw, torch.from_numpy(synth.uniform_f16([1, 1], (N, K // 256), 0.01, 0.1).view(np.int16)).cuda())
     x = torch.from_numpy(synth.gauss([1, 2], (1, K))).cuda()
     q = torch.empty((1, K), dtype=torch.int8, device="cuda")
     d = torch.empty((1, K // 32), dtype=torch.float32, device="cuda")

@@ -59,6 +59,10 @@ def load(path: str = LIB_PATH):
         "qfmt_packed_row_bytes": (i64, [i32, i32]),
         "qfmt_row_bytes": (i64, [i32, i32]),
         "qweight_check": (ctypes.c_int, [W]),
+        "qfmt_scale_group": (i32, [i32]),
+        "qfmt_scales_bytes": (i64, [i32, i32, i32]),
+        "qweight_set_scales": (ctypes.c_int, [W, P, P]),
+        "qweight_get_scales": (ctypes.c_int, [W, P, P]),
         "qweight_quantize": (ctypes.c_int, [i32, P, i32, i32, P, i64, P, P]),
         "qweight_pack": (ctypes.c_int, [i32, P, i32, i32, P, i64, P]),
         "qact_quant_i8": (ctypes.c_int, [P, i32, i32, i32, P, P, P, P]),
@@ -134,12 +138,13 @@ class PackedWeight:
 
         rb = qfmt_row_bytes(fmt, cols)
         codes = torch.empty((rows, rb), dtype=torch.uint8, device=device)
-        scales = torch.empty((rows, cols // qfmt_scale_block(fmt)), dtype=torch.int16, device=device)
+        scales = torch.zeros((qfmt_scales_bytes(fmt, rows, cols) // 2,), dtype=torch.int16, device=device)
         seeds = torch.empty((rows,), dtype=torch.int16, device=device) if fmt == QFMT_TRELLIS2 else None
         return cls(fmt, rows, cols, codes, scales, seeds, rb)
 
     @property
     def nbytes(self) -> int:
+        """Algorithmic bytes: codes, one fp16 per scale block, seeds (no padding)."""
         n = self.rows * self.row_bytes + self.rows * (self.cols // qfmt_scale_block(self.fmt)) * 2
         return n + (2 * self.rows if self.seeds is not None else 0)
 
@@ -155,6 +160,27 @@ def qweight_quantize(fmt: int, w, out: PackedWeight, stream=None):
     _check(load().qweight_quantize(fmt, _ptr(w), rows, cols, _ptr(out.codes), out.row_bytes, _ptr(out.scales),
                                    _stream(stream)), "qweight_quantize")
     return out
+
+
+def qfmt_scale_group(fmt: int) -> int:
+    return load().qfmt_scale_group(fmt)
+
+
+def qfmt_scales_bytes(fmt: int, rows: int, cols: int) -> int:
+    n = load().qfmt_scales_bytes(fmt, rows, cols)
+    _check(n if n < 0 else 0, "qfmt_scales_bytes")
+    return n
+
+
+def qweight_set_scales(w: PackedWeight, rowmajor, stream=None):
+    """rowmajor: device fp16 bits [rows][cols/block] (int16 or uint16 tensor)."""
+    _check(load().qweight_set_scales(ctypes.byref(w.desc), _ptr(rowmajor), _stream(stream)), "qweight_set_scales")
+    return w
+
+
+def qweight_get_scales(w: PackedWeight, rowmajor, stream=None):
+    _check(load().qweight_get_scales(ctypes.byref(w.desc), _ptr(rowmajor), _stream(stream)), "qweight_get_scales")
+    return rowmajor
 
 
 def qweight_pack(fmt: int, levels, out: PackedWeight, stream=None):

@@ -27,7 +27,7 @@ int check_weight(const qweight_t* w) {
   const int64_t packed = packed_row_bytes(w->fmt, w->cols);
   if (w->row_bytes < packed || w->row_bytes % 16 != 0) return QERR_SHAPE;
   if (w->row_bytes >= ((int64_t)1 << 26)) return QERR_SHAPE;  // 64-row tile offsets fit 32 bits
-  if (!aligned(w->codes, 16) || !aligned(w->scales, 2) || (w->seeds && !aligned(w->seeds, 2)))
+  if (!aligned(w->codes, 16) || !aligned(w->scales, 16) || (w->seeds && !aligned(w->seeds, 2)))
     return QERR_ALIGNMENT;
   return QERR_OK;
 }
@@ -113,7 +113,35 @@ int64_t qfmt_row_bytes(int32_t fmt, int32_t cols) {
   return b < 0 ? b : (b + 15) / 16 * 16;
 }
 
+int32_t qfmt_scale_group(int32_t fmt) { return scale_group(fmt); }
+
+int64_t qfmt_scales_bytes(int32_t fmt, int32_t rows, int32_t cols) {
+  const int32_t blk = scale_block(fmt);
+  if (blk == 0) return QERR_UNSUPPORTED_FMT;
+  if (rows < 0 || cols < 0) return QERR_INVALID_ARG;
+  if (cols == 0 || cols % blk != 0 || cols % 32 != 0) return QERR_SHAPE;
+  return 2 * scales_elems(fmt, rows, cols);
+}
+
 int qweight_check(const qweight_t* w) { return check_weight(w); }
+
+int qweight_set_scales(const qweight_t* w, const uint16_t* rowmajor, void* stream) {
+  const int rc = check_weight(w);
+  if (rc) return rc;
+  if (w->rows == 0) return QERR_OK;
+  if (!rowmajor) return QERR_INVALID_ARG;
+  if (!aligned(rowmajor, 2)) return QERR_ALIGNMENT;
+  return hip_rc(launch_scales_from_rows(w->fmt, w->rows, w->cols, rowmajor, (uint16_t*)w->scales, S(stream)));
+}
+
+int qweight_get_scales(const qweight_t* w, uint16_t* rowmajor, void* stream) {
+  const int rc = check_weight(w);
+  if (rc) return rc;
+  if (w->rows == 0) return QERR_OK;
+  if (!rowmajor) return QERR_INVALID_ARG;
+  if (!aligned(rowmajor, 2)) return QERR_ALIGNMENT;
+  return hip_rc(launch_scales_to_rows(w->fmt, w->rows, w->cols, w->scales, rowmajor, S(stream)));
+}
 
 int qweight_quantize(int32_t fmt, const float* w, int32_t rows, int32_t cols, void* codes, int64_t row_bytes,
                      uint16_t* scales, void* stream) {
@@ -210,7 +238,7 @@ int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B, void* ho
   std::memset(base, 0, (size_t)need);
   PlanHeader h{};
   h.magic = kPlanMagic;
-  h.version = 1;
+  h.version = kPlanVersion;
   h.n_items = n;
   h.n_tiles = (int32_t)ntiles;
   h.B = B;
@@ -222,41 +250,29 @@ int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B, void* ho
     it[i] = make_item(&items[i].w, items[i].q, items[i].d, items[i].qsum, items[i].y);
     if (items[i].w.rows > 0) h.fmt_mask |= 1 << items[i].w.fmt;
   }
-  // Tiles: longest first inside each format; formats interleaved in
-  // proportion to their total bytes so VALU-heavy and byte-heavy work overlap.
+  // Tiles: grouped by format, longest first inside each group.
   struct T { int64_t cost; uint32_t item, row0; };
   std::vector<std::vector<T>> q(6);
-  std::vector<int64_t> total(6, 0);
   for (int32_t i = 0; i < n; ++i) {
     const qweight_t& w = items[i].w;
     for (int32_t r = 0; r < w.rows; r += 64) {
       const int64_t rows = std::min(64, w.rows - r);
       const int64_t c = rows * (w.row_bytes + (int64_t)(w.cols / w.block) * 2);
       q[w.fmt].push_back({c, (uint32_t)i, (uint32_t)r});
-      total[w.fmt] += c;
     }
   }
-  for (auto& v : q)
-    std::stable_sort(v.begin(), v.end(), [](const T& a, const T& b) { return a.cost > b.cost; });
-  std::vector<size_t> pos(6, 0);
-  std::vector<int64_t> used(6, 0);
   GemvTile* tiles = (GemvTile*)(base + h.tiles_off);
-  for (int64_t k = 0; k < ntiles; ++k) {
-    int best = -1;
-    double bf = 2.0;
-    for (int f = 1; f <= 5; ++f) {
-      if (pos[f] >= q[f].size()) continue;
-      const double frac = (double)used[f] / (double)total[f];
-      if (frac < bf) {
-        bf = frac;
-        best = f;
-      }
+  int64_t k = 0;
+  for (int f = 1; f <= 5; ++f) {
+    std::stable_sort(q[f].begin(), q[f].end(), [](const T& a, const T& b) { return a.cost > b.cost; });
+    h.fmt_begin[f] = (int32_t)k;
+    for (const T& t : q[f]) {
+      tiles[k].item = t.item;
+      tiles[k].row0 = t.row0;
+      ++k;
     }
-    const T& t = q[best][pos[best]++];
-    used[best] += t.cost;
-    tiles[k].item = t.item;
-    tiles[k].row0 = t.row0;
   }
+  h.fmt_begin[6] = (int32_t)k;
   std::memcpy(base, &h, sizeof(h));
   return QERR_OK;
 }
@@ -266,7 +282,7 @@ int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* stream)
   if (!aligned(host_plan, 16) || !aligned(dev_plan, 16)) return QERR_ALIGNMENT;
   PlanHeader h;
   std::memcpy(&h, host_plan, sizeof(h));
-  if (h.magic != kPlanMagic || h.version != 1 || h.B < 1 || h.B > 8 || h.n_items < 1 || h.n_tiles < 0)
+  if (h.magic != kPlanMagic || h.version != kPlanVersion || h.B < 1 || h.B > 8 || h.n_items < 1 || h.n_tiles < 0)
     return QERR_BUFFER;
   if (h.n_tiles == 0) return QERR_OK;
   return hip_rc(kGrouped[h.B](h, dev_plan, S(stream)));

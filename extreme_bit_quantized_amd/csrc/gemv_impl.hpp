@@ -65,15 +65,6 @@ template <> struct Seg<QFMT_TERN_B3> {
 template <> struct Seg<QFMT_TRELLIS2> {
   static constexpr int CH = 8, K = 512, SPS = 8, WBLK = 64;
 };
-// LDS row pitch of the transposed tile: an odd number of 16-byte chunks so
-// that the 8 lanes of a ds_read_b128 phase hit 8 different bank groups.
-// Per-wave LDS tile region of a format (0: the largest over all formats).
-template <int FMT> constexpr int wave_lds_bytes() {
-  if constexpr (FMT == 0) return 13 * 1024;
-  else return Seg<FMT>::CH * 1024;
-}
-template <int CH> struct Pitch { static constexpr int value = (CH % 2 ? CH : CH + 1) * 16; };
-constexpr int kMaxWaveLds = 13 * 1024;  // largest per-wave tile region (ternary)
 
 // ---- activation sub-chunks and DPP-broadcast block dots ----------------------------------------
 // Activations reach the dot products as the DPP operand of v_dot4c: the 256
@@ -392,38 +383,23 @@ __device__ __forceinline__ void sub_trellis(const uint32_t (&T)[32], const uint3
 }
 
 // ---- scale loads ---------------------------------------------------------------------------------
-// SPS fp16 scales of one lane's row for one segment, as SPS/2 packed pairs.
+// The SPS fp16 scales of one lane's row for one segment: SPS contiguous values
+// of the tiled scale layout (16-byte aligned), as SPS/2 packed pairs.
 template <int SPS>
-__device__ __forceinline__ void load_scales(g_u16* p, bool vec_ok, uint32_t (&S)[SPS / 2]) {
-  if (vec_ok) {
-    if constexpr (SPS >= 8) {
+__device__ __forceinline__ void load_scales(g_u16* p, uint32_t (&S)[SPS / 2]) {
+  if constexpr (SPS >= 8) {
 #pragma unroll
-      for (int i = 0; i < SPS / 8; ++i) {
-        const u32x4 v = *(g_u32x4*)(p + 8 * i);
-        S[4 * i] = v.x;
-        S[4 * i + 1] = v.y;
-        S[4 * i + 2] = v.z;
-        S[4 * i + 3] = v.w;
-      }
-    } else {
-      const u32x2 v = *(g_u32x2*)p;
-      S[0] = v.x;
-      S[1] = v.y;
+    for (int i = 0; i < SPS / 8; ++i) {
+      const u32x4 v = *(g_u32x4*)(p + 8 * i);
+      S[4 * i] = v.x;
+      S[4 * i + 1] = v.y;
+      S[4 * i + 2] = v.z;
+      S[4 * i + 3] = v.w;
     }
   } else {
-#pragma unroll
-    for (int i = 0; i < SPS / 2; ++i) S[i] = (uint32_t)p[2 * i] | ((uint32_t)p[2 * i + 1] << 16);
-  }
-}
-
-// Tail segment scales: only nsc of them are valid.
-template <int SPS>
-__device__ __forceinline__ void load_scales_tail(g_u16* p, int nsc, uint32_t (&S)[SPS / 2]) {
-#pragma unroll
-  for (int i = 0; i < SPS / 2; ++i) {
-    const uint32_t lo = 2 * i < nsc ? p[2 * i] : 0u;
-    const uint32_t hi = 2 * i + 1 < nsc ? p[2 * i + 1] : 0u;
-    S[i] = lo | (hi << 16);
+    const u32x2 v = *(g_u32x2*)p;
+    S[0] = v.x;
+    S[1] = v.y;
   }
 }
 
@@ -494,7 +470,6 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   constexpr int CH = Seg<FMT>::CH;
   constexpr int SEGK = Seg<FMT>::K;
   constexpr int SPS = Seg<FMT>::SPS;
-  constexpr int PITCH = Pitch<CH>::value;
   constexpr int SEGB = CH * 16;
   constexpr int NSUB = SEGK / 256;
   const int lane = threadIdx.x & 63;
@@ -513,9 +488,11 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   AG.K = K;
   AG.kbs = K >> 5;
 
-  g_u16* srow = gptr<g_u16*>(it.scales) + (int64_t)row * nsb;
-  constexpr int SALIGN = SPS * 2 >= 16 ? 16 : SPS * 2;  // bytes per vector scale load
-  const bool svec = ((((uintptr_t)it.scales) | (uintptr_t)(nsb * 2)) & (SALIGN - 1)) == 0;
+  // This lane's scales for segment sg: slot `lane` of the tile's group sg (rows
+  // past the end read zero padding).
+  static_assert(SPS == scale_group(FMT) && SPS * Seg<FMT>::WBLK == SEGK, "scale groups are GEMV segments");
+  g_u16* stile = gptr<g_u16*>(it.scales) + (int64_t)(row0 >> 6) * ((nsb + SPS - 1) / SPS) * 64 * SPS + lane * SPS;
+  auto sptr = [&](int sg) { return stile + (int64_t)sg * 64 * SPS; };
   // Only lanes that own a row write the test-hook output.
   int32_t* Irow = (WI && lane < nvalid) ? Ibase + (int64_t)row * (K >> 5) : nullptr;
   g_u8* tile = gptr<g_u8*>(it.codes) + (int64_t)row0 * rb;
@@ -529,14 +506,18 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   // chunk k from slot 8 r + (k ^ (r % 8)) never has two lanes of a read phase
   // in one bank group; 13-chunk segments are plain row-major (an odd pitch is
   // conflict free).  Each load instruction still covers whole 128-byte lines.
-  uint32_t goff[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
+  auto tile_off = [&](int i) -> uint32_t {
     const int f = i * 64 + lane;
     const int r = f / CH, pos = f % CH;
     const int c = CH == 8 ? (pos ^ (r & 7)) : pos;
-    goff[i] = (uint32_t)(min(r, nvalid - 1) * rb + c * 16);
-  }
+    return (uint32_t)(min(r, nvalid - 1) * rb + c * 16);
+  };
+  // Batches up to 2 keep the offsets in registers; larger batches, short of
+  // registers, recompute them at each issue (a few VALU per load).
+  constexpr int NOFF = NB <= 2 ? CH : 1;
+  uint32_t goff[NOFF];
+#pragma unroll
+  for (int i = 0; i < NOFF; ++i) goff[i] = tile_off(i);
   // real == false: every lane re-reads the tile's first 16 bytes (one cached
   // line) so that each iteration issues the same loads, which keeps the
   // compiler's wait counts exact across the loop.
@@ -544,9 +525,11 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     g_u8* tseg = tile + (real ? (int64_t)sg * SEGB : 0);
     const uint32_t keep = real ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tseg + (goff[i] & keep)),
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t off = NB <= 2 ? goff[i < NOFF ? i : 0] : tile_off(i);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tseg + (off & keep)),
                                        (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0, 0);
+    }
   };
 
   uint32_t S[SPS / 2], Sn[SPS / 2];
@@ -591,7 +574,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     if (seg < nseg) {
 #pragma unroll
       for (int sc = 0; sc < NSUB; ++sc) load_act_all<FMT, NB>(anxt[sc], AG, seg * (SEGK / 32) + sc * 8, 8);
-      load_scales<SPS>(srow + seg * SPS, svec, Sn);
+      load_scales<SPS>(sptr(seg), Sn);
       prevn = trellis_prev_raw(seg);
       issue_tile(seg, true);
     }
@@ -615,7 +598,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
       const int nsg = more_seg ? nx : seg;  // a last iteration re-reads valid data
 #pragma unroll
       for (int sc = 0; sc < NSUB; ++sc) load_act_all<FMT, NB>(anxt[sc], AG, nsg * (SEGK / 32) + sc * 8, 8);
-      load_scales<SPS>(srow + nsg * SPS, svec, Sn);
+      load_scales<SPS>(sptr(nsg), Sn);
       prevn = trellis_prev_raw(nsg);
       issue_tile(nx, more_seg);
       __builtin_amdgcn_sched_barrier(0);
@@ -631,7 +614,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     if (seg < nseg) {
       prevn = trellis_prev_raw(seg);
       issue_tile(seg, true);
-      load_scales<SPS>(srow + seg * SPS, svec, Sn);
+      load_scales<SPS>(sptr(seg), Sn);
       load_act_all<FMT, NB>(cur, AG, seg * (SEGK / 32), 8);
     }
     for (; seg < nseg; seg += nwk) {
@@ -648,7 +631,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
       uint32_t prev = trellis_prev_fix(seg, prevn);
       prevn = trellis_prev_raw(more_seg ? nx : seg);
       issue_tile(nx, more_seg);
-      load_scales<SPS>(srow + (more_seg ? nx : seg) * SPS, svec, Sn);
+      load_scales<SPS>(sptr(more_seg ? nx : seg), Sn);
       static_for(std::make_integer_sequence<int, NSUB>{}, [&](auto scc) {
         constexpr int SUB = decltype(scc)::value;
         const int nkb = (SUB + 1 < NSUB) ? seg * (SEGK / 32) + (SUB + 1) * 8
@@ -670,7 +653,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
 #pragma unroll
     for (int i = 0; i < CH * 4; ++i) T[i] = 4 * i < tb ? rp[i] : 0u;
     uint32_t St[SPS / 2];
-    load_scales_tail<SPS>(srow + nseg * SPS, tailK / Seg<FMT>::WBLK, St);
+    load_scales<SPS>(sptr(nseg), St);  // the group is zero-padded
     uint32_t prev = 0;
     if constexpr (FMT == QFMT_TRELLIS2) {
       g_u8* rb8 = (g_u8*)rp;
@@ -743,33 +726,33 @@ __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float ga
 // The list is ordered longest first, so the snake balances the waves' totals.
 // No counter is shared: a single device-wide atomic per tile caps streaming
 // throughput well below what the HBM delivers.
-// ONLY = 0 serves plans of any format mix; ONLY = f serves plans whose items all
-// have format f (the other formats' code is compiled out, which frees registers).
+// One launch serves the plan's tiles [t_begin, t_end), all of format ONLY (the
+// other formats' code is not compiled in, which keeps the register count low).
 template <int NB, int ONLY>
-__global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict__ plan, V8Table v8t, float gain) {
-  constexpr int WAVE_LDS = wave_lds_bytes<ONLY>();
+__global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict__ plan, int t_begin, int t_end,
+                                                      V8Table v8t, float gain) {
+  static_assert(ONLY >= 1 && ONLY <= 5, "one format per launch");
+  constexpr int WAVE_LDS = Seg<ONLY>::CH * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * WAVE_LDS];
   __shared__ int8_t v8[256];
   const PlanHeader* hp = (const PlanHeader*)plan;
-  const int n_tiles = __builtin_amdgcn_readfirstlane(hp->n_tiles);
-  const int fmt_mask = __builtin_amdgcn_readfirstlane(hp->fmt_mask);
   const GemvItem* items = (const GemvItem*)(plan + hp->items_off);
   const GemvTile* tiles = (const GemvTile*)(plan + hp->tiles_off);
-  if (fmt_mask & (1 << QFMT_TRELLIS2)) {
+  if constexpr (ONLY == QFMT_TRELLIS2) {
     v8[threadIdx.x] = v8t.v[threadIdx.x];
     __syncthreads();
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint8_t* my = lds + wave * WAVE_LDS;
   const int nw = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
-  for (int base = 0, r = 0; base < n_tiles; base += nw, ++r) {
+  for (int base = t_begin, r = 0; base < t_end; base += nw, ++r) {
     const int t = base + ((r & 1) ? nw - 1 - gw : gw);
-    if (t >= n_tiles) break;  // the last, partial round
+    if (t >= t_end) break;  // the last, partial round
     const GemvTile tl = tiles[t];
     const int ii = __builtin_amdgcn_readfirstlane((int)tl.item);
     const int row0 = __builtin_amdgcn_readfirstlane((int)tl.row0);
     const GemvItem it = items[ii];
-    const int fmt = ONLY ? ONLY : __builtin_amdgcn_readfirstlane(it.fmt);
+    constexpr int fmt = ONLY;
     float y[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) y[b] = 0.0f;

@@ -14,7 +14,7 @@ namespace qk {
 namespace {
 // Grid of a persistent grouped launch: every CU filled to the kernel's occupancy.
 // Cached per variant and device (one device per process in practice).
-int grouped_grid(const void* kernel, int variant) {
+int grouped_grid(const void* kernel, int variant) {  // variant = format 1..5
   static int cached_dev[6] = {-1, -1, -1, -1, -1, -1}, cached_grid[6] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -28,10 +28,14 @@ int grouped_grid(const void* kernel, int variant) {
 }
 
 template <int NB, int ONLY>
-hipError_t launch_grouped_variant(const void* plan, const V8Table& v8, float gain, hipStream_t s) {
+hipError_t launch_grouped_variant(const PlanHeader& h, const void* plan, const V8Table& v8, float gain,
+                                  hipStream_t s) {
+  const int t0 = h.fmt_begin[ONLY], t1 = h.fmt_begin[ONLY + 1];
+  if (t1 <= t0) return hipSuccess;
   const int grid = grouped_grid((const void*)k_gemv_grouped<NB, ONLY>, ONLY);
   if (grid <= 0) return hipErrorInvalidDevice;
-  hipLaunchKernelGGL((k_gemv_grouped<NB, ONLY>), dim3(grid), dim3(256), 0, s, (const uint8_t*)plan, v8, gain);
+  hipLaunchKernelGGL((k_gemv_grouped<NB, ONLY>), dim3(grid), dim3(256), 0, s, (const uint8_t*)plan, t0, t1, v8,
+                     gain);
   return hipGetLastError();
 }
 }  // namespace
@@ -60,14 +64,14 @@ hipError_t QK_CAT(launch_grouped_b, QGEMV_NB)(const PlanHeader& h, const void* p
   V8Table v8;
   float gain = 0.0f;
   if (h.fmt_mask & (1 << QFMT_TRELLIS2)) trellis_tables(&v16, &v8, &gain);
-  switch (h.fmt_mask) {
-    case 1 << QFMT_SIGN1: return launch_grouped_variant<NB, QFMT_SIGN1>(plan, v8, gain, s);
-    case 1 << QFMT_INT2: return launch_grouped_variant<NB, QFMT_INT2>(plan, v8, gain, s);
-    case 1 << QFMT_INT4: return launch_grouped_variant<NB, QFMT_INT4>(plan, v8, gain, s);
-    case 1 << QFMT_TERN_B3: return launch_grouped_variant<NB, QFMT_TERN_B3>(plan, v8, gain, s);
-    case 1 << QFMT_TRELLIS2: return launch_grouped_variant<NB, QFMT_TRELLIS2>(plan, v8, gain, s);
-    default: return launch_grouped_variant<NB, 0>(plan, v8, gain, s);
-  }
+  // one launch per format present, in stream order
+  hipError_t e = hipSuccess;
+  if (e == hipSuccess) e = launch_grouped_variant<NB, QFMT_TERN_B3>(h, plan, v8, gain, s);
+  if (e == hipSuccess) e = launch_grouped_variant<NB, QFMT_INT2>(h, plan, v8, gain, s);
+  if (e == hipSuccess) e = launch_grouped_variant<NB, QFMT_SIGN1>(h, plan, v8, gain, s);
+  if (e == hipSuccess) e = launch_grouped_variant<NB, QFMT_INT4>(h, plan, v8, gain, s);
+  if (e == hipSuccess) e = launch_grouped_variant<NB, QFMT_TRELLIS2>(h, plan, v8, gain, s);
+  return e;
 }
 
 #if QGEMV_NB == 1

@@ -9,7 +9,7 @@
 namespace qk {
 
 // ---- format geometry ---------------------------------------------------------------
-__host__ __device__ inline int32_t scale_block(int32_t fmt) {
+__host__ __device__ constexpr int32_t scale_block(int32_t fmt) {
   switch (fmt) {
     case QFMT_TERN_B3: return 256;
     case QFMT_INT2: return 32;
@@ -18,6 +18,36 @@ __host__ __device__ inline int32_t scale_block(int32_t fmt) {
     case QFMT_TRELLIS2: return 64;
   }
   return 0;
+}
+
+// Scale storage: fp16 scales sit in tiles of 64 rows x G blocks, G =
+// scale_group(fmt) (the blocks one GEMV segment spans: 1024 weights for 1-bit
+// and ternary, 512 for 2-bit and trellis, 256 for 4-bit).  Tiles follow each
+// other in row-major order over (row tile, block group); inside a tile the
+// 64 rows' G scales are row-major.  A GEMV segment of a 64-row tile therefore
+// reads one contiguous 128 G-byte run.  Slots past the last row or block are
+// zero.
+__host__ __device__ constexpr int32_t scale_group(int32_t fmt) {
+  switch (fmt) {
+    case QFMT_TERN_B3: return 4;
+    case QFMT_INT2: return 16;
+    case QFMT_SIGN1: return 8;
+    case QFMT_INT4: return 8;
+    case QFMT_TRELLIS2: return 8;
+  }
+  return 0;
+}
+__host__ __device__ inline int64_t scale_groups(int32_t fmt, int64_t cols) {
+  const int64_t nsb = cols / scale_block(fmt);
+  return (nsb + scale_group(fmt) - 1) / scale_group(fmt);
+}
+// Index of the scale of (row r, scale block b).
+__host__ __device__ inline int64_t scale_index(int32_t fmt, int64_t cols, int64_t r, int64_t b) {
+  const int64_t G = scale_group(fmt);
+  return (((r >> 6) * scale_groups(fmt, cols) + b / G) * 64 + (r & 63)) * G + b % G;
+}
+__host__ __device__ inline int64_t scales_elems(int32_t fmt, int64_t rows, int64_t cols) {
+  return (rows + 63) / 64 * scale_groups(fmt, cols) * 64 * scale_group(fmt);
 }
 
 // Packed bytes per row: bits per weight x cols / 8, ternary 52 bytes per 256.
@@ -84,7 +114,10 @@ struct alignas(8) GemvTile {
   uint32_t row0;
 };
 
-// Plan blob: header, items, tiles (16-byte aligned sections).
+// Plan blob: header, items, tiles (16-byte aligned sections).  Tiles are
+// grouped by format (format f owns tiles [fmt_begin[f], fmt_begin[f + 1]),
+// f = 1..5), longest first inside each group; a run launches one kernel per
+// format present, each compiled for that format alone.
 struct alignas(16) PlanHeader {
   uint32_t magic;   // 'QGVP'
   uint32_t version;
@@ -95,8 +128,9 @@ struct alignas(16) PlanHeader {
   int64_t items_off;
   int64_t tiles_off;
   int64_t total_bytes;
-  int64_t pad;
+  int32_t fmt_begin[8];
 };
+constexpr uint32_t kPlanVersion = 2;
 constexpr uint32_t kPlanMagic = 0x50564751u;  // "QGVP"
 
 // Codebook tables passed by value to the kernels that need them.
@@ -114,11 +148,15 @@ hipError_t launch_quantize(int fmt, const float* w, int rows, int cols, uint8_t*
                            int64_t row_bytes, uint16_t* scales, hipStream_t s);
 hipError_t launch_pack(int fmt, const int8_t* levels, int rows, int cols, uint8_t* codes,
                        int64_t row_bytes, hipStream_t s);
+hipError_t launch_scales_from_rows(int fmt, int rows, int cols, const uint16_t* rowmajor, uint16_t* scales,
+                                  hipStream_t s);
+hipError_t launch_scales_to_rows(int fmt, int rows, int cols, const uint16_t* scales, uint16_t* rowmajor,
+                                hipStream_t s);
 hipError_t launch_unpack_i8(const GemvItem& it, int8_t* wq, float* dw, hipStream_t s);
 hipError_t launch_blockdots(const GemvItem& it, int32_t* out, hipStream_t s);
 #define QK_DECL_NB(n)                                                    \
   hipError_t launch_gemv_b##n(const GemvItem& it, hipStream_t s);        \
-  hipError_t launch_grouped_b##n(const PlanHeader& h, const void* plan, hipStream_t s);
+  hipError_t launch_grouped_b##n(const PlanHeader& h, const void* plan, hipStream_t s);  /* all formats */
 QK_DECL_NB(1)
 QK_DECL_NB(2)
 QK_DECL_NB(3)

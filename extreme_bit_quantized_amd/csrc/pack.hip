@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void k_quantize(int fmt, const float* __restri
     for (int i = 0; i < 128; ++i) sum += fabs((double)wb[i]);
     uint32_t* out = (uint32_t*)(rowp + (int64_t)kb * 16);
     for (int wd = 0; wd < 4; ++wd) out[wd] = plane_word([&](int k) { return wb[32 * wd + k] >= 0.0f ? 1 : 0; }, 1);
-    scales[row * nb + kb] = f64_to_f16_bits(sum / 128.0);
+    scales[scale_index(fmt, cols, row, kb)] = f64_to_f16_bits(sum / 128.0);
   } else if (fmt == QFMT_TERN_B3) {
     double sum = 0.0;
     for (int i = 0; i < 256; ++i) sum += fabs((double)wb[i]);
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void k_quantize(int fmt, const float* __restri
       return (int)fmin(fmax(r, -1.0), 1.0);
     };
     write_tern_block(tr, (uint32_t*)(rowp + (int64_t)kb * 52));
-    scales[row * nb + kb] = f64_to_f16_bits(sc);
+    scales[scale_index(fmt, cols, row, kb)] = f64_to_f16_bits(sc);
   } else {  // INT2 / INT4: nearest of L half-integer levels, ties up
     const int L = fmt == QFMT_INT2 ? 4 : 16;
     const int bits = fmt == QFMT_INT2 ? 2 : 4;
@@ -90,8 +90,52 @@ __global__ __launch_bounds__(256) void k_quantize(int fmt, const float* __restri
     const int per_word = 32 / bits;
     uint32_t* out = (uint32_t*)(rowp + (int64_t)kb * (32 * bits / 8));
     for (int wd = 0; wd < 32 / per_word; ++wd) out[wd] = plane_word([&](int k) { return code(wd * per_word + k); }, bits);
-    scales[row * nb + kb] = sh;
+    scales[scale_index(fmt, cols, row, kb)] = sh;
   }
+}
+
+// Tiled scale storage from row-major scales [rows][cols/block]: one thread per
+// slot of the tiled array; slots past the last row or block get zero.  With
+// rowmajor == nullptr only those padding slots are written.
+__global__ __launch_bounds__(256) void k_scales_from_rows(int fmt, int rows, int cols,
+                                                          const uint16_t* __restrict__ rowmajor,
+                                                          uint16_t* __restrict__ scales) {
+  const int64_t G = scale_group(fmt), ng = scale_groups(fmt, cols), nsb = cols / scale_block(fmt);
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= scales_elems(fmt, rows, cols)) return;
+  const int64_t j = id % G, rr = (id / G) % 64, g = (id / (G * 64)) % ng, rt = id / (G * 64 * ng);
+  const int64_t r = rt * 64 + rr, b = g * G + j;
+  const bool real = r < rows && b < nsb;
+  if (real && rowmajor) scales[id] = rowmajor[r * nsb + b];
+  else if (!real) scales[id] = 0;
+}
+
+// Row-major scales [rows][cols/block] from the tiled storage.
+__global__ __launch_bounds__(256) void k_scales_to_rows(int fmt, int rows, int cols,
+                                                        const uint16_t* __restrict__ scales,
+                                                        uint16_t* __restrict__ rowmajor) {
+  const int64_t nsb = cols / scale_block(fmt);
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= rows * nsb) return;
+  rowmajor[id] = scales[scale_index(fmt, cols, id / nsb, id % nsb)];
+}
+
+hipError_t launch_scales_from_rows(int fmt, int rows, int cols, const uint16_t* rowmajor, uint16_t* scales,
+                                  hipStream_t s) {
+  const int64_t n = scales_elems(fmt, rows, cols);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_scales_from_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, fmt, rows, cols,
+                     rowmajor, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_scales_to_rows(int fmt, int rows, int cols, const uint16_t* scales, uint16_t* rowmajor,
+                                hipStream_t s) {
+  const int64_t n = (int64_t)rows * (cols / scale_block(fmt));
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_scales_to_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, fmt, rows, cols,
+                     scales, rowmajor);
+  return hipGetLastError();
 }
 
 // Zero the row padding (bytes past the packed row inside the stride).
@@ -116,6 +160,8 @@ hipError_t launch_quantize(int fmt, const float* w, int rows, int cols, uint8_t*
   hipLaunchKernelGGL(k_quantize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, fmt, w, rows, cols, codes,
                      row_bytes, scales);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_scales_from_rows(fmt, rows, cols, nullptr, scales, s);  // zero the scale padding
   if (e != hipSuccess) return e;
   return zero_padding(codes, rows, cols, fmt, row_bytes, s);
 }
@@ -173,8 +219,7 @@ __global__ __launch_bounds__(256) void k_unpack_i8(GemvItem it, int8_t* __restri
   const int kb = (int)(id % nkb);
   const uint8_t* rowp = it.codes + row * it.row_bytes;
   int8_t* out = wq + row * it.cols + (int64_t)kb * 32;
-  const int nsb = it.cols / scale_block(it.fmt);
-  const uint16_t sh = it.scales[row * nsb + (kb * 32) / scale_block(it.fmt)];
+  const uint16_t sh = it.scales[scale_index(it.fmt, it.cols, row, (kb * 32) / scale_block(it.fmt))];
   const float s = __half2float(__ushort_as_half(sh));
   if (it.fmt == QFMT_TERN_B3) {
     // block of 256 = 13 words; act block kb covers words of 20 weights

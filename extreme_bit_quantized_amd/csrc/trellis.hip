@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, int oblock,
   const uint32_t b1 = g >= 1 ? rp[g - 1] : (seed & 0xFFu);
   const uint32_t b2 = g >= 2 ? rp[g - 2] : (g == 1 ? (seed & 0xFFu) : (seed >> 8));
   const uint32_t w24 = (b2 << 16) | (b1 << 8) | b0;
-  const float s = __half2float(__ushort_as_half(it.scales[row * (it.cols / 64) + (4 * g) / 64]));
+  const float s = __half2float(__ushort_as_half(it.scales[scale_index(QFMT_TRELLIS2, it.cols, row, (4 * g) / 64)]));
   float v[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

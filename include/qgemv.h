@@ -20,8 +20,10 @@
  *     run on the host before any HIP call, so a rejected call has no effect on
  *     the GPU.  QERR_HIP means a launch failed.  No exception crosses the ABI.
  *   - Calls are reentrant and keep no state between calls.
- *   - Formats are dense row-major: weight row n is `row_bytes` bytes at
- *     codes + n*row_bytes; scales are fp16 bit patterns [rows][cols/block].
+ *   - Codes are dense row-major: weight row n is `row_bytes` bytes at
+ *     codes + n*row_bytes.  Scales are fp16 bit patterns in the tiled order
+ *     described at qfmt_scales_bytes (convert with qweight_set_scales /
+ *     qweight_get_scales).
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -86,6 +88,20 @@ int64_t qfmt_packed_row_bytes(int32_t fmt, int32_t cols);
 /* Minimum legal row stride: packed bytes rounded up to 16. */
 int64_t qfmt_row_bytes(int32_t fmt, int32_t cols);
 
+/* Scale storage.  The scale of (row r, block b), b < cols/block, lives at
+ *   index ((r / 64 * NG + b / G) * 64 + r % 64) * G + b % G
+ * with G = qfmt_scale_group(fmt) and NG = ceil((cols/block) / G): tiles of
+ * 64 rows x G blocks, tiles in row-major order over (row tile, block group),
+ * each tile row-major.  G is the blocks of one GEMV segment (1024 weights for
+ * TERN_B3 and SIGN1, 512 for INT2 and TRELLIS2, 256 for INT4), so one
+ * segment of a 64-row tile reads one contiguous run of 128 G bytes instead of
+ * 2 G bytes from each of 64 rows.  Slots with r >= rows or b >= cols/block
+ * must be zero (qweight_quantize and qweight_set_scales write them).
+ * qfmt_scales_bytes: bytes of that array (rows, cols as in qweight_t); <0 on
+ * bad arguments. */
+int32_t qfmt_scale_group(int32_t fmt);
+int64_t qfmt_scales_bytes(int32_t fmt, int32_t rows, int32_t cols);
+
 /* Packed-weight descriptor.  All pointers (device). */
 typedef struct qweight {
   int32_t fmt;            /* QFMT_* */
@@ -94,7 +110,7 @@ typedef struct qweight {
   int32_t block;          /* must equal qfmt_scale_block(fmt) */
   const void* codes;      /* [rows][row_bytes] bytes, 16-byte aligned */
   int64_t row_bytes;      /* stride, a multiple of 16, >= qfmt_packed_row_bytes */
-  const uint16_t* scales; /* [rows][cols/block] fp16, 4-byte aligned */
+  const uint16_t* scales; /* qfmt_scales_bytes bytes, tiled (above), 16-byte aligned */
   const uint16_t* seeds;  /* [rows] uint16 trellis seeds; TRELLIS2 only, else NULL */
 } qweight_t;
 
@@ -112,10 +128,17 @@ int qweight_check(const qweight_t* w);
  *   SIGN1:   bit = (w >= 0), s = mean |w| per 128-block.
  * Sums run in index order; stored scale = fp16 (round to nearest even).
  * Output codes [rows][row_bytes] (16-byte aligned, padding zeroed) and
- * scales [rows][cols/block].  TRELLIS2 is not a quantizer target
- * (QERR_UNSUPPORTED_FMT). */
+ * scales (qfmt_scales_bytes, tiled, padding zeroed).  TRELLIS2 is not a
+ * quantizer target (QERR_UNSUPPORTED_FMT). */
 int qweight_quantize(int32_t fmt, const float* w, int32_t rows, int32_t cols,
                      void* codes, int64_t row_bytes, uint16_t* scales, void* stream);
+
+/* Write w->scales (device, tiled) from row-major fp16 scales rowmajor
+ * [rows][cols/block] (device); padding slots are zeroed.  Only w's geometry and
+ * scales pointer are used. */
+int qweight_set_scales(const qweight_t* w, const uint16_t* rowmajor, void* stream);
+/* Read w->scales back as row-major rowmajor [rows][cols/block] (device). */
+int qweight_get_scales(const qweight_t* w, uint16_t* rowmajor, void* stream);
 
 /* Pack per-weight integer codes levels [rows][cols] int8 (device) into the
  * format's bytes: TERN_B3 trits -1..1; INT2 0..3; SIGN1 0..1; INT4 0..15;

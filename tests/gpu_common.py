@@ -25,6 +25,17 @@ def host(t, dtype=None):
     return a.view(dtype) if dtype is not None else a
 
 
+def gpu_scales_rowmajor(pw):
+    """The packed matrix's scales read back as row-major fp16 bits [rows][cols/block]."""
+    import torch
+
+    import extreme_bit_quantized_amd as ebq
+
+    out = torch.empty((pw.rows, pw.cols // ebq.qfmt_scale_block(pw.fmt)), dtype=torch.int16, device="cuda")
+    ebq.qweight_get_scales(pw, out)
+    return host(out).view(np.uint16)
+
+
 def raw_weight(fmt, N, K, seed):
     """Raw draws for one matrix: floats for the quantized formats, integer
     codes + fp16 scales (+ seeds) for ternary-from-trits and trellis."""
@@ -52,7 +63,7 @@ def gpu_weight(fmt, raw, N, K):
         ebq.qweight_quantize(fmt, dev(raw["w"]), pw)
     else:
         ebq.qweight_pack(fmt, dev(raw["codes"]), pw)
-        pw.scales.copy_(dev(raw["scales"]))
+        ebq.qweight_set_scales(pw, dev(raw["scales"]))
         if raw.get("seeds") is not None:
             pw.seeds.copy_(dev(raw["seeds"]))
     return pw

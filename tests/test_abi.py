@@ -66,6 +66,27 @@ def test_binding_signatures_match_header(ebq):
     assert checked >= 15, checked
 
 
+def test_scale_storage_geometry(ebq, qref):
+    """Scale groups are one GEMV segment; sizes follow the tiled formula and
+    equal the plain [rows][cols/block] size when nothing is padded."""
+    seg = {ebq.QFMT_TERN_B3: 1024, ebq.QFMT_INT2: 512, ebq.QFMT_SIGN1: 1024, ebq.QFMT_INT4: 256,
+           ebq.QFMT_TRELLIS2: 512}
+    for fmt in qref.FORMATS:
+        blk = qref.scale_block(fmt)
+        G = ebq.qfmt_scale_group(fmt)
+        assert G * blk == seg[fmt]
+        for N, K in ((1, 256), (64, 5120), (100, 1280), (17408, 5120), (5120, 17408), (6144, 5120)):
+            if K % blk:
+                continue
+            nsb = K // blk
+            tiled = -(-N // 64) * -(-nsb // G) * 64 * G * 2
+            assert ebq.qfmt_scales_bytes(fmt, N, K) == tiled
+            if N % 64 == 0 and nsb % G == 0:
+                assert tiled == N * nsb * 2
+    assert ebq.load().qfmt_scales_bytes(9, 64, 256) == -2
+    assert ebq.load().qfmt_scales_bytes(ebq.QFMT_INT2, 64, 48) == -3
+
+
 def test_geometry_agrees_with_oracle(ebq, qref):
     for fmt in qref.FORMATS:
         assert ebq.qfmt_scale_block(fmt) == qref.scale_block(fmt)
@@ -155,8 +176,13 @@ def test_grouped_plan_on_host(ebq):
     got = sorted(map(tuple, tiles.tolist()))
     want = sorted((i, r) for i, (_, n, _) in enumerate(shapes) for r in range(0, n, 64))
     assert got == want
-    # within one format, tiles come longest first
+    # tiles are grouped by format: format f owns [fmt_begin[f], fmt_begin[f + 1])
     fmt_of = [s[0] for s in shapes]
+    fb = np.frombuffer(h[48:80].tobytes(), dtype=np.int32)
+    assert fb[1] == 0 and fb[6] == ntiles
+    for k, (i, r) in enumerate(tiles.tolist()):
+        assert fb[fmt_of[i]] <= k < fb[fmt_of[i] + 1]
+    # within one format, tiles come longest first
     for f in set(fmt_of):
         costs = [min(64, shapes[i][1] - r) * (descs[i].row_bytes + shapes[i][2] // descs[i].block * 2)
                  for i, r in tiles.tolist() if fmt_of[i] == f]

@@ -6,8 +6,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import (INT2, INT4, NAMES, SIGN1, TERN, TRELLIS, assert_close_terms, dev, gpu_act, gpu_weight,
-                        host, oracle_weight, raw_weight)
+from gpu_common import (INT2, INT4, NAMES, SIGN1, TERN, TRELLIS, assert_close_terms, dev, gpu_act, gpu_scales_rowmajor,
+                        gpu_weight, host, oracle_weight, raw_weight)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +81,32 @@ def test_quantize_pack_bit_exact(fmt, N, K):
     _sync()
     rp, rs, _ = oracle_weight(fmt, raw)
     assert (host(pw.codes) == rp).all(), NAMES[fmt]
-    assert (host(pw.scales).view(np.uint16) == rs).all(), NAMES[fmt]
+    assert (gpu_scales_rowmajor(pw) == rs).all(), NAMES[fmt]
+
+
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("N,K", [(64, 1024), (70, 1280), (1, 256), (130, 4352)])
+def test_scale_storage_layout(fmt, N, K):
+    """Tiled scale storage: every slot where the header's index formula puts it,
+    padding zero, and the row-major round trip exact."""
+    if K % oracle.scale_block(fmt):
+        pytest.skip("K not a multiple of the scale block")
+    nsb = K // oracle.scale_block(fmt)
+    G = ebq.qfmt_scale_group(fmt)
+    NG = -(-nsb // G)
+    rm = synth.uniform_f16([185, fmt, N, K], (N, nsb), 0.01, 0.1)
+    pw = ebq.PackedWeight.empty(fmt, N, K)
+    pw.scales.fill_(-1)                                      # padding must be rewritten
+    ebq.qweight_set_scales(pw, dev(rm))
+    _sync()
+    tiled = host(pw.scales).view(np.uint16)
+    assert tiled.size * 2 == ebq.qfmt_scales_bytes(fmt, N, K) == -(-N // 64) * NG * 64 * G * 2
+    want = np.zeros_like(tiled)
+    for r in range(N):
+        for b in range(nsb):
+            want[((r // 64 * NG + b // G) * 64 + r % 64) * G + b % G] = rm[r, b]
+    assert (tiled == want).all(), NAMES[fmt]
+    assert (gpu_scales_rowmajor(pw) == rm).all(), NAMES[fmt]
 
 
 @pytest.mark.parametrize("fmt", ALL)
