@@ -22,6 +22,8 @@ The same line carries:
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -228,22 +230,29 @@ def cpu_baseline(ebq, stack):
         rq, rd, _ = oracle.act_quant(x, 32)
         prep.append((fmt, packed, sc, K, rq, rd))
     nbytes = sum(p.nbytes + s.nbytes for _, p, s, _, _, _ in prep)
+    # the layer's GEMVs, repeated until about 10 s of CPU work have been timed
+    reps = 0
     t0 = time.perf_counter()
-    outs = [oracle.gemv(fmt, p, s, None, K, rq, rd) for fmt, p, s, K, rq, rd in prep]
-    dt = time.perf_counter() - t0
+    while True:
+        outs = [oracle.gemv(fmt, p, s, None, K, rq, rd) for fmt, p, s, K, rq, rd in prep]
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0:
+            break
     # full-layer parity of the GPU result against the oracle
     ok = True
     for (yr, absT, _), y in zip(outs, stack.y[layer]):
         yg = y.cpu().numpy().astype(np.float64)
         ok &= bool((np.abs(yg - yr) <= 1e-4 * absT).all())
     return {
-        "value": round(nbytes / dt / 1e9, 4),
+        "value": round(nbytes * reps / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "one full layer (7 matrices, %d weights, %d bytes) of the 1-bit stack at batch 1, "
-                  "OpenMP over rows; %.2f s" % (sum(p.shape[0] * K for _, p, _, K, _, _ in prep), nbytes, dt),
-        "equiv_tok_s": round(1.0 / (dt * stack.layers), 6),
+        "sample": "layer 0 of the 1-bit stack (7 matrices, %d weights, %d bytes) at batch 1, its 7 GEMVs run %d "
+                  "times (OpenMP over rows): %.2f s" % (sum(p.shape[0] * K for _, p, _, K, _, _ in prep), nbytes,
+                                                       reps, dt),
+        "equiv_tok_s": round(reps / (dt * stack.layers), 6),
         "layer_parity": "ok" if ok else "FAIL",
     }
 
@@ -381,14 +390,85 @@ def bench_copy_ceiling(reps):
 
 # ---------------------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------------------
+# measured HBM traffic of the headline kernel (rocprofv3 byte counters)
+# ---------------------------------------------------------------------------------------
+
+# Sources whose change invalidates recorded counters.
+GEMV_SOURCES = ("extreme_bit_quantized_amd/csrc/gemv_impl.hpp", "extreme_bit_quantized_amd/csrc/gemv_inst.hip",
+                "extreme_bit_quantized_amd/csrc/internal.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_grouped_sign1_64layer_stack_b1.traffic.json")
+HEADLINE_KERNEL = "k_gemv_grouped<1, 3>"  # batch 1, 1-bit (format code 3)
+
+
+def gemv_source_hash():
+    h = hashlib.sha256()
+    for p in GEMV_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per headline launch from the recorded counters, or None when
+    none are recorded or the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != gemv_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def _counter_rows(run_dir, counter):
+    out = []
+    for root, _, files in os.walk(run_dir):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    out += [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    return out
+
+
+def record_traffic(fetch_dir, write_dir):
+    """Write TRAFFIC_FILE from two rocprofv3 --pmc runs of `bench.py --quick`
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled by
+    what it reads for the run's 1 GiB device copy (2^30 bytes read and written)."""
+    rec = {"kernel": HEADLINE_KERNEL, "source_sha256": gemv_source_hash()}
+    total = 0.0
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, name)
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        kern = [float(r["Counter_Value"]) for r in rows if HEADLINE_KERNEL in r["Kernel_Name"]]
+        if not copies or not kern:
+            raise SystemExit("no %s rows for the copy or the headline kernel under %s" % (name, d))
+        factor = (1 << 30) / 1024.0 / max(copies)       # the largest copy is the 1 GiB one
+        kib = sum(kern) / len(kern)
+        rec[name] = {"kib_per_dispatch": kib, "dispatches": len(kern), "copy_kib": max(copies),
+                     "scale_factor": round(factor, 4), "bytes_per_launch": kib * 1024.0 * factor}
+        total += kib * 1024.0 * factor
+    rec["traffic_bytes_per_launch"] = round(total)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--quick", action="store_true", help="headline only (no secondary workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="record the headline kernel's HBM bytes from two rocprofv3 --pmc output folders and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
@@ -443,7 +523,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "bytes_per_launch": gemv_bytes,
             "avg_launch_us": round(t_kern * 1e6, 2),
             "median_launch_us": round(t_kern_med * 1e6, 2),
@@ -452,7 +532,7 @@ def main():
     extra = {}
     if not args.quick:
         try:
-            reps = max(5, args.steps // 2)
+            reps = min(30, max(5, args.steps // 2))
             extra["dependent_chain_hipgraph"] = {}
             t_chain = bench_dependent_chain(ebq, stack, reps)
             extra["dependent_chain_hipgraph"] = {
@@ -470,7 +550,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.quick:
-        reps = max(5, args.steps // 2)
+        reps = min(30, max(5, args.steps // 2))
         for B in (1, 8):
             log("mixed stack B=%d" % B)
             ms = Stack(ebq, "mixed", synth.N_LAYERS, B)
