@@ -301,7 +301,8 @@ def test_unpack_i8(fmt):
 
 
 @pytest.mark.parametrize("kblock", [256, 32])
-@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (17, 130, 512), (200, 64, 1024), (128, 257, 2048)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (17, 130, 512), (200, 64, 1024), (128, 257, 2048),
+                                   (300, 200, 1024), (513, 1300, 512), (256, 128, 1280)])
 def test_gemm_parity(kblock, M, N, K):
     xq = synth.integers([220, M, K], (M, K), -127, 127).astype(np.int8)
     wq = synth.integers([221, N, K], (N, K), -127, 127).astype(np.int8)
@@ -312,6 +313,27 @@ def test_gemm_parity(kblock, M, N, K):
     _sync()
     yr, absT = oracle.gemm_i8(xq, dx, wq, dw, kblock)
     assert_close_terms(host(y), yr, absT, what="gemm %dx%dx%d/%d" % (M, N, K, kblock))
+
+
+def test_gemm_full_size_sampled():
+    """The prefill GEMM at its benchmark shape (2048 x 17408 x 5120, 256-blocks),
+    checked on sampled rows and columns against the oracle."""
+    M, N, K = 2048, 17408, 5120
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.seed64(240))
+    xq = torch.randint(-127, 128, (M, K), generator=g, device="cuda", dtype=torch.int8)
+    wq = torch.randint(-127, 128, (N, K), generator=g, device="cuda", dtype=torch.int8)
+    dx = torch.rand((M, K // 256), generator=g, device="cuda") * 0.1 + 1e-3
+    dw = torch.rand((N, K // 256), generator=g, device="cuda") * 0.1 + 1e-3
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ebq.qgemm_i8(xq, dx, wq, dw, 256, y)
+    _sync()
+    rng = np.random.default_rng(241)
+    rows = np.sort(np.concatenate([[0, M - 1], rng.choice(M, 30, replace=False)]))
+    cols = np.sort(np.concatenate([[0, N - 1], rng.choice(N, 94, replace=False)]))
+    yr, absT = oracle.gemm_i8(host(xq)[rows], host(dx)[rows], host(wq)[cols], host(dw)[cols], 256)
+    assert_close_terms(host(y)[np.ix_(rows, cols)], yr, absT, what="gemm full size, sampled")
+    assert np.isfinite(host(y)).all()
 
 
 def test_prefill_pipeline_small():
