@@ -142,12 +142,16 @@ __global__ __launch_bounds__(256) void k_gemm_i8(const int8_t* __restrict__ xq, 
 // MFMA 32x32x32 tiles).  K advances 64 at a time.  Each stage (256 + 128 rows
 // of 64 bytes, 3 x 16 bytes per thread) is loaded into registers two stages
 // ahead, written to a double-buffered LDS tile and read back as MFMA operands.
-// A row's four 16-byte chunks are stored XOR-swizzled by (row >> 1) & 3, so the
-// 8 lanes of each 16-byte LDS access phase (rows r..r+7, one chunk) hit 8
-// different bank groups.  dx / dw of a 256-block go through a 2-slot LDS ring,
-// loaded at the previous block's first stage.  Tiles are numbered so that the
-// M tiles of one N tile (which share a weight slab) run on the same XCD
-// (workgroups are dealt to the 8 XCDs round robin).
+// A row's four 16-byte chunks are stored XOR-swizzled by (row >> 2) & 3.  gfx950
+// LDS behaves as 64 four-byte banks with a 16-byte access served 16 lanes at a
+// time, so the 16 lanes of a phase (rows r..r+15, one chunk) must land in 16
+// different 16-byte slots modulo 256 bytes: (row % 4, chunk ^ ((row >> 2) % 4))
+// does that (measured: no conflicts; (row >> 1) & 3 gave one conflict cycle per
+// access cycle, no swizzle three).  dx / dw of a 256-block go through a 2-slot
+// LDS ring, loaded at the previous block's first stage.  Workgroups are dealt to
+// the 8 XCDs round robin; each XCD takes a contiguous run of the tiles in M-major
+// order, so an XCD keeps one 256-row activation slab in its L2 while the XCDs
+// walk the weight slabs in step (shared through the last-level cache).
 constexpr int PBM = 256, PBN = 128, PBK = 64, PTHREADS = 512;
 
 __global__ __launch_bounds__(PTHREADS)
@@ -160,8 +164,10 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
   __shared__ __attribute__((aligned(16))) float Sw[2][PBN];
 
   const int b = blockIdx.x, xcd = b & 7, kx = b >> 3;
-  const int nt = xcd + 8 * (kx / m_tiles), mt = kx % m_tiles;
-  if (nt >= n_tiles) return;
+  const int per = (m_tiles * n_tiles + 7) / 8;
+  const int t = xcd * per + kx;
+  if (kx >= per || t >= m_tiles * n_tiles) return;
+  const int mt = t / n_tiles, nt = t % n_tiles;
   const int m0 = mt * PBM, n0 = nt * PBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -178,10 +184,10 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
   for (int j = 0; j < 2; ++j) {
     const int r = lr + 128 * j;
     asrc[j] = xq + (int64_t)min(m0 + r, M - 1) * K + lc * 16;
-    adst[j] = r * PBK + ((lc ^ ((r >> 1) & 3)) << 4);
+    adst[j] = r * PBK + ((lc ^ ((r >> 2) & 3)) << 4);
   }
   const int8_t* bsrc = wq + (int64_t)min(n0 + lr, N - 1) * K + lc * 16;
-  const int bdst = lr * PBK + ((lc ^ ((lr >> 1) & 3)) << 4);
+  const int bdst = lr * PBK + ((lc ^ ((lr >> 2) & 3)) << 4);
   // scales: threads 0..255 carry dx rows, 256..383 dw rows
   const bool sx_thr = tid < PBM, sw_thr = tid >= PBM && tid < PBM + PBN;
   const float* ssrc = sx_thr ? dx + (int64_t)min(m0 + tid, M - 1) * nkb
@@ -212,9 +218,9 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = wm * 64 + 32 * i + l32;
-      aoff[i][kk] = r * PBK + ((c ^ ((r >> 1) & 3)) << 4);
+      aoff[i][kk] = r * PBK + ((c ^ ((r >> 2) & 3)) << 4);
       const int rn = wn * 64 + 32 * i + l32;
-      boff[i][kk] = rn * PBK + ((c ^ ((rn >> 1) & 3)) << 4);
+      boff[i][kk] = rn * PBK + ((c ^ ((rn >> 2) & 3)) << 4);
     }
   }
 
@@ -305,7 +311,7 @@ hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* w
   // 256-blocks: the pipelined kernel.
   if (kblock == 256) {
     const int n_tiles = (N + PBN - 1) / PBN, m_tiles = (M + PBM - 1) / PBM;
-    const int blocks = 8 * ((n_tiles + 7) / 8) * m_tiles;
+    const int blocks = 8 * ((n_tiles * m_tiles + 7) / 8);
     hipLaunchKernelGGL(k_gemm_i8_p256, dim3(blocks), dim3(PTHREADS), 0, s, xq, dx, M, wq, dw, N, K, y, n_tiles,
                        m_tiles);
     return hipGetLastError();

@@ -502,14 +502,16 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   // the lanes that would own them compute on it and store nothing.
   // Tile loads go straight to LDS (global_load_lds_dwordx4): load i puts lane
   // l's 16 bytes at slot 64 i + l of this wave's region.  For 8-chunk segments
-  // slot s holds row s / 8, chunk (s % 8) ^ (row % 8), so lane r reading its
-  // chunk k from slot 8 r + (k ^ (r % 8)) never has two lanes of a read phase
-  // in one bank group; 13-chunk segments are plain row-major (an odd pitch is
-  // conflict free).  Each load instruction still covers whole 128-byte lines.
+  // slot s holds row s / 8, chunk (s % 8) ^ ((row / 2) % 8), so lane r reads its
+  // chunk k from slot 8 r + (k ^ ((r / 2) % 8)): the 16 lanes of a 16-byte read
+  // phase then hit 16 different 16-byte slots modulo 256 bytes (gfx950 LDS: 64
+  // four-byte banks), where (k ^ (r % 8)) pairs lanes r and r + 8 on one slot.
+  // 13-chunk segments are plain row-major (13 is odd: conflict free).  Each
+  // load instruction still covers whole 128-byte lines.
   auto tile_off = [&](int i) -> uint32_t {
     const int f = i * 64 + lane;
     const int r = f / CH, pos = f % CH;
-    const int c = CH == 8 ? (pos ^ (r & 7)) : pos;
+    const int c = CH == 8 ? (pos ^ ((r >> 1) & 7)) : pos;
     return (uint32_t)(min(r, nvalid - 1) * rb + c * 16);
   };
   // Batches up to 2 keep the offsets in registers; larger batches, short of
@@ -537,7 +539,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   auto read_row = [&](uint32_t (&T)[CH * 4]) {
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const int off = CH == 8 ? lane * 128 + ((k ^ (lane & 7)) << 4) : lane * (CH * 16) + 16 * k;
+      const int off = CH == 8 ? lane * 128 + ((k ^ ((lane >> 1) & 7)) << 4) : lane * (CH * 16) + 16 * k;
       const u32x4 v = *(const u32x4*)(lds + off);
       T[4 * k] = v.x;
       T[4 * k + 1] = v.y;
