@@ -17,6 +17,7 @@ namespace qk {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int GBM = 128, GBN = 128, GBK = 64, GPITCH = 80;
 
@@ -139,29 +140,60 @@ __global__ __launch_bounds__(256) void k_gemm_i8(const int8_t* __restrict__ xq, 
 
 // ---- pipelined GEMM for 256-blocks ---------------------------------------------------------------
 // Workgroup tile 256 (M) x 128 (N), 8 waves (two per SIMD) of 64 x 64 (2 x 2
-// MFMA 32x32x32 tiles).  K advances 64 at a time.  Each stage (256 + 128 rows
-// of 64 bytes, 3 x 16 bytes per thread) is loaded into registers two stages
-// ahead, written to a double-buffered LDS tile and read back as MFMA operands.
-// A row's four 16-byte chunks are stored XOR-swizzled by (row >> 2) & 3.  gfx950
-// LDS behaves as 64 four-byte banks with a 16-byte access served 16 lanes at a
-// time, so the 16 lanes of a phase (rows r..r+15, one chunk) must land in 16
-// different 16-byte slots modulo 256 bytes: (row % 4, chunk ^ ((row >> 2) % 4))
-// does that (measured: no conflicts; (row >> 1) & 3 gave one conflict cycle per
-// access cycle, no swizzle three).  dx / dw of a 256-block go through a 2-slot
-// LDS ring, loaded at the previous block's first stage.  Workgroups are dealt to
-// the 8 XCDs round robin; each XCD takes a contiguous run of the tiles in M-major
-// order, so an XCD keeps one 256-row activation slab in its L2 while the XCDs
-// walk the weight slabs in step (shared through the last-level cache).
-constexpr int PBM = 256, PBN = 128, PBK = 64, PTHREADS = 512;
+// MFMA 32x32x32 tiles).  K advances 64 at a time through a 4-stage LDS ring
+// filled by LDS DMA (global_load_lds_dwordx4, no staging registers): each stage
+// holds 256 A rows then 128 B rows of 64 bytes.  A row's four 16-byte chunks
+// are stored XOR-swizzled by (row >> 2) & 3.  gfx950 LDS behaves as 64
+// four-byte banks with a 16-byte access served 16 lanes at a time, so the 16
+// lanes of an MFMA operand read phase (rows r..r+15, one chunk) must land in 16
+// different 16-byte slots modulo 256 bytes, which (row % 4, chunk ^ ((row >> 2)
+// % 4)) does (measured: no conflicts; (row >> 1) & 3 gave one conflict cycle per
+// access cycle, no swizzle three).  Every wave issues 3 ring DMA instructions
+// per stage, so "stage s has landed" is a fixed vmcnt (extra loads issued in
+// between only make that wait stricter); the ring is ordered by a plain
+// s_barrier (a __syncthreads() fence would wait for every DMA in flight).  The
+// dx / dw values of four consecutive 256-blocks (16 bytes of each row) are
+// DMA'd once per 16 stages into a 2-slot ring and read by the epilogue in one
+// asm block that waits for its own reads (so the compiler adds no wait for the
+// DMAs in flight).  Workgroups are dealt to the 8 XCDs round robin; each XCD
+// takes a contiguous run of the tiles in M-major order, so an XCD keeps one
+// 256-row activation slab in its L2 while the XCDs walk the weight slabs in
+// step (shared through the last-level cache).
+constexpr int PBM = 256, PBN = 128, PBK = 64, PTHREADS = 512, PST = 4;
+constexpr int RING_B = PBM * PBK;             // B rows start here inside a stage
+constexpr int RING_STAGE = (PBM + PBN) * PBK; // 24 KB
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+// s_waitcnt vmcnt(n) (n < 64) and lgkmcnt(0)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+}
+// Workgroup barrier that the compiler may not move memory accesses across (the
+// builtin alone carries no memory ordering) and that adds no wait of its own.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
 __global__ __launch_bounds__(PTHREADS)
 void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx, int M,
                     const int8_t* __restrict__ wq, const float* __restrict__ dw, int N, int K,
                     float* __restrict__ y, int n_tiles, int m_tiles) {
-  __shared__ __attribute__((aligned(16))) int8_t As[2][PBM * PBK];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[2][PBN * PBK];
-  __shared__ __attribute__((aligned(16))) float Sx[2][PBM];
-  __shared__ __attribute__((aligned(16))) float Sw[2][PBN];
+  __shared__ __attribute__((aligned(1024))) int8_t R0[RING_STAGE], R1[RING_STAGE], R2[RING_STAGE], R3[RING_STAGE];
+  __shared__ __attribute__((aligned(16))) float Sx[2][PBM][4];
+  __shared__ __attribute__((aligned(16))) float Sw[2][PBN][4];
+  int8_t* const ring[PST] = {R0, R1, R2, R3};
 
   const int b = blockIdx.x, xcd = b & 7, kx = b >> 3;
   const int per = (m_tiles * n_tiles + 7) / 8;
@@ -169,44 +201,37 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
   if (kx >= per || t >= m_tiles * n_tiles) return;
   const int mt = t / n_tiles, nt = t % n_tiles;
   const int m0 = mt * PBM, n0 = nt * PBN;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int nkb = K / 256;
+  const int nkb = K / 256, nst = K / PBK, ngroups = nkb / 4;
 
-  // This thread's loads: A rows (tid >> 2) and 128 + (tid >> 2), B row (tid >> 2),
-  // 16-byte chunk tid & 3; rows clamped into the matrix (clamped rows are
-  // computed and never stored).
-  const int lr = tid >> 2, lc = tid & 3;
+  // DMA sources of this lane: wave w fills A rows 32 w + 16 j + lane / 4 (j < 2)
+  // and B rows 16 w + lane / 4, chunk lane % 4 (swizzled); rows clamped into
+  // the matrix (clamped rows are computed and never stored).
   const int8_t* asrc[2];
-  int adst[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int r = lr + 128 * j;
-    asrc[j] = xq + (int64_t)min(m0 + r, M - 1) * K + lc * 16;
-    adst[j] = r * PBK + ((lc ^ ((r >> 2) & 3)) << 4);
+    const int r = 32 * wave + 16 * j + (lane >> 2);
+    asrc[j] = xq + (int64_t)min(m0 + r, M - 1) * K + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
   }
-  const int8_t* bsrc = wq + (int64_t)min(n0 + lr, N - 1) * K + lc * 16;
-  const int bdst = lr * PBK + ((lc ^ ((lr >> 2) & 3)) << 4);
-  // scales: threads 0..255 carry dx rows, 256..383 dw rows
-  const bool sx_thr = tid < PBM, sw_thr = tid >= PBM && tid < PBM + PBN;
-  const float* ssrc = sx_thr ? dx + (int64_t)min(m0 + tid, M - 1) * nkb
-                             : dw + (int64_t)min(n0 + (sw_thr ? tid - PBM : 0), N - 1) * nkb;
-  float* sdst0 = sx_thr ? &Sx[0][tid] : &Sw[0][sw_thr ? tid - PBM : 0];
-  float* sdst1 = sx_thr ? &Sx[1][tid] : &Sw[1][sw_thr ? tid - PBM : 0];
-  const bool s_thr = sx_thr || sw_thr;
-
-  v4i ra[2][2], rb[2];
-  auto gload = [&](int st, v4i (&a)[2], v4i& bb) {
-    const int k0 = min(st, K / PBK - 1) * PBK;  // past the end: reload the last stage
-#pragma unroll
-    for (int j = 0; j < 2; ++j) a[j] = *(const v4i*)(asrc[j] + k0);
-    bb = *(const v4i*)(bsrc + k0);
+  const int rbn = 16 * wave + (lane >> 2);
+  const int8_t* bsrc = wq + (int64_t)min(n0 + rbn, N - 1) * K + (((lane & 3) ^ ((rbn >> 2) & 3)) << 4);
+  // scale rows: waves 0-3 carry dx rows 64 w + lane, waves 4-5 dw rows 64 (w - 4) + lane
+  const bool sxw = wave < 4, sww = wave == 4 || wave == 5;
+  const int srow = sxw ? 64 * wave + lane : 64 * (wave & 1) + lane;
+  const float* ssrc = sxw ? dx + (int64_t)min(m0 + srow, M - 1) * nkb : dw + (int64_t)min(n0 + srow, N - 1) * nkb;
+  auto issue_scales = [&](int g) {  // group g (4 blocks) into slot g & 1
+    if (sxw) lds_dma16(ssrc + 4 * g, &Sx[g & 1][64 * wave][0]);
+    else if (sww) lds_dma16(ssrc + 4 * g, &Sw[g & 1][64 * (wave & 1)][0]);
   };
-  auto lstore = [&](int buf, const v4i (&a)[2], const v4i& bb) {
+
+  // Issue stage s (stages past the end reload the last one: same count of loads).
+  auto issue = [&](int s, int8_t* R) {
+    const int k0 = min(s, nst - 1) * PBK;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) *(v4i*)(&As[buf][adst[j]]) = a[j];
-    *(v4i*)(&Bs[buf][bdst]) = bb;
+    for (int j = 0; j < 2; ++j) lds_dma16(asrc[j] + k0, R + (2 * wave + j) * 1024);
+    lds_dma16(bsrc + k0, R + RING_B + wave * 1024);
   };
 
   // MFMA operand offsets (row r, 16-byte chunk c = 2 kk + lane / 32).
@@ -220,7 +245,7 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
       const int r = wm * 64 + 32 * i + l32;
       aoff[i][kk] = r * PBK + ((c ^ ((r >> 2) & 3)) << 4);
       const int rn = wn * 64 + 32 * i + l32;
-      boff[i][kk] = rn * PBK + ((c ^ ((rn >> 2) & 3)) << 4);
+      boff[i][kk] = RING_B + rn * PBK + ((c ^ ((rn >> 2) & 3)) << 4);
     }
   }
 
@@ -236,61 +261,90 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
         facc[i][j][e] = 0.0f;
       }
 
-  auto compute = [&](int buf) {
+  auto compute = [&](const int8_t* R) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       v4i fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = *(const v4i*)(&As[buf][aoff[i][kk]]);
+      for (int i = 0; i < 2; ++i) fa[i] = *(const v4i*)(R + aoff[i][kk]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = *(const v4i*)(&Bs[buf][boff[j][kk]]);
+      for (int j = 0; j < 2; ++j) fb[j] = *(const v4i*)(R + boff[j][kk]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
   };
-  // After the last stage of K-block kb: T = dx * dw * I into the fp32 sums.
-  auto epilogue = [&](int slot) {
-    float sw[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) sw[j] = Sw[slot][wn * 64 + 32 * j + l32];
+  // This lane's scale-row bases (bytes) in slot 0; rows 4 lhi + 32 i + 8 q + t.
+  const uint32_t xbase = lds_addr(&Sx[0][wm * 64 + 4 * lhi][0]);
+  const uint32_t wbase = lds_addr(&Sw[0][wn * 64 + l32][0]);
+  // After the last stage of 256-block kb: T = dx * dw * I into the fp32 sums.
+  auto epilogue = [&](int kb) {
+    const uint32_t so = (uint32_t)(kb & 3) * 4u;  // block kb's float inside each row's 16 bytes
+    const uint32_t xa = xbase + ((kb >> 2) & 1) * (PBM * 16) + so;
+    const uint32_t wa = wbase + ((kb >> 2) & 1) * (PBN * 16) + so;
+    v2f p[2][4][2], pw;
+    // early-clobber outputs: no result register may share the address registers,
+    // which the later reads of the block still use
+    asm volatile(
+        "ds_read2_b32 %0, %17 offset0:0 offset1:4\n\t"
+        "ds_read2_b32 %1, %17 offset0:8 offset1:12\n\t"
+        "ds_read2_b32 %2, %17 offset0:32 offset1:36\n\t"
+        "ds_read2_b32 %3, %17 offset0:40 offset1:44\n\t"
+        "ds_read2_b32 %4, %17 offset0:64 offset1:68\n\t"
+        "ds_read2_b32 %5, %17 offset0:72 offset1:76\n\t"
+        "ds_read2_b32 %6, %17 offset0:96 offset1:100\n\t"
+        "ds_read2_b32 %7, %17 offset0:104 offset1:108\n\t"
+        "ds_read2_b32 %8, %17 offset0:128 offset1:132\n\t"
+        "ds_read2_b32 %9, %17 offset0:136 offset1:140\n\t"
+        "ds_read2_b32 %10, %17 offset0:160 offset1:164\n\t"
+        "ds_read2_b32 %11, %17 offset0:168 offset1:172\n\t"
+        "ds_read2_b32 %12, %17 offset0:192 offset1:196\n\t"
+        "ds_read2_b32 %13, %17 offset0:200 offset1:204\n\t"
+        "ds_read2_b32 %14, %17 offset0:224 offset1:228\n\t"
+        "ds_read2_b32 %15, %17 offset0:232 offset1:236\n\t"
+        "ds_read2_b32 %16, %18 offset0:0 offset1:128\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(p[0][0][0]), "=&v"(p[0][0][1]), "=&v"(p[0][1][0]), "=&v"(p[0][1][1]), "=&v"(p[0][2][0]),
+          "=&v"(p[0][2][1]), "=&v"(p[0][3][0]), "=&v"(p[0][3][1]), "=&v"(p[1][0][0]), "=&v"(p[1][0][1]),
+          "=&v"(p[1][1][0]), "=&v"(p[1][1][1]), "=&v"(p[1][2][0]), "=&v"(p[1][2][1]), "=&v"(p[1][3][0]),
+          "=&v"(p[1][3][1]), "=&v"(pw)
+        : "v"(xa), "v"(wa)
+        : "memory");
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const v4f sx4 = *(const v4f*)(&Sx[slot][wm * 64 + 32 * i + 8 * q + 4 * lhi]);
+      for (int e = 0; e < 16; ++e) {
+        const float sx = p[i][e >> 2][(e & 3) >> 1][e & 1];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int e = 4 * q + t;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            facc[i][j][e] = __builtin_fmaf(sx4[t] * sw[j], (float)acc[i][j][e], facc[i][j][e]);
-            acc[i][j][e] = 0;
-          }
+        for (int j = 0; j < 2; ++j) {
+          facc[i][j][e] = __builtin_fmaf(sx * pw[j], (float)acc[i][j][e], facc[i][j][e]);
+          acc[i][j][e] = 0;
         }
       }
   };
 
-  // prologue: stages 0 and 1 in registers, block 0's scales in slot 0
-  gload(0, ra[0], rb[0]);
-  gload(1, ra[1], rb[1]);
-  if (s_thr) *sdst0 = ssrc[0];
-  float sn = 0.0f;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int s0 = 4 * kb;
+  // prologue: group 0's scales, stages 0 .. PST-2 in flight
+  issue_scales(0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = u & 1;  // stage parity: LDS buffer and register set
-      lstore(p, ra[p], rb[p]);
-      gload(s0 + u + 2, ra[p], rb[p]);
-      if (u == 0 && s_thr) sn = ssrc[min(kb + 1, nkb - 1)];
-      if (u == 2 && s_thr) *((kb & 1) ? sdst0 : sdst1) = sn;  // slot (kb + 1) & 1
-      __syncthreads();
-      compute(p);
+  for (int s = 0; s < PST - 1; ++s) issue(s, ring[s]);
+  // main loop, unrolled by the ring size so every buffer is a fixed array
+  for (int s0 = 0; s0 < nst; s0 += PST) {
+#pragma unroll
+    for (int u = 0; u < PST; ++u) {
+      const int s = s0 + u;
+      // this wave's part of stage s has landed and its reads of stage s-1 are done
+      wait_vmcnt_lgkm0<(PST - 2) * 3>();
+      ring_barrier();  // ... for every wave: stage s readable, stage s-1's buffer free
+      issue(s + PST - 1, ring[(u + PST - 1) % PST]);
+      // next group's scales: its slot was last read by the epilogues of group
+      // (s >> 4) - 1, all before this barrier
+      if (u == 0 && (s & 15) == 0 && (s >> 4) + 1 < ngroups) issue_scales((s >> 4) + 1);
+      compute(ring[u]);
+      if (u == 3) epilogue(s >> 2);
     }
-    epilogue(kb & 1);
   }
+  wait_vmcnt_lgkm0<0>();  // no DMA may still be landing when the wave ends
 
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -308,8 +362,9 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
 
 hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* wq, const float* dw, int N, int K,
                        int kblock, float* y, hipStream_t s) {
-  // 256-blocks: the pipelined kernel.
-  if (kblock == 256) {
+  // 256-blocks, K a multiple of 1024 (scales in 16-byte groups of four blocks):
+  // the pipelined kernel.
+  if (kblock == 256 && K % 1024 == 0) {
     const int n_tiles = (N + PBN - 1) / PBN, m_tiles = (M + PBM - 1) / PBM;
     const int blocks = 8 * ((n_tiles * m_tiles + 7) / 8);
     hipLaunchKernelGGL(k_gemm_i8_p256, dim3(blocks), dim3(PTHREADS), 0, s, xq, dx, M, wq, dw, N, K, y, n_tiles,
