@@ -140,26 +140,27 @@ __global__ __launch_bounds__(256) void k_gemm_i8(const int8_t* __restrict__ xq, 
 
 // ---- pipelined GEMM for 256-blocks ---------------------------------------------------------------
 // Workgroup tile 256 (M) x 128 (N), 8 waves (two per SIMD) of 64 x 64 (2 x 2
-// MFMA 32x32x32 tiles).  K advances 64 at a time through a 4-stage LDS ring
+// MFMA 32x32x32 tiles).  K advances 128 at a time through a 3-stage LDS ring
 // filled by LDS DMA (global_load_lds_dwordx4, no staging registers): each stage
-// holds 256 A rows then 128 B rows of 64 bytes.  A row's four 16-byte chunks
-// are stored XOR-swizzled by (row >> 2) & 3.  gfx950 LDS behaves as 64
+// holds 256 A rows then 128 B rows of 128 bytes.  A row's eight 16-byte chunks
+// are stored XOR-swizzled by (row >> 1) & 7.  gfx950 LDS behaves as 64
 // four-byte banks with a 16-byte access served 16 lanes at a time, so the 16
 // lanes of an MFMA operand read phase (rows r..r+15, one chunk) must land in 16
-// different 16-byte slots modulo 256 bytes, which (row % 4, chunk ^ ((row >> 2)
-// % 4)) does (measured: no conflicts; (row >> 1) & 3 gave one conflict cycle per
-// access cycle, no swizzle three).  Every wave issues 3 ring DMA instructions
-// per stage, so "stage s has landed" is a fixed vmcnt (extra loads issued in
+// different 16-byte slots modulo 256 bytes, which (row % 2, chunk ^ ((row >> 1)
+// % 8)) does (measured with 64-byte rows: the matching swizzle had no conflicts,
+// a swizzle that paired rows r and r + 8 one conflict cycle per access cycle).
+// Every wave issues 6 ring DMA instructions per stage, so "stage s has landed"
+// is a fixed vmcnt (extra loads issued in
 // between only make that wait stricter); the ring is ordered by a plain
 // s_barrier (a __syncthreads() fence would wait for every DMA in flight).  The
 // dx / dw values of four consecutive 256-blocks (16 bytes of each row) are
-// DMA'd once per 16 stages into a 2-slot ring and read by the epilogue in one
+// DMA'd once per 8 stages into a 2-slot ring and read by the epilogue in one
 // asm block that waits for its own reads (so the compiler adds no wait for the
 // DMAs in flight).  Workgroups are dealt to the 8 XCDs round robin; each XCD
 // takes a contiguous run of the tiles in M-major order, so an XCD keeps one
 // 256-row activation slab in its L2 while the XCDs walk the weight slabs in
 // step (shared through the last-level cache).
-constexpr int PBM = 256, PBN = 128, PBK = 64, PTHREADS = 512, PST = 4;
+constexpr int PBM = 256, PBN = 128, PBK = 128, PTHREADS = 512, PST = 3;
 constexpr int RING_B = PBM * PBK;             // B rows start here inside a stage
 constexpr int RING_STAGE = (PBM + PBN) * PBK; // 24 KB
 
@@ -190,10 +191,11 @@ __global__ __launch_bounds__(PTHREADS)
 void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx, int M,
                     const int8_t* __restrict__ wq, const float* __restrict__ dw, int N, int K,
                     float* __restrict__ y, int n_tiles, int m_tiles) {
-  __shared__ __attribute__((aligned(1024))) int8_t R0[RING_STAGE], R1[RING_STAGE], R2[RING_STAGE], R3[RING_STAGE];
-  __shared__ __attribute__((aligned(16))) float Sx[2][PBM][4];
-  __shared__ __attribute__((aligned(16))) float Sw[2][PBN][4];
-  int8_t* const ring[PST] = {R0, R1, R2, R3};
+  __shared__ __attribute__((aligned(1024))) int8_t R0[RING_STAGE], R1[RING_STAGE], R2[RING_STAGE];
+  // scales of four 256-blocks: rows 0..255 dx of the tile's A rows, rows
+  // 256..383 dw of its B rows (one array: the only scale DMA target)
+  __shared__ __attribute__((aligned(16))) float Sc[2][PBM + PBN][4];
+  int8_t* const ring[PST] = {R0, R1, R2};
 
   const int b = blockIdx.x, xcd = b & 7, kx = b >> 3;
   const int per = (m_tiles * n_tiles + 7) / 8;
@@ -206,46 +208,54 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
   const int wm = wave >> 1, wn = wave & 1;
   const int nkb = K / 256, nst = K / PBK, ngroups = nkb / 4;
 
-  // DMA sources of this lane: wave w fills A rows 32 w + 16 j + lane / 4 (j < 2)
-  // and B rows 16 w + lane / 4, chunk lane % 4 (swizzled); rows clamped into
-  // the matrix (clamped rows are computed and never stored).
-  const int8_t* asrc[2];
+  // DMA sources of this lane: wave w fills A rows 32 w + 8 j + lane / 8 (j < 4)
+  // and B rows 16 w + 8 j + lane / 8 (j < 2), chunk lane % 8 (swizzled); rows
+  // clamped into the matrix (clamped rows are computed and never stored).
+  const int8_t* asrc[4];
+  const int8_t* bsrc[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * wave + 8 * j + (lane >> 3);
+    asrc[j] = xq + (int64_t)min(m0 + r, M - 1) * K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int r = 32 * wave + 16 * j + (lane >> 2);
-    asrc[j] = xq + (int64_t)min(m0 + r, M - 1) * K + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
+    const int r = 16 * wave + 8 * j + (lane >> 3);
+    bsrc[j] = wq + (int64_t)min(n0 + r, N - 1) * K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
   }
-  const int rbn = 16 * wave + (lane >> 2);
-  const int8_t* bsrc = wq + (int64_t)min(n0 + rbn, N - 1) * K + (((lane & 3) ^ ((rbn >> 2) & 3)) << 4);
-  // scale rows: waves 0-3 carry dx rows 64 w + lane, waves 4-5 dw rows 64 (w - 4) + lane
-  const bool sxw = wave < 4, sww = wave == 4 || wave == 5;
+  // scale rows: waves 0-3 carry dx rows 64 w + lane, waves 4-5 dw rows
+  // 64 (w - 4) + lane, waves 6-7 repeat waves 4-5 (same bytes to the same place)
+  // so that every wave issues the same loads without a branch.
+  const bool sxw = wave < 4;
   const int srow = sxw ? 64 * wave + lane : 64 * (wave & 1) + lane;
   const float* ssrc = sxw ? dx + (int64_t)min(m0 + srow, M - 1) * nkb : dw + (int64_t)min(n0 + srow, N - 1) * nkb;
-  auto issue_scales = [&](int g) {  // group g (4 blocks) into slot g & 1
-    if (sxw) lds_dma16(ssrc + 4 * g, &Sx[g & 1][64 * wave][0]);
-    else if (sww) lds_dma16(ssrc + 4 * g, &Sw[g & 1][64 * (wave & 1)][0]);
+  const int sdst = sxw ? 64 * wave : PBM + 64 * (wave & 1);
+  auto issue_scales = [&](int g) {  // group g (4 blocks, clamped) into slot g & 1
+    g = min(g, ngroups - 1);  // past the end: the last group again, same bytes
+    lds_dma16(ssrc + 4 * g, &Sc[g & 1][sdst][0]);
   };
 
   // Issue stage s (stages past the end reload the last one: same count of loads).
   auto issue = [&](int s, int8_t* R) {
     const int k0 = min(s, nst - 1) * PBK;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lds_dma16(asrc[j] + k0, R + (2 * wave + j) * 1024);
-    lds_dma16(bsrc + k0, R + RING_B + wave * 1024);
+    for (int j = 0; j < 4; ++j) lds_dma16(asrc[j] + k0, R + (4 * wave + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lds_dma16(bsrc[j] + k0, R + RING_B + (2 * wave + j) * 1024);
   };
 
   // MFMA operand offsets (row r, 16-byte chunk c = 2 kk + lane / 32).
   const int l32 = lane & 31, lhi = lane >> 5;
-  int aoff[2][2], boff[2][2];
+  int aoff[2][4], boff[2][4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < 4; ++kk) {
     const int c = 2 * kk + lhi;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = wm * 64 + 32 * i + l32;
-      aoff[i][kk] = r * PBK + ((c ^ ((r >> 2) & 3)) << 4);
+      aoff[i][kk] = r * PBK + ((c ^ ((r >> 1) & 7)) << 4);
       const int rn = wn * 64 + 32 * i + l32;
-      boff[i][kk] = RING_B + rn * PBK + ((c ^ ((rn >> 2) & 3)) << 4);
+      boff[i][kk] = RING_B + rn * PBK + ((c ^ ((rn >> 1) & 7)) << 4);
     }
   }
 
@@ -263,7 +273,7 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
 
   auto compute = [&](const int8_t* R) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < 4; ++kk) {
       v4i fa[2], fb[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) fa[i] = *(const v4i*)(R + aoff[i][kk]);
@@ -276,13 +286,13 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
     }
   };
   // This lane's scale-row bases (bytes) in slot 0; rows 4 lhi + 32 i + 8 q + t.
-  const uint32_t xbase = lds_addr(&Sx[0][wm * 64 + 4 * lhi][0]);
-  const uint32_t wbase = lds_addr(&Sw[0][wn * 64 + l32][0]);
+  const uint32_t xbase = lds_addr(&Sc[0][wm * 64 + 4 * lhi][0]);
+  const uint32_t wbase = lds_addr(&Sc[0][PBM + wn * 64 + l32][0]);
   // After the last stage of 256-block kb: T = dx * dw * I into the fp32 sums.
   auto epilogue = [&](int kb) {
     const uint32_t so = (uint32_t)(kb & 3) * 4u;  // block kb's float inside each row's 16 bytes
-    const uint32_t xa = xbase + ((kb >> 2) & 1) * (PBM * 16) + so;
-    const uint32_t wa = wbase + ((kb >> 2) & 1) * (PBN * 16) + so;
+    const uint32_t xa = xbase + ((kb >> 2) & 1) * ((PBM + PBN) * 16) + so;
+    const uint32_t wa = wbase + ((kb >> 2) & 1) * ((PBM + PBN) * 16) + so;
     v2f p[2][4][2], pw;
     // early-clobber outputs: no result register may share the address registers,
     // which the later reads of the block still use
@@ -328,20 +338,22 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
   issue_scales(0);
 #pragma unroll
   for (int s = 0; s < PST - 1; ++s) issue(s, ring[s]);
-  // main loop, unrolled by the ring size so every buffer is a fixed array
-  for (int s0 = 0; s0 < nst; s0 += PST) {
+  // main loop, unrolled by 24 stages (ring of 3, scale groups of 8) so every
+  // buffer and every scale load has a fixed place
+  for (int s0 = 0; s0 < nst; s0 += 24) {
 #pragma unroll
-    for (int u = 0; u < PST; ++u) {
+    for (int u = 0; u < 24; ++u) {
       const int s = s0 + u;
+      if (s >= nst) break;  // the last pass may be partial (uniform)
       // this wave's part of stage s has landed and its reads of stage s-1 are done
-      wait_vmcnt_lgkm0<(PST - 2) * 3>();
+      wait_vmcnt_lgkm0<(PST - 2) * 6>();
       ring_barrier();  // ... for every wave: stage s readable, stage s-1's buffer free
       issue(s + PST - 1, ring[(u + PST - 1) % PST]);
       // next group's scales: its slot was last read by the epilogues of group
-      // (s >> 4) - 1, all before this barrier
-      if (u == 0 && (s & 15) == 0 && (s >> 4) + 1 < ngroups) issue_scales((s >> 4) + 1);
-      compute(ring[u]);
-      if (u == 3) epilogue(s >> 2);
+      // (s >> 3) - 1, all before this barrier
+      if ((u & 7) == 0) issue_scales((s >> 3) + 1);
+      compute(ring[u % PST]);
+      if (u & 1) epilogue(s >> 1);
     }
   }
   wait_vmcnt_lgkm0<0>();  // no DMA may still be landing when the wave ends
