@@ -11,6 +11,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -54,13 +55,34 @@ def _units():
     return units
 
 
+def _scratch_users(remarks: str):
+    """Kernels whose resource-usage remark reports scratch memory (bytes/lane > 0)."""
+    users, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            users.append((name, int(m.group(1))))
+    return users
+
+
 def _compile(hipcc, src, obj, extra):
-    cmd = [hipcc] + FLAGS + extra + ["-c", src, "-o", obj]
+    cmd = [hipcc] + FLAGS + extra + ["-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line
-    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line,
+    # and the per-kernel resource remarks (checked below)
+    lines = [l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l]
+    err = "\n".join(l for l in lines if "kernel-resource-usage" not in l)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (os.path.basename(obj), err))
+    # A kernel in scratch memory means a register array indexed at run time or a
+    # spill: an order of magnitude slower, and never intended here.
+    users = _scratch_users(r.stderr)
+    if users:
+        raise RuntimeError("%s: kernels using scratch memory: %s" % (os.path.basename(obj), users))
     return err
 
 

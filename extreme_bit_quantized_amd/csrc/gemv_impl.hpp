@@ -318,26 +318,29 @@ __device__ __forceinline__ void sub_tern(const uint32_t (&T)[52], const uint32_t
   float acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+  // Words and digits are walked with compile-time indices (static_for), so the
+  // code words stay in registers even where a loop of this size would not be
+  // fully unrolled (an indexed register array would fall back to scratch).
   uint32_t p[8];
-#pragma unroll
-  for (int m = 0; m < 13; ++m) {
+  static_for(std::make_integer_sequence<int, 13>{}, [&](auto mc) {
+    constexpr int m = decltype(mc)::value;
     const uint32_t W = T[13 * SUB + m];
     uint32_t xl = W & 0x00FF00FFu;         // bytes 0, 2 in 16-bit lanes
     uint32_t xh = (W >> 8) & 0x00FF00FFu;  // bytes 1, 3
-    const int ndig = m < 12 ? 5 : 4;
-#pragma unroll
-    for (int i = 0; i < ndig; ++i) {
+    constexpr int ndig = m < 12 ? 5 : 4;
+    static_for(std::make_integer_sequence<int, ndig>{}, [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
       const uint32_t yl = xl * 3u, yh = xh * 3u;
-      const int g = m < 12 ? 5 * m + i : 60 + i;
+      constexpr int g = m < 12 ? 5 * m + i : 60 + i;
       // the next digit of every byte sits in bits 8..9 of its 16-bit lane
       p[g & 7] = __builtin_amdgcn_perm(yh, yl, 0x07030501u);
-      if (i + 1 < ndig) {
+      if constexpr (i + 1 < ndig) {
         xl = yl & 0x00FF00FFu;
         xh = yh & 0x00FF00FFu;
       }
-      if ((g & 7) == 7) blk_any<NB, WI, 2>(g >> 3, acc, AS, p, Iout, SUB * 8 + (g >> 3));
-    }
-  }
+      if constexpr ((g & 7) == 7) blk_any<NB, WI, 2>(g >> 3, acc, AS, p, Iout, SUB * 8 + (g >> 3));
+    });
+  });
   const float s = scale_half(S[SUB >> 1], SUB & 1);
 #pragma unroll
   for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, acc[b], y[b]);
@@ -610,7 +613,10 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
       });
     }
   } else {
-    // Larger batches: activations prefetched one sub-chunk ahead.
+    // Larger batches, short of registers: each 256-weight sub-chunk's codes are
+    // read from LDS just before use (the same registers serve every sub-chunk),
+    // so the next segment's DMA is issued after the last sub-chunk's reads;
+    // activations are prefetched one sub-chunk ahead.
     ActSub cur[NB], nxt[NB];
     uint32_t prevn = 0;
     if (seg < nseg) {
@@ -621,21 +627,35 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     }
     for (; seg < nseg; seg += nwk) {
       wait_vm_all();
-      uint32_t T[CH * 4];
-      read_row(T);
 #pragma unroll
       for (int i = 0; i < SPS / 2; ++i) S[i] = Sn[i];
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads done before the next DMA
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
       const int nx = seg + nwk;
       const bool more_seg = nx < nseg;
       uint32_t prev = trellis_prev_fix(seg, prevn);
-      prevn = trellis_prev_raw(more_seg ? nx : seg);
-      issue_tile(nx, more_seg);
-      load_scales<SPS>(sptr(more_seg ? nx : seg), Sn);
       static_for(std::make_integer_sequence<int, NSUB>{}, [&](auto scc) {
         constexpr int SUB = decltype(scc)::value;
+        // dwords [D0, D1) of the row feed this sub-chunk: 16-byte chunks C0..C1
+        constexpr int D0 = SUB * CH * 4 / NSUB, D1 = (SUB + 1) * CH * 4 / NSUB;
+        constexpr int C0 = D0 / 4, C1 = (D1 + 3) / 4;
+        uint32_t T[CH * 4];
+        static_for(std::make_integer_sequence<int, C1 - C0>{}, [&](auto kc) {
+          constexpr int k = C0 + decltype(kc)::value;
+          const int off = CH == 8 ? lane * 128 + ((k ^ ((lane >> 1) & 7)) << 4) : lane * (CH * 16) + 16 * k;
+          const u32x4 v = *(const u32x4*)(lds + off);
+          T[4 * k] = v.x;
+          T[4 * k + 1] = v.y;
+          T[4 * k + 2] = v.z;
+          T[4 * k + 3] = v.w;
+        });
+        if constexpr (SUB == NSUB - 1) {
+          // the tile reads are complete before the next DMA overwrites the region
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+          prevn = trellis_prev_raw(more_seg ? nx : seg);
+          issue_tile(nx, more_seg);
+          load_scales<SPS>(sptr(more_seg ? nx : seg), Sn);
+        }
         const int nkb = (SUB + 1 < NSUB) ? seg * (SEGK / 32) + (SUB + 1) * 8
                                          : (more_seg ? nx : seg) * (SEGK / 32);
         load_act_all<FMT, NB>(nxt, AG, nkb, 8);
@@ -645,6 +665,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
       });
     }
   }
+
 
   // Tail: fewer than SEGK weights left; this lane loads its own row directly.
   const int tailK = K - nseg * SEGK;
