@@ -464,6 +464,10 @@ __device__ __forceinline__ void wait_vm_all() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Cache policy of the weight-tile loads: non-temporal (weights stream through
+// once per call; the activations and scales they would evict are reused).
+constexpr int kTileCachePolicy = 2;  // nt
+
 // ---- one 64-row tile ----------------------------------------------------------------------------------
 // Accumulates (unscaled by final_scale) into y for segments wk, wk + nwk, ...
 // and the tail segment if (nseg % nwk) == wk.  lds: this wave's region.
@@ -533,7 +537,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     for (int i = 0; i < CH; ++i) {
       const uint32_t off = NB <= 2 ? goff[i < NOFF ? i : 0] : tile_off(i);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tseg + (off & keep)),
-                                       (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0, kTileCachePolicy);
     }
   };
 
