@@ -57,6 +57,7 @@ def _L():
                 "qref_f16_to_f64": (d, [u16]),
                 "qref_q8_block": (None, [P, i32, P, P, P]),
                 "qref_act_quant": (None, [P, i32, i32, i32, P, P, P]),
+                "qref_act_planes": (None, [P, i32, i32, P]),
                 "qref_quant_tern": (None, [P, i32, i32, P, P]),
                 "qref_quant_int2": (None, [P, i32, i32, P, P]),
                 "qref_quant_sign1": (None, [P, i32, i32, P, P]),
@@ -126,6 +127,17 @@ def act_quant(x, qblock: int = 32):
     s = np.empty((B, K // qblock), np.int32)
     _L().qref_act_quant(_p(x), B, K, qblock, _p(q), _p(d), _p(s))
     return q, d, s
+
+
+def act_planes(q):
+    """q int8 [B][K] -> 4-bit planes uint32 [B][K/32][8] (lo words of the four
+    8-value groups, then hi words; value n of a group in nibble n)."""
+    q = _c(np.atleast_2d(q), np.int8)
+    B, K = q.shape
+    assert K % 32 == 0
+    out = np.empty((B, K // 32, 8), np.uint32)
+    _L().qref_act_planes(_p(q), B, K, _p(out))
+    return out
 
 
 def q8_block(v):

@@ -133,6 +133,32 @@ void qref_act_quant(const float* x, int B, int K, int qblock, int8_t* q, float* 
     }
 }
 
+/* Split of int8 activations into 4-bit planes: x = 16 * hi + lo with lo =
+ * x mod 16 in [0, 15] and hi = floor(x / 16) in [-8, 7] (two's complement
+ * nibble).  For every 32-block and each group g of 8 values (x[8g + n], n =
+ * 0..7) the block's 8 words are lo of groups 0..3, then hi of groups 0..3,
+ * value n in nibble n.  A layout of the same integers (exact); the 1- and 2-bit
+ * GEMV multiplies it nibble by nibble against the codes' planes above. */
+void qref_act_planes(const int8_t* q, int B, int K, uint32_t* planes) {
+  for (int b = 0; b < B; ++b)
+    for (int kb = 0; kb < K / 32; ++kb) {
+      const int8_t* x = q + (size_t)b * K + (size_t)kb * 32;
+      uint32_t* o = planes + ((size_t)b * (K / 32) + kb) * 8;
+      for (int g = 0; g < 4; ++g) {
+        uint32_t lo = 0, hi = 0;
+        for (int n = 0; n < 8; ++n) {
+          int v = x[8 * g + n];
+          int h = (v - (((v % 16) + 16) % 16)) / 16; /* floor(v / 16) */
+          int l = v - 16 * h;
+          lo |= (uint32_t)l << (4 * n);
+          hi |= (uint32_t)(h & 15) << (4 * n);
+        }
+        o[g] = lo;
+        o[4 + g] = hi;
+      }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Weight quantizers (host-side data preparation), fp64 decisions            */
 /* ------------------------------------------------------------------------ */
@@ -250,12 +276,16 @@ static void tern_decode(uint8_t q, int t[5]) {
   }
 }
 
-/* Bit position of weight k (within its group) for the plane formats:
- * weight 4j + lane (lane = 0..3) lives in byte `lane` of the 32-bit word at
- * bit offset j * bits.  Words are little-endian. */
+/* Bit position of weight k (within its 32-bit word) for the plane formats.
+ * The pages fix the bits per weight, not their order.  1- and 2-bit codes are
+ * nibble-lane interleaved: weight 8j + n (n = 0..7) lives in nibble n of the
+ * word at bit offset j * bits, so the j-th plane of a word holds the codes of
+ * 8 consecutive weights, one per nibble.  4-bit codes are byte-lane
+ * interleaved: weight 4j + lane (lane = 0..3) lives in byte `lane` at bit
+ * offset 4j.  Words are little-endian. */
 static int plane_bitpos(int k_in_word, int bits) {
-  int j = k_in_word / 4, lane = k_in_word % 4;
-  return 8 * lane + j * bits;
+  if (bits == 4) return 8 * (k_in_word % 4) + 4 * (k_in_word / 4);
+  return 4 * (k_in_word % 8) + (k_in_word / 8) * bits;
 }
 
 int qref_pack(int fmt, const int8_t* codes, int N, int K, uint8_t* packed) {

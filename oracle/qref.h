@@ -59,6 +59,9 @@ double qref_f16_to_f64(uint16_t h);
 void qref_q8_block(const float* v, int n, int8_t* q, float* d, int32_t* qsum);
 /* Activation quantization: x [B][K] -> q [B][K], d and qsum [B][K/qblock]. */
 void qref_act_quant(const float* x, int B, int K, int qblock, int8_t* q, float* d, int32_t* qsum);
+/* 4-bit planes of int8 activations q [B][K] (K a multiple of 32) ->
+ * planes [B][K/32][8] (see qref.c). */
+void qref_act_planes(const int8_t* q, int B, int K, uint32_t* planes);
 
 /* Weight quantizers: w [N][K] fp32 -> integer codes [N][K] + fp16 scales
  * [N][K/block].  Code meaning per format:

@@ -249,9 +249,18 @@ def test_ternary_position_map(qref):
         assert p[0, diff[0]] == -(-256 * b // 243)
 
 
+def _plane_bit(k, bits):
+    """Bit of weight k of a little-endian 32-bit word: 1- and 2-bit codes
+    nibble-lane (weight 8j+n in nibble n at offset j*bits), 4-bit codes
+    byte-lane (weight 4j+b in byte b at offset 4j)."""
+    if bits == 4:
+        return 8 * (k % 4) + 4 * (k // 4)
+    return 4 * (k % 8) + (k // 8) * bits
+
+
 @pytest.mark.parametrize("name,bits", [("INT2", 2), ("SIGN1", 1), ("INT4", 4)])
 def test_plane_position_map(qref, name, bits):
-    """Weight k of a 32-bit word sits in byte k%4 at bit offset (k%per_word)//4*bits."""
+    """A single set code lands at the bit the layout names and nowhere else."""
     fmt = getattr(qref, name)
     per_word = 32 // bits
     K = 256
@@ -260,13 +269,90 @@ def test_plane_position_map(qref, name, bits):
         codes[0, k] = (1 << bits) - 1 if bits > 1 else 1
         p = qref.pack(fmt, codes)
         word = int.from_bytes(bytes(p[0, 4 * (k // per_word): 4 * (k // per_word) + 4]), "little")
-        kk = k % per_word
-        want = ((1 << bits) - 1) << (8 * (kk % 4) + (kk // 4) * bits)
+        want = ((1 << bits) - 1) << _plane_bit(k % per_word, bits)
         assert word == want, (name, k)
         # nothing else in the row is set
         rest = p[0].copy()
         rest[4 * (k // per_word): 4 * (k // per_word) + 4] = 0
         assert not rest.any()
+
+
+def test_plane_masks_select_eight_consecutive_weights(qref):
+    """(word >> j*bits) & 0x11111111 (1-bit) / 0x33333333 (2-bit) holds the codes of
+    weights 8j .. 8j+7 of the word, weight 8j+n in nibble n."""
+    rng = np.random.default_rng(3)
+    for name, bits, mask in (("SIGN1", 1, 0x11111111), ("INT2", 2, 0x33333333)):
+        fmt = getattr(qref, name)
+        per_word = 32 // bits
+        codes = rng.integers(0, 1 << bits, (1, 256)).astype(np.int8)
+        p = qref.pack(fmt, codes)
+        for w in range(256 // per_word):
+            word = int.from_bytes(bytes(p[0, 4 * w: 4 * w + 4]), "little")
+            for j in range(4 // bits):
+                plane = (word >> (j * bits)) & mask
+                got = [(plane >> (4 * n)) & 15 for n in range(8)]
+                assert got == list(codes[0, w * per_word + 8 * j: w * per_word + 8 * j + 8]), (name, w, j)
+
+
+def test_act_planes_reconstruct_every_byte(qref):
+    """Every int8 value v comes back as 16 * sext4(hi) + lo with lo in [0, 15]."""
+    v = np.arange(-128, 128, dtype=np.int16)
+    q = np.zeros((1, 256 * 32), np.int8)
+    q[0, ::32] = v  # value v at position 0 of block v+128, the rest zero
+    pl = qref.act_planes(q)
+    assert pl.shape == (1, 256, 8) and pl.dtype == np.uint32
+    lo = pl[0, :, 0] & 15
+    hi = pl[0, :, 4] & 15
+    hi_s = np.where(hi >= 8, hi.astype(np.int64) - 16, hi)
+    assert (16 * hi_s + lo == v).all()
+    # nothing else set: the other positions are zero
+    rest = pl[0].copy()
+    rest[:, 0] &= ~np.uint32(15)
+    rest[:, 4] &= ~np.uint32(15)
+    assert not rest.any()
+
+
+def test_act_planes_positions(qref):
+    """Value i of a 32-block lands in nibble i%8 of word i//8 (lo) and 4 + i//8 (hi)."""
+    for i in range(32):
+        q = np.zeros((1, 64), np.int8)
+        q[0, 32 + i] = -17  # lo 15, hi -2 (nibble 14)
+        pl = qref.act_planes(q)
+        assert not pl[0, 0].any()
+        want = np.zeros(8, np.uint32)
+        want[i // 8] = 15 << (4 * (i % 8))
+        want[4 + i // 8] = 14 << (4 * (i % 8))
+        assert (pl[0, 1] == want).all(), i
+
+
+@pytest.mark.parametrize("name,bits", [("SIGN1", 1), ("INT2", 2)])
+def test_nibble_dots_equal_block_dots(qref, name, bits):
+    """Brute force: multiplying code planes and activation planes nibble by nibble
+    (lo unsigned, hi signed) gives the integer dot sum(code * q) of every 32-block."""
+    rng = np.random.default_rng(11)
+    fmt = getattr(qref, name)
+    K = 512
+    codes = rng.integers(0, 1 << bits, (3, K)).astype(np.int8)
+    q = rng.integers(-127, 128, (1, K)).astype(np.int8)
+    p = qref.pack(fmt, codes)
+    pl = qref.act_planes(q)
+    words = p[:, : K * bits // 8].view("<u4").astype(np.int64)
+    mask = 0x11111111 if bits == 1 else 0x33333333
+    nib = lambda x, n: (x >> (4 * n)) & 15
+    for r in range(3):
+        for kb in range(K // 32):
+            acc = 0
+            for g in range(4):
+                # group g of the block: word and plane index inside the block's words
+                wi, j = divmod(g, 4 // bits)
+                word = int(words[r, kb * bits + wi])
+                cp = (word >> (j * bits)) & mask
+                lo, hi = int(pl[0, kb, g]), int(pl[0, kb, 4 + g])
+                for n in range(8):
+                    h = nib(hi, n)
+                    acc += nib(cp, n) * (16 * (h - 16 if h >= 8 else h) + nib(lo, n))
+            want = int((codes[r, kb * 32: kb * 32 + 32].astype(np.int64) * q[0, kb * 32: kb * 32 + 32]).sum())
+            assert acc == want, (name, r, kb)
 
 
 @pytest.mark.parametrize("name", ["TERN_B3", "INT2", "SIGN1", "INT4", "TRELLIS2"])
