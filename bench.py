@@ -92,32 +92,40 @@ class Stack:
         self.q = {K: torch.empty((layers * B, K), dtype=torch.int8, device="cuda") for K in WIDTHS}
         self.d = {K: torch.empty((layers * B, K // 32), dtype=torch.float32, device="cuda") for K in WIDTHS}
         self.s = {K: torch.empty((layers * B, K // 32), dtype=torch.int32, device="cuda") for K in WIDTHS}
+        # 4-bit planes of q, read by the 1- and 2-bit GEMV instead of q
+        self.planes = kind in ("sign1", "int2")
+        self.pl = {K: torch.empty((layers * B, K // 32, 8), dtype=torch.int32, device="cuda") for K in WIDTHS} \
+            if self.planes else None
         self.y = [[torch.empty((B, N), dtype=torch.float32, device="cuda") for (_, N, _) in shapes]
                   for _ in range(layers)]
         torch.cuda.synchronize()
 
     def act(self, l, K):
+        """(q, planes or None, d, qsum) of layer l's tokens at input width K."""
         B = self.B
-        return (self.q[K][l * B:(l + 1) * B], self.d[K][l * B:(l + 1) * B], self.s[K][l * B:(l + 1) * B])
+        sl = slice(l * B, (l + 1) * B)
+        return (self.q[K][sl], self.pl[K][sl] if self.planes else None, self.d[K][sl], self.s[K][sl])
 
     def entries(self):
         out = []
         for l in range(self.layers):
             for mi, (name, N, K) in enumerate(self.shapes):
-                q, d, s = self.act(l, K)
-                out.append((self.weights[l][mi], q, d, s, self.y[l][mi]))
+                q, pl, d, s = self.act(l, K)
+                out.append((self.weights[l][mi], q, pl, d, s, self.y[l][mi]))
         return out
 
     def quantize_acts(self, ebq):
         for K in WIDTHS:
             ebq.qact_quant_i8(self.x[K], 32, self.q[K], self.d[K], self.s[K])
+            if self.planes:
+                ebq.qact_planes(self.q[K], self.pl[K])
 
     def weight_bytes(self):
         return sum(w.nbytes for row in self.weights for w in row)
 
     def gemv_bytes(self):
         """Algorithmic bytes of one grouped launch: weights + activation reads
-        (q, d, qsum per matrix) + fp32 outputs."""
+        (q or its planes, same size, + d, qsum per matrix) + fp32 outputs."""
         b = self.weight_bytes()
         for l in range(self.layers):
             for (name, N, K) in self.shapes:
@@ -126,10 +134,10 @@ class Stack:
 
     def step_bytes(self):
         """Algorithmic bytes of one step: the grouped launch + activation quantization
-        (fp32 in, int8 + scales + sums out)."""
+        (fp32 in, int8 + scales + sums out) + the planes pass (q in, planes out)."""
         b = self.gemv_bytes()
         for K in WIDTHS:
-            b += self.layers * self.B * (K * 4 + K + (K // 32) * 8)
+            b += self.layers * self.B * (K * 4 + K + (K // 32) * 8 + (2 * K if self.planes else 0))
         return b
 
     def n_weights(self):
@@ -282,11 +290,11 @@ def bench_dependent_chain(ebq, stack, reps):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         for e in ents:                                  # warm the launch path first
-            ebq.qgemv(e[0], e[1], e[2], e[3], stack.B, e[4])
+            ebq.qgemv(e[0], e[1], e[2], e[3], e[4], stack.B, e[5])
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
             for e in ents:
-                ebq.qgemv(e[0], e[1], e[2], e[3], stack.B, e[4])
+                ebq.qgemv(e[0], e[1], e[2], e[3], e[4], stack.B, e[5])
     torch.cuda.synchronize()
     t, _ = time_region(g.replay, reps, 2)
     return t
@@ -354,10 +362,10 @@ def bench_small_ternary(ebq, reps):
 
     def step():
         ebq.qact_quant_i8(x, 32, q, d, s)
-        ebq.qgemv(pw, q, d, s, 1, y)
+        ebq.qgemv(pw, q, None, d, s, 1, y)
 
     t, _ = time_region(step, reps, 10)
-    tk, _ = time_kernel(lambda: ebq.qgemv(pw, q, d, s, 1, y), reps, 10)
+    tk, _ = time_kernel(lambda: ebq.qgemv(pw, q, None, d, s, 1, y), reps, 10)
     return {"step_us": round(t * 1e6, 2), "gemv_us": round(tk * 1e6, 2)}
 
 

@@ -36,7 +36,7 @@ class qweight_t(ctypes.Structure):
 
 
 class qgemv_item_t(ctypes.Structure):
-    _fields_ = [("w", qweight_t), ("q", ctypes.c_void_p), ("d", ctypes.c_void_p),
+    _fields_ = [("w", qweight_t), ("q", ctypes.c_void_p), ("planes", ctypes.c_void_p), ("d", ctypes.c_void_p),
                 ("qsum", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
@@ -67,8 +67,9 @@ def load(path: str = LIB_PATH):
         "qweight_pack": (ctypes.c_int, [i32, P, i32, i32, P, i64, P]),
         "qact_quant_i8": (ctypes.c_int, [P, i32, i32, i32, P, P, P, P]),
         "qact_hadamard_quant_i8": (ctypes.c_int, [P, i32, i32, P, i32, P, P, P, P]),
-        "qgemv": (ctypes.c_int, [W, P, P, P, i32, P, P]),
-        "qgemv_blockdots": (ctypes.c_int, [W, P, P, P, P]),
+        "qact_planes": (ctypes.c_int, [P, i32, i32, P, P]),
+        "qgemv": (ctypes.c_int, [W, P, P, P, P, i32, P, P]),
+        "qgemv_blockdots": (ctypes.c_int, [W, P, P, P, P, P]),
         "qgemv_grouped_plan_bytes": (i64, [ctypes.POINTER(qgemv_item_t), i32, i32]),
         "qgemv_grouped_plan": (ctypes.c_int, [ctypes.POINTER(qgemv_item_t), i32, i32, P, i64]),
         "qgemv_grouped_run": (ctypes.c_int, [P, P, P]),
@@ -202,21 +203,27 @@ def qact_hadamard_quant_i8(x, sign_bits, qblock, q, d, qsum, stream=None):
                                          _stream(stream)), "qact_hadamard_quant_i8")
 
 
-def qgemv(w: PackedWeight, q, d, qsum, B: int, y, stream=None):
-    _check(load().qgemv(ctypes.byref(w.desc), _ptr(q), _ptr(d), _ptr(qsum), B, _ptr(y), _stream(stream)), "qgemv")
+def qact_planes(q, planes, stream=None):
+    B, K = q.shape
+    _check(load().qact_planes(_ptr(q), B, K, _ptr(planes), _stream(stream)), "qact_planes")
 
 
-def qgemv_blockdots(w: PackedWeight, q, qsum, out, stream=None):
-    _check(load().qgemv_blockdots(ctypes.byref(w.desc), _ptr(q), _ptr(qsum), _ptr(out), _stream(stream)),
-           "qgemv_blockdots")
+def qgemv(w: PackedWeight, q, planes, d, qsum, B: int, y, stream=None):
+    _check(load().qgemv(ctypes.byref(w.desc), _ptr(q), _ptr(planes), _ptr(d), _ptr(qsum), B, _ptr(y),
+                        _stream(stream)), "qgemv")
+
+
+def qgemv_blockdots(w: PackedWeight, q, planes, qsum, out, stream=None):
+    _check(load().qgemv_blockdots(ctypes.byref(w.desc), _ptr(q), _ptr(planes), _ptr(qsum), _ptr(out),
+                                  _stream(stream)), "qgemv_blockdots")
 
 
 def make_items(entries):
-    """entries: iterable of (PackedWeight, q, d, qsum, y) -> ctypes array of qgemv_item_t."""
+    """entries: iterable of (PackedWeight, q, planes, d, qsum, y) -> ctypes array of qgemv_item_t."""
     entries = list(entries)
     arr = (qgemv_item_t * len(entries))()
-    for i, (w, q, d, qs, y) in enumerate(entries):
-        arr[i] = qgemv_item_t(w.desc, _ptr(q), _ptr(d), _ptr(qs), _ptr(y))
+    for i, (w, q, pl, d, qs, y) in enumerate(entries):
+        arr[i] = qgemv_item_t(w.desc, _ptr(q), _ptr(pl), _ptr(d), _ptr(qs), _ptr(y))
     return arr
 
 

@@ -81,6 +81,33 @@ hipError_t launch_act_quant(const float* x, int B, int K, int qblock, int8_t* q,
   return hipGetLastError();
 }
 
+// 4-bit planes of int8 activations: one thread per output word.  Word w of a
+// 32-block (8 words) covers values 8g .. 8g+7, g = w % 4: w < 4 takes the low
+// nibble of each byte (x mod 16), w >= 4 the high one (floor(x / 16) as a
+// two's complement nibble); value n of the group goes to nibble n.
+__global__ __launch_bounds__(256) void k_act_planes(const uint32_t* __restrict__ q, int64_t nwords,
+                                                    uint32_t* __restrict__ planes) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nwords) return;
+  const int w = (int)(i & 7), g = w & 3;
+  const int64_t src = (i >> 3) * 8 + 2 * g;  // the group's two q words (4 values each)
+  const uint32_t a0 = q[src], a1 = q[src + 1];
+  const int sh = w < 4 ? 0 : 4;
+  // nibble of byte k of a word, moved to nibble k (k = 0..3)
+  auto nib4 = [&](uint32_t a) {
+    const uint32_t t = (a >> sh) & 0x0F0F0F0Fu;  // nibbles at bits 8k
+    return (t & 0xFu) | ((t >> 4) & 0xF0u) | ((t >> 8) & 0xF00u) | ((t >> 12) & 0xF000u);
+  };
+  planes[i] = nib4(a0) | (nib4(a1) << 16);
+}
+
+hipError_t launch_act_planes(const int8_t* q, int B, int K, uint32_t* planes, hipStream_t s) {
+  const int64_t nwords = (int64_t)B * K / 4;  // 8 words per 32 values
+  const int64_t grid = (nwords + 255) / 256;
+  hipLaunchKernelGGL(k_act_planes, dim3((unsigned)grid), dim3(256), 0, s, (const uint32_t*)q, nwords, planes);
+  return hipGetLastError();
+}
+
 // One wave per (token, 256-block): lane l holds values 4l .. 4l+3.
 __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict__ x, int K, int64_t nblocks,
                                                         const uint32_t* __restrict__ sign_bits, int qblock,

@@ -32,12 +32,17 @@ int check_weight(const qweight_t* w) {
   return QERR_OK;
 }
 
-GemvItem make_item(const qweight_t* w, const int8_t* q, const float* d, const int32_t* qsum, float* y) {
+// INT2 and SIGN1 read 4-bit activation planes instead of q.
+inline bool uses_planes(int32_t fmt) { return fmt == QFMT_INT2 || fmt == QFMT_SIGN1; }
+
+// it.q carries the planes (as bytes) for the formats that read them.
+GemvItem make_item(const qweight_t* w, const int8_t* q, const uint32_t* planes, const float* d,
+                   const int32_t* qsum, float* y) {
   GemvItem it{};
   it.codes = (const uint8_t*)w->codes;
   it.scales = w->scales;
   it.seeds = w->seeds;
-  it.q = q;
+  it.q = uses_planes(w->fmt) ? (const int8_t*)planes : q;
   it.d = d;
   it.qsum = qsum;
   it.y = y;
@@ -48,9 +53,16 @@ GemvItem make_item(const qweight_t* w, const int8_t* q, const float* d, const in
   return it;
 }
 
-int check_act(const int8_t* q, const float* d, const int32_t* qsum) {
-  if (!q || !d || !qsum) return QERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(d, 4) || !aligned(qsum, 4)) return QERR_ALIGNMENT;
+int check_act(int32_t fmt, const int8_t* q, const uint32_t* planes, const float* d, const int32_t* qsum) {
+  if (!d || !qsum) return QERR_INVALID_ARG;
+  if (uses_planes(fmt)) {
+    if (!planes) return QERR_INVALID_ARG;
+    if (!aligned(planes, 32)) return QERR_ALIGNMENT;
+  } else {
+    if (!q) return QERR_INVALID_ARG;
+    if (!aligned(q, 16)) return QERR_ALIGNMENT;
+  }
+  if (!aligned(d, 4) || !aligned(qsum, 4)) return QERR_ALIGNMENT;
   return QERR_OK;
 }
 
@@ -58,7 +70,7 @@ int check_item(const qgemv_item_t& it, int32_t B) {
   int rc = check_weight(&it.w);
   if (rc) return rc;
   if (it.w.rows == 0) return QERR_OK;
-  rc = check_act(it.q, it.d, it.qsum);
+  rc = check_act(it.w.fmt, it.q, it.planes, it.d, it.qsum);
   if (rc) return rc;
   if (!it.y) return QERR_INVALID_ARG;
   if (!aligned(it.y, 4)) return QERR_ALIGNMENT;
@@ -180,6 +192,16 @@ int qact_quant_i8(const float* x, int32_t B, int32_t K, int32_t qblock, int8_t* 
   return hip_rc(launch_act_quant(x, B, K, qblock, q, d, qsum, S(stream)));
 }
 
+int qact_planes(const int8_t* q, int32_t B, int32_t K, uint32_t* planes, void* stream) {
+  if (B < 0 || K < 0) return QERR_INVALID_ARG;
+  if (B == 0) return QERR_OK;
+  if (K == 0 || K % 32 != 0) return QERR_SHAPE;
+  if (!q || !planes) return QERR_INVALID_ARG;
+  if (!aligned(q, 4) || !aligned(planes, 32)) return QERR_ALIGNMENT;
+  if ((int64_t)B * K >= ((int64_t)1 << 40)) return QERR_SHAPE;
+  return hip_rc(launch_act_planes(q, B, K, planes, S(stream)));
+}
+
 int qact_hadamard_quant_i8(const float* x, int32_t B, int32_t K, const uint32_t* sign_bits, int32_t qblock,
                            int8_t* q, float* d, int32_t* qsum, void* stream) {
   if (B < 0 || K < 0) return QERR_INVALID_ARG;
@@ -193,27 +215,30 @@ int qact_hadamard_quant_i8(const float* x, int32_t B, int32_t K, const uint32_t*
   return hip_rc(launch_hadamard_quant(x, B, K, sign_bits, qblock, q, d, qsum, S(stream)));
 }
 
-int qgemv(const qweight_t* w, const int8_t* q, const float* d, const int32_t* qsum, int32_t B, float* y,
-          void* stream) {
+int qgemv(const qweight_t* w, const int8_t* q, const uint32_t* planes, const float* d, const int32_t* qsum,
+          int32_t B, float* y, void* stream) {
   int rc = check_weight(w);
   if (rc) return rc;
   if (B < 0 || B > 8) return QERR_INVALID_ARG;
   if (B == 0 || w->rows == 0) return QERR_OK;
-  rc = check_act(q, d, qsum);
+  rc = check_act(w->fmt, q, planes, d, qsum);
   if (rc) return rc;
   if (!y) return QERR_INVALID_ARG;
   if (!aligned(y, 4)) return QERR_ALIGNMENT;
-  return hip_rc(kGemv[B](make_item(w, q, d, qsum, y), S(stream)));
+  return hip_rc(kGemv[B](make_item(w, q, planes, d, qsum, y), S(stream)));
 }
 
-int qgemv_blockdots(const qweight_t* w, const int8_t* q, const int32_t* qsum, int32_t* out, void* stream) {
+int qgemv_blockdots(const qweight_t* w, const int8_t* q, const uint32_t* planes, const int32_t* qsum, int32_t* out,
+                    void* stream) {
   int rc = check_weight(w);
   if (rc) return rc;
   if (w->rows == 0) return QERR_OK;
-  if (!q || !qsum || !out) return QERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(qsum, 4) || !aligned(out, 4)) return QERR_ALIGNMENT;
   // the scale path is unused by the hook; pass qsum for d so no pointer is null
-  return hip_rc(launch_blockdots(make_item(w, q, (const float*)qsum, qsum, nullptr), out, S(stream)));
+  rc = check_act(w->fmt, q, planes, (const float*)qsum, qsum);
+  if (rc) return rc;
+  if (!out) return QERR_INVALID_ARG;
+  if (!aligned(out, 4)) return QERR_ALIGNMENT;
+  return hip_rc(launch_blockdots(make_item(w, q, planes, (const float*)qsum, qsum, nullptr), out, S(stream)));
 }
 
 int64_t qgemv_grouped_plan_bytes(const qgemv_item_t* items, int32_t n, int32_t B) {
@@ -247,7 +272,7 @@ int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B, void* ho
   h.total_bytes = need;
   GemvItem* it = (GemvItem*)(base + h.items_off);
   for (int32_t i = 0; i < n; ++i) {
-    it[i] = make_item(&items[i].w, items[i].q, items[i].d, items[i].qsum, items[i].y);
+    it[i] = make_item(&items[i].w, items[i].q, items[i].planes, items[i].d, items[i].qsum, items[i].y);
     if (items[i].w.rows > 0) h.fmt_mask |= 1 << items[i].w.fmt;
   }
   // Tiles: grouped by format, longest first inside each group.
@@ -297,7 +322,8 @@ int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw
   if (w->rows == 0) return QERR_OK;
   if (!wq || !dw) return QERR_INVALID_ARG;
   if (!aligned(wq, 4) || !aligned(dw, 4)) return QERR_ALIGNMENT;
-  return hip_rc(launch_trellis_decode(make_item(w, nullptr, nullptr, nullptr, nullptr), oblock, wq, dw, S(stream)));
+  const GemvItem it = make_item(w, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return hip_rc(launch_trellis_decode(it, oblock, wq, dw, S(stream)));
 }
 
 int qweight_unpack_i8(const qweight_t* w, int8_t* wq, float* dw, void* stream) {
@@ -307,7 +333,7 @@ int qweight_unpack_i8(const qweight_t* w, int8_t* wq, float* dw, void* stream) {
   if (w->rows == 0) return QERR_OK;
   if (!wq || !dw) return QERR_INVALID_ARG;
   if (!aligned(dw, 4)) return QERR_ALIGNMENT;
-  return hip_rc(launch_unpack_i8(make_item(w, nullptr, nullptr, nullptr, nullptr), wq, dw, S(stream)));
+  return hip_rc(launch_unpack_i8(make_item(w, nullptr, nullptr, nullptr, nullptr, nullptr), wq, dw, S(stream)));
 }
 
 int qgemm_i8(const int8_t* xq, const float* dx, int32_t M, const int8_t* wq, const float* dw, int32_t N, int32_t K,

@@ -6,17 +6,17 @@
 // non-temporal 16-byte loads (8 rows x 128 bytes per wave instruction), writes
 // it to its own LDS region and reads back the 16-byte chunks of its own row, so
 // every HBM transaction is a full cache line while each lane ends up with a
-// whole row of codes.  Activations are the same for all 64 rows, so they are
-// read with scalar loads into SGPRs and enter v_dot4 as the scalar operand;
-// the integer block dot I of every 32-block is exact, and the fp32 scaling is
-// folded so that the per-row cost per 32 weights is the unpack, 8 dot4 and
-// three or four VALU ops.
+// whole row of codes.  Activations are the same for all 64 rows: they enter
+// the dot products as a wave-uniform operand (a scalar register, or a DPP row
+// broadcast); the integer block dot I of every 32-block is exact, and the fp32
+// scaling costs one convert and one or two FMAs per block.
 //
-// Decode per format (levels come out as bytes lined up with activation dwords):
-//   SIGN1  word w, weight 4j+b at bit 8b+j: (w>>j) & 0x01010101 for j = 0..3
-//          and (w>>j) & 0x10101010 (16x, a second dot chain) for j = 4..7.
-//   INT2   weight 4j+b at bits 8b+2j: masks 0x03030303 / 0x30303030 of w, w>>2.
-//   INT4   weight 4j+b at bits 8b+4j: w & 0x0F0F0F0F, (w>>4) & 0x0F0F0F0F.
+// Decode per format (codes come out lined up with activation words):
+//   SIGN1  word w (32 weights): (w >> j) & 0x11111111, j = 0..3, holds weights
+//          8j .. 8j+7 one per nibble; multiplied with 8-way nibble dots against
+//          the activations split as x = 16 hi + lo.
+//   INT2   two words per 32 weights, (w >> 2j) & 0x33333333, the same way.
+//   INT4   weight 4j+b at bits 8b+4j: w & 0x0F0F0F0F, (w>>4) & 0x0F0F0F0F, int8 dots.
 //   TERN   byte = fixed-point base-3 fraction of 5 trits: multiplying the byte
 //          by 3 brings the next digit into bits 8..9 and leaves the rest below;
 //          two bytes per 32-bit register (16-bit lanes), a v_perm gathers the
@@ -80,10 +80,29 @@ template <> struct Seg<QFMT_TRELLIS2> {
 // (v_subrev_*) the broadcast lands on the other source, so the qsum term is
 // stored negated and added with v_add_u32_dpp.
 struct ActSub {
-  int32_t a[4];  // q dwords 4i .. 4i+3 of the sub-chunk in row lane i
+  int32_t a[4];  // q dwords (1- and 2-bit: plane words) 4i .. 4i+3 of the sub-chunk in row lane i
   float d;       // lane kb (0..7): scale of activation block kb
   int32_t Q;     // lane kb (0..7): minus the format multiple of the block's qsum
 };
+
+// 1-bit extras of one token's sub-chunk, made from d and Q where it is used.
+struct ActS1 {
+  float d2;  // lane kb: 2 d
+  float e;   // lanes 3 and 7: sum of d * Q over blocks 0..3 resp. 4..7
+};
+__device__ __forceinline__ ActS1 act_s1(const ActSub& s) {
+  ActS1 r;
+  r.d2 = s.d + s.d;
+  const float t = (float)s.Q * s.d;
+  // sum over each 4 lanes by row shifts of 1 and 2 (lanes 3 and 7 end with the sums)
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %1, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf"
+      : "=&v"(r.e)
+      : "v"(t));
+  return r;
+}
 
 // Global views of one token's activations (token b at offset b * K).
 struct ActG {
@@ -109,48 +128,6 @@ __device__ __forceinline__ void load_act(ActSub& s, const ActG& A, int b, int kb
 }
 
 #define QK_DOT(ACC, A, P, L) "v_dot4c_i32_i8_dpp " ACC ", " A ", " P " row_newbcast:" L " row_mask:0xf bank_mask:0xf\n\t"
-
-// Two dot chains (16x weight plane in the second): R = 16*x + z + Q[KB] (Q holds -mult*qsum);
-// acc += d[KB] * R.  Dword j of the block is a[j % 4] at row lane 2KB + j/4.
-// SIGN1: chain z = dwords 4..7.   INT2: chain z = dwords 2, 3, 6, 7.
-template <int KB, bool INT2>
-__device__ __forceinline__ int blk_two_chain_fmac(float& acc, const ActSub& s, const uint32_t (&p)[8]) {
-  int x, z;
-  if constexpr (!INT2) {
-    asm("s_nop 1\n\t"
-        "v_mov_b32 %1, 0\n\t"
-        "v_mov_b32 %2, 0\n\t"
-        QK_DOT("%1", "%3", "%7", "%c17") QK_DOT("%2", "%3", "%11", "%c18")
-        QK_DOT("%1", "%4", "%8", "%c17") QK_DOT("%2", "%4", "%12", "%c18")
-        QK_DOT("%1", "%5", "%9", "%c17") QK_DOT("%2", "%5", "%13", "%c18")
-        QK_DOT("%1", "%6", "%10", "%c17") QK_DOT("%2", "%6", "%14", "%c18")
-        "s_nop 2\n\t"
-        "v_lshl_add_u32 %1, %1, 4, %2\n\t"
-        "v_add_u32_dpp %1, %16, %1 row_newbcast:%c19 row_mask:0xf bank_mask:0xf\n\t"
-        "v_cvt_f32_i32 %2, %1\n\t"
-        "v_fmac_f32_dpp %0, %15, %2 row_newbcast:%c19 row_mask:0xf bank_mask:0xf"
-        : "+v"(acc), "=&v"(x), "=&v"(z)
-        : "v"(s.a[0]), "v"(s.a[1]), "v"(s.a[2]), "v"(s.a[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]),
-          "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(s.d), "v"(s.Q), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
-  } else {
-    asm("s_nop 1\n\t"
-        "v_mov_b32 %1, 0\n\t"
-        "v_mov_b32 %2, 0\n\t"
-        QK_DOT("%1", "%3", "%7", "%c17") QK_DOT("%1", "%4", "%8", "%c17")
-        QK_DOT("%2", "%5", "%9", "%c17") QK_DOT("%2", "%6", "%10", "%c17")
-        QK_DOT("%1", "%3", "%11", "%c18") QK_DOT("%1", "%4", "%12", "%c18")
-        QK_DOT("%2", "%5", "%13", "%c18") QK_DOT("%2", "%6", "%14", "%c18")
-        "s_nop 2\n\t"
-        "v_lshl_add_u32 %1, %1, 4, %2\n\t"
-        "v_add_u32_dpp %1, %16, %1 row_newbcast:%c19 row_mask:0xf bank_mask:0xf\n\t"
-        "v_cvt_f32_i32 %2, %1\n\t"
-        "v_mul_f32_dpp %0, %15, %2 row_newbcast:%c19 row_mask:0xf bank_mask:0xf"
-        : "=v"(acc), "=&v"(x), "=&v"(z)
-        : "v"(s.a[0]), "v"(s.a[1]), "v"(s.a[2]), "v"(s.a[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]),
-          "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(s.d), "v"(s.Q), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
-  }
-  return x;  // R (8 * I)
-}
 
 // One dot chain.  INT4: R = 2x + Q[KB] (Q = -15 qsum), out = d[KB] * R.
 template <int KB>
@@ -198,48 +175,333 @@ __device__ __forceinline__ float scale_half(uint32_t pair, int hi) {
   return __half2float(__ushort_as_half((unsigned short)(hi ? (pair >> 16) : (pair & 0xFFFFu))));
 }
 
+template <int... I, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// ---- 1- and 2-bit codes against 4-bit activation planes ------------------------------------------
+// Codes are nibble-lane packed: (word >> j*bits) & 0x11111111 (1-bit) or
+// & 0x33333333 (2-bit) holds the codes of 8 consecutive weights, one per
+// nibble.  Activations come split as x = 16 hi + lo (lo in 0..15, hi a signed
+// nibble), 8 words per 32-block: lo of the block's 4 groups of 8 values, then
+// hi.  The block's integer dot is 4 unsigned and 4 signed 8-way nibble dots:
+//   sum c x = 16 sum c hi + sum c lo,   I = 2 sum c x - m qsum
+// (m = 1 for 1-bit levels 2b - 1, m = 3 for 2-bit levels 2c - 3).
+//
+// Batches up to 2 read the planes, d and qsum of the block with scalar loads
+// (wave-uniform) and use them as the scalar operand of v_dot8 / v_fma: no DPP,
+// no accumulator initialisation (the first dot adds to an inline 0) and the
+// qsum term folds into one shift-add.
+typedef const uint32_t __attribute__((address_space(4))) k_u32;
+typedef const int32_t __attribute__((address_space(4))) k_i32;
+typedef const float __attribute__((address_space(4))) k_f32;
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef const u32x8 __attribute__((address_space(4))) k_u32x8;
+
+struct ActK {  // wave-uniform views of one item's activations (token b at block b * kbs)
+  k_u32* pl;   // planes [B][kbs][8] (32-byte aligned)
+  k_f32* d;
+  k_i32* qs;
+  int kbs;
+};
+
+// A constant the compiler keeps in an SGPR (a VOP2 operand) instead of a
+// 32-bit literal in every instruction that uses it.
+__device__ __forceinline__ uint32_t sgpr_const(uint32_t v) {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
+  return r;
+}
+
+// The scalar operands of one block for one token: its 8 plane words, d and
+// qsum (multiplied out where it is used, so that nothing reads the loaded
+// values before the wait for their generation).
+struct BlkK {
+  u32x8 x;
+  float d;
+  int qs;
+};
+__device__ __forceinline__ BlkK load_blk(const ActK& A, int b, int kb) {
+  const int64_t blk = (int64_t)b * A.kbs + kb;
+  BlkK r;
+  r.x = *(k_u32x8*)(A.pl + blk * 8);
+  r.d = A.d[blk];
+  r.qs = A.qs[blk];
+  return r;
+}
+
+// I of one block from its four code planes p and the token's scalar operands.
+template <int M>
+__device__ __forceinline__ int nib_I(const uint32_t (&p)[4], const BlkK& k) {
+  uint32_t L = __builtin_amdgcn_udot8(k.x[0], p[0], 0u, false);
+  // the first signed dot adds to an inline 0 (the compiler's choice, the
+  // accumulating VOP2 form, would need a zeroed register first)
+  int H;
+  asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(H) : "s"(k.x[4]), "v"(p[0]));
+  L = __builtin_amdgcn_udot8(k.x[1], p[1], L, false);
+  H = __builtin_amdgcn_sdot8((int)k.x[5], (int)p[1], H, false);
+  L = __builtin_amdgcn_udot8(k.x[2], p[2], L, false);
+  H = __builtin_amdgcn_sdot8((int)k.x[6], (int)p[2], H, false);
+  L = __builtin_amdgcn_udot8(k.x[3], p[3], L, false);
+  H = __builtin_amdgcn_sdot8((int)k.x[7], (int)p[3], H, false);
+  // 32 H + 2 L - m qsum as two shift-adds, -m qsum a scalar operand (written
+  // out: the compiler would rather shift and subtract separately)
+  int r;
+  asm("v_lshl_add_u32 %0, %1, 1, %2\n\t"
+      "v_lshl_add_u32 %0, %3, 5, %0"
+      : "=&v"(r)
+      : "v"(L), "s"(-M * k.qs), "v"(H));
+  return r;
+}
+
+// Scalar-operand pipeline of the 1- and 2-bit formats at batches up to 2.  A
+// wait for any scalar load waits for all of them (they return out of order),
+// so the operands of G blocks (every token) travel as one generation: right
+// after the wait for generation i the loads of generation i + 1 are issued,
+// and they land while generation i is computed.  Two generations of 20 scalar
+// registers are live.
+template <int NB>
+struct KPipe {
+  static constexpr int G = NB <= 2 ? 2 / NB : 1;  // blocks per generation (batches up to 2)
+  BlkK buf[2][G][NB];
+};
+
+template <int M, int PAR, int NB>
+__device__ __forceinline__ void kpipe_issue(KPipe<NB>& kp, const ActK& A, int kb) {
+  // The generation's base addresses pass through an empty asm: its loads can
+  // neither move above this point nor merge with another generation's loads
+  // (a merged load would be waited for with the current generation).
+  ActK a = A;
+  asm volatile("" : "+s"(a.pl), "+s"(a.d), "+s"(a.qs));
+  static_for(std::make_integer_sequence<int, KPipe<NB>::G>{}, [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) kp.buf[PAR][j][b] = load_blk(a, b, kb + j);
+  });
+}
+
+// Waits for every scalar (and LDS) load of the wave; nothing moves across.
+__device__ __forceinline__ void kpipe_wait() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Generation GI of a sub-chunk (blocks GI*G ..): with PIPE, wait for it and
+// issue the next one (the first of the following sub-chunk, kb_after, after
+// the last); without, load it and let the compiler wait.
+template <int M, int GI, bool PIPE, int NB>
+__device__ __forceinline__ void kpipe_step(KPipe<NB>& kp, const ActK& A, int kb0, int kbv, int kb_after) {
+  constexpr int G = KPipe<NB>::G, NGS = 8 / G;
+  if constexpr (PIPE) {
+    kpipe_wait();
+    if constexpr (GI + 1 < NGS) kpipe_issue<M, (GI + 1) & 1>(kp, A, kb0 + (GI + 1) * G);
+    else kpipe_issue<M, 0>(kp, A, kb_after);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    static_for(std::make_integer_sequence<int, G>{}, [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if (GI * G + j < kbv)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) kp.buf[GI & 1][j][b] = load_blk(A, b, kb0 + GI * G + j);
+    });
+  }
+}
+
+#define QK_DOT8(ACC, A, P, L) "v_dot8c_i32_i4_dpp " ACC ", " A ", " P " row_newbcast:" L " row_mask:0xf bank_mask:0xf\n\t"
+
+// Larger batches keep the DPP row-broadcast activations (ActSub, here holding
+// planes: lane 2KB of a row the lo words of block KB, lane 2KB+1 the hi words).
+// v_dot8c is signed on both sides, so the lo words arrive xor 0x88888888
+// (lo - 8 as a signed nibble) and c16 = 16 * (sum of the block's codes) adds
+// the 8 sum c back:  I = 2 (16 H + L') + c16 + Q,  Q = -m qsum.
+// out = d * I (MUL) or acc += d * I.
+template <int KB, bool MUL>
+__device__ __forceinline__ void nib_blk_dpp(float& acc, const ActSub& s, const uint32_t (&p)[4], uint32_t c16) {
+  int x, z;
+  if constexpr (MUL) {
+    asm("s_nop 1\n\t"
+        "v_mov_b32 %1, 0\n\t"
+        "v_mov_b32 %2, 0\n\t"
+        QK_DOT8("%1", "%3", "%7", "%c14") QK_DOT8("%2", "%3", "%7", "%c15")
+        QK_DOT8("%1", "%4", "%8", "%c14") QK_DOT8("%2", "%4", "%8", "%c15")
+        QK_DOT8("%1", "%5", "%9", "%c14") QK_DOT8("%2", "%5", "%9", "%c15")
+        QK_DOT8("%1", "%6", "%10", "%c14") QK_DOT8("%2", "%6", "%10", "%c15")
+        "s_nop 2\n\t"
+        "v_lshl_add_u32 %1, %2, 4, %1\n\t"
+        "v_lshl_add_u32 %1, %1, 1, %11\n\t"
+        "v_add_u32_dpp %1, %13, %1 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_cvt_f32_i32 %2, %1\n\t"
+        "v_mul_f32_dpp %0, %12, %2 row_newbcast:%c16 row_mask:0xf bank_mask:0xf"
+        : "=v"(acc), "=&v"(x), "=&v"(z)
+        : "v"(s.a[0]), "v"(s.a[1]), "v"(s.a[2]), "v"(s.a[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]),
+          "v"(c16), "v"(s.d), "v"(s.Q), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
+  } else {
+    asm("s_nop 1\n\t"
+        "v_mov_b32 %1, 0\n\t"
+        "v_mov_b32 %2, 0\n\t"
+        QK_DOT8("%1", "%3", "%7", "%c14") QK_DOT8("%2", "%3", "%7", "%c15")
+        QK_DOT8("%1", "%4", "%8", "%c14") QK_DOT8("%2", "%4", "%8", "%c15")
+        QK_DOT8("%1", "%5", "%9", "%c14") QK_DOT8("%2", "%5", "%9", "%c15")
+        QK_DOT8("%1", "%6", "%10", "%c14") QK_DOT8("%2", "%6", "%10", "%c15")
+        "s_nop 2\n\t"
+        "v_lshl_add_u32 %1, %2, 4, %1\n\t"
+        "v_lshl_add_u32 %1, %1, 1, %11\n\t"
+        "v_add_u32_dpp %1, %13, %1 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_cvt_f32_i32 %2, %1\n\t"
+        "v_fmac_f32_dpp %0, %12, %2 row_newbcast:%c16 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc), "=&v"(x), "=&v"(z)
+        : "v"(s.a[0]), "v"(s.a[1]), "v"(s.a[2]), "v"(s.a[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]),
+          "v"(c16), "v"(s.d), "v"(s.Q), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
+  }
+}
+
+// 1-bit block KB against DPP planes: acc += 2 d R, R = sum b x.  L starts at
+// 8 (sum of the block's bits), which puts back the 8 subtracted from every lo
+// word; the -qsum part, linear in d, is added once per scale block (ActSub::e).
+template <int KB>
+__device__ __forceinline__ int nib1_blk_dpp(float& acc, const ActSub& s, const ActS1& s1, const uint32_t (&p)[4],
+                                            uint32_t c8) {
+  int x = (int)c8, z;
+  asm("s_nop 1\n\t"
+      "v_mov_b32 %2, 0\n\t"
+      QK_DOT8("%1", "%3", "%7", "%c12") QK_DOT8("%2", "%3", "%7", "%c13")
+      QK_DOT8("%1", "%4", "%8", "%c12") QK_DOT8("%2", "%4", "%8", "%c13")
+      QK_DOT8("%1", "%5", "%9", "%c12") QK_DOT8("%2", "%5", "%9", "%c13")
+      QK_DOT8("%1", "%6", "%10", "%c12") QK_DOT8("%2", "%6", "%10", "%c13")
+      "s_nop 2\n\t"
+      "v_lshl_add_u32 %1, %2, 4, %1\n\t"
+      "v_cvt_f32_i32 %2, %1\n\t"
+      "v_fmac_f32_dpp %0, %11, %2 row_newbcast:%c14 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc), "+v"(x), "=&v"(z)
+      : "v"(s.a[0]), "v"(s.a[1]), "v"(s.a[2]), "v"(s.a[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]),
+        "v"(s1.d2), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
+  return x;
+}
+
+// 2 R + Q[KB]: the exact block dot I from R (test hook).  Volatile: the
+// broadcast reads lane KB, so it must run with the whole wave active (never
+// inside a branch on the lane's row).
+template <int KB>
+__device__ __forceinline__ int blk_I_dpp(int R, const ActSub& s) {
+  int t;
+  asm volatile("s_nop 1\n\t"
+      "v_add_u32_dpp %0, %1, %2 row_newbcast:%c3 row_mask:0xf bank_mask:0xf"
+      : "=v"(t)
+      : "v"(s.Q), "v"(R), "n"(KB));
+  return t + R;
+}
+
+// acc + e[LANE] (the scale block's -qsum part).
+template <int LANE>
+__device__ __forceinline__ float add_e_dpp(float acc, const ActS1& s) {
+  float r;
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %1, %2 row_newbcast:%c3 row_mask:0xf bank_mask:0xf"
+      : "=v"(r)
+      : "v"(s.e), "v"(acc), "n"(LANE));
+  return r;
+}
+
 // ---- per-format compute of one 256-weight sub-chunk --------------------------------------------------
 // T: the lane's row codes of the whole segment (dwords), SUB: sub-chunk index
-// in the segment, S: the segment's fp16 scales (pairs).  AS[b]: activations of
-// token b.  y accumulates (final per-format factor applied by the caller).
-template <int NB, int SUB, bool WI>
+// in the segment, S: the segment's fp16 scales (pairs).  AS[b]: DPP activations
+// of token b (batches above 2 and the byte formats), AK: scalar activation
+// views (1- and 2-bit at batches up to 2), kb0: the sub-chunk's first block,
+// kbv: its valid blocks (8 except in a tail).  y accumulates (final per-format
+// factor applied by the caller).
+template <int NB, int SUB, bool WI, bool PIPE>
 __device__ __forceinline__ void sub_sign1(const uint32_t (&T)[32], const uint32_t (&S)[4], const ActSub (&AS)[NB],
+                                          KPipe<NB>& kp, const ActK& AK, int kb0, int kbv, int kb_after,
                                           float (&y)[NB], int32_t* Iout) {
+  const uint32_t m1 = sgpr_const(0x11111111u);
+  ActS1 A1[NB];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {  // two 128-weight scale blocks
+  for (int b = 0; b < NB; ++b) A1[b] = act_s1(AS[b]);
+  static_for(std::make_integer_sequence<int, 2>{}, [&](auto hc) {  // two 128-weight scale blocks
+    constexpr int h = decltype(hc)::value;
     float acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+    static_for(std::make_integer_sequence<int, 4>{}, [&](auto jc) {
+      constexpr int kb = 4 * h + decltype(jc)::value;  // activation block within the sub-chunk
+      if (kb < kbv) {
+        const uint32_t W = T[SUB * 8 + kb];
+        const uint32_t p[4] = {W & m1, (W >> 1) & m1, (W >> 2) & m1, (W >> 3) & m1};
+        const uint32_t c8 = (uint32_t)__builtin_popcount(W) << 3;
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      const int kb = h * 4 + j4;  // activation block within the sub-chunk
-      const uint32_t W = T[SUB * 8 + kb];
-      uint32_t p[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t t = W >> j;
-        p[j] = t & 0x01010101u;
-        p[j + 4] = t & 0x10101010u;
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        int R;
-        switch (kb) {
-          case 0: R = blk_two_chain_fmac<0, false>(acc[b], AS[b], p); break;
-          case 1: R = blk_two_chain_fmac<1, false>(acc[b], AS[b], p); break;
-          case 2: R = blk_two_chain_fmac<2, false>(acc[b], AS[b], p); break;
-          case 3: R = blk_two_chain_fmac<3, false>(acc[b], AS[b], p); break;
-          case 4: R = blk_two_chain_fmac<4, false>(acc[b], AS[b], p); break;
-          case 5: R = blk_two_chain_fmac<5, false>(acc[b], AS[b], p); break;
-          case 6: R = blk_two_chain_fmac<6, false>(acc[b], AS[b], p); break;
-          default: R = blk_two_chain_fmac<7, false>(acc[b], AS[b], p); break;
+        for (int b = 0; b < NB; ++b) {
+          const int R = nib1_blk_dpp<kb>(acc[b], AS[b], A1[b], p, c8);
+          if constexpr (WI) {
+            if (b == 0) {
+              const int I = blk_I_dpp<kb>(R, AS[0]);
+              if (Iout) Iout[SUB * 8 + kb] = I;
+            }
+          }
         }
-        if (WI && b == 0 && Iout) Iout[SUB * 8 + kb] = R >> 3;
       }
-    }
+    });
     const float s = scale_half(S[SUB], h);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, acc[b], y[b]);
+    for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, add_e_dpp<4 * h + 3>(acc[b], A1[b]), y[b]);
+  });
+}
+
+template <int NB, int SUB, bool WI, bool PIPE>
+__device__ __forceinline__ void sub_int2(const uint32_t (&T)[32], const uint32_t (&S)[8], const ActSub (&AS)[NB],
+                                         KPipe<NB>& kp, const ActK& AK, int kb0, int kbv, int kb_after,
+                                         float (&y)[NB], int32_t* Iout) {
+  const uint32_t m3 = sgpr_const(0x33333333u);
+  auto planes = [&](int kb, uint32_t (&p)[4]) {
+    const uint32_t W0 = T[SUB * 16 + 2 * kb], W1 = T[SUB * 16 + 2 * kb + 1];
+    p[0] = W0 & m3;
+    p[1] = (W0 >> 2) & m3;
+    p[2] = W1 & m3;
+    p[3] = (W1 >> 2) & m3;
+  };
+  auto scale = [&](int kb) {
+    const int si = SUB * 8 + kb;  // scale index within the segment
+    return scale_half(S[si >> 1], si & 1);
+  };
+  if constexpr (NB <= 2) {
+    constexpr int G = KPipe<NB>::G;
+    static_for(std::make_integer_sequence<int, 8 / G>{}, [&](auto gc) {
+      constexpr int GI = decltype(gc)::value;
+      kpipe_step<3, GI, PIPE>(kp, AK, kb0, kbv, kb_after);
+      static_for(std::make_integer_sequence<int, G>{}, [&](auto jc) {
+        constexpr int kb = GI * G + decltype(jc)::value;
+        if (kb < kbv) {
+          uint32_t p[4];
+          planes(kb, p);
+          const float s = scale(kb);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const BlkK& k = kp.buf[GI & 1][kb - GI * G][b];
+            const int I = nib_I<3>(p, k);
+            if (WI && b == 0 && Iout) Iout[SUB * 8 + kb] = I;
+            y[b] = __builtin_fmaf(s, k.d * (float)I, y[b]);
+          }
+        }
+      });
+    });
+  } else {
+    static_for(std::make_integer_sequence<int, 8>{}, [&](auto kc) {
+      constexpr int kb = decltype(kc)::value;
+      if (kb < kbv) {
+        uint32_t p[4];
+        planes(kb, p);
+        const float s = scale(kb);
+        // sum of the block's 32 codes: nibble sums of the 4 planes stay below 16
+        const uint32_t csum = __builtin_amdgcn_udot8(p[0] + p[1] + p[2] + p[3], 0x11111111u, 0u, false);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          float t;
+          nib_blk_dpp<kb, true>(t, AS[b], p, csum << 4);
+          y[b] = __builtin_fmaf(s, t, y[b]);
+        }
+      }
+    });
   }
 }
 
@@ -249,8 +511,7 @@ __device__ __forceinline__ void blk_dispatch(float (&out)[NB], const ActSub (&AS
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     int R;
-    if constexpr (MODE == 0) R = blk_two_chain_fmac<KB, true>(out[b], AS[b], p) >> 3;   // INT2: R = 8 I
-    else if constexpr (MODE == 1) R = blk_one_chain_mul2<KB>(out[b], AS[b], p);          // INT4
+    if constexpr (MODE == 1) R = blk_one_chain_mul2<KB>(out[b], AS[b], p);               // INT4
     else R = blk_one_chain_fmac<KB>(out[b], AS[b], p);                                   // TERN, TRELLIS
     if (WI && b == 0 && Iout) Iout[idx] = R;
   }
@@ -268,25 +529,6 @@ __device__ __forceinline__ void blk_any(int kb, float (&out)[NB], const ActSub (
     case 5: blk_dispatch<5, NB, WI, MODE>(out, AS, p, Iout, idx); break;
     case 6: blk_dispatch<6, NB, WI, MODE>(out, AS, p, Iout, idx); break;
     default: blk_dispatch<7, NB, WI, MODE>(out, AS, p, Iout, idx); break;
-  }
-}
-
-template <int NB, int SUB, bool WI>
-__device__ __forceinline__ void sub_int2(const uint32_t (&T)[32], const uint32_t (&S)[8], const ActSub (&AS)[NB],
-                                         float (&y)[NB], int32_t* Iout) {
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb) {
-    const uint32_t W0 = T[SUB * 16 + 2 * kb], W1 = T[SUB * 16 + 2 * kb + 1];
-    const uint32_t V0 = W0 >> 2, V1 = W1 >> 2;
-    // levels of activation dwords 0..7 (dwords 2, 3, 6, 7 carry 16x)
-    const uint32_t p[8] = {W0 & 0x03030303u, V0 & 0x03030303u, W0 & 0x30303030u, V0 & 0x30303030u,
-                           W1 & 0x03030303u, V1 & 0x03030303u, W1 & 0x30303030u, V1 & 0x30303030u};
-    float t[NB];
-    blk_any<NB, WI, 0>(kb, t, AS, p, Iout, SUB * 8 + kb);
-    const int si = SUB * 8 + kb;  // scale index within the segment
-    const float s = scale_half(S[si >> 1], si & 1);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, t[b], y[b]);
   }
 }
 
@@ -406,15 +648,10 @@ __device__ __forceinline__ void load_scales(g_u16* p, uint32_t (&S)[SPS / 2]) {
   }
 }
 
-template <int... I, typename F>
-__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-
 // Multiple of qsum each format's block result subtracts (see the asm blocks).
 template <int FMT> struct QMul;
-template <> struct QMul<QFMT_SIGN1> { static constexpr int v = 8; };
-template <> struct QMul<QFMT_INT2> { static constexpr int v = 24; };
+template <> struct QMul<QFMT_SIGN1> { static constexpr int v = 1; };
+template <> struct QMul<QFMT_INT2> { static constexpr int v = 3; };
 template <> struct QMul<QFMT_INT4> { static constexpr int v = 15; };
 template <> struct QMul<QFMT_TERN_B3> { static constexpr int v = 1; };
 template <> struct QMul<QFMT_TRELLIS2> { static constexpr int v = 0; };
@@ -424,6 +661,12 @@ __device__ __forceinline__ void load_act_all(ActSub (&dst)[NB], const ActG& AG, 
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     load_act<QMul<FMT>::v>(dst[b], AG, b, kb_base);
+    if constexpr (FMT == QFMT_SIGN1 || FMT == QFMT_INT2) {
+      // plane words: even lanes of a row hold lo words, used as lo - 8 (signed)
+      const uint32_t f = (threadIdx.x & 1) ? 0u : 0x88888888u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[b].a[k] = (int32_t)((uint32_t)dst[b].a[k] ^ f);
+    }
     if (kbv < 8 && (int)(threadIdx.x & 7) >= kbv) {  // blocks past the end of K contribute nothing
       dst[b].d = 0.0f;
       dst[b].Q = 0;
@@ -433,12 +676,13 @@ __device__ __forceinline__ void load_act_all(ActSub (&dst)[NB], const ActG& AG, 
 
 // One sub-chunk of a segment; Ib: test-hook row output at the sub-chunk's
 // first activation block (entries below ivalid are written).
-template <int FMT, int NB, int SUB, bool WI>
+template <int FMT, int NB, int SUB, bool WI, bool PIPE = false>
 __device__ __forceinline__ void sub_compute(const uint32_t (&T)[Seg<FMT>::CH * 4], const uint32_t (&S)[Seg<FMT>::SPS / 2],
-                                            const ActSub (&AS)[NB], uint32_t& prev, const int8_t* v8, float (&y)[NB],
+                                            const ActSub (&AS)[NB], KPipe<NB>& kp, const ActK& AK, int kb0, int kbv,
+                                            int kb_after, uint32_t& prev, const int8_t* v8, float (&y)[NB],
                                             int32_t* Iseg) {
-  if constexpr (FMT == QFMT_SIGN1) sub_sign1<NB, SUB, WI>(T, S, AS, y, Iseg);
-  else if constexpr (FMT == QFMT_INT2) sub_int2<NB, SUB, WI>(T, S, AS, y, Iseg);
+  if constexpr (FMT == QFMT_SIGN1) sub_sign1<NB, SUB, WI, PIPE>(T, S, AS, kp, AK, kb0, kbv, kb_after, y, Iseg);
+  else if constexpr (FMT == QFMT_INT2) sub_int2<NB, SUB, WI, PIPE>(T, S, AS, kp, AK, kb0, kbv, kb_after, y, Iseg);
   else if constexpr (FMT == QFMT_INT4) sub_int4<NB, WI>(T, S, AS, y, Iseg);
   else if constexpr (FMT == QFMT_TERN_B3) sub_tern<NB, SUB, WI>(T, S, AS, y, Iseg);
   else sub_trellis<NB, SUB, WI>(T, S, AS, prev, v8, y, Iseg);
@@ -447,8 +691,8 @@ __device__ __forceinline__ void sub_compute(const uint32_t (&T)[Seg<FMT>::CH * 4
 // Result scale applied once per row after accumulation.
 template <int FMT>
 __device__ __forceinline__ float final_scale(float trellis_gain) {
-  if constexpr (FMT == QFMT_SIGN1) return 0.125f;
-  else if constexpr (FMT == QFMT_INT2) return 0.0625f;
+  if constexpr (FMT == QFMT_SIGN1) return 1.0f;
+  else if constexpr (FMT == QFMT_INT2) return 0.5f;
   else if constexpr (FMT == QFMT_INT4) return 0.5f;
   else if constexpr (FMT == QFMT_TERN_B3) return 1.0f;
   else return trellis_gain;
@@ -460,6 +704,13 @@ __device__ __forceinline__ float final_scale(float trellis_gain) {
 // the wait before an LDS read of a DMA'd region.
 __device__ __forceinline__ void wait_vm_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Waits for every load of the wave (vector, LDS-DMA, scalar and LDS).
+__device__ __forceinline__ void wait_all() {
+  __builtin_amdgcn_s_waitcnt(0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -494,6 +745,14 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   AG.qs = gptr<const int32_t __attribute__((address_space(1)))*>(it.qsum);
   AG.K = K;
   AG.kbs = K >> 5;
+  // 2-bit at batches up to 2: activations by scalar loads only
+  constexpr bool KACT = FMT == QFMT_INT2 && NB <= 2;
+  ActK AK;
+  AK.pl = gptr<k_u32*>(it.q);
+  AK.d = gptr<k_f32*>(it.d);
+  AK.qs = gptr<k_i32*>(it.qsum);
+  AK.kbs = K >> 5;
+  KPipe<NB> kp;
 
   // This lane's scales for segment sg: slot `lane` of the tile's group sg (rows
   // past the end read zero padding).
@@ -521,8 +780,9 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     const int c = CH == 8 ? (pos ^ ((r >> 1) & 7)) : pos;
     return (uint32_t)(min(r, nvalid - 1) * rb + c * 16);
   };
-  // Batches up to 2 keep the offsets in registers; larger batches, short of
-  // registers, recompute them at each issue (a few VALU per load).
+  // The whole-segment pipeline (batches up to 2) keeps the offsets
+  // in registers; the sub-chunk loop, short of registers, recomputes them at
+  // each issue (a few VALU per load).
   constexpr int NOFF = NB <= 2 ? CH : 1;
   uint32_t goff[NOFF];
 #pragma unroll
@@ -535,7 +795,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     const uint32_t keep = real ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const uint32_t off = NB <= 2 ? goff[i < NOFF ? i : 0] : tile_off(i);
+      const uint32_t off = NOFF == CH ? goff[i < NOFF ? i : 0] : tile_off(i);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tseg + (off & keep)),
                                        (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0, kTileCachePolicy);
     }
@@ -571,18 +831,23 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     if constexpr (FMT == QFMT_TRELLIS2) return sg == 0 ? raw : (((raw & 0xFFu) << 8) | (raw >> 8));
     else return 0u;
   };
-  if constexpr (NB <= 2) {
+  constexpr bool SEGPIPE = NB <= 2;
+  if constexpr (SEGPIPE) {
     // Whole-segment pipeline: at the top of a segment everything in flight is
-    // waited for once; then the next segment's activations, scales and tile DMA
-    // are issued (activations first) and the current segment is computed from
-    // registers with no further waits.  (LDS-DMA loads and ordinary loads in
-    // flight together make any later wait a full drain, so no ordinary load may
-    // be waited for between a DMA issue and the next segment top.)
-    ActSub acur[NSUB][NB], anxt[NSUB][NB];
+    // waited for once; then the next segment's scales and tile DMA are issued
+    // and the current segment is computed from registers with no further
+    // vector-memory waits.  Each sub-chunk's activation registers are refilled
+    // with the next segment's right after the sub-chunk is computed.  (LDS-DMA
+    // loads and ordinary loads in flight together make any later wait a full
+    // drain, so no ordinary load may be waited for between a DMA issue and the
+    // next segment top.)
+    ActSub act[NSUB][NB];
     uint32_t prevn = 0;
     if (seg < nseg) {
+      if constexpr (KACT) kpipe_issue<QMul<FMT>::v, 0>(kp, AK, seg * (SEGK / 32));  // first generation
 #pragma unroll
-      for (int sc = 0; sc < NSUB; ++sc) load_act_all<FMT, NB>(anxt[sc], AG, seg * (SEGK / 32) + sc * 8, 8);
+      for (int sc = 0; sc < NSUB; ++sc)
+        if constexpr (!KACT) load_act_all<FMT, NB>(act[sc], AG, seg * (SEGK / 32) + sc * 8, 8);
       load_scales<SPS>(sptr(seg), Sn);
       prevn = trellis_prev_raw(seg);
       issue_tile(seg, true);
@@ -593,10 +858,6 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
       read_row(T);
 #pragma unroll
       for (int i = 0; i < SPS / 2; ++i) S[i] = Sn[i];
-#pragma unroll
-      for (int sc = 0; sc < NSUB; ++sc)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acur[sc][b] = anxt[sc][b];
       uint32_t prev = trellis_prev_fix(seg, prevn);
       // the tile reads must be complete before the next DMA overwrites the region
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -605,15 +866,22 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
       const int nx = seg + nwk;
       const bool more_seg = nx < nseg;
       const int nsg = more_seg ? nx : seg;  // a last iteration re-reads valid data
-#pragma unroll
-      for (int sc = 0; sc < NSUB; ++sc) load_act_all<FMT, NB>(anxt[sc], AG, nsg * (SEGK / 32) + sc * 8, 8);
       load_scales<SPS>(sptr(nsg), Sn);
       prevn = trellis_prev_raw(nsg);
       issue_tile(nx, more_seg);
       __builtin_amdgcn_sched_barrier(0);
       static_for(std::make_integer_sequence<int, NSUB>{}, [&](auto scc) {
         constexpr int SUB = decltype(scc)::value;
-        sub_compute<FMT, NB, SUB, WI>(T, S, acur[SUB], prev, v8, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
+        // the block the scalar pipeline loads after this sub-chunk
+        const int kb_after = SUB + 1 < NSUB ? seg * (SEGK / 32) + (SUB + 1) * 8 : nsg * (SEGK / 32);
+        sub_compute<FMT, NB, SUB, WI, KACT>(T, S, act[SUB], kp, AK, seg * (SEGK / 32) + SUB * 8, 8, kb_after, prev,
+                                            v8, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
+        if constexpr (!KACT) {
+          // kept after the sub-chunk's compute: the new values take its registers
+          __builtin_amdgcn_sched_barrier(0);
+          load_act_all<FMT, NB>(act[SUB], AG, nsg * (SEGK / 32) + SUB * 8, 8);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       });
     }
   } else {
@@ -663,7 +931,8 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
         const int nkb = (SUB + 1 < NSUB) ? seg * (SEGK / 32) + (SUB + 1) * 8
                                          : (more_seg ? nx : seg) * (SEGK / 32);
         load_act_all<FMT, NB>(nxt, AG, nkb, 8);
-        sub_compute<FMT, NB, SUB, WI>(T, S, cur, prev, v8, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
+        sub_compute<FMT, NB, SUB, WI>(T, S, cur, kp, AK, seg * (SEGK / 32) + SUB * 8, 8, 0, prev, v8, y,
+                                      Irow ? Irow + seg * (SEGK / 32) : nullptr);
 #pragma unroll
         for (int b = 0; b < NB; ++b) cur[b] = nxt[b];
       });
@@ -694,12 +963,13 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
       const int kbv = nkb_tail - SUB * 8;  // valid activation blocks in this sub-chunk
       if (kbv > 0) {
         ActSub at[NB];
-        load_act_all<FMT, NB>(at, AG, kb0 + SUB * 8, kbv);
+        if constexpr (!KACT) load_act_all<FMT, NB>(at, AG, kb0 + SUB * 8, kbv);
         float yt[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) yt[b] = 0.0f;
         // the test hook must not write past the row's last block: bounded copy
-        sub_compute<FMT, NB, SUB, WI>(T, St, at, prev, v8, yt, WI && Irow ? Ib : nullptr);
+        sub_compute<FMT, NB, SUB, WI>(T, St, at, kp, AK, kb0 + SUB * 8, kbv, 0, prev, v8, yt,
+                                      WI && Irow ? Ib : nullptr);
         if (WI && Irow) {
 #pragma unroll
           for (int j = 0; j < 8; ++j)
@@ -733,7 +1003,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float ga
 #pragma unroll
   for (int b = 0; b < NB; ++b) y[b] = 0.0f;
   gemv_tile<FMT, NB, WI>(it, row0, wave, 4, lds + wave * Seg<FMT>::CH * 1024, v8, y, Iout);
-  wait_vm_all();  // no tile DMA may still be landing in LDS when the wave ends
+  wait_all();  // no tile DMA or scalar load may still be landing when the wave ends
   if (WI) return;
 #pragma unroll
   for (int b = 0; b < NB; ++b) red[wave][b][lane] = y[b];
@@ -783,20 +1053,14 @@ __global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict_
     float y[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) y[b] = 0.0f;
-    float fs = 1.0f;
-    switch (fmt) {
-      case QFMT_SIGN1: gemv_tile<QFMT_SIGN1, NB, false>(it, row0, 0, 1, my, v8, y, nullptr); fs = 0.125f; break;
-      case QFMT_INT2: gemv_tile<QFMT_INT2, NB, false>(it, row0, 0, 1, my, v8, y, nullptr); fs = 0.0625f; break;
-      case QFMT_INT4: gemv_tile<QFMT_INT4, NB, false>(it, row0, 0, 1, my, v8, y, nullptr); fs = 0.5f; break;
-      case QFMT_TERN_B3: gemv_tile<QFMT_TERN_B3, NB, false>(it, row0, 0, 1, my, v8, y, nullptr); fs = 1.0f; break;
-      default: gemv_tile<QFMT_TRELLIS2, NB, false>(it, row0, 0, 1, my, v8, y, nullptr); fs = gain; break;
-    }
+    gemv_tile<fmt, NB, false>(it, row0, 0, 1, my, v8, y, nullptr);
+    const float fs = final_scale<fmt>(gain);
     if (row0 + lane < it.rows) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) gptr<g_f32*>(it.y)[(int64_t)b * it.rows + row0 + lane] = y[b] * fs;
     }
   }
-  wait_vm_all();  // no tile DMA may still be landing in LDS when the wave ends
+  wait_all();  // no tile DMA or scalar load may still be landing when the wave ends
 }
 
 }  // namespace qk

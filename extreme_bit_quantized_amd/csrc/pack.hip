@@ -38,12 +38,18 @@ __device__ __forceinline__ void write_tern_block(Get tr, uint32_t* out) {
   }
 }
 
-// Plane word of `per_word` codes with `bits` bits: code k at 8*(k%4) + (k/4)*bits.
+// Bit offset of code k inside its 32-bit word: 1- and 2-bit codes nibble-lane
+// (code 8j + n in nibble n at offset j * bits), 4-bit codes byte-lane (code
+// 4j + b in byte b at offset 4j).
+__device__ __forceinline__ int plane_bitpos(int k, int bits) {
+  return bits == 4 ? 8 * (k & 3) + 4 * (k >> 2) : 4 * (k & 7) + (k >> 3) * bits;
+}
+// Plane word of `per_word` codes with `bits` bits: code k at plane_bitpos(k, bits).
 template <typename Get>
 __device__ __forceinline__ uint32_t plane_word(Get c, int bits) {
   const int per_word = 32 / bits;
   uint32_t w = 0;
-  for (int k = 0; k < per_word; ++k) w |= ((uint32_t)c(k) & ((1u << bits) - 1)) << (8 * (k & 3) + (k >> 2) * bits);
+  for (int k = 0; k < per_word; ++k) w |= ((uint32_t)c(k) & ((1u << bits) - 1)) << plane_bitpos(k, bits);
   return w;
 }
 
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(256) void k_unpack_i8(GemvItem it, int8_t* __restri
     for (int k = 0; k < 32; ++k) {
       const uint32_t wv = words[k / per_word];
       const int kk = k % per_word;
-      const int c = (int)((wv >> (8 * (kk & 3) + (kk >> 2) * bits)) & ((1u << bits) - 1));
+      const int c = (int)((wv >> plane_bitpos(kk, bits)) & ((1u << bits) - 1));
       out[k] = (int8_t)(it.fmt == QFMT_INT2 ? 2 * c - 3 : it.fmt == QFMT_SIGN1 ? 2 * c - 1 : 2 * c - 15);
     }
     dw[id] = (it.fmt == QFMT_SIGN1) ? s : 0.5f * s;

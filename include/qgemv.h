@@ -61,9 +61,12 @@ const char* qstrerror(int err);
  *    i holds weight 20m + 4i + p; word 12, byte p, digit i < 4 holds weight
  *    240 + 4i + p and its digit 4 is 1.  Row bytes 52*cols/256.
  *  QFMT_INT2 (block 32): four levels (2c - 3)/2 * s, c = 0..3.  One 32-bit
- *    word per 16 weights; weight 4j + b (j, b = 0..3) is bits 8b+2j .. 8b+2j+1.
- *  QFMT_SIGN1 (block 128): levels (2b - 1) * s.  One 32-bit word per 32 weights;
- *    weight 4j + b (j = 0..7, b = 0..3) is bit 8b + j.
+ *    word per 16 weights; weight 8j + n (j = 0..1, n = 0..7) is bits
+ *    4n+2j .. 4n+2j+1 (nibble-lane order: (word >> 2j) & 0x33333333 holds
+ *    weights 8j .. 8j+7, one per nibble).
+ *  QFMT_SIGN1 (block 128): levels (2b - 1) * s, 8 weights per byte ([P5] §二).
+ *    One 32-bit word per 32 weights; weight 8j + n (j = 0..3, n = 0..7) is bit
+ *    4n + j (nibble-lane order, as for INT2).
  *  QFMT_INT4 (block 32): sixteen levels (2c - 15)/2 * s.  One 32-bit word per 8
  *    weights; weight 4j + b (j = 0..1) is bits 8b+4j .. 8b+4j+3.
  *  QFMT_TRELLIS2 (block 64): 2-bit bit-shift trellis codes with a codebook
@@ -159,6 +162,16 @@ int qweight_pack(int32_t fmt, const int8_t* levels, int32_t rows, int32_t cols,
 int qact_quant_i8(const float* x, int32_t B, int32_t K, int32_t qblock,
                   int8_t* q, float* d, int32_t* qsum, void* stream);
 
+/* 4-bit planes of int8 activations, the form in which the INT2 and SIGN1 GEMV
+ * read the int8 activations of qact_quant_i8 (it multiplies 4-bit code planes
+ * against them with 8-way nibble dot products).  q [B][K] int8 (device,
+ * 4-byte aligned), K a positive multiple of 32 -> planes [B][K/32][8] uint32
+ * (device, 32-byte aligned).  For every 32-block and group g = 0..3 of the
+ * values x_n = q[32 kb + 8 g + n], n = 0..7: word g = sum_n (x_n mod 16) << 4n
+ * and word 4 + g = sum_n (floor(x_n / 16) mod 16) << 4n, so x_n = 16 hi + lo
+ * with lo unsigned and hi a two's complement nibble.  Integer, bit-exact. */
+int qact_planes(const int8_t* q, int32_t B, int32_t K, uint32_t* planes, void* stream);
+
 /* Block-randomized Walsh-Hadamard rotation then Q8 (the random Hadamard
  * rotation of [P2] "12 GB 装下 27B", applied to activations): per token and
  * 256-block, u = sigma * x with sigma_k = -1 where bit k%32 of sign_bits[k/32]
@@ -181,16 +194,20 @@ int qact_hadamard_quant_i8(const float* x, int32_t B, int32_t K, const uint32_t*
  * weights are decoded once for all tokens ([P5] §五: checking 16 tokens costs
  * about as much as 1 when the product is bandwidth-bound).
  * Inputs (device): q [B][K] int8 (16-byte aligned), d [B][K/32] fp32,
- * qsum [B][K/32] int32 (block sums of q, as written by qact_quant_i8).
+ * qsum [B][K/32] int32 (block sums of q, as written by qact_quant_i8), and
+ * planes [B][K/32][8] (32-byte aligned, qact_planes of q).  INT2 and SIGN1
+ * read planes and may get q = NULL; the other formats read q and may get
+ * planes = NULL.
  * Output y [B][rows] fp32 (device), overwritten.  1 <= B <= 8.
  * Accuracy: I exact; |y - y_exact| <= 1e-4 * sum|T| (fp32 accumulation). */
-int qgemv(const qweight_t* w, const int8_t* q, const float* d, const int32_t* qsum,
-          int32_t B, float* y, void* stream);
+int qgemv(const qweight_t* w, const int8_t* q, const uint32_t* planes, const float* d,
+          const int32_t* qsum, int32_t B, float* y, void* stream);
 
 /* Test hook: the exact integer block dots I [rows][cols/32] int32 (device) of
- * the GEMV above for a single token (B = 1), written by the same decode. */
-int qgemv_blockdots(const qweight_t* w, const int8_t* q, const int32_t* qsum,
-                    int32_t* out, void* stream);
+ * the GEMV above for a single token (B = 1), written by the same decode
+ * (q and planes as for qgemv). */
+int qgemv_blockdots(const qweight_t* w, const int8_t* q, const uint32_t* planes,
+                    const int32_t* qsum, int32_t* out, void* stream);
 
 /* ---- grouped GEMV: many matrices in one persistent launch --------------------------
  * Fusing many small single-token kernels was part of the 3x decode gain of the
@@ -199,8 +216,9 @@ int qgemv_blockdots(const qweight_t* w, const int8_t* q, const int32_t* qsum,
  * stores the device pointers of every item; it stays valid while they do. */
 typedef struct qgemv_item {
   qweight_t w;
-  const int8_t* q;      /* [B][w.cols] (device) */
-  const float* d;       /* [B][w.cols/32] (device) */
+  const int8_t* q;          /* [B][w.cols] (device); may be NULL for INT2, SIGN1 */
+  const uint32_t* planes;   /* [B][w.cols/32][8] (device); may be NULL except for INT2, SIGN1 */
+  const float* d;           /* [B][w.cols/32] (device) */
   const int32_t* qsum;  /* [B][w.cols/32] (device) */
   float* y;             /* [B][w.rows] (device), must not overlap another item's y */
 } qgemv_item_t;

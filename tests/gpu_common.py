@@ -83,6 +83,19 @@ def gpu_act(x, qblock=32):
     return q, d, s
 
 
+def gpu_act_planes(x):
+    """Q8 per 32 plus the 4-bit planes of q: (q, planes, d, qsum) on the device."""
+    import torch
+
+    import extreme_bit_quantized_amd as ebq
+
+    q, d, s = gpu_act(x)
+    B, K = q.shape
+    planes = torch.empty((B, K // 32, 8), dtype=torch.int32, device="cuda")
+    ebq.qact_planes(q, planes)
+    return q, planes, d, s
+
+
 def assert_close_terms(y_gpu, y_ref, absT, rel=1e-4, what=""):
     """|y_gpu - y_ref| <= rel * sum|T|, and y_gpu == 0 exactly where sum|T| == 0."""
     y_gpu = np.asarray(y_gpu, np.float64)

@@ -131,11 +131,25 @@ def test_call_validation_without_gpu(ebq):
     d = _desc(ebq)
     w = ctypes.byref(d)
     A = 1 << 20  # fake, aligned "device" addresses: every call below is rejected before launch
-    assert L.qgemv(w, A, A, A, 9, A, None) == -1
-    assert L.qgemv(w, A, A, A, 0, A, None) == 0            # empty batch: no-op
-    assert L.qgemv(w, A + 4, A, A, 1, A, None) == -4
-    assert L.qgemv(w, None, A, A, 1, A, None) == -1
-    assert L.qgemv(w, A, A, A, 1, A + 2, None) == -4
+    assert L.qgemv(w, A, A, A, A, 9, A, None) == -1
+    assert L.qgemv(w, A, A, A, A, 0, A, None) == 0         # empty batch: no-op
+    # 1-bit reads the activation planes (32-byte aligned); q is not needed
+    assert L.qgemv(w, A, A + 16, A, A, 1, A, None) == -4
+    assert L.qgemv(w, A, None, A, A, 1, A, None) == -1
+    assert L.qgemv(w, None, A, A, A, 1, A + 2, None) == -4
+    assert L.qgemv(w, None, A, None, A, 1, A, None) == -1
+    # ternary reads q (16-byte aligned); planes are not needed
+    t = ctypes.byref(_desc(ebq, fmt=1))
+    assert L.qgemv(t, A + 4, None, A, A, 1, A, None) == -4
+    assert L.qgemv(t, None, A, A, A, 1, A, None) == -1
+    assert L.qgemv(t, A, None, A, A, 1, A + 2, None) == -4
+    assert L.qgemv_blockdots(w, A, None, A, A, None) == -1
+    assert L.qgemv_blockdots(t, A, None, A, A + 2, None) == -4
+    assert L.qact_planes(A, 1, 48, A, None) == -3
+    assert L.qact_planes(A, 1, 64, A + 16, None) == -4
+    assert L.qact_planes(A + 2, 1, 64, A, None) == -4
+    assert L.qact_planes(A, 0, 64, A, None) == 0
+    assert L.qact_planes(None, 1, 64, A, None) == -1
     assert L.qact_quant_i8(A, 1, 1024, 64, A, A, A, None) == -1
     assert L.qact_quant_i8(A, 1, 48, 32, A, A, A, None) == -3
     assert L.qact_quant_i8(A, 0, 1024, 32, A, A, A, None) == 0
@@ -148,7 +162,7 @@ def test_call_validation_without_gpu(ebq):
     assert L.qtrellis_decode_i8(w, 256, A, A, None) == -2   # not a trellis matrix
     assert L.qweight_quantize(5, A, 4, 256, A, 64, A, None) == -2
     assert L.qweight_pack(2, A, 4, 48, A, 16, None) == -3
-    assert L.qgemv_grouped_run(None, A, A, 256, None) == -1
+    assert L.qgemv_grouped_run(None, A, None) == -1
     assert ebq.load().qstrerror(-4).decode().startswith("pointer")
 
 
@@ -160,7 +174,7 @@ def test_grouped_plan_on_host(ebq):
     descs = [_desc(ebq, fmt=f, rows=n, cols=k, codes=A, scales=A) for f, n, k in shapes]
     items = (ebq.qgemv_item_t * len(descs))()
     for i, d in enumerate(descs):
-        items[i] = ebq.qgemv_item_t(d, A, A, A, A)
+        items[i] = ebq.qgemv_item_t(d, A, A, A, A, A)
     nb = ebq.qgemv_grouped_plan_bytes(items, 2)
     raw = torch.zeros(nb + 16, dtype=torch.uint8)
     off = (-raw.data_ptr()) % 16

@@ -6,8 +6,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import (INT2, INT4, NAMES, SIGN1, TERN, TRELLIS, assert_close_terms, dev, gpu_act, gpu_scales_rowmajor,
-                        gpu_weight, host, oracle_weight, raw_weight)
+from gpu_common import (INT2, INT4, NAMES, SIGN1, TERN, TRELLIS, assert_close_terms, dev, gpu_act, gpu_act_planes,
+                        gpu_scales_rowmajor, gpu_weight, host, oracle_weight, raw_weight)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,16 @@ def test_act_quant_bit_exact(B, K, qblock):
     assert (host(q) == rq).all()
     assert (host(d).view(np.uint32) == rd.view(np.uint32)).all()
     assert (host(s) == rs).all()
+
+
+@pytest.mark.parametrize("B,K", [(1, 32), (3, 1024), (5, 17408), (64, 5120)])
+def test_act_planes_bit_exact(B, K):
+    x = synth.gauss([105, B, K], (B, K))
+    n = min(K, 64)
+    x[0, :n] = np.linspace(-127, 127, n, dtype=np.float32)      # the whole int8 range
+    q, pl, d, s = gpu_act_planes(x)
+    _sync()
+    assert (host(pl).view(np.uint32) == oracle.act_planes(host(q))).all()
 
 
 def test_act_quant_empty_batch():
@@ -136,9 +146,9 @@ def _prep(fmt, N, K, seed, B=1):
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_blockdots_bit_exact(fmt, N, K):
     raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 140 + fmt)
-    q, d, s = gpu_act(x)
+    q, pl, d, s = gpu_act_planes(x)
     out = torch.full((N, K // 32), -7, dtype=torch.int32, device="cuda")
-    ebq.qgemv_blockdots(pw, q, s, out)
+    ebq.qgemv_blockdots(pw, q, pl, s, out)
     _sync()
     rq, rd, _ = oracle.act_quant(x)
     _, _, I = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd, want_I=True)
@@ -150,9 +160,9 @@ def test_blockdots_bit_exact(fmt, N, K):
 @pytest.mark.parametrize("B", [1, 3, 8])
 def test_gemv_parity(fmt, N, K, B):
     raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 150 + fmt + B, B)
-    q, d, s = gpu_act(x)
+    q, pl, d, s = gpu_act_planes(x)
     y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
-    ebq.qgemv(pw, q, d, s, B, y)
+    ebq.qgemv(pw, q, pl, d, s, B, y)
     _sync()
     rq, rd, _ = oracle.act_quant(x)
     yr, absT, _ = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd)
@@ -163,9 +173,9 @@ def test_gemv_parity(fmt, N, K, B):
 def test_gemv_every_batch_size(B):
     fmt, N, K = SIGN1, 96, 2048
     raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 160 + B, B)
-    q, d, s = gpu_act(x)
+    q, pl, d, s = gpu_act_planes(x)
     y = torch.empty((B, N), dtype=torch.float32, device="cuda")
-    ebq.qgemv(pw, q, d, s, B, y)
+    ebq.qgemv(pw, q, pl, d, s, B, y)
     _sync()
     rq, rd, _ = oracle.act_quant(x)
     yr, absT, _ = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd)
@@ -175,11 +185,11 @@ def test_gemv_every_batch_size(B):
 def test_gemv_deterministic():
     fmt, N, K = TERN, 300, 5120
     raw, pw, _, x = _prep(fmt, N, K, 170)
-    q, d, s = gpu_act(x)
+    q, pl, d, s = gpu_act_planes(x)
     y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
     y2 = torch.empty_like(y1)
-    ebq.qgemv(pw, q, d, s, 1, y1)
-    ebq.qgemv(pw, q, d, s, 1, y2)
+    ebq.qgemv(pw, q, pl, d, s, 1, y1)
+    ebq.qgemv(pw, q, pl, d, s, 1, y2)
     _sync()
     assert (host(y1).view(np.uint32) == host(y2).view(np.uint32)).all()
 
@@ -202,9 +212,9 @@ def test_gemv_edge_cases(fmt):
     x = synth.gauss([182], (3, K))
     x[1] = 0.0                                              # zero activations
     x[2, :] = 127.0                                         # every q = 127
-    q, d, s = gpu_act(x)
+    q, pl, d, s = gpu_act_planes(x)
     y = torch.empty((3, N), dtype=torch.float32, device="cuda")
-    ebq.qgemv(pw, q, d, s, 3, y)
+    ebq.qgemv(pw, q, pl, d, s, 3, y)
     _sync()
     rq, rd, _ = oracle.act_quant(x)
     yr, absT, _ = oracle.gemv(fmt, rp, rs, None, K, rq, rd)
@@ -221,9 +231,9 @@ def test_sign_balanced_rows_give_exact_zero():
     scales = synth.uniform_f16([183], (N, K // 128), 0.5, 1.0)
     pw = gpu_weight(SIGN1, {"codes": codes, "scales": scales}, N, K)
     x = np.full((1, K), 3.0, np.float32)
-    q, d, s = gpu_act(x)
+    q, pl, d, s = gpu_act_planes(x)
     y = torch.empty((1, N), dtype=torch.float32, device="cuda")
-    ebq.qgemv(pw, q, d, s, 1, y)
+    ebq.qgemv(pw, q, pl, d, s, 1, y)
     _sync()
     assert (host(y) == 0).all()
 
@@ -239,19 +249,19 @@ def test_grouped_parity_and_reuse(B):
     entries, refs = [], []
     for i, (fmt, N, K) in enumerate(specs):
         raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 190 + i, B)
-        q, d, s = gpu_act(x)
+        q, pl, d, s = gpu_act_planes(x)
         y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
-        entries.append((pw, q, d, s, y))
+        entries.append((pw, q, pl, d, s, y))
         rq, rd, _ = oracle.act_quant(x)
         refs.append(oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd))
     plan = ebq.GroupedPlan(entries, B)
     first = None
     for rep in range(3):                                      # a plan runs any number of times
         for e in entries:
-            e[4].fill_(float("nan"))
+            e[5].fill_(float("nan"))
         plan.run()
         _sync()
-        outs = [host(e[4]).copy() for e in entries]
+        outs = [host(e[5]).copy() for e in entries]
         for (fmt, N, K), o, (yr, absT, _) in zip(specs, outs, refs):
             assert_close_terms(o, yr, absT, what="grouped %s rep %d" % (NAMES[fmt], rep))
         if first is None:
