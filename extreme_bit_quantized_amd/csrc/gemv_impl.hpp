@@ -85,22 +85,17 @@ struct ActSub {
   int32_t Q;     // lane kb (0..7): minus the format multiple of the block's qsum
 };
 
-// 1-bit extras of one token's sub-chunk, made from d and Q where it is used.
+// 1-bit extras of one token's sub-chunk, made from d and Q where it is used:
+// d I = 2 d (R + Q / 2), and R + Q / 2 is exact in fp32 (a half-integer far
+// below 2^23), so a block whose I is 0 adds exactly 0.
 struct ActS1 {
   float d2;  // lane kb: 2 d
-  float e;   // lanes 3 and 7: sum of d * Q over blocks 0..3 resp. 4..7
+  float qh;  // lane kb: Q / 2
 };
 __device__ __forceinline__ ActS1 act_s1(const ActSub& s) {
   ActS1 r;
   r.d2 = s.d + s.d;
-  const float t = (float)s.Q * s.d;
-  // sum over each 4 lanes by row shifts of 1 and 2 (lanes 3 and 7 end with the sums)
-  asm("s_nop 1\n\t"
-      "v_add_f32_dpp %0, %1, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 1\n\t"
-      "v_add_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf"
-      : "=&v"(r.e)
-      : "v"(t));
+  r.qh = (float)s.Q * 0.5f;
   return r;
 }
 
@@ -357,26 +352,27 @@ __device__ __forceinline__ void nib_blk_dpp(float& acc, const ActSub& s, const u
   }
 }
 
-// 1-bit block KB against DPP planes: acc += 2 d R, R = sum b x.  L starts at
-// 8 (sum of the block's bits), which puts back the 8 subtracted from every lo
-// word; the -qsum part, linear in d, is added once per scale block (ActSub::e).
+// 1-bit block KB against DPP planes: acc += 2 d (R + Q / 2) = d I, with
+// R = sum b x = 16 H + L.  The lo words arrive as lo - 8, so sum b lo = L' + 8 n
+// (n = the block's set bits); the chains start at H = n and L = -8 n, which
+// adds exactly 16 n - 8 n.
 template <int KB>
 __device__ __forceinline__ int nib1_blk_dpp(float& acc, const ActSub& s, const ActS1& s1, const uint32_t (&p)[4],
-                                            uint32_t c8) {
-  int x = (int)c8, z;
+                                            uint32_t n, int m8n) {
+  int x = m8n, z = (int)n;
   asm("s_nop 1\n\t"
-      "v_mov_b32 %2, 0\n\t"
-      QK_DOT8("%1", "%3", "%7", "%c12") QK_DOT8("%2", "%3", "%7", "%c13")
-      QK_DOT8("%1", "%4", "%8", "%c12") QK_DOT8("%2", "%4", "%8", "%c13")
-      QK_DOT8("%1", "%5", "%9", "%c12") QK_DOT8("%2", "%5", "%9", "%c13")
-      QK_DOT8("%1", "%6", "%10", "%c12") QK_DOT8("%2", "%6", "%10", "%c13")
+      QK_DOT8("%1", "%3", "%7", "%c13") QK_DOT8("%2", "%3", "%7", "%c14")
+      QK_DOT8("%1", "%4", "%8", "%c13") QK_DOT8("%2", "%4", "%8", "%c14")
+      QK_DOT8("%1", "%5", "%9", "%c13") QK_DOT8("%2", "%5", "%9", "%c14")
+      QK_DOT8("%1", "%6", "%10", "%c13") QK_DOT8("%2", "%6", "%10", "%c14")
       "s_nop 2\n\t"
       "v_lshl_add_u32 %1, %2, 4, %1\n\t"
       "v_cvt_f32_i32 %2, %1\n\t"
-      "v_fmac_f32_dpp %0, %11, %2 row_newbcast:%c14 row_mask:0xf bank_mask:0xf"
-      : "+v"(acc), "+v"(x), "=&v"(z)
+      "v_add_f32_dpp %2, %12, %2 row_newbcast:%c15 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %11, %2 row_newbcast:%c15 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc), "+v"(x), "+v"(z)
       : "v"(s.a[0]), "v"(s.a[1]), "v"(s.a[2]), "v"(s.a[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]),
-        "v"(s1.d2), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
+        "v"(s1.d2), "v"(s1.qh), "n"(2 * KB), "n"(2 * KB + 1), "n"(KB));
   return x;
 }
 
@@ -391,17 +387,6 @@ __device__ __forceinline__ int blk_I_dpp(int R, const ActSub& s) {
       : "=v"(t)
       : "v"(s.Q), "v"(R), "n"(KB));
   return t + R;
-}
-
-// acc + e[LANE] (the scale block's -qsum part).
-template <int LANE>
-__device__ __forceinline__ float add_e_dpp(float acc, const ActS1& s) {
-  float r;
-  asm("s_nop 1\n\t"
-      "v_add_f32_dpp %0, %1, %2 row_newbcast:%c3 row_mask:0xf bank_mask:0xf"
-      : "=v"(r)
-      : "v"(s.e), "v"(acc), "n"(LANE));
-  return r;
 }
 
 // ---- per-format compute of one 256-weight sub-chunk --------------------------------------------------
@@ -429,10 +414,12 @@ __device__ __forceinline__ void sub_sign1(const uint32_t (&T)[32], const uint32_
       if (kb < kbv) {
         const uint32_t W = T[SUB * 8 + kb];
         const uint32_t p[4] = {W & m1, (W >> 1) & m1, (W >> 2) & m1, (W >> 3) & m1};
-        const uint32_t c8 = (uint32_t)__builtin_popcount(W) << 3;
+        const uint32_t n = (uint32_t)__builtin_popcount(W);
+        int m8n;  // -8 n in one multiply (the compiler would shift and negate)
+        asm("v_mul_i32_i24 %0, -8, %1" : "=v"(m8n) : "v"(n));
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          const int R = nib1_blk_dpp<kb>(acc[b], AS[b], A1[b], p, c8);
+          const int R = nib1_blk_dpp<kb>(acc[b], AS[b], A1[b], p, n, m8n);
           if constexpr (WI) {
             if (b == 0) {
               const int I = blk_I_dpp<kb>(R, AS[0]);
@@ -444,7 +431,7 @@ __device__ __forceinline__ void sub_sign1(const uint32_t (&T)[32], const uint32_
     });
     const float s = scale_half(S[SUB], h);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, add_e_dpp<4 * h + 3>(acc[b], A1[b]), y[b]);
+    for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, acc[b], y[b]);
   });
 }
 
