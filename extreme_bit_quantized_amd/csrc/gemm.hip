@@ -10,6 +10,9 @@
 // 16-byte LDS read phase hit different banks); the next stage's global loads
 // are in flight while the current one runs on the matrix cores.  At the end of
 // each K-block the int32 accumulators are scaled into fp32 accumulators.
+#include <algorithm>
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace qk {
@@ -187,6 +190,32 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Work split (stream-K): the T tiles x NG groups of 1024 K are one sequence,
+// tile-major, dealt in G equal runs, one per workgroup (G <= T, so a run spans
+// at least one tile's worth of groups and a tile is cut at most once).  A tile
+// cut by a run boundary gets two partial sums, added into y with fp32 atomics
+// after k_gemm_zero_cut has zeroed it: two adds to zero commute, so the result
+// does not depend on their order.  Runs are numbered XCD-major, so each XCD
+// walks a contiguous stretch of tiles (one 256-row activation slab stays in its
+// L2 while the XCDs stream the weight slabs).
+__device__ __forceinline__ int64_t run_begin(int64_t total, int c, int G) { return total * c / G; }
+__device__ __forceinline__ int run_index(int b, int G) {
+  return (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
+}
+
+__global__ __launch_bounds__(256) void k_gemm_zero_cut(float* __restrict__ y, int M, int N, int n_tiles, int ng,
+                                                       int64_t total, int G) {
+  const int c = blockIdx.x + 1;  // boundary between runs c - 1 and c
+  const int64_t g = run_begin(total, c, G);
+  if (g % ng == 0 || g >= total) return;  // on a tile edge: nothing cut
+  const int t = (int)(g / ng);
+  const int m0 = (t / n_tiles) * PBM, n0 = (t % n_tiles) * PBN;
+  for (int i = threadIdx.x; i < PBM * PBN; i += 256) {
+    const int m = m0 + i / PBN, n = n0 + i % PBN;
+    if (m < M && n < N) y[(int64_t)m * N + n] = 0.0f;
+  }
+}
+
 __global__ __launch_bounds__(PTHREADS)
 void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx, int M,
                     const int8_t* __restrict__ wq, const float* __restrict__ dw, int N, int K,
@@ -197,179 +226,206 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
   __shared__ __attribute__((aligned(16))) float Sc[2][PBM + PBN][4];
   int8_t* const ring[PST] = {R0, R1, R2};
 
-  const int b = blockIdx.x, xcd = b & 7, kx = b >> 3;
-  const int per = (m_tiles * n_tiles + 7) / 8;
-  const int t = xcd * per + kx;
-  if (kx >= per || t >= m_tiles * n_tiles) return;
-  const int mt = t / n_tiles, nt = t % n_tiles;
-  const int m0 = mt * PBM, n0 = nt * PBN;
+  const int G = gridDim.x;
+  const int ng = K / 1024, nkb = K / 256;
+  const int64_t total = (int64_t)m_tiles * n_tiles * ng;
+  const int c = run_index(blockIdx.x, G);
+  const int64_t g_end = run_begin(total, c + 1, G);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int nkb = K / 256, nst = K / PBK, ngroups = nkb / 4;
-
-  // DMA sources of this lane: wave w fills A rows 32 w + 8 j + lane / 8 (j < 4)
-  // and B rows 16 w + 8 j + lane / 8 (j < 2), chunk lane % 8 (swizzled); rows
-  // clamped into the matrix (clamped rows are computed and never stored).
-  const int8_t* asrc[4];
-  const int8_t* bsrc[2];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 32 * wave + 8 * j + (lane >> 3);
-    asrc[j] = xq + (int64_t)min(m0 + r, M - 1) * K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = 16 * wave + 8 * j + (lane >> 3);
-    bsrc[j] = wq + (int64_t)min(n0 + r, N - 1) * K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
-  }
-  // scale rows: waves 0-3 carry dx rows 64 w + lane, waves 4-5 dw rows
-  // 64 (w - 4) + lane, waves 6-7 repeat waves 4-5 (same bytes to the same place)
-  // so that every wave issues the same loads without a branch.
-  const bool sxw = wave < 4;
-  const int srow = sxw ? 64 * wave + lane : 64 * (wave & 1) + lane;
-  const float* ssrc = sxw ? dx + (int64_t)min(m0 + srow, M - 1) * nkb : dw + (int64_t)min(n0 + srow, N - 1) * nkb;
-  const int sdst = sxw ? 64 * wave : PBM + 64 * (wave & 1);
-  auto issue_scales = [&](int g) {  // group g (4 blocks, clamped) into slot g & 1
-    g = min(g, ngroups - 1);  // past the end: the last group again, same bytes
-    lds_dma16(ssrc + 4 * g, &Sc[g & 1][sdst][0]);
-  };
-
-  // Issue stage s (stages past the end reload the last one: same count of loads).
-  auto issue = [&](int s, int8_t* R) {
-    const int k0 = min(s, nst - 1) * PBK;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lds_dma16(asrc[j] + k0, R + (4 * wave + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) lds_dma16(bsrc[j] + k0, R + RING_B + (2 * wave + j) * 1024);
-  };
 
   // MFMA operand offsets (row r, 16-byte chunk c = 2 kk + lane / 32).
   const int l32 = lane & 31, lhi = lane >> 5;
   int aoff[2][4], boff[2][4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const int c = 2 * kk + lhi;
+    const int ch = 2 * kk + lhi;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = wm * 64 + 32 * i + l32;
-      aoff[i][kk] = r * PBK + ((c ^ ((r >> 1) & 7)) << 4);
+      aoff[i][kk] = r * PBK + ((ch ^ ((r >> 1) & 7)) << 4);
       const int rn = wn * 64 + 32 * i + l32;
-      boff[i][kk] = RING_B + rn * PBK + ((c ^ ((rn >> 1) & 7)) << 4);
+      boff[i][kk] = RING_B + rn * PBK + ((ch ^ ((rn >> 1) & 7)) << 4);
     }
   }
-
-  v16i acc[2][2];
-  float facc[2][2][16];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        acc[i][j][e] = 0;
-        facc[i][j][e] = 0.0f;
-      }
-
-  auto compute = [&](const int8_t* R) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      v4i fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = *(const v4i*)(R + aoff[i][kk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = *(const v4i*)(R + boff[j][kk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-  };
   // This lane's scale-row bases (bytes) in slot 0; rows 4 lhi + 32 i + 8 q + t.
   const uint32_t xbase = lds_addr(&Sc[0][wm * 64 + 4 * lhi][0]);
   const uint32_t wbase = lds_addr(&Sc[0][PBM + wn * 64 + l32][0]);
-  // After the last stage of 256-block kb: T = dx * dw * I into the fp32 sums.
-  auto epilogue = [&](int kb) {
-    const uint32_t so = (uint32_t)(kb & 3) * 4u;  // block kb's float inside each row's 16 bytes
-    const uint32_t xa = xbase + ((kb >> 2) & 1) * ((PBM + PBN) * 16) + so;
-    const uint32_t wa = wbase + ((kb >> 2) & 1) * ((PBM + PBN) * 16) + so;
-    v2f p[2][4][2], pw;
-    // early-clobber outputs: no result register may share the address registers,
-    // which the later reads of the block still use
-    asm volatile(
-        "ds_read2_b32 %0, %17 offset0:0 offset1:4\n\t"
-        "ds_read2_b32 %1, %17 offset0:8 offset1:12\n\t"
-        "ds_read2_b32 %2, %17 offset0:32 offset1:36\n\t"
-        "ds_read2_b32 %3, %17 offset0:40 offset1:44\n\t"
-        "ds_read2_b32 %4, %17 offset0:64 offset1:68\n\t"
-        "ds_read2_b32 %5, %17 offset0:72 offset1:76\n\t"
-        "ds_read2_b32 %6, %17 offset0:96 offset1:100\n\t"
-        "ds_read2_b32 %7, %17 offset0:104 offset1:108\n\t"
-        "ds_read2_b32 %8, %17 offset0:128 offset1:132\n\t"
-        "ds_read2_b32 %9, %17 offset0:136 offset1:140\n\t"
-        "ds_read2_b32 %10, %17 offset0:160 offset1:164\n\t"
-        "ds_read2_b32 %11, %17 offset0:168 offset1:172\n\t"
-        "ds_read2_b32 %12, %17 offset0:192 offset1:196\n\t"
-        "ds_read2_b32 %13, %17 offset0:200 offset1:204\n\t"
-        "ds_read2_b32 %14, %17 offset0:224 offset1:228\n\t"
-        "ds_read2_b32 %15, %17 offset0:232 offset1:236\n\t"
-        "ds_read2_b32 %16, %18 offset0:0 offset1:128\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(p[0][0][0]), "=&v"(p[0][0][1]), "=&v"(p[0][1][0]), "=&v"(p[0][1][1]), "=&v"(p[0][2][0]),
-          "=&v"(p[0][2][1]), "=&v"(p[0][3][0]), "=&v"(p[0][3][1]), "=&v"(p[1][0][0]), "=&v"(p[1][0][1]),
-          "=&v"(p[1][1][0]), "=&v"(p[1][1][1]), "=&v"(p[1][2][0]), "=&v"(p[1][2][1]), "=&v"(p[1][3][0]),
-          "=&v"(p[1][3][1]), "=&v"(pw)
-        : "v"(xa), "v"(wa)
-        : "memory");
+
+  for (int64_t g = run_begin(total, c, G); g < g_end;) {
+    // one tile's part: groups [ga, gb) of tile t
+    const int t = (int)(g / ng);
+    const int ga = (int)(g - (int64_t)t * ng);
+    const int gb = (int)min((int64_t)ng, ga + (g_end - g));
+    g += gb - ga;
+    const bool whole = ga == 0 && gb == ng;
+    const int mt = t / n_tiles, nt = t % n_tiles;
+    const int m0 = mt * PBM, n0 = nt * PBN;
+    const int nst = (gb - ga) * 8;      // 128-wide stages of this part
+    const int kbase = ga * 1024;        // first K of this part
+    const int ngroups = gb - ga;
+
+    // the previous part's LDS reads are done before this part's DMA refills the ring
+    wait_vmcnt_lgkm0<0>();
+    ring_barrier();
+
+    // DMA sources of this lane: wave w fills A rows 32 w + 8 j + lane / 8 (j < 4)
+    // and B rows 16 w + 8 j + lane / 8 (j < 2), chunk lane % 8 (swizzled); rows
+    // clamped into the matrix (clamped rows are computed and never stored).
+    // (uniform tile bases plus 32-bit per-lane offsets: the tile spans at most
+    // 256 rows of K bytes)
+    const int8_t* const abase = xq + (int64_t)m0 * K + kbase;
+    const int8_t* const bbase = wq + (int64_t)n0 * K + kbase;
+    uint32_t aoff_g[4], boff_g[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 32 * wave + 8 * j + (lane >> 3);
+      aoff_g[j] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + (((lane & 7) ^ ((r >> 1) & 7)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 16 * wave + 8 * j + (lane >> 3);
+      boff_g[j] = (uint32_t)((min(n0 + r, N - 1) - n0) * K + (((lane & 7) ^ ((r >> 1) & 7)) << 4));
+    }
+    // scale rows: waves 0-3 carry dx rows 64 w + lane, waves 4-5 dw rows
+    // 64 (w - 4) + lane, waves 6-7 repeat waves 4-5 (same bytes to the same place)
+    // so that every wave issues the same loads without a branch.
+    const bool sxw = wave < 4;
+    const int srow = sxw ? 64 * wave + lane : 64 * (wave & 1) + lane;
+    const float* ssrc = (sxw ? dx + (int64_t)min(m0 + srow, M - 1) * nkb : dw + (int64_t)min(n0 + srow, N - 1) * nkb) +
+                        ga * 4;
+    const int sdst = sxw ? 64 * wave : PBM + 64 * (wave & 1);
+    auto issue_scales = [&](int gr) {  // group gr of this part (4 blocks, clamped) into slot gr & 1
+      gr = min(gr, ngroups - 1);  // past the end: the last group again, same bytes
+      lds_dma16(ssrc + 4 * gr, &Sc[gr & 1][sdst][0]);
+    };
+
+    // Issue stage s (stages past the end reload the last one: same count of loads).
+    auto issue = [&](int s, int8_t* R) {
+      const int k0 = min(s, nst - 1) * PBK;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lds_dma16(abase + k0 + aoff_g[j], R + (4 * wave + j) * 1024);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) lds_dma16(bbase + k0 + boff_g[j], R + RING_B + (2 * wave + j) * 1024);
+    };
+
+    v16i acc[2][2];
+    float facc[2][2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float sx = p[i][e >> 2][(e & 3) >> 1][e & 1];
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          acc[i][j][e] = 0;
+          facc[i][j][e] = 0.0f;
+        }
+    auto compute = [&](const int8_t* R) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        v4i fa[2], fb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fa[i] = *(const v4i*)(R + aoff[i][kk]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = *(const v4i*)(R + boff[j][kk]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    };
+    // After the last stage of 256-block kb: T = dx * dw * I into the fp32 sums.
+    auto epilogue = [&](int kb) {
+      const uint32_t so = (uint32_t)(kb & 3) * 4u;  // block kb's float inside each row's 16 bytes
+      const uint32_t xa = xbase + ((kb >> 2) & 1) * ((PBM + PBN) * 16) + so;
+      const uint32_t wa = wbase + ((kb >> 2) & 1) * ((PBM + PBN) * 16) + so;
+      v2f p[2][4][2], pw;
+      // early-clobber outputs: no result register may share the address registers,
+      // which the later reads of the block still use
+      asm volatile(
+          "ds_read2_b32 %0, %17 offset0:0 offset1:4\n\t"
+          "ds_read2_b32 %1, %17 offset0:8 offset1:12\n\t"
+          "ds_read2_b32 %2, %17 offset0:32 offset1:36\n\t"
+          "ds_read2_b32 %3, %17 offset0:40 offset1:44\n\t"
+          "ds_read2_b32 %4, %17 offset0:64 offset1:68\n\t"
+          "ds_read2_b32 %5, %17 offset0:72 offset1:76\n\t"
+          "ds_read2_b32 %6, %17 offset0:96 offset1:100\n\t"
+          "ds_read2_b32 %7, %17 offset0:104 offset1:108\n\t"
+          "ds_read2_b32 %8, %17 offset0:128 offset1:132\n\t"
+          "ds_read2_b32 %9, %17 offset0:136 offset1:140\n\t"
+          "ds_read2_b32 %10, %17 offset0:160 offset1:164\n\t"
+          "ds_read2_b32 %11, %17 offset0:168 offset1:172\n\t"
+          "ds_read2_b32 %12, %17 offset0:192 offset1:196\n\t"
+          "ds_read2_b32 %13, %17 offset0:200 offset1:204\n\t"
+          "ds_read2_b32 %14, %17 offset0:224 offset1:228\n\t"
+          "ds_read2_b32 %15, %17 offset0:232 offset1:236\n\t"
+          "ds_read2_b32 %16, %18 offset0:0 offset1:128\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(p[0][0][0]), "=&v"(p[0][0][1]), "=&v"(p[0][1][0]), "=&v"(p[0][1][1]), "=&v"(p[0][2][0]),
+            "=&v"(p[0][2][1]), "=&v"(p[0][3][0]), "=&v"(p[0][3][1]), "=&v"(p[1][0][0]), "=&v"(p[1][0][1]),
+            "=&v"(p[1][1][0]), "=&v"(p[1][1][1]), "=&v"(p[1][2][0]), "=&v"(p[1][2][1]), "=&v"(p[1][3][0]),
+            "=&v"(p[1][3][1]), "=&v"(pw)
+          : "v"(xa), "v"(wa)
+          : "memory");
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float sx = p[i][e >> 2][(e & 3) >> 1][e & 1];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            facc[i][j][e] = __builtin_fmaf(sx * pw[j], (float)acc[i][j][e], facc[i][j][e]);
+            acc[i][j][e] = 0;
+          }
+        }
+    };
+
+    // prologue: group 0's scales, stages 0 .. PST-2 in flight
+    issue_scales(0);
+#pragma unroll
+    for (int s = 0; s < PST - 1; ++s) issue(s, ring[s]);
+    // main loop, unrolled by 24 stages (ring of 3, scale groups of 8) so every
+    // buffer and every scale load has a fixed place
+    for (int s0 = 0; s0 < nst; s0 += 24) {
+#pragma unroll
+      for (int u = 0; u < 24; ++u) {
+        const int s = s0 + u;
+        if (s >= nst) break;  // the last pass may be partial (uniform)
+        // this wave's part of stage s has landed and its reads of stage s-1 are done
+        wait_vmcnt_lgkm0<(PST - 2) * 6>();
+        ring_barrier();  // ... for every wave: stage s readable, stage s-1's buffer free
+        issue(s + PST - 1, ring[(u + PST - 1) % PST]);
+        // next group's scales: its slot was last read by the epilogues of group
+        // (s >> 3) - 1, all before this barrier
+        if ((u & 7) == 0) issue_scales((s >> 3) + 1);
+        compute(ring[u % PST]);
+        if (u & 1) epilogue(s >> 1);
+      }
+    }
+    wait_vmcnt_lgkm0<0>();  // no DMA may still be landing when the part ends
+
+    // a cut tile's partial sums are added (it was zeroed; two adds per entry)
+    auto store = [&](auto atomic) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          facc[i][j][e] = __builtin_fmaf(sx * pw[j], (float)acc[i][j][e], facc[i][j][e]);
-          acc[i][j][e] = 0;
+          const int n = n0 + wn * 64 + 32 * j + l32;
+          if (n >= N) continue;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * lhi + (e & 3);
+            if (m < M) {
+              if constexpr (decltype(atomic)::value) atomicAdd(&y[(int64_t)m * N + n], facc[i][j][e]);
+              else y[(int64_t)m * N + n] = facc[i][j][e];
+            }
+          }
         }
-      }
-  };
-
-  // prologue: group 0's scales, stages 0 .. PST-2 in flight
-  issue_scales(0);
-#pragma unroll
-  for (int s = 0; s < PST - 1; ++s) issue(s, ring[s]);
-  // main loop, unrolled by 24 stages (ring of 3, scale groups of 8) so every
-  // buffer and every scale load has a fixed place
-  for (int s0 = 0; s0 < nst; s0 += 24) {
-#pragma unroll
-    for (int u = 0; u < 24; ++u) {
-      const int s = s0 + u;
-      if (s >= nst) break;  // the last pass may be partial (uniform)
-      // this wave's part of stage s has landed and its reads of stage s-1 are done
-      wait_vmcnt_lgkm0<(PST - 2) * 6>();
-      ring_barrier();  // ... for every wave: stage s readable, stage s-1's buffer free
-      issue(s + PST - 1, ring[(u + PST - 1) % PST]);
-      // next group's scales: its slot was last read by the epilogues of group
-      // (s >> 3) - 1, all before this barrier
-      if ((u & 7) == 0) issue_scales((s >> 3) + 1);
-      compute(ring[u % PST]);
-      if (u & 1) epilogue(s >> 1);
-    }
+    };
+    if (whole) store(std::false_type{});
+    else store(std::true_type{});
   }
-  wait_vmcnt_lgkm0<0>();  // no DMA may still be landing when the wave ends
-
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + 32 * j + l32;
-      if (n >= N) continue;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * lhi + (e & 3);
-        if (m < M) y[(int64_t)m * N + n] = facc[i][j][e];
-      }
-    }
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* wq, const float* dw, int N, int K,
@@ -378,9 +434,33 @@ hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* w
   // the pipelined kernel.
   if (kblock == 256 && K % 1024 == 0) {
     const int n_tiles = (N + PBN - 1) / PBN, m_tiles = (M + PBM - 1) / PBM;
-    const int blocks = 8 * ((n_tiles * m_tiles + 7) / 8);
-    hipLaunchKernelGGL(k_gemm_i8_p256, dim3(blocks), dim3(PTHREADS), 0, s, xq, dx, M, wq, dw, N, K, y, n_tiles,
-                       m_tiles);
+    const int tiles = n_tiles * m_tiles;
+    // one run per resident workgroup (one per CU: the ring fills its LDS), at most
+    // one per tile; a multiple of 8 so runs can be numbered XCD-major
+    static int cached_dev = -1, cached_slots = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (dev != cached_dev) {
+      int cus = 0, per_cu = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorInvalidDevice;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_gemm_i8_p256, PTHREADS, 0) != hipSuccess ||
+          per_cu < 1)
+        per_cu = 1;
+      cached_slots = cus * per_cu;
+      cached_dev = dev;
+    }
+    // Whole tiles, one workgroup each, unless the last round would leave more
+    // than a quarter of the rounds' time idle: then runs of equal length, one per
+    // slot (the idle tail of a short last round is cheaper than cutting tiles:
+    // with few CUs busy the clock rises).
+    const int S = cached_slots;
+    const int rounds = (tiles + S - 1) / S;
+    const bool even_runs = tiles > S && 4 * ((int64_t)rounds * S - tiles) > (int64_t)rounds * S;
+    const int G = even_runs ? (S >= 8 ? S & ~7 : S) : tiles;
+    const int ng = K / 1024;
+    const int64_t total = (int64_t)tiles * ng;
+    if (G > 1) hipLaunchKernelGGL(k_gemm_zero_cut, dim3(G - 1), dim3(256), 0, s, y, M, N, n_tiles, ng, total, G);
+    hipLaunchKernelGGL(k_gemm_i8_p256, dim3(G), dim3(PTHREADS), 0, s, xq, dx, M, wq, dw, N, K, y, n_tiles, m_tiles);
     return hipGetLastError();
   }
   const dim3 grid((N + GBN - 1) / GBN, (M + GBM - 1) / GBM), block(256);
