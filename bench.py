@@ -345,6 +345,31 @@ def bench_prefill(ebq, reps):
     return out
 
 
+def bench_mfma_ceiling(ebq):
+    """The dense int8 matrix-core rate this part sustains: MFMA 32x32x32 i8 only,
+    two waves per SIMD on every CU, and the shader clock it ran at (the waves'
+    cycle counter over the launch's elapsed time)."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 50000
+    clocks = torch.zeros(4 * blocks, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t, _ = time_kernel(lambda: ebq.qcalib_mfma_i8(blocks, iters, clocks, sink), 5, 1)
+    c = clocks.view(blocks, 4).cpu().numpy().astype(np.float64)
+    cycles = float(np.mean(c[:, 1] - c[:, 0]))
+    ref = float(np.mean(c[:, 3] - c[:, 2]))
+    tops = blocks * 4 * iters * 16 * 65536 / t / 1e12
+    return {
+        "tops": round(tops, 1),
+        "frac_of_published": round(tops / INT8_PEAK_TOPS, 4),
+        "kernel_us": round(t * 1e6, 1),
+        "shader_clock_mhz": round(cycles / t / 1e6, 1),
+        "reference_counter_mhz": round(ref / t / 1e6, 2),
+        "cycles_per_mfma_per_simd": round(cycles / (2 * iters * 16), 2),
+    }
+
+
 def bench_small_ternary(ebq, reps):
     """1024x1024 ternary GEMV (L2-resident: reported as latency)."""
     import torch
@@ -591,7 +616,12 @@ def main():
         log("ternary 1024x1024")
         extra["ternary_1024x1024_latency"] = bench_small_ternary(ebq, 50)
         log("prefill")
-        extra["prefill_2048_tokens"] = bench_prefill(ebq, reps)
+        ceiling = bench_mfma_ceiling(ebq)
+        extra["mfma_i8_ceiling"] = ceiling
+        pre = bench_prefill(ebq, reps)
+        for v in pre.values():
+            v["mfma_frac_of_measured"] = round(v["gemm_tops"] / ceiling["tops"], 4)
+        extra["prefill_2048_tokens"] = pre
         extra["hbm_copy_ceiling_gbs"] = bench_copy_ceiling(5)
         res["extra"] = extra
     elif extra:

@@ -76,6 +76,7 @@ def load(path: str = LIB_PATH):
         "qtrellis_decode_i8": (ctypes.c_int, [W, i32, P, P, P]),
         "qweight_unpack_i8": (ctypes.c_int, [W, P, P, P]),
         "qgemm_i8": (ctypes.c_int, [P, P, i32, P, P, i32, i32, i32, P, P]),
+        "qcalib_mfma_i8": (ctypes.c_int, [i32, i32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -277,3 +278,8 @@ def qgemm_i8(xq, dx, wq, dw, kblock: int, y, stream=None):
     N = wq.shape[0]
     _check(load().qgemm_i8(_ptr(xq), _ptr(dx), M, _ptr(wq), _ptr(dw), N, K, kblock, _ptr(y), _stream(stream)),
            "qgemm_i8")
+
+
+def qcalib_mfma_i8(blocks: int, iters: int, clocks, sink, stream=None):
+    """clocks: int64 tensor of 4 * blocks entries, sink: int32 tensor (both on the device)."""
+    _check(load().qcalib_mfma_i8(blocks, iters, _ptr(clocks), _ptr(sink), _stream(stream)), "qcalib_mfma_i8")

@@ -348,4 +348,12 @@ int qgemm_i8(const int8_t* xq, const float* dx, int32_t M, const int8_t* wq, con
   return hip_rc(launch_gemm(xq, dx, M, wq, dw, N, K, kblock, y, S(stream)));
 }
 
+int qcalib_mfma_i8(int32_t blocks, int32_t iters, uint64_t* clocks, int32_t* sink, void* stream) {
+  if (blocks < 0 || iters < 0) return QERR_INVALID_ARG;
+  if (blocks == 0) return QERR_OK;
+  if (!clocks || !sink) return QERR_INVALID_ARG;
+  if (!aligned(clocks, 8) || !aligned(sink, 4)) return QERR_ALIGNMENT;
+  return hip_rc(launch_mfma_peak(blocks, iters, clocks, sink, S(stream)));
+}
+
 }  // extern "C"

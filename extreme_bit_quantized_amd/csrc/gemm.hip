@@ -156,10 +156,13 @@ __global__ __launch_bounds__(256) void k_gemm_i8(const int8_t* __restrict__ xq, 
 // is a fixed vmcnt (extra loads issued in
 // between only make that wait stricter); the ring is ordered by a plain
 // s_barrier (a __syncthreads() fence would wait for every DMA in flight).  The
-// dx / dw values of four consecutive 256-blocks (16 bytes of each row) are
-// DMA'd once per 8 stages into a 2-slot ring and read by the epilogue in one
-// asm block that waits for its own reads (so the compiler adds no wait for the
-// DMAs in flight).  Workgroups are dealt to the 8 XCDs round robin; each XCD
+// dx / dw values of four consecutive 256-blocks are DMA'd once per 8 stages
+// into a 2-slot ring, block-major (Sc[slot][block][row], 4 bytes per lane), so
+// the epilogue gets four consecutive rows' scales with one 16-byte read; it
+// reads them in one asm block that waits for its own reads (so the compiler
+// adds no wait for the DMAs in flight).  The first MFMA of each 256-block
+// starts from a zero C operand (no accumulator clearing), and each stage reads
+// the operands of step kk + 1 while the MFMAs of step kk run.  Workgroups are dealt to the 8 XCDs round robin; each XCD
 // takes a contiguous run of the tiles in M-major order, so an XCD keeps one
 // 256-row activation slab in its L2 while the XCDs walk the weight slabs in
 // step (shared through the last-level cache).
@@ -167,9 +170,18 @@ constexpr int PBM = 256, PBN = 128, PBK = 128, PTHREADS = 512, PST = 3;
 constexpr int RING_B = PBM * PBK;             // B rows start here inside a stage
 constexpr int RING_STAGE = (PBM + PBN) * PBK; // 24 KB
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+// LDS-typed views of the ring: every access through them is a ds_* instruction
+// whatever the compiler infers about generic pointers (a generic pointer to
+// LDS that it once took for a global one turned the operand reads into
+// global loads of LDS offsets).
+typedef __attribute__((address_space(3))) int8_t lds_i8;
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
+__device__ __forceinline__ void lds_dma16(const void* g, lds_i8* l) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  lds_dma16(g, (lds_i8*)l);
 }
 // s_waitcnt vmcnt(n) (n < 64) and lgkmcnt(0)
 template <int n>
@@ -223,8 +235,8 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
   __shared__ __attribute__((aligned(1024))) int8_t R0[RING_STAGE], R1[RING_STAGE], R2[RING_STAGE];
   // scales of four 256-blocks: rows 0..255 dx of the tile's A rows, rows
   // 256..383 dw of its B rows (one array: the only scale DMA target)
-  __shared__ __attribute__((aligned(16))) float Sc[2][PBM + PBN][4];
-  int8_t* const ring[PST] = {R0, R1, R2};
+  __shared__ __attribute__((aligned(16))) float Sc[2][4][PBM + PBN];
+  lds_i8* const ring[PST] = {(lds_i8*)R0, (lds_i8*)R1, (lds_i8*)R2};
 
   const int G = gridDim.x;
   const int ng = K / 1024, nkb = K / 256;
@@ -250,8 +262,8 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
     }
   }
   // This lane's scale-row bases (bytes) in slot 0; rows 4 lhi + 32 i + 8 q + t.
-  const uint32_t xbase = lds_addr(&Sc[0][wm * 64 + 4 * lhi][0]);
-  const uint32_t wbase = lds_addr(&Sc[0][PBM + wn * 64 + l32][0]);
+  const uint32_t xbase = lds_addr(&Sc[0][0][wm * 64 + 4 * lhi]);
+  const uint32_t wbase = lds_addr(&Sc[0][0][PBM + wn * 64 + l32]);
 
   for (int64_t g = run_begin(total, c, G); g < g_end;) {
     // one tile's part: groups [ga, gb) of tile t
@@ -298,11 +310,14 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
     const int sdst = sxw ? 64 * wave : PBM + 64 * (wave & 1);
     auto issue_scales = [&](int gr) {  // group gr of this part (4 blocks, clamped) into slot gr & 1
       gr = min(gr, ngroups - 1);  // past the end: the last group again, same bytes
-      lds_dma16(ssrc + 4 * gr, &Sc[gr & 1][sdst][0]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(ssrc + 4 * gr + b),
+                                         (__attribute__((address_space(3))) void*)&Sc[gr & 1][b][sdst], 4, 0, 0);
     };
 
     // Issue stage s (stages past the end reload the last one: same count of loads).
-    auto issue = [&](int s, int8_t* R) {
+    auto issue = [&](int s, lds_i8* R) {
       const int k0 = min(s, nst - 1) * PBK;
 #pragma unroll
       for (int j = 0; j < 4; ++j) lds_dma16(abase + k0 + aoff_g[j], R + (4 * wave + j) * 1024);
@@ -321,62 +336,75 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
           acc[i][j][e] = 0;
           facc[i][j][e] = 0.0f;
         }
-    auto compute = [&](const int8_t* R) {
+    // first: stage opens a 256-block, whose first MFMAs start from zero
+    auto compute = [&](const lds_i8* R, auto first) {
+      v4i fa[2][2], fb[2][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[0][i] = *(lds_v4i*)(R + aoff[i][0]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[0][j] = *(lds_v4i*)(R + boff[j][0]);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        v4i fa[2], fb[2];
+        const int cb = kk & 1;
+        if (kk + 1 < 4) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = *(const v4i*)(R + aoff[i][kk]);
+          for (int i = 0; i < 2; ++i) fa[cb ^ 1][i] = *(lds_v4i*)(R + aoff[i][kk + 1]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = *(const v4i*)(R + boff[j][kk]);
+          for (int j = 0; j < 2; ++j) fb[cb ^ 1][j] = *(lds_v4i*)(R + boff[j][kk + 1]);
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < 2; ++j) {
+            if (decltype(first)::value && kk == 0) {
+              const v16i z = {};
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cb][i], fb[cb][j], z, 0, 0, 0);
+            } else {
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
+            }
+          }
       }
+      // issue order: reads(0) | reads(1) MFMAs(0) | reads(2) MFMAs(1) | reads(3) MFMAs(2) | MFMAs(3)
+      // (0x100 = LDS reads, 0x008 = MFMAs); left alone, the compiler clusters the reads
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int kk = 0; kk < 3; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
     // After the last stage of 256-block kb: T = dx * dw * I into the fp32 sums.
     auto epilogue = [&](int kb) {
-      const uint32_t so = (uint32_t)(kb & 3) * 4u;  // block kb's float inside each row's 16 bytes
-      const uint32_t xa = xbase + ((kb >> 2) & 1) * ((PBM + PBN) * 16) + so;
-      const uint32_t wa = wbase + ((kb >> 2) & 1) * ((PBM + PBN) * 16) + so;
-      v2f p[2][4][2], pw;
+      const uint32_t so = ((kb >> 2) & 1) * (4 * (PBM + PBN) * 4) + (kb & 3) * ((PBM + PBN) * 4);
+      const uint32_t xa = xbase + so, wa = wbase + so;
+      v4f p[2][4];
+      v2f pw;
       // early-clobber outputs: no result register may share the address registers,
       // which the later reads of the block still use
       asm volatile(
-          "ds_read2_b32 %0, %17 offset0:0 offset1:4\n\t"
-          "ds_read2_b32 %1, %17 offset0:8 offset1:12\n\t"
-          "ds_read2_b32 %2, %17 offset0:32 offset1:36\n\t"
-          "ds_read2_b32 %3, %17 offset0:40 offset1:44\n\t"
-          "ds_read2_b32 %4, %17 offset0:64 offset1:68\n\t"
-          "ds_read2_b32 %5, %17 offset0:72 offset1:76\n\t"
-          "ds_read2_b32 %6, %17 offset0:96 offset1:100\n\t"
-          "ds_read2_b32 %7, %17 offset0:104 offset1:108\n\t"
-          "ds_read2_b32 %8, %17 offset0:128 offset1:132\n\t"
-          "ds_read2_b32 %9, %17 offset0:136 offset1:140\n\t"
-          "ds_read2_b32 %10, %17 offset0:160 offset1:164\n\t"
-          "ds_read2_b32 %11, %17 offset0:168 offset1:172\n\t"
-          "ds_read2_b32 %12, %17 offset0:192 offset1:196\n\t"
-          "ds_read2_b32 %13, %17 offset0:200 offset1:204\n\t"
-          "ds_read2_b32 %14, %17 offset0:224 offset1:228\n\t"
-          "ds_read2_b32 %15, %17 offset0:232 offset1:236\n\t"
-          "ds_read2_b32 %16, %18 offset0:0 offset1:128\n\t"
+          "ds_read_b128 %0, %9 offset:0\n\t"
+          "ds_read_b128 %1, %9 offset:32\n\t"
+          "ds_read_b128 %2, %9 offset:64\n\t"
+          "ds_read_b128 %3, %9 offset:96\n\t"
+          "ds_read_b128 %4, %9 offset:128\n\t"
+          "ds_read_b128 %5, %9 offset:160\n\t"
+          "ds_read_b128 %6, %9 offset:192\n\t"
+          "ds_read_b128 %7, %9 offset:224\n\t"
+          "ds_read2_b32 %8, %10 offset0:0 offset1:32\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=&v"(p[0][0][0]), "=&v"(p[0][0][1]), "=&v"(p[0][1][0]), "=&v"(p[0][1][1]), "=&v"(p[0][2][0]),
-            "=&v"(p[0][2][1]), "=&v"(p[0][3][0]), "=&v"(p[0][3][1]), "=&v"(p[1][0][0]), "=&v"(p[1][0][1]),
-            "=&v"(p[1][1][0]), "=&v"(p[1][1][1]), "=&v"(p[1][2][0]), "=&v"(p[1][2][1]), "=&v"(p[1][3][0]),
-            "=&v"(p[1][3][1]), "=&v"(pw)
+          : "=&v"(p[0][0]), "=&v"(p[0][1]), "=&v"(p[0][2]), "=&v"(p[0][3]), "=&v"(p[1][0]), "=&v"(p[1][1]),
+            "=&v"(p[1][2]), "=&v"(p[1][3]), "=&v"(pw)
           : "v"(xa), "v"(wa)
           : "memory");
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float sx = p[i][e >> 2][(e & 3) >> 1][e & 1];
+          const float sx = p[i][e >> 2][e & 3];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             facc[i][j][e] = __builtin_fmaf(sx * pw[j], (float)acc[i][j][e], facc[i][j][e]);
-            acc[i][j][e] = 0;
           }
         }
     };
@@ -399,7 +427,8 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
         // next group's scales: its slot was last read by the epilogues of group
         // (s >> 3) - 1, all before this barrier
         if ((u & 7) == 0) issue_scales((s >> 3) + 1);
-        compute(ring[u % PST]);
+        if (u & 1) compute(ring[u % PST], std::false_type{});
+        else compute(ring[u % PST], std::true_type{});
         if (u & 1) epilogue(s >> 1);
       }
     }

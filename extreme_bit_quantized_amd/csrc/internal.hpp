@@ -168,6 +168,7 @@ QK_DECL_NB(7)
 QK_DECL_NB(8)
 #undef QK_DECL_NB
 hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, float* dw, hipStream_t s);
+hipError_t launch_mfma_peak(int blocks, int iters, uint64_t* clocks, int32_t* sink, hipStream_t s);
 hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* wq, const float* dw,
                        int N, int K, int kblock, float* y, hipStream_t s);
 

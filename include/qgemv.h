@@ -260,6 +260,19 @@ int qweight_unpack_i8(const qweight_t* w, int8_t* wq, float* dw, void* stream);
 int qgemm_i8(const int8_t* xq, const float* dx, int32_t M, const int8_t* wq, const float* dw,
              int32_t N, int32_t K, int32_t kblock, float* y, void* stream);
 
+/* Calibration for the GEMM's roofline (not part of the method): measures the
+ * dense int8 matrix-core rate this device sustains, running only
+ * v_mfma_i32_32x32x32_i8 (the GEMM's instruction) over four independent
+ * accumulators, iters x 16 instructions per wave, blocks x 4 waves (launch
+ * 2 blocks per compute unit for two waves per SIMD).  Each block's first
+ * thread writes clocks[4 b .. 4 b + 3] = shader-cycle counter at start and end,
+ * constant-rate reference counter at start and end (device, 8-byte aligned,
+ * 4 x blocks entries, caller-owned; the reference rate is the device's wall
+ * clock rate).  sink (device int32) is written only in a case that does not
+ * occur, to keep the work live.  Time the call with events on the stream: the
+ * rate is blocks x 4 x iters x 16 x 65536 ops over the elapsed time. */
+int qcalib_mfma_i8(int32_t blocks, int32_t iters, uint64_t* clocks, int32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

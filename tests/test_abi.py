@@ -163,6 +163,10 @@ def test_call_validation_without_gpu(ebq):
     assert L.qweight_quantize(5, A, 4, 256, A, 64, A, None) == -2
     assert L.qweight_pack(2, A, 4, 48, A, 16, None) == -3
     assert L.qgemv_grouped_run(None, A, None) == -1
+    assert L.qcalib_mfma_i8(-1, 10, A, A, None) == -1
+    assert L.qcalib_mfma_i8(0, 10, A, A, None) == 0
+    assert L.qcalib_mfma_i8(2, 10, None, A, None) == -1
+    assert L.qcalib_mfma_i8(2, 10, A + 4, A, None) == -4
     assert ebq.load().qstrerror(-4).decode().startswith("pointer")
 
 
