@@ -198,9 +198,68 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
+__device__ __forceinline__ uint32_t lds_addr(const lds_i8* p) { return (uint32_t)(uintptr_t)p; }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+
+// One 128-wide K stage of a wave's 64 x 64 tile, written out as one asm block so
+// that every wait is exact: the operands of each 32-wide K step are read while
+// the MFMAs of the previous step run (LDS reads return in order, so lgkmcnt(4)
+// waits for all but the four just issued), and the stage's six ring DMAs go out
+// two at a time between the MFMA groups (issued back to back they stall the
+// wave behind the texture path before its first MFMA).  Operand names:
+// c00..c11 the accumulators (A tile i, B tile j); x0 x1 y0 y1 and u0 u1 w0 w1
+// two operand sets (A rows i = 0, 1 and B rows j = 0, 1 of one K step);
+// pa0..pa3 / pb0..pb3 the LDS addresses of the four steps' i = 0 / j = 0 rows
+// (rows i, j = 1 are 32 rows = 4096 bytes further, same swizzle); m0..m5,
+// v0..v5, sb0 / sb1 the DMAs' LDS destinations, 32-bit source offsets and
+// 64-bit source bases (A, B).  An MFMA reads its A / B registers when issued,
+// so the next reads into the same set may follow it directly.
+#define QG_RD(D, A, OFF) "ds_read_b128 %[" D "], %[" A "]" OFF "\n\t"
+#define QG_RD4(X0, X1, Y0, Y1, PA, PB) \
+  QG_RD(X0, PA, "") QG_RD(X1, PA, " offset:4096") QG_RD(Y0, PB, "") QG_RD(Y1, PB, " offset:4096")
+#define QG_MF(D, A, B, C) "v_mfma_i32_32x32x32_i8 %[" D "], %[" A "], %[" B "], " C "\n\t"
+#define QG_MF4(X0, X1, Y0, Y1, C00, C01, C10, C11) \
+  QG_MF("c00", X0, Y0, C00) QG_MF("c01", X0, Y1, C01) QG_MF("c10", X1, Y0, C10) QG_MF("c11", X1, Y1, C11)
+// (QG_MF4X expands its arguments first, so QG_ACC4 / QG_ZERO4 count as four)
+#define QG_MF4X(...) QG_MF4(__VA_ARGS__)
+#define QG_ACC4 "%[c00]", "%[c01]", "%[c10]", "%[c11]"
+#define QG_ZERO4 "0", "0", "0", "0"
+// M0 written by SALU needs one wait state before the LDS DMA reads it
+#define QG_DMA(M, V, SB) "s_mov_b32 m0, %[" M "]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[" V "], %[" SB "]\n\t"
+#define QG_WAIT(N) "s_waitcnt lgkmcnt(" #N ")\n\t"
+// K steps 0..2 and the six DMAs; C0: the first step's C operands
+#define QG_STAGE_HEAD(C0)                                                                         \
+  QG_RD4("x0", "x1", "y0", "y1", "pa0", "pb0") QG_RD4("u0", "u1", "w0", "w1", "pa1", "pb1") QG_WAIT(4) \
+  QG_MF4X("x0", "x1", "y0", "y1", C0) QG_DMA("m0", "v0", "sb0") QG_DMA("m1", "v1", "sb0")         \
+  QG_RD4("x0", "x1", "y0", "y1", "pa2", "pb2") QG_WAIT(4)                                         \
+  QG_MF4X("u0", "u1", "w0", "w1", QG_ACC4) QG_DMA("m2", "v2", "sb0") QG_DMA("m3", "v3", "sb0")    \
+  QG_RD4("u0", "u1", "w0", "w1", "pa3", "pb3") QG_WAIT(4)                                         \
+  QG_MF4X("x0", "x1", "y0", "y1", QG_ACC4) QG_DMA("m4", "v4", "sb1") QG_DMA("m5", "v5", "sb1")
+// Step 3 of a block's first stage.
+#define QG_TAIL_FIRST QG_WAIT(0) QG_MF4X("u0", "u1", "w0", "w1", QG_ACC4)
+// Step 3 of a block's last stage, which also brings the epilogue's scales into
+// the operand registers as each set frees up (rows i = 0 of dx into x0..y1, rows
+// i = 1 into u0..w1, the two dw into pw), then the wait states a VALU read of an
+// MFMA result needs (the compiler cannot see the MFMAs in here).
+#define QG_TAIL_LAST                                                                                   \
+  "ds_read_b128 %[x0], %[xa] offset:0\n\t" "ds_read_b128 %[x1], %[xa] offset:32\n\t"                   \
+  "ds_read_b128 %[y0], %[xa] offset:64\n\t" "ds_read_b128 %[y1], %[xa] offset:96\n\t" QG_WAIT(4)        \
+  QG_MF4X("u0", "u1", "w0", "w1", QG_ACC4)                                                              \
+  "ds_read_b128 %[u0], %[xa] offset:128\n\t" "ds_read_b128 %[u1], %[xa] offset:160\n\t"                \
+  "ds_read_b128 %[w0], %[xa] offset:192\n\t" "ds_read_b128 %[w1], %[xa] offset:224\n\t"                \
+  "ds_read2_b32 %[pw], %[wa] offset0:0 offset1:32\n\t" QG_WAIT(0) "s_nop 7\n\ts_nop 7\n\ts_nop 3\n\t"
+#define QG_OUTS                                                                                       \
+  [c00] "+v"(acc[0][0]), [c01] "+v"(acc[0][1]), [c10] "+v"(acc[1][0]), [c11] "+v"(acc[1][1]),       \
+  [x0] "=&v"(x0), [x1] "=&v"(x1), [y0] "=&v"(y0), [y1] "=&v"(y1), [u0] "=&v"(u0), [u1] "=&v"(u1),   \
+  [w0] "=&v"(w0), [w1] "=&v"(w1)
+#define QG_INS                                                                                         \
+  [pa0] "v"(pa[0]), [pa1] "v"(pa[1]), [pa2] "v"(pa[2]), [pa3] "v"(pa[3]), [pb0] "v"(pb[0]),           \
+  [pb1] "v"(pb[1]), [pb2] "v"(pb[2]), [pb3] "v"(pb[3]), [m0] "s"(dm[0]), [m1] "s"(dm[1]),              \
+  [m2] "s"(dm[2]), [m3] "s"(dm[3]), [m4] "s"(dm[4]), [m5] "s"(dm[5]), [v0] "v"(aoff_g[0]),             \
+  [v1] "v"(aoff_g[1]), [v2] "v"(aoff_g[2]), [v3] "v"(aoff_g[3]), [v4] "v"(boff_g[0]),                  \
+  [v5] "v"(boff_g[1]), [sb0] "s"(sa), [sb1] "s"(sb)
 
 // Work split (stream-K): the T tiles x NG groups of 1024 K are one sequence,
 // tile-major, dealt in G equal runs, one per workgroup (G <= T, so a run spans
@@ -316,7 +375,9 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
                                          (__attribute__((address_space(3))) void*)&Sc[gr & 1][b][sdst], 4, 0, 0);
     };
 
-    // Issue stage s (stages past the end reload the last one: same count of loads).
+    // Ring DMA of stage s (past the end: the last stage again, same count of
+    // loads) into buffer R; the first PST - 1 stages are issued here, the rest
+    // inside the stage asm.
     auto issue = [&](int s, lds_i8* R) {
       const int k0 = min(s, nst - 1) * PBK;
 #pragma unroll
@@ -336,67 +397,53 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
           acc[i][j][e] = 0;
           facc[i][j][e] = 0.0f;
         }
-    // first: stage opens a 256-block, whose first MFMAs start from zero
-    auto compute = [&](const lds_i8* R, auto first) {
-      v4i fa[2][2], fb[2][2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) fa[0][i] = *(lds_v4i*)(R + aoff[i][0]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) fb[0][j] = *(lds_v4i*)(R + boff[j][0]);
+    // Stage s from ring buffer R, issuing the DMA of stage s + PST - 1 into D.
+    // Even stages open a 256-block (their first MFMAs start from zero); odd
+    // stages close block kb = s / 2 and leave its scales in x0..w1, pw.
+    v4i x0, x1, y0, y1, u0, u1, w0, w1;
+    v2f pw;
+    auto compute = [&](const lds_i8* R, auto last, const lds_i8* D, int s) {
+      // named here so that the generic lambda captures them (asm operands alone do not)
+      (void)acc, (void)x0, (void)x1, (void)y0, (void)y1, (void)u0, (void)u1, (void)w0, (void)w1, (void)pw;
+      (void)aoff_g, (void)boff_g, (void)xbase, (void)wbase;
+      const uint32_t rb = lds_addr(R);
+      uint32_t pa[4], pb[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int cb = kk & 1;
-        if (kk + 1 < 4) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) fa[cb ^ 1][i] = *(lds_v4i*)(R + aoff[i][kk + 1]);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) fb[cb ^ 1][j] = *(lds_v4i*)(R + boff[j][kk + 1]);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            if (decltype(first)::value && kk == 0) {
-              const v16i z = {};
-              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cb][i], fb[cb][j], z, 0, 0, 0);
-            } else {
-              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
-            }
-          }
+        pa[kk] = rb + aoff[0][kk];
+        pb[kk] = rb + boff[0][kk];
       }
-      // issue order: reads(0) | reads(1) MFMAs(0) | reads(2) MFMAs(1) | reads(3) MFMAs(2) | MFMAs(3)
-      // (0x100 = LDS reads, 0x008 = MFMAs); left alone, the compiler clusters the reads
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      const int k0 = min(s + PST - 1, nst - 1) * PBK;
+      const int8_t* const sa = abase + k0;
+      const int8_t* const sb = bbase + k0;
+      const uint32_t db = lds_addr(D);
+      uint32_t dm[6];
 #pragma unroll
-      for (int kk = 0; kk < 3; ++kk) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      for (int j = 0; j < 4; ++j) dm[j] = db + (4 * wave + j) * 1024;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dm[4 + j] = db + RING_B + (2 * wave + j) * 1024;
+      if constexpr (decltype(last)::value) {
+        const int kb = s >> 1;
+        const uint32_t so = ((kb >> 2) & 1) * (4 * (PBM + PBN) * 4) + (kb & 3) * ((PBM + PBN) * 4);
+        const uint32_t xa = xbase + so, wa = wbase + so;
+        asm volatile(QG_STAGE_HEAD(QG_ACC4) QG_TAIL_LAST
+                     : QG_OUTS, [pw] "=&v"(pw)
+                     : QG_INS, [xa] "v"(xa), [wa] "v"(wa)
+                     : "memory", "m0");
+      } else {
+        asm volatile(QG_STAGE_HEAD(QG_ZERO4) QG_TAIL_FIRST
+                     : QG_OUTS
+                     : QG_INS
+                     : "memory", "m0");
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
-    // After the last stage of 256-block kb: T = dx * dw * I into the fp32 sums.
-    auto epilogue = [&](int kb) {
-      const uint32_t so = ((kb >> 2) & 1) * (4 * (PBM + PBN) * 4) + (kb & 3) * ((PBM + PBN) * 4);
-      const uint32_t xa = xbase + so, wa = wbase + so;
-      v4f p[2][4];
-      v2f pw;
-      // early-clobber outputs: no result register may share the address registers,
-      // which the later reads of the block still use
-      asm volatile(
-          "ds_read_b128 %0, %9 offset:0\n\t"
-          "ds_read_b128 %1, %9 offset:32\n\t"
-          "ds_read_b128 %2, %9 offset:64\n\t"
-          "ds_read_b128 %3, %9 offset:96\n\t"
-          "ds_read_b128 %4, %9 offset:128\n\t"
-          "ds_read_b128 %5, %9 offset:160\n\t"
-          "ds_read_b128 %6, %9 offset:192\n\t"
-          "ds_read_b128 %7, %9 offset:224\n\t"
-          "ds_read2_b32 %8, %10 offset0:0 offset1:32\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(p[0][0]), "=&v"(p[0][1]), "=&v"(p[0][2]), "=&v"(p[0][3]), "=&v"(p[1][0]), "=&v"(p[1][1]),
-            "=&v"(p[1][2]), "=&v"(p[1][3]), "=&v"(pw)
-          : "v"(xa), "v"(wa)
-          : "memory");
+    // After block kb's last stage (scales in the operand registers):
+    // T = dx * dw * I into the fp32 sums.
+    auto epilogue = [&]() {
+      const v4f p[2][4] = {{__builtin_bit_cast(v4f, x0), __builtin_bit_cast(v4f, x1), __builtin_bit_cast(v4f, y0),
+                            __builtin_bit_cast(v4f, y1)},
+                           {__builtin_bit_cast(v4f, u0), __builtin_bit_cast(v4f, u1), __builtin_bit_cast(v4f, w0),
+                            __builtin_bit_cast(v4f, w1)}};
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -423,13 +470,15 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
         // this wave's part of stage s has landed and its reads of stage s-1 are done
         wait_vmcnt_lgkm0<(PST - 2) * 6>();
         ring_barrier();  // ... for every wave: stage s readable, stage s-1's buffer free
-        issue(s + PST - 1, ring[(u + PST - 1) % PST]);
-        // next group's scales: its slot was last read by the epilogues of group
+        // next group's scales: its slot was last read by the last stages of group
         // (s >> 3) - 1, all before this barrier
         if ((u & 7) == 0) issue_scales((s >> 3) + 1);
-        if (u & 1) compute(ring[u % PST], std::false_type{});
-        else compute(ring[u % PST], std::true_type{});
-        if (u & 1) epilogue(s >> 1);
+        if (u & 1) {
+          compute(ring[u % PST], std::true_type{}, ring[(u + PST - 1) % PST], s);
+          epilogue();
+        } else {
+          compute(ring[u % PST], std::false_type{}, ring[(u + PST - 1) % PST], s);
+        }
       }
     }
     wait_vmcnt_lgkm0<0>();  // no DMA may still be landing when the part ends
