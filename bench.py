@@ -496,6 +496,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--quick", action="store_true", help="headline only (no secondary workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill pieces (--steps launches each) and the 1 GiB copy, for counter runs")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="record the headline kernel's HBM bytes from two rocprofv3 --pmc output folders and exit")
     args = ap.parse_args()
@@ -515,6 +517,11 @@ def main():
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
     torch.cuda.init()
     log("device", torch.cuda.get_device_name(0))
+    if args.prefill_only:
+        pre = bench_prefill(ebq, max(2, args.steps))
+        copy_calibration()
+        print(json.dumps({"prefill_2048_tokens": pre}), flush=True)
+        return
 
     # ---- headline: 1-bit 64-layer stack, batch 1 ----
     log("building the 1-bit 64-layer stack")

@@ -281,6 +281,14 @@ __global__ __launch_bounds__(256) void k_gemm_zero_cut(float* __restrict__ y, in
   if (g % ng == 0 || g >= total) return;  // on a tile edge: nothing cut
   const int t = (int)(g / ng);
   const int m0 = (t / n_tiles) * PBM, n0 = (t % n_tiles) * PBN;
+  if ((N & 3) == 0 && ((uintptr_t)y & 15) == 0) {
+    // 16-byte stores (n0 and N are multiples of 4, so a quad is all in or all out)
+    for (int i = threadIdx.x; i < PBM * PBN / 4; i += 256) {
+      const int m = m0 + i / (PBN / 4), n = n0 + 4 * (i % (PBN / 4));
+      if (m < M && n < N) *(float4*)&y[(int64_t)m * N + n] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    return;
+  }
   for (int i = threadIdx.x; i < PBM * PBN; i += 256) {
     const int m = m0 + i / PBN, n = n0 + i % PBN;
     if (m < M && n < N) y[(int64_t)m * N + n] = 0.0f;

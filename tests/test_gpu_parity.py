@@ -369,6 +369,31 @@ def test_gemm_full_size_sampled(N, K):
     assert np.isfinite(host(y)).all()
 
 
+@pytest.mark.parametrize("M,N", [(2000, 5118), (2048, 4100)])
+def test_gemm_cut_tiles_ragged(M, N):
+    """Equal runs of K-groups with ragged edges: 2000 x 5118 (N not a multiple of 4:
+    the cut tiles are zeroed 4 bytes at a time) and 2048 x 4100 (16-byte zeroing, a
+    partial last column tile), K = 2048; every entry written, sampled rows and columns
+    (with both edges) against the oracle."""
+    K = 2048
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.seed64(226, N))
+    xq = torch.randint(-127, 128, (M, K), generator=g, device="cuda", dtype=torch.int8)
+    wq = torch.randint(-127, 128, (N, K), generator=g, device="cuda", dtype=torch.int8)
+    dx = torch.rand((M, K // 256), generator=g, device="cuda") * 0.1 + 1e-3
+    dw = torch.rand((N, K // 256), generator=g, device="cuda") * 0.1 + 1e-3
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ebq.qgemm_i8(xq, dx, wq, dw, 256, y)
+    _sync()
+    yh = host(y)
+    assert np.isfinite(yh).all()
+    rng = np.random.default_rng(227)
+    rows = np.sort(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 30, replace=False)]))
+    cols = np.sort(np.concatenate([[0, N - 1], rng.choice(np.arange(1, N - 1), 62, replace=False)]))
+    yr, absT = oracle.gemm_i8(host(xq)[rows], host(dx)[rows], host(wq)[cols], host(dw)[cols], 256)
+    assert_close_terms(yh[np.ix_(rows, cols)], yr, absT, what="gemm cut tiles, ragged")
+
+
 def test_prefill_pipeline_small():
     """Rotation + Q8, trellis decode, GEMM chained as in prefill."""
     M, K, N = 96, 1024, 160
