@@ -115,10 +115,10 @@ class Stack:
         return out
 
     def quantize_acts(self, ebq):
-        for K in WIDTHS:
-            ebq.qact_quant_i8(self.x[K], 32, self.q[K], self.d[K], self.s[K])
-            if self.planes:
-                ebq.qact_planes(self.q[K], self.pl[K])
+        """Q8 per 32 of every input width in one launch: 4-bit planes for the 1- and
+        2-bit formats (which read nothing else of q), int8 q for the others."""
+        ebq.qact_quant_batch([(self.x[K], None if self.planes else self.q[K], self.pl[K] if self.planes else None,
+                               self.d[K], self.s[K]) for K in WIDTHS])
 
     def weight_bytes(self):
         return sum(w.nbytes for row in self.weights for w in row)
@@ -134,10 +134,10 @@ class Stack:
 
     def step_bytes(self):
         """Algorithmic bytes of one step: the grouped launch + activation quantization
-        (fp32 in, int8 + scales + sums out) + the planes pass (q in, planes out)."""
+        (fp32 in; int8 q or its 4-bit planes, same size, + scales + sums out)."""
         b = self.gemv_bytes()
         for K in WIDTHS:
-            b += self.layers * self.B * (K * 4 + K + (K // 32) * 8 + (2 * K if self.planes else 0))
+            b += self.layers * self.B * (K * 4 + K + (K // 32) * 8)
         return b
 
     def n_weights(self):

@@ -40,6 +40,13 @@ class qgemv_item_t(ctypes.Structure):
                 ("qsum", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
+class qact_job_t(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("q", ctypes.c_void_p),
+                ("planes", ctypes.c_void_p), ("d", ctypes.c_void_p), ("qsum", ctypes.c_void_p)]
+
+
+QACT_BATCH_MAX = 16
+
 _lib = None
 
 
@@ -68,6 +75,7 @@ def load(path: str = LIB_PATH):
         "qact_quant_i8": (ctypes.c_int, [P, i32, i32, i32, P, P, P, P]),
         "qact_hadamard_quant_i8": (ctypes.c_int, [P, i32, i32, P, i32, P, P, P, P]),
         "qact_planes": (ctypes.c_int, [P, i32, i32, P, P]),
+        "qact_quant_batch": (ctypes.c_int, [ctypes.POINTER(qact_job_t), i32, P]),
         "qgemv": (ctypes.c_int, [W, P, P, P, P, i32, P, P]),
         "qgemv_blockdots": (ctypes.c_int, [W, P, P, P, P, P]),
         "qgemv_grouped_plan_bytes": (i64, [ctypes.POINTER(qgemv_item_t), i32, i32]),
@@ -207,6 +215,15 @@ def qact_hadamard_quant_i8(x, sign_bits, qblock, q, d, qsum, stream=None):
 def qact_planes(q, planes, stream=None):
     B, K = q.shape
     _check(load().qact_planes(_ptr(q), B, K, _ptr(planes), _stream(stream)), "qact_planes")
+
+
+def qact_quant_batch(jobs, stream=None):
+    """jobs: (x [B][K] fp32, q or None, planes or None, d, qsum) per input; one launch."""
+    arr = (qact_job_t * max(1, len(jobs)))()
+    for i, (x, q, planes, d, qsum) in enumerate(jobs):
+        B, K = x.shape
+        arr[i] = qact_job_t(_ptr(x), B, K, _ptr(q), _ptr(planes), _ptr(d), _ptr(qsum))
+    _check(load().qact_quant_batch(arr, len(jobs), _stream(stream)), "qact_quant_batch")
 
 
 def qgemv(w: PackedWeight, q, planes, d, qsum, B: int, y, stream=None):

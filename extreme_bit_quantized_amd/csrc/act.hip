@@ -108,6 +108,67 @@ hipError_t launch_act_planes(const int8_t* q, int B, int K, uint32_t* planes, hi
   return hipGetLastError();
 }
 
+// Batched Q8 per 32 + planes: job j owns threads [start[j], start[j + 1]) (one
+// per 4 values, starts multiples of 256, so a workgroup serves one job).  The 8
+// lanes of a block then hold its 32 codes, 4 each; lanes 2g and 2g + 1 (values
+// 8g .. 8g + 7) swap their code words and write plane word g (lo nibbles) and
+// 4 + g (hi nibbles) as k_act_planes does.
+struct ActBatch {
+  int n;
+  int64_t start[QACT_BATCH_MAX + 1];
+  qact_job_t job[QACT_BATCH_MAX];
+};
+
+__global__ __launch_bounds__(256) void k_act_quant_batch(const ActBatch b) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int j = 0;
+  while (j + 1 < b.n && t >= b.start[j + 1]) ++j;  // uniform over the workgroup
+  const qact_job_t& J = b.job[j];
+  const int64_t i = t - b.start[j];
+  const int64_t n4 = (int64_t)J.B * J.K / 4;
+  const bool ok = i < n4;
+  const f32x4 v = ok ? *(const f32x4*)(J.x + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  uint32_t q4;
+  float dd;
+  int32_t s;
+  const int lt = threadIdx.x & 7;  // lane within the 32-block
+  q8_lane4(v, 8, lt == 0, &q4, &dd, &s);
+  const uint32_t other = __shfl_xor(q4, 1);
+  if (!ok) return;
+  const int64_t blk = i >> 3;
+  if (J.q) *(uint32_t*)(J.q + 4 * i) = q4;
+  if (lt == 0) {
+    J.d[blk] = dd;
+    J.qsum[blk] = s;
+  }
+  if (J.planes) {
+    const int g = lt >> 1, hi = lt & 1;
+    const uint32_t a0 = hi ? other : q4, a1 = hi ? q4 : other;  // values 8g..8g+3, 8g+4..8g+7
+    const int sh = hi ? 4 : 0;
+    auto nib4 = [&](uint32_t a) {
+      const uint32_t u = (a >> sh) & 0x0F0F0F0Fu;
+      return (u & 0xFu) | ((u >> 4) & 0xF0u) | ((u >> 8) & 0xF00u) | ((u >> 12) & 0xF000u);
+    };
+    J.planes[blk * 8 + 4 * hi + g] = nib4(a0) | (nib4(a1) << 16);
+  }
+}
+
+hipError_t launch_act_quant_batch(const qact_job_t* jobs, int n, hipStream_t s) {
+  ActBatch b{};
+  b.n = n;
+  int64_t acc = 0;
+  for (int j = 0; j < n; ++j) {
+    b.job[j] = jobs[j];
+    b.start[j] = acc;
+    const int64_t n4 = (int64_t)jobs[j].B * jobs[j].K / 4;
+    acc += (n4 + 255) / 256 * 256;
+  }
+  b.start[n] = acc;
+  if (acc == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_act_quant_batch, dim3((unsigned)(acc / 256)), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
 // One wave per (token, 256-block): lane l holds values 4l .. 4l+3.
 __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict__ x, int K, int64_t nblocks,
                                                         const uint32_t* __restrict__ sign_bits, int qblock,

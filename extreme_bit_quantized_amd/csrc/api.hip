@@ -202,6 +202,23 @@ int qact_planes(const int8_t* q, int32_t B, int32_t K, uint32_t* planes, void* s
   return hip_rc(launch_act_planes(q, B, K, planes, S(stream)));
 }
 
+int qact_quant_batch(const qact_job_t* jobs, int32_t n, void* stream) {
+  if (n < 0 || n > QACT_BATCH_MAX) return QERR_INVALID_ARG;
+  if (n == 0) return QERR_OK;
+  if (!jobs) return QERR_INVALID_ARG;
+  for (int j = 0; j < n; ++j) {
+    const qact_job_t& J = jobs[j];
+    if (J.B < 0 || J.K < 0) return QERR_INVALID_ARG;
+    if (J.B == 0) continue;
+    if (J.K == 0 || J.K % 32 != 0) return QERR_SHAPE;
+    if (!J.x || !J.d || !J.qsum || (!J.q && !J.planes)) return QERR_INVALID_ARG;
+    if (!aligned(J.x, 16) || !aligned(J.q, 4) || !aligned(J.planes, 32) || !aligned(J.d, 4) || !aligned(J.qsum, 4))
+      return QERR_ALIGNMENT;
+    if ((int64_t)J.B * J.K >= ((int64_t)1 << 36)) return QERR_SHAPE;
+  }
+  return hip_rc(launch_act_quant_batch(jobs, n, S(stream)));
+}
+
 int qact_hadamard_quant_i8(const float* x, int32_t B, int32_t K, const uint32_t* sign_bits, int32_t qblock,
                            int8_t* q, float* d, int32_t* qsum, void* stream) {
   if (B < 0 || K < 0) return QERR_INVALID_ARG;

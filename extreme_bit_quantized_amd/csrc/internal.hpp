@@ -143,6 +143,7 @@ void trellis_tables(V16Table* v16, V8Table* v8, float* gain);
 hipError_t launch_act_quant(const float* x, int B, int K, int qblock, int8_t* q, float* d,
                             int32_t* qsum, hipStream_t s);
 hipError_t launch_act_planes(const int8_t* q, int B, int K, uint32_t* planes, hipStream_t s);
+hipError_t launch_act_quant_batch(const qact_job_t* jobs, int n, hipStream_t s);
 hipError_t launch_hadamard_quant(const float* x, int B, int K, const uint32_t* sign_bits, int qblock,
                                  int8_t* q, float* d, int32_t* qsum, hipStream_t s);
 hipError_t launch_quantize(int fmt, const float* w, int rows, int cols, uint8_t* codes,

@@ -172,6 +172,28 @@ int qact_quant_i8(const float* x, int32_t B, int32_t K, int32_t qblock,
  * with lo unsigned and hi a two's complement nibble.  Integer, bit-exact. */
 int qact_planes(const int8_t* q, int32_t B, int32_t K, uint32_t* planes, void* stream);
 
+/* One activation input of qact_quant_batch: x [B][K] fp32 (16-byte aligned),
+ * K a positive multiple of 32; outputs as qact_quant_i8 with qblock 32 (q
+ * 4-byte aligned) and qact_planes (planes 32-byte aligned), either of q and
+ * planes may be NULL but not both; d and qsum are required. */
+typedef struct qact_job {
+  const float* x;
+  int32_t B, K;
+  int8_t* q;
+  uint32_t* planes;
+  float* d;
+  int32_t* qsum;
+} qact_job_t;
+#define QACT_BATCH_MAX 16
+
+/* Q8 per 32 values of up to QACT_BATCH_MAX activation inputs in one launch
+ * (the inputs of every matrix of a decode step: same results as qact_quant_i8
+ * with qblock 32 followed by qact_planes, bit for bit, without the int8
+ * round trip).  jobs: host array of n entries (0 <= n <= QACT_BATCH_MAX);
+ * QERR_INVALID_ARG for a bad count, size or missing pointer, QERR_SHAPE for
+ * K % 32, QERR_ALIGNMENT for misaligned pointers, all before any launch. */
+int qact_quant_batch(const qact_job_t* jobs, int32_t n, void* stream);
+
 /* Block-randomized Walsh-Hadamard rotation then Q8 (the random Hadamard
  * rotation of [P2] "12 GB 装下 27B", applied to activations): per token and
  * 256-block, u = sigma * x with sigma_k = -1 where bit k%32 of sign_bits[k/32]

@@ -163,6 +163,20 @@ def test_call_validation_without_gpu(ebq):
     assert L.qweight_quantize(5, A, 4, 256, A, 64, A, None) == -2
     assert L.qweight_pack(2, A, 4, 48, A, 16, None) == -3
     assert L.qgemv_grouped_run(None, A, None) == -1
+    J = ebq.qact_job_t
+    def jobs(*js):
+        arr = (J * max(1, len(js)))(*js)
+        return arr, len(js)
+    ok = J(A, 2, 64, A, A, A, A)
+    assert L.qact_quant_batch(jobs(ok)[0], 17, None) == -1
+    assert L.qact_quant_batch(jobs(ok)[0], -1, None) == -1
+    assert L.qact_quant_batch(None, 0, None) == 0
+    assert L.qact_quant_batch(*jobs(J(A, 2, 48, A, A, A, A)), None) == -3
+    assert L.qact_quant_batch(*jobs(ok, J(A + 4, 2, 64, A, A, A, A)), None) == -4
+    assert L.qact_quant_batch(*jobs(J(A, 2, 64, A, A + 16, A, A)), None) == -4
+    assert L.qact_quant_batch(*jobs(J(A, 2, 64, None, None, A, A)), None) == -1
+    assert L.qact_quant_batch(*jobs(J(A, 2, 64, A, None, None, A)), None) == -1
+    assert L.qact_quant_batch(*jobs(J(A, 0, 64, None, None, None, None)), None) == 0   # empty input: no launch
     assert L.qcalib_mfma_i8(-1, 10, A, A, None) == -1
     assert L.qcalib_mfma_i8(0, 10, A, A, None) == 0
     assert L.qcalib_mfma_i8(2, 10, None, A, None) == -1

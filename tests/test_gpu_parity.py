@@ -55,6 +55,37 @@ def test_act_planes_bit_exact(B, K):
     assert (host(pl).view(np.uint32) == oracle.act_planes(host(q))).all()
 
 
+def test_act_quant_batch_bit_exact():
+    """One batched launch over inputs of every width (q only, planes only, both,
+    and an empty one): the oracle's Q8 per 32 and planes, bit for bit."""
+    shapes = [(1, 32, "both"), (3, 1024, "planes"), (64, 5120, "both"), (2, 6144, "q"), (0, 512, "both"),
+              (5, 17408, "planes"), (7, 96, "q")]
+    jobs, ref = [], []
+    for i, (B, K, kind) in enumerate(shapes):
+        x = synth.gauss([115, i, K], (B, K)) * synth.uniform([116, i], (B, 1), 1e-3, 1e3)
+        if B:
+            x[0, :32] = 0.0                                            # zero block
+            n = min(K - 32, 64)
+            if n > 0:
+                x[0, 32:32 + n] = np.linspace(-127, 127, n, dtype=np.float32) / 2   # ties
+        q = torch.full((B, K), 99, dtype=torch.int8, device="cuda") if kind in ("q", "both") else None
+        pl = torch.zeros((B, K // 32, 8), dtype=torch.int32, device="cuda") if kind in ("planes", "both") else None
+        d = torch.full((B, K // 32), -1.0, dtype=torch.float32, device="cuda")
+        sm = torch.full((B, K // 32), 7, dtype=torch.int32, device="cuda")
+        jobs.append((dev(x), q, pl, d, sm))
+        ref.append((x, q, pl, d, sm))
+    ebq.qact_quant_batch(jobs)
+    _sync()
+    for x, q, pl, d, sm in ref:
+        rq, rd, rs = oracle.act_quant(x, 32)
+        assert (host(d).view(np.uint32) == rd.view(np.uint32)).all()
+        assert (host(sm) == rs).all()
+        if q is not None:
+            assert (host(q) == rq).all()
+        if pl is not None:
+            assert (host(pl).view(np.uint32) == oracle.act_planes(rq)).all()
+
+
 def test_act_quant_empty_batch():
     x = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
     q = torch.zeros((0, 64), dtype=torch.int8, device="cuda")
