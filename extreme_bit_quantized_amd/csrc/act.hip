@@ -4,6 +4,9 @@
 // Both kernels are bit-exact against their definitions: every float op below
 // is one IEEE fp32 op in the definition's order (contraction off), division
 // and reciprocal correctly rounded, rint rounds half to even.
+#include <algorithm>
+#include <type_traits>
+
 #include "internal.hpp"
 
 #pragma clang fp contract(off)
@@ -169,71 +172,138 @@ hipError_t launch_act_quant_batch(const qact_job_t* jobs, int n, hipStream_t s) 
   return hipGetLastError();
 }
 
-// One wave per (token, 256-block): lane l holds values 4l .. 4l+3.
+// Lane exchange inside 16-lane groups: partner lane t ^ M.  M = 1, 2: DPP
+// quad permutes; M = 4, 8: ds_swizzle in its bit mode (xor mask M).
+template <int M>
+__device__ __forceinline__ float xlane(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  if constexpr (M == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false));
+  else if constexpr (M == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false));
+  else return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(b, 0x1F | (M << 10)));
+}
+template <int M>
+__device__ __forceinline__ int xlane_i(int v) {
+  return __builtin_bit_cast(int, xlane<M>(__builtin_bit_cast(float, v)));
+}
+
+// One 256-block per 16 lanes, four per wave, in a grid-stride loop: lane t of
+// a quarter holds elements 16t .. 16t+15, so stages h = 1, 2, 4, 8 run inside
+// the lane and h = 16, 32, 64, 128 pair lanes t ^ 1, t ^ 2, t ^ 4, t ^ 8.
+// (Every stage adds and subtracts the same pairs in the same order as the
+// definition, so the rounding is the same.)  Then Q8 per qblock over
+// qblock / 16 lanes and one 16-byte store per lane.
 __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict__ x, int K, int64_t nblocks,
                                                         const uint32_t* __restrict__ sign_bits, int qblock,
                                                         int8_t* __restrict__ q, float* __restrict__ d,
                                                         int32_t* __restrict__ qsum) {
-  const int lane = threadIdx.x & 63;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= nblocks) return;  // whole wave leaves together
+  const int lane = threadIdx.x & 63, t = lane & 15;
   const int nkb = K / 256;
-  const int64_t tok = blk / nkb;
-  const int kb = (int)(blk % nkb);
-  const int64_t off = tok * K + (int64_t)kb * 256 + 4 * lane;
-  const f32x4 v = *(const f32x4*)(x + off);
-  const int k0 = kb * 256 + 4 * lane;
-  const uint32_t sw = sign_bits[k0 >> 5] >> (k0 & 31);
-  float u[4] = {v.x, v.y, v.z, v.w};
+  const int width = qblock / 16;  // lanes per Q8 block: 16 or 2
+  const bool vec = ((uintptr_t)q & 15) == 0;
+  for (int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4; base < nblocks;
+       base += (int64_t)gridDim.x * 16) {
+    const int64_t blk = base + (lane >> 4);
+    const bool ok = blk < nblocks;  // the whole 16-lane group agrees
+    const int64_t tok = ok ? blk / nkb : 0;
+    const int kb = ok ? (int)(blk - tok * nkb) : 0;
+    const int64_t off = tok * K + (int64_t)kb * 256 + 16 * t;
+    float u[16];
+    if (ok) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if ((sw >> i) & 1u) u[i] = -u[i];
-  // stage h = 1: pairs (0,1), (2,3); stage h = 2: pairs (0,2), (1,3)
-  {
-    const float a0 = u[0], a1 = u[1], a2 = u[2], a3 = u[3];
-    u[0] = a0 + a1;
-    u[1] = a0 - a1;
-    u[2] = a2 + a3;
-    u[3] = a2 - a3;
-  }
-  {
-    const float a0 = u[0], a1 = u[1], a2 = u[2], a3 = u[3];
-    u[0] = a0 + a2;
-    u[2] = a0 - a2;
-    u[1] = a1 + a3;
-    u[3] = a1 - a3;
-  }
-  // stages h = 4 .. 128 pair lane l with lane l ^ (h/4)
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 v = *(const f32x4*)(x + off + 4 * c);
+        u[4 * c] = v.x;
+        u[4 * c + 1] = v.y;
+        u[4 * c + 2] = v.z;
+        u[4 * c + 3] = v.w;
+      }
+    } else {
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float other = __shfl_xor(u[i], m);
-      // lower element: u_i + u_{i+h}; upper element: u_i - u_{i+h}
-      u[i] = upper ? other - u[i] : u[i] + other;
+      for (int i = 0; i < 16; ++i) u[i] = 0.0f;
     }
-  }
-  const f32x4 r = {u[0] * 0.0625f, u[1] * 0.0625f, u[2] * 0.0625f, u[3] * 0.0625f};
-  const int width = qblock / 4;
-  uint32_t q4;
-  float dd;
-  int32_t s;
-  const bool first = (lane % width) == 0;
-  q8_lane4(r, width, first, &q4, &dd, &s);
-  *(uint32_t*)(q + off) = q4;
-  if (first) {
-    const int64_t nq = K / qblock;
-    const int64_t qi = tok * nq + ((int64_t)kb * 256 + 4 * lane) / qblock;
-    d[qi] = dd;
-    qsum[qi] = s;
+    const int k0 = kb * 256 + 16 * t;
+    const uint32_t sw = ok ? sign_bits[k0 >> 5] >> (k0 & 31) : 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((sw >> i) & 1u) u[i] = -u[i];
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((i & h) == 0) {
+          const float a = u[i], b = u[i + h];
+          u[i] = a + b;
+          u[i + h] = a - b;
+        }
+    // lower element: u_i + u_{i+h}; upper element: u_i - u_{i+h} (u_i the lower partner's)
+    auto cross = [&](auto m_c) {
+      constexpr int m = decltype(m_c)::value;
+      const bool upper = (t & m) != 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float other = xlane<m>(u[i]);
+        u[i] = upper ? other - u[i] : u[i] + other;
+      }
+    };
+    cross(std::integral_constant<int, 1>{});
+    cross(std::integral_constant<int, 2>{});
+    cross(std::integral_constant<int, 4>{});
+    cross(std::integral_constant<int, 8>{});
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] *= 0.0625f;
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(u[i]));
+    if (width > 1) am = fmaxf(am, xlane<1>(am));
+    if (width > 2) {
+      am = fmaxf(am, xlane<2>(am));
+      am = fmaxf(am, xlane<4>(am));
+      am = fmaxf(am, xlane<8>(am));
+    }
+    const float dd = am / 127.0f;
+    const float id = am == 0.0f ? 0.0f : 1.0f / dd;
+    uint32_t pk[4];
+    int sum = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float r = rintf(u[4 * w + j] * id);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        const int qi = (int)r;
+        sum += qi;
+        packed |= ((uint32_t)(qi & 0xFF)) << (8 * j);
+      }
+      pk[w] = packed;
+    }
+    if (width > 1) sum += xlane_i<1>(sum);
+    if (width > 2) {
+      sum += xlane_i<2>(sum);
+      sum += xlane_i<4>(sum);
+      sum += xlane_i<8>(sum);
+    }
+    if (ok) {
+      int8_t* o = q + off;
+      if (vec) {
+        *(uint4*)o = uint4{pk[0], pk[1], pk[2], pk[3]};
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ((uint32_t*)o)[w] = pk[w];
+      }
+      if ((t & (width - 1)) == 0) {
+        const int64_t qi = tok * (K / qblock) + (kb * 256 + 16 * t) / qblock;
+        d[qi] = dd;
+        qsum[qi] = sum;
+      }
+    }
   }
 }
 
 hipError_t launch_hadamard_quant(const float* x, int B, int K, const uint32_t* sign_bits, int qblock, int8_t* q,
                                  float* d, int32_t* qsum, hipStream_t s) {
   const int64_t nblocks = (int64_t)B * (K / 256);
-  const int64_t grid = (nblocks + 3) / 4;
+  const int64_t grid = std::min<int64_t>((nblocks + 15) / 16, 8192);
   hipLaunchKernelGGL(k_hadamard_quant, dim3((unsigned)grid), dim3(256), 0, s, x, K, nblocks, sign_bits, qblock, q, d,
                      qsum);
   return hipGetLastError();

@@ -8,6 +8,7 @@
 // Because the state is 16 bits and each symbol shifts in 2 bits, the state
 // after symbol 4g+j is the 16-bit window of seed||bytes ending with that
 // symbol, so every weight decodes independently.
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 
@@ -64,56 +65,88 @@ void trellis_tables(V16Table* v16, V8Table* v8, float* gain) {
   if (gain) *gain = t.gain;
 }
 
-// One wave per (row, 256 weights): lane l decodes byte l of the 64-byte run
-// (4 weights), then the wave quantizes per oblock (256: whole wave, 32: 8 lanes).
+// One wave per (row, 1024 weights): lane l decodes code bytes 4l .. 4l+3 of the
+// unit (16 weights), one 16-lane quarter per 256-block, with one 4-byte load;
+// the two bytes before its first byte come from the previous lane (lane 0:
+// from memory, or the seed at the row start).  Then Q8 per oblock (256: 16
+// lanes, 32: 2 lanes) and one 16-byte store per lane.  Waves walk the units
+// in a grid-stride loop, so the codebook is copied to LDS once per workgroup.
 __global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, int oblock, V16Table v16t, int8_t* __restrict__ wq,
-                                                        float* __restrict__ dw) {
+                                                        float* __restrict__ dw, int64_t units, int upr) {
   __shared__ uint16_t v16[256];
   v16[threadIdx.x] = v16t.v[threadIdx.x];
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int nblk = it.cols / 256;
-  const int64_t job = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (job >= (int64_t)it.rows * nblk) return;
-  const int64_t row = job / nblk;
-  const int blk = (int)(job % nblk);
-  const uint8_t* rp = it.codes + row * it.row_bytes;
-  const int g = blk * 64 + lane;  // byte index in the row
-  const uint32_t seed = it.seeds[row];
-  const uint32_t b0 = rp[g];
-  const uint32_t b1 = g >= 1 ? rp[g - 1] : (seed & 0xFFu);
-  const uint32_t b2 = g >= 2 ? rp[g - 2] : (g == 1 ? (seed & 0xFFu) : (seed >> 8));
-  const uint32_t w24 = (b2 << 16) | (b1 << 8) | b0;
-  const float s = __half2float(__ushort_as_half(it.scales[scale_index(QFMT_TRELLIS2, it.cols, row, (4 * g) / 64)]));
-  float v[4];
+  const int width = oblock / 16;
+  const bool vec = ((uintptr_t)wq & 15) == 0;
+  for (int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); u < units; u += (int64_t)gridDim.x * 4) {
+    const int64_t row = u / upr;
+    const int ub = (int)(u - row * upr);
+    const bool ok = ub * 4 + (lane >> 4) < nblk;  // this lane's 256-block exists
+    const uint8_t* rp = it.codes + row * it.row_bytes;
+    const int g0 = ub * 256 + 4 * lane;  // first code byte of the lane
+    const uint32_t cur = ok ? *(const uint32_t*)(rp + g0) : 0u;
+    uint32_t prev = __shfl_up(cur, 1);
+    if (lane == 0) {
+      const uint32_t seed = it.seeds[row];
+      // bytes -1 and -2 of a row are the seed's low and high byte
+      prev = ub == 0 ? ((seed & 0xFFu) << 24) | (((seed >> 8) & 0xFFu) << 16) : *(const uint32_t*)(rp + g0 - 4);
+    }
+    const uint64_t x = ((uint64_t)cur << 32) | prev;
+    const float s = ok ? __half2float(__ushort_as_half(it.scales[scale_index(QFMT_TRELLIS2, it.cols, row, g0 / 16)]))
+                       : 0.0f;
+    float v[16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t st = (w24 >> (6 - 2 * j)) & 0xFFFFu;
-    const uint32_t h = ((st * 0x9E37u) ^ (st >> 7)) & 0xFFu;
-    v[j] = s * __half2float(__ushort_as_half(v16[h]));  // exact: 11-bit x 11-bit significands
-  }
-  // Q8 over `oblock` values = oblock/4 lanes
-  const int width = oblock / 4;
-  float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  for (int m = 1; m < width; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
-  const float dd = am / 127.0f;
-  const float id = am == 0.0f ? 0.0f : 1.0f / dd;
-  uint32_t packed = 0;
+    for (int k = 0; k < 4; ++k) {
+      // bytes g-2, g-1, g (g = g0 + k) as the big-endian window g-2 | g-1 | g
+      const uint32_t y3 = (uint32_t)(x >> (16 + 8 * k));
+      const uint32_t w24 = ((y3 & 0xFFu) << 16) | (y3 & 0xFF00u) | ((y3 >> 16) & 0xFFu);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float r = rintf(v[j] * id);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    packed |= ((uint32_t)((int)r & 0xFF)) << (8 * j);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t st = (w24 >> (6 - 2 * j)) & 0xFFFFu;
+        const uint32_t h = ((st * 0x9E37u) ^ (st >> 7)) & 0xFFu;
+        v[4 * k + j] = s * __half2float(__ushort_as_half(v16[h]));  // exact: 11-bit x 11-bit significands
+      }
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
+    for (int m = 1; m < width; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+    const float dd = am / 127.0f;
+    const float id = am == 0.0f ? 0.0f : 1.0f / dd;
+    uint32_t pk[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float r = rintf(v[4 * w + j] * id);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        packed |= ((uint32_t)((int)r & 0xFF)) << (8 * j);
+      }
+      pk[w] = packed;
+    }
+    if (ok) {
+      int8_t* o = wq + row * it.cols + 4 * (int64_t)g0;
+      if (vec) {
+        *(uint4*)o = uint4{pk[0], pk[1], pk[2], pk[3]};
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ((uint32_t*)o)[w] = pk[w];
+      }
+      if (lane % width == 0) dw[row * (it.cols / oblock) + (4 * g0) / oblock] = dd;
+    }
   }
-  *(uint32_t*)(wq + row * it.cols + 4 * (int64_t)g) = packed;
-  if (lane % width == 0) dw[row * (it.cols / oblock) + (4 * g) / oblock] = dd;
 }
 
 hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, float* dw, hipStream_t s) {
   V16Table v16;
   trellis_tables(&v16, nullptr, nullptr);
-  const int64_t jobs = (int64_t)it.rows * (it.cols / 256);
-  hipLaunchKernelGGL(k_trellis_decode, dim3((unsigned)((jobs + 3) / 4)), dim3(256), 0, s, it, oblock, v16, wq, dw);
+  const int upr = (it.cols / 256 + 3) / 4;  // 1024-weight units per row
+  const int64_t units = (int64_t)it.rows * upr;
+  const int64_t grid = std::min<int64_t>((units + 3) / 4, 8192);
+  hipLaunchKernelGGL(k_trellis_decode, dim3((unsigned)grid), dim3(256), 0, s, it, oblock, v16, wq, dw, units, upr);
   return hipGetLastError();
 }
 

@@ -307,7 +307,7 @@ def test_grouped_parity_and_reuse(B):
 # ---------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("oblock", [256, 32])
-@pytest.mark.parametrize("N,K", [(1, 256), (33, 1024), (17, 5120)])
+@pytest.mark.parametrize("N,K", [(1, 256), (33, 1024), (17, 5120), (5, 1280)])
 def test_trellis_decode_bit_exact(oblock, N, K):
     raw = raw_weight(TRELLIS, N, K, 200)
     pw = gpu_weight(TRELLIS, raw, N, K)
@@ -319,6 +319,24 @@ def test_trellis_decode_bit_exact(oblock, N, K):
     rwq, rdw = oracle.trellis_decode_i8(rp, rseeds, rs, K, oblock)
     assert (host(wq) == rwq).all()
     assert (host(dw).view(np.uint32) == rdw.view(np.uint32)).all()
+
+
+def test_trellis_decode_unaligned_output():
+    """int8 output at a 4-byte (not 16-byte) aligned address: the same bytes."""
+    N, K = 9, 1280
+    raw = raw_weight(TRELLIS, N, K, 201)
+    pw = gpu_weight(TRELLIS, raw, N, K)
+    buf = torch.zeros(N * K + 16, dtype=torch.int8, device="cuda")
+    wq = buf[4:4 + N * K].view(N, K)
+    assert wq.data_ptr() % 16 == 4
+    dw = torch.empty((N, K // 256), dtype=torch.float32, device="cuda")
+    ebq.qtrellis_decode_i8(pw, 256, wq, dw)
+    _sync()
+    rp, rs, rseeds = oracle_weight(TRELLIS, raw)
+    rwq, rdw = oracle.trellis_decode_i8(rp, rseeds, rs, K, 256)
+    assert (host(wq) == rwq).all()
+    assert (host(dw).view(np.uint32) == rdw.view(np.uint32)).all()
+    assert (host(buf[:4]) == 0).all() and (host(buf[4 + N * K:]) == 0).all()
 
 
 @pytest.mark.parametrize("fmt", [TERN, INT2, SIGN1, INT4])
