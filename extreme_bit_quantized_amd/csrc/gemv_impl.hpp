@@ -146,18 +146,18 @@ __device__ __forceinline__ int blk_one_chain_mul2(float& out, const ActSub& s, c
 }
 
 // One dot chain.  TERN: R = x + Q[KB] (Q = -qsum, digits are t + 1); TRELLIS:
-// Q = 0.  acc += d[KB] * R.
+// Q = 0.  acc += d[KB] * R.  The chain starts from Q[KB] itself (a DPP move),
+// so R needs no separate add.
 template <int KB>
 __device__ __forceinline__ int blk_one_chain_fmac(float& acc, const ActSub& s, const uint32_t (&p)[8]) {
   int x, t;
   asm("s_nop 1\n\t"
-      "v_mov_b32 %1, 0\n\t"
+      "v_mov_b32_dpp %1, %16 row_newbcast:%c19 row_mask:0xf bank_mask:0xf\n\t"
       QK_DOT("%1", "%3", "%7", "%c17") QK_DOT("%1", "%4", "%8", "%c17")
       QK_DOT("%1", "%5", "%9", "%c17") QK_DOT("%1", "%6", "%10", "%c17")
       QK_DOT("%1", "%3", "%11", "%c18") QK_DOT("%1", "%4", "%12", "%c18")
       QK_DOT("%1", "%5", "%13", "%c18") QK_DOT("%1", "%6", "%14", "%c18")
       "s_nop 2\n\t"
-      "v_add_u32_dpp %1, %16, %1 row_newbcast:%c19 row_mask:0xf bank_mask:0xf\n\t"
       "v_cvt_f32_i32 %2, %1\n\t"
       "v_fmac_f32_dpp %0, %15, %2 row_newbcast:%c19 row_mask:0xf bank_mask:0xf"
       : "+v"(acc), "=&v"(x), "=&v"(t)
