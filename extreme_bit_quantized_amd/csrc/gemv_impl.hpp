@@ -107,9 +107,24 @@ struct ActG {
   int K, kbs;
 };
 
-template <int QMUL>
+// FULL: the sub-chunk lies wholly inside K and kb_base is wave-uniform, so
+// each load is a scalar base plus a fixed per-lane offset (no per-lane address
+// arithmetic).  Otherwise (a row's tail) offsets are clamped to stay inside K.
+template <int QMUL, bool FULL>
 __device__ __forceinline__ void load_act(ActSub& s, const ActG& A, int b, int kb_base) {
   const int i = threadIdx.x & 15;
+  if constexpr (FULL) {
+    g_u8* qb = A.q + ((int64_t)b * A.K + (int64_t)kb_base * 32);
+    const u32x4 v = *(g_u32x4*)(qb + (uint32_t)(16 * i));
+    s.a[0] = (int32_t)v.x;
+    s.a[1] = (int32_t)v.y;
+    s.a[2] = (int32_t)v.z;
+    s.a[3] = (int32_t)v.w;
+    const int64_t kb0 = (int64_t)b * A.kbs + kb_base;
+    s.d = (A.d + kb0)[(uint32_t)(i & 7)];
+    s.Q = (A.qs + kb0)[(uint32_t)(i & 7)] * -QMUL;
+    return;
+  }
   // bytes 16i.. of the sub-chunk; a partial last sub-chunk re-reads valid bytes
   const int off = min(kb_base * 32 + 16 * i, A.K - 16);
   const u32x4 v = *(g_u32x4*)(A.q + (int64_t)b * A.K + off);
@@ -643,11 +658,11 @@ template <> struct QMul<QFMT_INT4> { static constexpr int v = 15; };
 template <> struct QMul<QFMT_TERN_B3> { static constexpr int v = 1; };
 template <> struct QMul<QFMT_TRELLIS2> { static constexpr int v = 0; };
 
-template <int FMT, int NB>
+template <int FMT, int NB, bool FULL = true>
 __device__ __forceinline__ void load_act_all(ActSub (&dst)[NB], const ActG& AG, int kb_base, int kbv) {
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    load_act<QMul<FMT>::v>(dst[b], AG, b, kb_base);
+    load_act<QMul<FMT>::v, FULL>(dst[b], AG, b, kb_base);
     if constexpr (FMT == QFMT_SIGN1 || FMT == QFMT_INT2) {
       // plane words: even lanes of a row hold lo words, used as lo - 8 (signed)
       const uint32_t f = (threadIdx.x & 1) ? 0u : 0x88888888u;
@@ -774,14 +789,23 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   uint32_t goff[NOFF];
 #pragma unroll
   for (int i = 0; i < NOFF; ++i) goff[i] = tile_off(i);
-  // real == false: every lane re-reads the tile's first 16 bytes (one cached
-  // line) so that each iteration issues the same loads, which keeps the
-  // compiler's wait counts exact across the loop.
+  // real == false: no tile data is needed.  With the offsets in registers
+  // (batches up to 2) nothing is loaded (a wave-uniform branch; every segment
+  // top waits for all loads in flight, so nothing depends on the count
+  // issued), and the lane offsets are made opaque at each issue so that each
+  // address stays a scalar base plus a 32-bit lane offset (no 64-bit per-lane
+  // pointers hoisted out of the loop).  Otherwise every lane re-reads the
+  // tile's first 16 bytes (one cached line), which keeps the register count
+  // of the larger batches down.
   auto issue_tile = [&](int sg, bool real) {
+    if constexpr (NOFF == CH) {
+      if (!real) return;
+    }
     g_u8* tseg = tile + (real ? (int64_t)sg * SEGB : 0);
-    const uint32_t keep = real ? 0xFFFFFFFFu : 0u;
+    const uint32_t keep = (NOFF == CH || real) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
+      if constexpr (NOFF == CH) asm volatile("" : "+v"(goff[i < NOFF ? i : 0]));
       const uint32_t off = NOFF == CH ? goff[i < NOFF ? i : 0] : tile_off(i);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tseg + (off & keep)),
                                        (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0, kTileCachePolicy);
@@ -834,7 +858,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
       if constexpr (KACT) kpipe_issue<QMul<FMT>::v, 0>(kp, AK, seg * (SEGK / 32));  // first generation
 #pragma unroll
       for (int sc = 0; sc < NSUB; ++sc)
-        if constexpr (!KACT) load_act_all<FMT, NB>(act[sc], AG, seg * (SEGK / 32) + sc * 8, 8);
+        if constexpr (!KACT) load_act_all<FMT, NB, FMT != QFMT_TRELLIS2>(act[sc], AG, seg * (SEGK / 32) + sc * 8, 8);
       load_scales<SPS>(sptr(seg), Sn);
       prevn = trellis_prev_raw(seg);
       issue_tile(seg, true);
@@ -866,7 +890,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
         if constexpr (!KACT) {
           // kept after the sub-chunk's compute: the new values take its registers
           __builtin_amdgcn_sched_barrier(0);
-          load_act_all<FMT, NB>(act[SUB], AG, nsg * (SEGK / 32) + SUB * 8, 8);
+          load_act_all<FMT, NB, FMT != QFMT_TRELLIS2>(act[SUB], AG, nsg * (SEGK / 32) + SUB * 8, 8);
           __builtin_amdgcn_sched_barrier(0);
         }
       });
@@ -882,7 +906,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
       prevn = trellis_prev_raw(seg);
       issue_tile(seg, true);
       load_scales<SPS>(sptr(seg), Sn);
-      load_act_all<FMT, NB>(cur, AG, seg * (SEGK / 32), 8);
+      load_act_all<FMT, NB, false>(cur, AG, seg * (SEGK / 32), 8);
     }
     for (; seg < nseg; seg += nwk) {
       wait_vm_all();
@@ -917,7 +941,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
         }
         const int nkb = (SUB + 1 < NSUB) ? seg * (SEGK / 32) + (SUB + 1) * 8
                                          : (more_seg ? nx : seg) * (SEGK / 32);
-        load_act_all<FMT, NB>(nxt, AG, nkb, 8);
+        load_act_all<FMT, NB, false>(nxt, AG, nkb, 8);
         sub_compute<FMT, NB, SUB, WI>(T, S, cur, kp, AK, seg * (SEGK / 32) + SUB * 8, 8, 0, prev, v8, y,
                                       Irow ? Irow + seg * (SEGK / 32) : nullptr);
 #pragma unroll
@@ -950,7 +974,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
       const int kbv = nkb_tail - SUB * 8;  // valid activation blocks in this sub-chunk
       if (kbv > 0) {
         ActSub at[NB];
-        if constexpr (!KACT) load_act_all<FMT, NB>(at, AG, kb0 + SUB * 8, kbv);
+        if constexpr (!KACT) load_act_all<FMT, NB, false>(at, AG, kb0 + SUB * 8, kbv);
         float yt[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) yt[b] = 0.0f;
