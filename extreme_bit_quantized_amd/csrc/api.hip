@@ -265,7 +265,8 @@ int64_t qgemv_grouped_plan_bytes(const qgemv_item_t* items, int32_t n, int32_t B
     if (rc) return rc;
   }
   return align16(sizeof(PlanHeader)) + align16((int64_t)sizeof(GemvItem) * n) +
-         align16((int64_t)sizeof(GemvTile) * count_tiles(items, n));
+         align16((int64_t)sizeof(GemvTile) * count_tiles(items, n)) +
+         align16((int64_t)sizeof(int32_t) * 6 * (kPlanWorkers + 1));
 }
 
 int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B, void* host_plan, int64_t plan_bytes) {
@@ -286,13 +287,17 @@ int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B, void* ho
   h.B = B;
   h.items_off = align16(sizeof(PlanHeader));
   h.tiles_off = h.items_off + align16((int64_t)sizeof(GemvItem) * n);
+  h.workers_off = h.tiles_off + align16((int64_t)sizeof(GemvTile) * ntiles);
+  h.n_workers = kPlanWorkers;
   h.total_bytes = need;
   GemvItem* it = (GemvItem*)(base + h.items_off);
   for (int32_t i = 0; i < n; ++i) {
     it[i] = make_item(&items[i].w, items[i].q, items[i].planes, items[i].d, items[i].qsum, items[i].y);
     if (items[i].w.rows > 0) h.fmt_mask |= 1 << items[i].w.fmt;
   }
-  // Tiles: grouped by format, longest first inside each group.
+  // Tiles: grouped by format; inside a format, dealt longest first to the
+  // list with the fewest bytes so far (ties: the lowest list), stored list by
+  // list.  Cost of a tile: its code and scale bytes.
   struct T { int64_t cost; uint32_t item, row0; };
   std::vector<std::vector<T>> q(6);
   for (int32_t i = 0; i < n; ++i) {
@@ -304,15 +309,31 @@ int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B, void* ho
     }
   }
   GemvTile* tiles = (GemvTile*)(base + h.tiles_off);
+  int32_t* wb_all = (int32_t*)(base + h.workers_off);
   int64_t k = 0;
   for (int f = 1; f <= 5; ++f) {
     std::stable_sort(q[f].begin(), q[f].end(), [](const T& a, const T& b) { return a.cost > b.cost; });
-    h.fmt_begin[f] = (int32_t)k;
-    for (const T& t : q[f]) {
-      tiles[k].item = t.item;
-      tiles[k].row0 = t.row0;
-      ++k;
+    std::vector<std::vector<uint32_t>> lists(kPlanWorkers);
+    std::vector<std::pair<int64_t, int>> heap;  // (bytes so far, list), a min-heap
+    for (int w = 0; w < kPlanWorkers; ++w) heap.push_back({0, w});
+    auto later = [](const std::pair<int64_t, int>& a, const std::pair<int64_t, int>& b) { return a > b; };
+    for (size_t j = 0; j < q[f].size(); ++j) {
+      std::pop_heap(heap.begin(), heap.end(), later);
+      lists[heap.back().second].push_back((uint32_t)j);
+      heap.back().first += q[f][j].cost;
+      std::push_heap(heap.begin(), heap.end(), later);
     }
+    h.fmt_begin[f] = (int32_t)k;
+    int32_t* wb = wb_all + f * (kPlanWorkers + 1);
+    for (int w = 0; w < kPlanWorkers; ++w) {
+      wb[w] = (int32_t)k;
+      for (uint32_t j : lists[w]) {
+        tiles[k].item = q[f][j].item;
+        tiles[k].row0 = q[f][j].row0;
+        ++k;
+      }
+    }
+    wb[kPlanWorkers] = (int32_t)k;
   }
   h.fmt_begin[6] = (int32_t)k;
   std::memcpy(base, &h, sizeof(h));
@@ -324,7 +345,8 @@ int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* stream)
   if (!aligned(host_plan, 16) || !aligned(dev_plan, 16)) return QERR_ALIGNMENT;
   PlanHeader h;
   std::memcpy(&h, host_plan, sizeof(h));
-  if (h.magic != kPlanMagic || h.version != kPlanVersion || h.B < 1 || h.B > 8 || h.n_items < 1 || h.n_tiles < 0)
+  if (h.magic != kPlanMagic || h.version != kPlanVersion || h.B < 1 || h.B > 8 || h.n_items < 1 || h.n_tiles < 0 ||
+      h.n_workers != kPlanWorkers)
     return QERR_BUFFER;
   if (h.n_tiles == 0) return QERR_OK;
   return hip_rc(kGrouped[h.B](h, dev_plan, S(stream)));

@@ -1029,33 +1029,65 @@ __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float ga
   }
 }
 
-// Grouped: persistent waves walk the plan's tile list in a fixed snake order:
-// in round r, wave w of W takes tile r W + w (r even) or r W + W - 1 - w (r odd).
-// The list is ordered longest first, so the snake balances the waves' totals.
-// No counter is shared: a single device-wide atomic per tile caps streaming
-// throughput well below what the HBM delivers.
-// One launch serves the plan's tiles [t_begin, t_end), all of format ONLY (the
-// other formats' code is not compiled in, which keeps the register count low).
+// Waves per workgroup of the grouped kernel for batch NB and format FMT: every
+// wave a CU holds at the kernel's register count (at most 16), so one
+// workgroup fills a CU; the ternary tile (13 KB of LDS per wave) allows 12.
+// The kernel's launch bound follows from it, and the build fails if that bound
+// forces register spills.
+constexpr int grouped_wpg(int nb, int fmt) {
+  constexpr int t[8][5] = {{12, 16, 16, 16, 16}, {8, 16, 12, 16, 12}, {12, 16, 16, 16, 12}, {12, 12, 16, 12, 12},
+                           {8, 12, 12, 12, 12},  {8, 12, 12, 12, 8},  {8, 8, 12, 12, 8},   {8, 8, 8, 8, 8}};
+  return t[nb - 1][fmt - 1];
+}
+
+// Grouped: persistent workgroups, one per CU.  The plan deals each format's
+// tiles to lists of nearly equal bytes (longest first inside a list);
+// workgroup g of G works through lists g, g + G, ... and its waves take the
+// tiles in that order through an LDS counter.  A fixed share per wave would
+// not do: the waves of a SIMD do not progress at equal rates (the instruction
+// arbiter favours the oldest), so SIMDs would be left with one wave, or none,
+// long before the last one ends.  No counter is shared between workgroups (a
+// device-wide atomic per tile caps streaming well below what the HBM delivers).
+// One launch serves the plan's tiles of format ONLY (the other formats' code
+// is not compiled in, which keeps the register count low).
 template <int NB, int ONLY>
-__global__ __launch_bounds__(256) void k_gemv_grouped(const uint8_t* __restrict__ plan, int t_begin, int t_end,
-                                                      V8Table v8t, float gain) {
+__global__ __launch_bounds__(64 * grouped_wpg(NB, ONLY)) void k_gemv_grouped(const uint8_t* __restrict__ plan,
+                                                                            V8Table v8t, float gain) {
   static_assert(ONLY >= 1 && ONLY <= 5, "one format per launch");
+  constexpr int P = grouped_wpg(NB, ONLY);
   constexpr int WAVE_LDS = Seg<ONLY>::CH * 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * WAVE_LDS];
+  static_assert(P * WAVE_LDS + 256 + 4 <= 160 * 1024, "LDS per workgroup");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[P * WAVE_LDS];
   __shared__ int8_t v8[256];
+  __shared__ int next_k;
   const PlanHeader* hp = (const PlanHeader*)plan;
   const GemvItem* items = (const GemvItem*)(plan + hp->items_off);
   const GemvTile* tiles = (const GemvTile*)(plan + hp->tiles_off);
+  const int nwk = hp->n_workers;
+  const int32_t* wb = (const int32_t*)(plan + hp->workers_off) + ONLY * (nwk + 1);
   if constexpr (ONLY == QFMT_TRELLIS2) {
-    v8[threadIdx.x] = v8t.v[threadIdx.x];
-    __syncthreads();
+    if (threadIdx.x < 256) v8[threadIdx.x] = v8t.v[threadIdx.x];
   }
+  if (threadIdx.x == 0) next_k = 0;
+  __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint8_t* my = lds + wave * WAVE_LDS;
-  const int nw = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
-  for (int base = t_begin, r = 0; base < t_end; base += nw, ++r) {
-    const int t = base + ((r & 1) ? nw - 1 - gw : gw);
-    if (t >= t_end) break;  // the last, partial round
+  for (;;) {
+    int k = 0;
+    if (lane == 0) k = __hip_atomic_fetch_add(&next_k, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    k = __builtin_amdgcn_readfirstlane(k);
+    // the k-th tile of this workgroup's lists, taken in order
+    int w = blockIdx.x, t = -1;
+    while (w < nwk) {
+      const int b0 = wb[w], n = wb[w + 1] - b0;
+      if (k < n) {
+        t = b0 + k;
+        break;
+      }
+      k -= n;
+      w += gridDim.x;
+    }
+    if (t < 0) break;
     const GemvTile tl = tiles[t];
     const int ii = __builtin_amdgcn_readfirstlane((int)tl.item);
     const int row0 = __builtin_amdgcn_readfirstlane((int)tl.row0);

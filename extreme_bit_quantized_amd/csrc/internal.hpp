@@ -114,10 +114,15 @@ struct alignas(8) GemvTile {
   uint32_t row0;
 };
 
-// Plan blob: header, items, tiles (16-byte aligned sections).  Tiles are
-// grouped by format (format f owns tiles [fmt_begin[f], fmt_begin[f + 1]),
-// f = 1..5), longest first inside each group; a run launches one kernel per
-// format present, each compiled for that format alone.
+// Plan blob: header, items, tiles, worker table (16-byte aligned sections).
+// Tiles are grouped by format (format f owns tiles [fmt_begin[f],
+// fmt_begin[f + 1]), f = 1..5); a run launches one kernel per format present,
+// each compiled for that format alone.  Inside a format the tiles are dealt
+// to n_workers lists of nearly equal total bytes (longest tile first, each to
+// the list with the fewest bytes so far) and stored list by list, longest
+// first inside a list: list w of format f is tiles [wb[w], wb[w + 1]) with
+// wb = workers + f (n_workers + 1).  Workgroup g of a G-workgroup launch works
+// through lists g, g + G, ...
 struct alignas(16) PlanHeader {
   uint32_t magic;   // 'QGVP'
   uint32_t version;
@@ -129,8 +134,14 @@ struct alignas(16) PlanHeader {
   int64_t tiles_off;
   int64_t total_bytes;
   int32_t fmt_begin[8];
+  int32_t n_workers;
+  int32_t pad_;
+  int64_t workers_off;  // int32 [6][n_workers + 1]
 };
-constexpr uint32_t kPlanVersion = 2;
+static_assert(sizeof(PlanHeader) == 96, "plan header layout");
+constexpr uint32_t kPlanVersion = 3;
+// Lists per format: one per CU of a 256-CU part (one workgroup per CU).
+constexpr int kPlanWorkers = 256;
 constexpr uint32_t kPlanMagic = 0x50564751u;  // "QGVP"
 
 // Codebook tables passed by value to the kernels that need them.

@@ -214,10 +214,24 @@ def test_grouped_plan_on_host(ebq):
     assert fb[1] == 0 and fb[6] == ntiles
     for k, (i, r) in enumerate(tiles.tolist()):
         assert fb[fmt_of[i]] <= k < fb[fmt_of[i] + 1]
-    # within one format, tiles come longest first
+    # inside a format the tiles are dealt to 256 lists, stored list by list:
+    # longest first inside a list, and the lists' byte totals differ by at most
+    # one tile (each tile, longest first, went to the list with the fewest bytes)
+    nwk = int(np.frombuffer(h[80:84].tobytes(), dtype=np.int32)[0])
+    workers_off = int(np.frombuffer(h[88:96].tobytes(), dtype=np.int64)[0])
+    assert nwk == 256
+    wb_all = np.frombuffer(h[workers_off:workers_off + 4 * 6 * (nwk + 1)].tobytes(), dtype=np.int32)
+    cost = lambda i, r: min(64, shapes[i][1] - r) * (descs[i].row_bytes + shapes[i][2] // descs[i].block * 2)
+    tl = tiles.tolist()
     for f in set(fmt_of):
-        costs = [min(64, shapes[i][1] - r) * (descs[i].row_bytes + shapes[i][2] // descs[i].block * 2)
-                 for i, r in tiles.tolist() if fmt_of[i] == f]
-        assert costs == sorted(costs, reverse=True)
+        wb = wb_all[f * (nwk + 1):(f + 1) * (nwk + 1)]
+        assert wb[0] == fb[f] and wb[-1] == fb[f + 1] and (np.diff(wb) >= 0).all()
+        loads = []
+        for w in range(nwk):
+            c = [cost(*tl[k]) for k in range(wb[w], wb[w + 1])]
+            assert c == sorted(c, reverse=True)
+            loads.append(sum(c))
+        fcosts = [cost(i, r) for i, r in tl if fmt_of[i] == f]
+        assert max(loads) - min(loads) <= max(fcosts)
     # too small a buffer is refused
     assert ebq.load().qgemv_grouped_plan(items, 4, 2, host.data_ptr(), nb - 16) == -6
