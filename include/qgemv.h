@@ -248,14 +248,18 @@ typedef struct qgemv_item {
 /* Bytes of the plan for these items (host); <0 on invalid items. */
 int64_t qgemv_grouped_plan_bytes(const qgemv_item_t* items, int32_t n, int32_t B);
 /* Validate the items and write the plan to host_plan [plan_bytes] (host).
- * The work is cut into 64-row tiles, ordered longest first. */
+ * The work is cut into 64-row tiles; inside each format they are dealt,
+ * longest first, to 256 lists of nearly equal bytes (one per CU of the
+ * part). */
 int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B,
                        void* host_plan, int64_t plan_bytes);
 /* Run a plan: host_plan (host) is the plan as written by qgemv_grouped_plan,
  * dev_plan (device, 16-byte aligned) a byte copy of it.  The launch needs no
- * scratch memory: every wave takes its tiles in a fixed order, so runs are
- * deterministic and independent of one another.  QERR_BUFFER if host_plan is
- * not a plan. */
+ * scratch memory: one workgroup per CU works through its lists, its waves
+ * taking the tiles in list order through a counter in LDS.  Each tile is
+ * computed whole by one wave, so results do not depend on which wave takes
+ * it: runs are deterministic (bit-identical) and independent of one another.
+ * QERR_BUFFER if host_plan is not a plan (of this library's version). */
 int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* stream);
 
 /* ---- prefill: trellis decode to int8 and the int8 MFMA GEMM --------------------------- */
