@@ -302,6 +302,44 @@ def test_grouped_parity_and_reuse(B):
                 assert (a.view(np.uint32) == b.view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408)])
+@pytest.mark.parametrize("B", [1, 8])
+def test_gemv_full_size_sampled(fmt, N, K, B):
+    """Every format at the 27B FFN shapes (gate / up 17408 x 5120, down
+    5120 x 17408), batch 1 and 8, run as a grouped plan (the launch the stack
+    benchmarks time), checked against the oracle on sampled rows: the first
+    and last tiles and 62 rows between.  Quantization and packing are per row,
+    so the oracle builds only the sampled rows from the same draws."""
+    seed = [500, fmt, N, B]
+    rng = np.random.default_rng(synth.seed64(*seed))
+    rows = np.sort(np.concatenate([np.arange(64), rng.choice(np.arange(64, N - 64), 62, replace=False),
+                                   np.arange(N - 64, N)]))
+    if fmt == TRELLIS:
+        raw = {"codes": synth.symbols(seed + [1], (N, K), 4),
+               "scales": synth.uniform_f16(seed + [2], (N, K // 64), 0.01, 0.03),
+               "seeds": synth.u16(seed + [3], N)}
+        pw = gpu_weight(fmt, raw, N, K)
+        sub = {"codes": raw["codes"][rows], "scales": raw["scales"][rows], "seeds": raw["seeds"][rows]}
+        del raw
+    else:
+        w = synth.gauss_torch(seed, (N, K), 0.02)
+        pw = ebq.PackedWeight.empty(fmt, N, K)
+        ebq.qweight_quantize(fmt, w, pw)
+        sub = {"w": host(w[torch.from_numpy(rows).cuda()])}
+        del w
+    rp, rs, rseeds = oracle_weight(fmt, sub)
+    x = synth.gauss(seed + [9], (B, K))
+    q, pl, d, s = gpu_act_planes(x)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    plan = ebq.GroupedPlan([(pw, q, pl, d, s, y)], B)
+    plan.run()
+    _sync()
+    rq, rd, _ = oracle.act_quant(x)
+    yr, absT, _ = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd)
+    assert_close_terms(host(y)[:, rows], yr, absT, what="%s %dx%d B=%d" % (NAMES[fmt], N, K, B))
+
+
 # ---------------------------------------------------------------------------------------------
 # trellis decode, unpack, GEMM
 # ---------------------------------------------------------------------------------------------
