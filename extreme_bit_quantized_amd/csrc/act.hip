@@ -172,19 +172,6 @@ hipError_t launch_act_quant_batch(const qact_job_t* jobs, int n, hipStream_t s) 
   return hipGetLastError();
 }
 
-// Lane exchange inside 16-lane groups: partner lane t ^ M.  M = 1, 2: DPP
-// quad permutes; M = 4, 8: ds_swizzle in its bit mode (xor mask M).
-template <int M>
-__device__ __forceinline__ float xlane(float v) {
-  const int b = __builtin_bit_cast(int, v);
-  if constexpr (M == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false));
-  else if constexpr (M == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false));
-  else return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(b, 0x1F | (M << 10)));
-}
-template <int M>
-__device__ __forceinline__ int xlane_i(int v) {
-  return __builtin_bit_cast(int, xlane<M>(__builtin_bit_cast(float, v)));
-}
 
 // One 256-block per 16 lanes, four per wave, in a grid-stride loop: lane t of
 // a quarter holds elements 16t .. 16t+15, so stages h = 1, 2, 4, 8 run inside

@@ -50,6 +50,20 @@ __host__ __device__ inline int64_t scales_elems(int32_t fmt, int64_t rows, int64
   return (rows + 63) / 64 * scale_groups(fmt, cols) * 64 * scale_group(fmt);
 }
 
+// Lane exchange inside 16-lane groups: partner lane t ^ M.  M = 1, 2: DPP
+// quad permutes; M = 4, 8: ds_swizzle in its bit mode (xor mask M).
+template <int M>
+__device__ __forceinline__ float xlane(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  if constexpr (M == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false));
+  else if constexpr (M == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false));
+  else return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(b, 0x1F | (M << 10)));
+}
+template <int M>
+__device__ __forceinline__ int xlane_i(int v) {
+  return __builtin_bit_cast(int, xlane<M>(__builtin_bit_cast(float, v)));
+}
+
 // Packed bytes per row: bits per weight x cols / 8, ternary 52 bytes per 256.
 __host__ __device__ inline int64_t packed_row_bytes(int32_t fmt, int64_t cols) {
   switch (fmt) {

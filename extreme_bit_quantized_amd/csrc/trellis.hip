@@ -68,23 +68,39 @@ void trellis_tables(V16Table* v16, V8Table* v8, float* gain) {
 // One wave per (row, 1024 weights): lane l decodes code bytes 4l .. 4l+3 of the
 // unit (16 weights), one 16-lane quarter per 256-block, with one 4-byte load;
 // the two bytes before its first byte come from the previous lane (lane 0:
-// from memory, or the seed at the row start).  Then Q8 per oblock (256: 16
-// lanes, 32: 2 lanes) and one 16-byte store per lane.  Waves walk the units
-// in a grid-stride loop, so the codebook is copied to LDS once per workgroup.
-__global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, int oblock, V16Table v16t, int8_t* __restrict__ wq,
-                                                        float* __restrict__ dw, int64_t units, int upr) {
-  __shared__ uint16_t v16[256];
-  v16[threadIdx.x] = v16t.v[threadIdx.x];
+// from memory, or the seed at the row start).  Then Q8 per oblock (WIDTH
+// lanes: 16 for 256, 2 for 32) and one 16-byte store per lane.  Waves walk
+// the units in a grid-stride loop (the unit's row and position advance by a
+// fixed quotient and remainder, no division per unit), so the codebook is
+// copied to LDS once per workgroup, as fp32 (exact for fp16 values).
+// Per weight: the state st is the 16-bit window ending at its symbol, and
+// 4 h = ((220 st) ^ (st >> 5)) & 0x3FC is the table byte offset (the low 8 bits
+// of 0x9E37 st are those of 55 st, so bits 2..9 of 220 st are bits 0..7 of
+// 0x9E37 st, and bits 2..9 of st >> 5 are bits 0..7 of st >> 7); a multiply
+// takes only the window's low 24 bits, and bits above the state land outside
+// the mask.  q = rint(v / d) comes from the fp32 sum 1.5 * 2^23 + v * (1 / d):
+// that sum has a unit ulp, so it rounds v * (1 / d) to the nearest integer
+// with ties to even, and its low byte is q in two's complement.  No clamp:
+// |v| <= amax, so |v * (1 / d)| <= 127 (1 + 3 ulp) and q stays in [-127, 127].
+template <int WIDTH>
+__global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, V16Table v16t, int8_t* __restrict__ wq,
+                                                        float* __restrict__ dw, int upr, int step_rows,
+                                                        int step_units) {
+  __shared__ float v32[256];
+  v32[threadIdx.x] = __half2float(__ushort_as_half(v16t.v[threadIdx.x]));
   __syncthreads();
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nblk = it.cols / 256;
-  const int width = oblock / 16;
+  constexpr int OBLOCK = 16 * WIDTH;
   const bool vec = ((uintptr_t)wq & 15) == 0;
-  for (int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); u < units; u += (int64_t)gridDim.x * 4) {
-    const int64_t row = u / upr;
-    const int ub = (int)(u - row * upr);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)v32;
+  // this wave's first unit, then (row, ub) += (step_rows, step_units) per turn
+  const int u0 = blockIdx.x * 4 + wave;
+  int row = u0 / upr, ub = u0 - row * upr;
+  for (; row < it.rows;) {
     const bool ok = ub * 4 + (lane >> 4) < nblk;  // this lane's 256-block exists
-    const uint8_t* rp = it.codes + row * it.row_bytes;
+    const uint8_t* rp = it.codes + (int64_t)row * it.row_bytes;
     const int g0 = ub * 256 + 4 * lane;  // first code byte of the lane
     const uint32_t cur = ok ? *(const uint32_t*)(rp + g0) : 0u;
     uint32_t prev = __shfl_up(cur, 1);
@@ -104,38 +120,48 @@ __global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, int oblock,
       const uint32_t w24 = ((y3 & 0xFFu) << 16) | (y3 & 0xFF00u) | ((y3 >> 16) & 0xFFu);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t st = (w24 >> (6 - 2 * j)) & 0xFFFFu;
-        const uint32_t h = ((st * 0x9E37u) ^ (st >> 7)) & 0xFFu;
-        v[4 * k + j] = s * __half2float(__ushort_as_half(v16[h]));  // exact: 11-bit x 11-bit significands
+        const uint32_t a = w24 >> (6 - 2 * j);      // st in the low 16 bits
+        const uint32_t off = ((a * 220u) ^ (a >> 5)) & 0x3FCu;  // 4 h
+        const float val = *(const __attribute__((address_space(3))) float*)(uintptr_t)(lds_base + off);
+        v[4 * k + j] = s * val;  // exact: 11-bit x 11-bit significands
       }
     }
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
-    for (int m = 1; m < width; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+    am = fmaxf(am, xlane<1>(am));
+    if constexpr (WIDTH > 2) {
+      am = fmaxf(am, xlane<2>(am));
+      am = fmaxf(am, xlane<4>(am));
+      am = fmaxf(am, xlane<8>(am));
+    }
     const float dd = am / 127.0f;
     const float id = am == 0.0f ? 0.0f : 1.0f / dd;
     uint32_t pk[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t packed = 0;
+      uint32_t b[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float r = rintf(v[4 * w + j] * id);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        packed |= ((uint32_t)((int)r & 0xFF)) << (8 * j);
-      }
-      pk[w] = packed;
+      for (int j = 0; j < 4; ++j) b[j] = __builtin_bit_cast(uint32_t, v[4 * w + j] * id + 12582912.0f);
+      const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // q0 | q1 << 8
+      const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);  // q2 | q3 << 8
+      pk[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
     }
     if (ok) {
-      int8_t* o = wq + row * it.cols + 4 * (int64_t)g0;
+      int8_t* o = wq + (int64_t)row * it.cols + 4 * (int64_t)g0;
       if (vec) {
         *(uint4*)o = uint4{pk[0], pk[1], pk[2], pk[3]};
       } else {
 #pragma unroll
         for (int w = 0; w < 4; ++w) ((uint32_t*)o)[w] = pk[w];
       }
-      if (lane % width == 0) dw[row * (it.cols / oblock) + (4 * g0) / oblock] = dd;
+      if (lane % WIDTH == 0) dw[(int64_t)row * (it.cols / OBLOCK) + (4 * g0) / OBLOCK] = dd;
+    }
+    ub += step_units;
+    row += step_rows;
+    if (ub >= upr) {
+      ub -= upr;
+      ++row;
     }
   }
 }
@@ -145,8 +171,14 @@ hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, flo
   trellis_tables(&v16, nullptr, nullptr);
   const int upr = (it.cols / 256 + 3) / 4;  // 1024-weight units per row
   const int64_t units = (int64_t)it.rows * upr;
-  const int64_t grid = std::min<int64_t>((units + 3) / 4, 8192);
-  hipLaunchKernelGGL(k_trellis_decode, dim3((unsigned)grid), dim3(256), 0, s, it, oblock, v16, wq, dw, units, upr);
+  const int grid = (int)std::min<int64_t>((units + 3) / 4, 8192);
+  const int stride = grid * 4;  // units per turn of the grid
+  if (oblock == 256)
+    hipLaunchKernelGGL(k_trellis_decode<16>, dim3(grid), dim3(256), 0, s, it, v16, wq, dw, upr, stride / upr,
+                       stride % upr);
+  else
+    hipLaunchKernelGGL(k_trellis_decode<2>, dim3(grid), dim3(256), 0, s, it, v16, wq, dw, upr, stride / upr,
+                       stride % upr);
   return hipGetLastError();
 }
 
