@@ -177,23 +177,31 @@ hipError_t launch_act_quant_batch(const qact_job_t* jobs, int n, hipStream_t s) 
 // a quarter holds elements 16t .. 16t+15, so stages h = 1, 2, 4, 8 run inside
 // the lane and h = 16, 32, 64, 128 pair lanes t ^ 1, t ^ 2, t ^ 4, t ^ 8.
 // (Every stage adds and subtracts the same pairs in the same order as the
-// definition, so the rounding is the same.)  Then Q8 per qblock over
-// qblock / 16 lanes and one 16-byte store per lane.
-__global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict__ x, int K, int64_t nblocks,
-                                                        const uint32_t* __restrict__ sign_bits, int qblock,
+// definition, so the rounding is the same: a cross stage forms
+// fma(own, +-1, partner's), which is the partner's value plus or minus its
+// own, rounded once.)  The final 1/16 is a power of two, so it is applied to
+// amax and the reciprocal instead of every element: the products are the
+// same numbers (barring subnormal values).  Then Q8 per qblock over
+// WIDTH = qblock / 16 lanes (q from the low byte of 1.5 * 2^23 + v * (1 / d),
+// which rounds to the nearest integer with ties to even, |q| <= 127 without a
+// clamp) and one 16-byte store per lane.  Each lane's block advances by a fixed quotient and remainder per turn
+// of the grid (no division per block).
+template <int WIDTH>
+__global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict__ x, int K, int nblocks,
+                                                        const uint32_t* __restrict__ sign_bits,
                                                         int8_t* __restrict__ q, float* __restrict__ d,
-                                                        int32_t* __restrict__ qsum) {
+                                                        int32_t* __restrict__ qsum, int step_tok, int step_kb) {
+  constexpr int QBLOCK = 16 * WIDTH;
   const int lane = threadIdx.x & 63, t = lane & 15;
   const int nkb = K / 256;
-  const int width = qblock / 16;  // lanes per Q8 block: 16 or 2
   const bool vec = ((uintptr_t)q & 15) == 0;
-  for (int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4; base < nblocks;
-       base += (int64_t)gridDim.x * 16) {
-    const int64_t blk = base + (lane >> 4);
+  int blk = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  int tok = blk / nkb, kb = blk - tok * nkb;
+  const int step = gridDim.x * 16;  // blocks per turn of the grid
+  for (int base = (blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * 4; base < nblocks;
+       base += step) {
     const bool ok = blk < nblocks;  // the whole 16-lane group agrees
-    const int64_t tok = ok ? blk / nkb : 0;
-    const int kb = ok ? (int)(blk - tok * nkb) : 0;
-    const int64_t off = tok * K + (int64_t)kb * 256 + 16 * t;
+    const int64_t off = (int64_t)tok * K + kb * 256 + 16 * t;
     float u[16];
     if (ok) {
 #pragma unroll
@@ -211,8 +219,8 @@ __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict_
     const int k0 = kb * 256 + 16 * t;
     const uint32_t sw = ok ? sign_bits[k0 >> 5] >> (k0 & 31) : 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if ((sw >> i) & 1u) u[i] = -u[i];
+    for (int i = 0; i < 16; ++i)  // sign bit i of the word onto element i
+      u[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, u[i]) ^ ((sw << (31 - i)) & 0x80000000u));
 #pragma unroll
     for (int h = 1; h < 16; h <<= 1)
 #pragma unroll
@@ -225,47 +233,43 @@ __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict_
     // lower element: u_i + u_{i+h}; upper element: u_i - u_{i+h} (u_i the lower partner's)
     auto cross = [&](auto m_c) {
       constexpr int m = decltype(m_c)::value;
-      const bool upper = (t & m) != 0;
+      const float sg = (t & m) != 0 ? -1.0f : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float other = xlane<m>(u[i]);
-        u[i] = upper ? other - u[i] : u[i] + other;
-      }
+      for (int i = 0; i < 16; ++i) u[i] = __builtin_fmaf(u[i], sg, xlane<m>(u[i]));
     };
     cross(std::integral_constant<int, 1>{});
     cross(std::integral_constant<int, 2>{});
     cross(std::integral_constant<int, 4>{});
     cross(std::integral_constant<int, 8>{});
-#pragma unroll
-    for (int i = 0; i < 16; ++i) u[i] *= 0.0625f;
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(u[i]));
-    if (width > 1) am = fmaxf(am, xlane<1>(am));
-    if (width > 2) {
+    am = fmaxf(am, xlane<1>(am));
+    if constexpr (WIDTH > 2) {
       am = fmaxf(am, xlane<2>(am));
       am = fmaxf(am, xlane<4>(am));
       am = fmaxf(am, xlane<8>(am));
     }
+    am *= 0.0625f;
     const float dd = am / 127.0f;
-    const float id = am == 0.0f ? 0.0f : 1.0f / dd;
+    const float id = (am == 0.0f ? 0.0f : 1.0f / dd) * 0.0625f;
     uint32_t pk[4];
-    int sum = 0;
+    uint32_t bsum = 0;  // sum of the 16 biased values: 16 * 0x4B400000 + sum of q, mod 2^32
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t packed = 0;
+      uint32_t b[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float r = rintf(u[4 * w + j] * id);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        const int qi = (int)r;
-        sum += qi;
-        packed |= ((uint32_t)(qi & 0xFF)) << (8 * j);
+        b[j] = __builtin_bit_cast(uint32_t, u[4 * w + j] * id + 12582912.0f);
+        bsum += b[j];
       }
-      pk[w] = packed;
+      const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // q0 | q1 << 8
+      const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);  // q2 | q3 << 8
+      pk[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
     }
-    if (width > 1) sum += xlane_i<1>(sum);
-    if (width > 2) {
+    int sum = (int)(bsum - 16u * 0x4B400000u);
+    sum += xlane_i<1>(sum);
+    if constexpr (WIDTH > 2) {
       sum += xlane_i<2>(sum);
       sum += xlane_i<4>(sum);
       sum += xlane_i<8>(sum);
@@ -278,11 +282,18 @@ __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict_
 #pragma unroll
         for (int w = 0; w < 4; ++w) ((uint32_t*)o)[w] = pk[w];
       }
-      if ((t & (width - 1)) == 0) {
-        const int64_t qi = tok * (K / qblock) + (kb * 256 + 16 * t) / qblock;
+      if ((t & (WIDTH - 1)) == 0) {
+        const int64_t qi = (int64_t)tok * (K / QBLOCK) + (kb * 256 + 16 * t) / QBLOCK;
         d[qi] = dd;
         qsum[qi] = sum;
       }
+    }
+    blk += step;
+    kb += step_kb;
+    tok += step_tok;
+    if (kb >= nkb) {
+      kb -= nkb;
+      ++tok;
     }
   }
 }
@@ -290,9 +301,15 @@ __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict_
 hipError_t launch_hadamard_quant(const float* x, int B, int K, const uint32_t* sign_bits, int qblock, int8_t* q,
                                  float* d, int32_t* qsum, hipStream_t s) {
   const int64_t nblocks = (int64_t)B * (K / 256);
-  const int64_t grid = std::min<int64_t>((nblocks + 15) / 16, 8192);
-  hipLaunchKernelGGL(k_hadamard_quant, dim3((unsigned)grid), dim3(256), 0, s, x, K, nblocks, sign_bits, qblock, q, d,
-                     qsum);
+  if (nblocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int grid = (int)std::min<int64_t>((nblocks + 15) / 16, 8192);
+  const int nkb = K / 256, step = grid * 16;
+  if (qblock == 256)
+    hipLaunchKernelGGL(k_hadamard_quant<16>, dim3(grid), dim3(256), 0, s, x, K, (int)nblocks, sign_bits, q, d, qsum,
+                       step / nkb, step % nkb);
+  else
+    hipLaunchKernelGGL(k_hadamard_quant<2>, dim3(grid), dim3(256), 0, s, x, K, (int)nblocks, sign_bits, q, d, qsum,
+                       step / nkb, step % nkb);
   return hipGetLastError();
 }
 
