@@ -184,8 +184,8 @@ hipError_t launch_act_quant_batch(const qact_job_t* jobs, int n, hipStream_t s) 
 // same numbers (barring subnormal values).  Then Q8 per qblock over
 // WIDTH = qblock / 16 lanes (q from the low byte of 1.5 * 2^23 + v * (1 / d),
 // which rounds to the nearest integer with ties to even, |q| <= 127 without a
-// clamp) and one 16-byte store per lane.  Each lane's block advances by a fixed quotient and remainder per turn
-// of the grid (no division per block).
+// clamp) and one 16-byte store per lane.  Each lane's block advances by a
+// fixed quotient and remainder per turn of the grid (no division per block).
 template <int WIDTH>
 __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict__ x, int K, int nblocks,
                                                         const uint32_t* __restrict__ sign_bits,
