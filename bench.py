@@ -345,6 +345,107 @@ def bench_prefill(ebq, reps):
     return out
 
 
+def bench_mixed_b64_gemv(ebq, reps):
+    """Mixed stack at 64 tokens through the packed weights: one Q8 launch for all
+    64 tokens of every layer, then the grouped GEMV for 8 tokens at a time, 8
+    plans over consecutive token slices (weights read 8 times per step)."""
+    import torch
+
+    B, sub = 64, 8
+    ms = Stack(ebq, "mixed", synth.N_LAYERS, B)
+    plans = []
+    for j in range(B // sub):
+        sl = slice(j * sub, (j + 1) * sub)
+        ents = [(w, q[sl] if q is not None else None, pl[sl] if pl is not None else None, d[sl], s_[sl], y[sl])
+                for (w, q, pl, d, s_, y) in ms.entries()]
+        plans.append(ebq.GroupedPlan(ents, sub))
+
+    def step():
+        ms.quantize_acts(ebq)
+        for p in plans:
+            p.run()
+
+    t, _ = time_region(step, reps, 2)
+    ok, worst = sampled_parity(ebq, ms, [0, 63], rows_per_matrix=8)
+    out = {
+        "step_us": round(t * 1e6, 1),
+        "plans": "%d grouped launches of %d tokens" % (B // sub, sub),
+        "weight_bytes_read": (B // sub) * ms.weight_bytes(),
+        "gbs": round((B // sub) * ms.weight_bytes() / t / 1e9, 1),
+        "equiv_tok_s": round(B / t, 1),
+        "parity": "ok" if ok else "FAIL",
+        "worst_err_over_sum_abs_terms": worst,
+    }
+    del plans, ms
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_mixed_b64_int8_gemm(ebq, reps, layers=2, seed=0):
+    """Mixed stack at 64 tokens: weights unpacked once to int8 levels with fp32
+    per-32 factors (qweight_unpack_i8: W = dw * wq exactly), activations Q8 per
+    32, and a layer's seven products as int8 matrix-core GEMMs rescaled per 32.
+    `layers` distinct layers (more bytes than the last-level cache) are timed
+    back to back; the 64-layer figure is that time x 64 / layers (stated)."""
+    import torch
+
+    import oracle
+
+    B = 64
+    mats = []
+    for l in range(layers):
+        for mi, (name, N, K) in enumerate(synth.LAYER_SHAPES):
+            pw = build_matrix(ebq, "mixed", l, mi, name, N, K)
+            wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+            dw = torch.empty((N, K // 32), dtype=torch.float32, device="cuda")
+            ebq.qweight_unpack_i8(pw, wq, dw)
+            del pw
+            mats.append((l, mi, name, N, K, wq, dw, torch.empty((B, N), dtype=torch.float32, device="cuda")))
+    x = {K: synth.gauss_torch([seed_of("mixed"), 2000, K, B], (B, K)) for K in WIDTHS}
+    xq = {K: torch.empty((B, K), dtype=torch.int8, device="cuda") for K in WIDTHS}
+    dx = {K: torch.empty((B, K // 32), dtype=torch.float32, device="cuda") for K in WIDTHS}
+    sx = {K: torch.empty((B, K // 32), dtype=torch.int32, device="cuda") for K in WIDTHS}
+
+    def step():
+        for K in WIDTHS:
+            ebq.qact_quant_i8(x[K], 32, xq[K], dx[K], sx[K])
+        for (_, _, _, N, K, wq, dw, y) in mats:
+            ebq.qgemm_i8(xq[K], dx[K], wq, dw, 32, y)
+
+    t, _ = time_region(step, reps, 2)
+    ops = sum(2.0 * B * N * K for (_, _, _, N, K, _, _, _) in mats)
+    int8_bytes = sum(wq.numel() + dw.numel() * 4 for (_, _, _, _, _, wq, dw, _) in mats)
+    # parity: sampled rows of every product of layer 0 against the oracle's GEMV
+    # from the same float draws (the unpacked product is the same sum)
+    rng = np.random.default_rng(seed)
+    ok, worst = True, 0.0
+    for (l, mi, name, N, K, _, _, y) in mats:
+        if l != 0:
+            continue
+        fmt = layer_fmt("mixed", name)
+        rows = np.sort(rng.choice(N, size=8, replace=False))
+        w = synth.gauss_torch([seed_of("mixed"), l, mi], (N, K), 0.02)[rows].cpu().numpy()
+        codes, sc = oracle.quantize(fmt, w)
+        rq, rd, _ = oracle.act_quant(x[K].cpu().numpy(), 32)
+        yr, absT, _ = oracle.gemv(fmt, oracle.pack(fmt, codes), sc, None, K, rq, rd)
+        err = np.abs(y.cpu().numpy()[:, rows].astype(np.float64) - yr)
+        worst = max(worst, float((err / np.maximum(absT, 1e-300)).max()))
+        ok = ok and bool((err <= 1e-4 * absT).all())
+    per_layer = t / layers
+    del mats, x, xq, dx, sx
+    return {
+        "layers_timed": layers,
+        "per_layer_us": round(per_layer * 1e6, 1),
+        "step_us_64_layers": round(per_layer * 64 * 1e6, 1),
+        "extrapolation": "64 x the per-layer time of %d distinct layers timed back to back" % layers,
+        "tops": round(ops / t / 1e12, 1),
+        "int8_weight_gbs": round(int8_bytes / t / 1e9, 1),
+        "equiv_tok_s": round(B / (per_layer * 64), 1),
+        "parity": "ok" if ok else "FAIL",
+        "worst_err_over_sum_abs_terms": worst,
+    }
+
+
 def bench_mfma_ceiling(ebq):
     """The dense int8 matrix-core rate this part sustains: MFMA 32x32x32 i8 only,
     two waves per SIMD on every CU, and the shader clock it ran at (the waves'
@@ -607,6 +708,10 @@ def main():
             }
             del plan, ms
             torch.cuda.empty_cache()
+        log("mixed stack B=64")
+        extra["mixed_int4_attn_ternary_ffn_B64"] = bench_mixed_b64_gemv(ebq, min(reps, 10))
+        extra["mixed_int4_attn_ternary_ffn_B64_int8_gemm"] = bench_mixed_b64_int8_gemm(ebq, min(reps, 10))
+        torch.cuda.empty_cache()
         log("2-bit layer x8 copies")
         l2 = Stack(ebq, "int2", 8, 1, shapes=synth.LAYER_SHAPES_FUSED, copies_of=lambda l: l)
         plan, t, tk, _ = bench_stack_grouped(ebq, l2, reps, 2)
