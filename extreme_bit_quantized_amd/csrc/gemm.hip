@@ -22,50 +22,84 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-constexpr int GBM = 128, GBN = 128, GBK = 64, GPITCH = 80;
+constexpr int GBK = 64, GPITCH = 80;
 
-template <int KB>
-__global__ __launch_bounds__(256) void k_gemm_i8(const int8_t* __restrict__ xq, const float* __restrict__ dx, int M,
+// Workgroup tile (64 MW) x (256 / MW): MW = 2 gives 128 x 128 (waves 2 x 2),
+// MW = 1 gives 64 x 256 (waves 1 x 4, for M <= 64: no idle rows).  The scales of
+// the K-blocks that end in a stage travel with its tiles (register-staged into
+// LDS, block-major, so four consecutive rows' dx are one 16-byte read).
+template <int KB, int MW>
+__global__ __launch_bounds__(256, KB == 256 ? 2 : 1) void k_gemm_i8(const int8_t* __restrict__ xq, const float* __restrict__ dx, int M,
                                                  const int8_t* __restrict__ wq, const float* __restrict__ dw, int N,
                                                  int K, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) int8_t As[2][GBM * GPITCH];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[2][GBN * GPITCH];
+  constexpr int TM = 64 * MW, TN = 256 / MW;
+  constexpr int AH = TM * 4 / 256, BH = TN * 4 / 256;  // 16-byte chunks per thread and stage
+  constexpr int NSB = KB == 32 ? GBK / 32 : 1;         // scale blocks staged per stage
+  constexpr int NS = (NSB * (TM + TN) + 255) / 256;    // scale values per thread and stage
+  __shared__ __attribute__((aligned(16))) int8_t As[2][TM * GPITCH];
+  __shared__ __attribute__((aligned(16))) int8_t Bs[2][TN * GPITCH];
+  __shared__ __attribute__((aligned(16))) float Sx[2][NSB][TM];
+  __shared__ __attribute__((aligned(16))) float Sw[2][NSB][TN];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+  const int wm = (wave / (4 / MW)) * 64, wn = (wave % (4 / MW)) * 64;
   const int nkb = K / KB;
 
-  // Global -> LDS loader: chunk c = tid + 256 h (h = 0, 1): row c / 4, 16-byte column c % 4.
-  int lrow[2], lcol[2];
-  bool aok[2], bok[2];
+  // Global -> LDS loader: chunk c = tid + 256 h: row c / 4, 16-byte column c % 4.
+  const int8_t* ag[AH];
+  const int8_t* bg[BH];
+  bool aok[AH], bok[BH];
+  int aoffl[AH], boffl[BH];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = tid + 256 * h;
-    lrow[h] = c >> 2;
-    lcol[h] = (c & 3) * 16;
-    aok[h] = m0 + lrow[h] < M;
-    bok[h] = n0 + lrow[h] < N;
+  for (int h = 0; h < AH; ++h) {
+    const int c = tid + 256 * h, r = c >> 2, col = (c & 3) * 16;
+    aok[h] = m0 + r < M;
+    ag[h] = xq + (int64_t)(aok[h] ? m0 + r : 0) * K + col;
+    aoffl[h] = r * GPITCH + col;
   }
-  const int8_t* ag[2];
-  const int8_t* bg[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    ag[h] = xq + (int64_t)(aok[h] ? m0 + lrow[h] : 0) * K + lcol[h];
-    bg[h] = wq + (int64_t)(bok[h] ? n0 + lrow[h] : 0) * K + lcol[h];
+  for (int h = 0; h < BH; ++h) {
+    const int c = tid + 256 * h, r = c >> 2, col = (c & 3) * 16;
+    bok[h] = n0 + r < N;
+    bg[h] = wq + (int64_t)(bok[h] ? n0 + r : 0) * K + col;
+    boffl[h] = r * GPITCH + col;
   }
-  v4i ra[2], rb[2];
-  auto gload = [&](int k0) {
+  v4i ra[AH], rb[BH];
+  float rs[NS];
+  // the scale blocks of stage st: KB = 32: 2 st, 2 st + 1; KB = 256: the block of stage st
+  auto gload = [&](int st) {
+    const int k0 = st * GBK;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      ra[h] = aok[h] ? *(const v4i*)(ag[h] + k0) : v4i{0, 0, 0, 0};
-      rb[h] = bok[h] ? *(const v4i*)(bg[h] + k0) : v4i{0, 0, 0, 0};
+    for (int h = 0; h < AH; ++h) ra[h] = aok[h] ? *(const v4i*)(ag[h] + k0) : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < BH; ++h) rb[h] = bok[h] ? *(const v4i*)(bg[h] + k0) : v4i{0, 0, 0, 0};
+    const int kb0 = KB == 32 ? st * NSB : k0 / KB;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int c = tid + 256 * i, blk = c / (TM + TN), r = c % (TM + TN);
+      float v = 0.0f;
+      if (blk < NSB) {
+        if (r < TM) {
+          if (m0 + r < M) v = dx[(int64_t)(m0 + r) * nkb + kb0 + blk];
+        } else if (n0 + r - TM < N) {
+          v = dw[(int64_t)(n0 + r - TM) * nkb + kb0 + blk];
+        }
+      }
+      rs[i] = v;
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      *(v4i*)(&As[buf][lrow[h] * GPITCH + lcol[h]]) = ra[h];
-      *(v4i*)(&Bs[buf][lrow[h] * GPITCH + lcol[h]]) = rb[h];
+    for (int h = 0; h < AH; ++h) *(v4i*)(&As[buf][aoffl[h]]) = ra[h];
+#pragma unroll
+    for (int h = 0; h < BH; ++h) *(v4i*)(&Bs[buf][boffl[h]]) = rb[h];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int c = tid + 256 * i, blk = c / (TM + TN), r = c % (TM + TN);
+      if (blk < NSB) {
+        if (r < TM) Sx[buf][blk][r] = rs[i];
+        else Sw[buf][blk][r - TM] = rs[i];
+      }
     }
   };
 
@@ -81,23 +115,28 @@ __global__ __launch_bounds__(256) void k_gemm_i8(const int8_t* __restrict__ xq, 
         facc[i][j][e] = 0.0f;
       }
 
-  // Rows / columns of this lane's accumulator entries.
+  // Rows / columns of this lane's accumulator entries: row wm + 32 i + 8 (e / 4)
+  // + 4 lg + e % 4, column wn + 32 j + lm.
   const int lm = lane & 31, lg = lane >> 5;
-  auto epilogue = [&](int kb) {
+  auto epilogue = [&](int buf, int blk) {
+    float sw[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn + 32 * j + lm;
-      const float sw = n < N ? dw[(int64_t)n * nkb + kb] : 0.0f;
+    for (int j = 0; j < 2; ++j) sw[j] = Sw[buf][blk][wn + 32 * j + lm];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * lg + (e & 3);
-          const float sx = m < M ? dx[(int64_t)m * nkb + kb] : 0.0f;
-          facc[i][j][e] = __builtin_fmaf(sx * sw, (float)acc[i][j][e], facc[i][j][e]);
-          acc[i][j][e] = 0;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const v4f sx = *(const v4f*)&Sx[buf][blk][wm + 32 * i + 8 * q4 + 4 * lg];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int e = 4 * q4 + t;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            facc[i][j][e] = __builtin_fmaf(sx[t] * sw[j], (float)acc[i][j][e], facc[i][j][e]);
+            acc[i][j][e] = 0;
+          }
         }
-    }
+      }
   };
 
   const int nstage = K / GBK;
@@ -106,7 +145,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(const int8_t* __restrict__ xq, 
   __syncthreads();
   for (int s = 0; s < nstage; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nstage) gload((s + 1) * GBK);
+    if (s + 1 < nstage) gload(s + 1);
 #pragma unroll
     for (int kk = 0; kk < GBK; kk += 32) {
       v4i fa[2], fb[2];
@@ -118,10 +157,11 @@ __global__ __launch_bounds__(256) void k_gemm_i8(const int8_t* __restrict__ xq, 
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      if (KB == 32) epilogue((s * GBK + kk) / 32);
+      if (KB == 32) epilogue(buf, kk / 32);
     }
-    if (KB == 256 && ((s + 1) * GBK) % 256 == 0) epilogue((s * GBK) / 256);
+    if (KB == 256 && ((s + 1) * GBK) % 256 == 0) epilogue(buf, 0);
     if (s + 1 < nstage) {
+      // buffer buf ^ 1 (stage s - 1) was released by the previous barrier
       lstore(buf ^ 1);
       __syncthreads();
     }
@@ -549,9 +589,18 @@ hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* w
     hipLaunchKernelGGL(k_gemm_i8_p256, dim3(G), dim3(PTHREADS), 0, s, xq, dx, M, wq, dw, N, K, y, n_tiles, m_tiles);
     return hipGetLastError();
   }
-  const dim3 grid((N + GBN - 1) / GBN, (M + GBM - 1) / GBM), block(256);
-  if (kblock == 256) hipLaunchKernelGGL(k_gemm_i8<256>, grid, block, 0, s, xq, dx, M, wq, dw, N, K, y);
-  else hipLaunchKernelGGL(k_gemm_i8<32>, grid, block, 0, s, xq, dx, M, wq, dw, N, K, y);
+  // Other shapes: 64 x 256 workgroup tiles for up to 64 rows (small batches),
+  // else 128 x 128.
+  const dim3 block(256);
+  if (M <= 64) {
+    const dim3 grid((N + 255) / 256, 1);
+    if (kblock == 256) hipLaunchKernelGGL((k_gemm_i8<256, 1>), grid, block, 0, s, xq, dx, M, wq, dw, N, K, y);
+    else hipLaunchKernelGGL((k_gemm_i8<32, 1>), grid, block, 0, s, xq, dx, M, wq, dw, N, K, y);
+  } else {
+    const dim3 grid((N + 127) / 128, (M + 127) / 128);
+    if (kblock == 256) hipLaunchKernelGGL((k_gemm_i8<256, 2>), grid, block, 0, s, xq, dx, M, wq, dw, N, K, y);
+    else hipLaunchKernelGGL((k_gemm_i8<32, 2>), grid, block, 0, s, xq, dx, M, wq, dw, N, K, y);
+  }
   return hipGetLastError();
 }
 
