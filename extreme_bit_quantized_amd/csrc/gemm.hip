@@ -4,12 +4,14 @@
 // xq[m] and wq[n] over K-block kb.  Both operands are K-contiguous rows, which
 // is exactly what v_mfma_i32_32x32x32_i8 wants per lane (16 int8 of one row).
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile of y; each wave a
-// 64 x 64 quarter as 2 x 2 MFMA tiles.  K advances in 64-wide stages staged
-// through LDS (double buffered, rows padded to 80 bytes so the 8 lanes of a
-// 16-byte LDS read phase hit different banks); the next stage's global loads
-// are in flight while the current one runs on the matrix cores.  At the end of
-// each K-block the int32 accumulators are scaled into fp32 accumulators.
+// Generic kernel (any shape): a 256-thread workgroup computes a 128 x 128 tile
+// of y (64 x 256 when M <= 64); each wave a 64 x 64 part as 2 x 2 MFMA tiles.
+// K advances in 64-wide stages staged through LDS (double buffered, rows padded
+// to 80 bytes so the 8 lanes of a 16-byte LDS read phase hit different banks);
+// the next stage's global loads are in flight while the current one runs on
+// the matrix cores.  At the end of each K-block the int32 accumulators are
+// scaled into fp32 accumulators.  256-blocks with K a multiple of 1024 take the
+// pipelined kernel further below.
 #include <algorithm>
 #include <type_traits>
 
