@@ -112,10 +112,12 @@ hipError_t launch_act_planes(const int8_t* q, int B, int K, uint32_t* planes, hi
 }
 
 // Batched Q8 per 32 + planes: job j owns threads [start[j], start[j + 1]) (one
-// per 4 values, starts multiples of 256, so a workgroup serves one job).  The 8
-// lanes of a block then hold its 32 codes, 4 each; lanes 2g and 2g + 1 (values
-// 8g .. 8g + 7) swap their code words and write plane word g (lo nibbles) and
-// 4 + g (hi nibbles) as k_act_planes does.
+// per 16 values, starts multiples of 256, so a workgroup serves one job).  Lanes
+// 2k and 2k + 1 hold the two halves of 32-block k (DPP partners for the block's
+// max and sum); q = rint(v / d) comes from the low byte of the fp32 sum
+// 1.5 * 2^23 + v * (1 / d) (unit ulp: nearest integer, ties to even; |q| <= 127,
+// so no clamp), and each lane writes plane words g (lo nibbles) and 4 + g (hi
+// nibbles) of its two 8-value groups g as k_act_planes does.
 struct ActBatch {
   int n;
   int64_t start[QACT_BATCH_MAX + 1];
@@ -127,32 +129,68 @@ __global__ __launch_bounds__(256) void k_act_quant_batch(const ActBatch b) {
   int j = 0;
   while (j + 1 < b.n && t >= b.start[j + 1]) ++j;  // uniform over the workgroup
   const qact_job_t& J = b.job[j];
-  const int64_t i = t - b.start[j];
-  const int64_t n4 = (int64_t)J.B * J.K / 4;
-  const bool ok = i < n4;
-  const f32x4 v = ok ? *(const f32x4*)(J.x + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
-  uint32_t q4;
-  float dd;
-  int32_t s;
-  const int lt = threadIdx.x & 7;  // lane within the 32-block
-  q8_lane4(v, 8, lt == 0, &q4, &dd, &s);
-  const uint32_t other = __shfl_xor(q4, 1);
+  const int64_t i = t - b.start[j];                 // 16-value chunk of the job
+  const int64_t n16 = (int64_t)J.B * J.K / 16;
+  const bool ok = i < n16;  // both lanes of a block agree
+  float v[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const f32x4 x4 = ok ? *(const f32x4*)(J.x + 16 * i + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    v[4 * c] = x4.x;
+    v[4 * c + 1] = x4.y;
+    v[4 * c + 2] = x4.z;
+    v[4 * c + 3] = x4.w;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) am = fmaxf(am, fabsf(v[k]));
+  am = fmaxf(am, xlane<1>(am));
+  const float dd = am / 127.0f;
+  const float id = am == 0.0f ? 0.0f : 1.0f / dd;
+  uint32_t pk[4];
+  uint32_t bsum = 0;  // 16 x 0x4B400000 + the sum of the 16 codes, mod 2^32
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t bb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bb[k] = __builtin_bit_cast(uint32_t, v[4 * w + k] * id + 12582912.0f);
+      bsum += bb[k];
+    }
+    const uint32_t lo = __builtin_amdgcn_perm(bb[1], bb[0], 0x0C0C0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(bb[3], bb[2], 0x0C0C0400u);
+    pk[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+  int sum = (int)(bsum - 16u * 0x4B400000u);
+  sum += xlane_i<1>(sum);
   if (!ok) return;
-  const int64_t blk = i >> 3;
-  if (J.q) *(uint32_t*)(J.q + 4 * i) = q4;
-  if (lt == 0) {
+  const int64_t blk = i >> 1;
+  const int half = (int)(i & 1);
+  if (J.q) {
+    int8_t* o = J.q + 16 * i;
+    if (((uintptr_t)o & 15) == 0) {
+      *(uint4*)o = uint4{pk[0], pk[1], pk[2], pk[3]};
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) ((uint32_t*)o)[w] = pk[w];
+    }
+  }
+  if (half == 0) {
     J.d[blk] = dd;
-    J.qsum[blk] = s;
+    J.qsum[blk] = sum;
   }
   if (J.planes) {
-    const int g = lt >> 1, hi = lt & 1;
-    const uint32_t a0 = hi ? other : q4, a1 = hi ? q4 : other;  // values 8g..8g+3, 8g+4..8g+7
-    const int sh = hi ? 4 : 0;
-    auto nib4 = [&](uint32_t a) {
+    // nibbles at bits 8k + sh of a code word, moved to nibble k
+    auto nib4 = [](uint32_t a, int sh) {
       const uint32_t u = (a >> sh) & 0x0F0F0F0Fu;
       return (u & 0xFu) | ((u >> 4) & 0xF0u) | ((u >> 8) & 0xF00u) | ((u >> 12) & 0xF000u);
     };
-    J.planes[blk * 8 + 4 * hi + g] = nib4(a0) | (nib4(a1) << 16);
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      const int g = 2 * half + gg;  // values 8g .. 8g + 7 of the block: code words 2gg, 2gg + 1 of this lane
+      J.planes[blk * 8 + g] = nib4(pk[2 * gg], 0) | (nib4(pk[2 * gg + 1], 0) << 16);
+      J.planes[blk * 8 + 4 + g] = nib4(pk[2 * gg], 4) | (nib4(pk[2 * gg + 1], 4) << 16);
+    }
   }
 }
 
@@ -163,8 +201,8 @@ hipError_t launch_act_quant_batch(const qact_job_t* jobs, int n, hipStream_t s) 
   for (int j = 0; j < n; ++j) {
     b.job[j] = jobs[j];
     b.start[j] = acc;
-    const int64_t n4 = (int64_t)jobs[j].B * jobs[j].K / 4;
-    acc += (n4 + 255) / 256 * 256;
+    const int64_t n16 = (int64_t)jobs[j].B * jobs[j].K / 16;
+    acc += (n16 + 255) / 256 * 256;
   }
   b.start[n] = acc;
   if (acc == 0) return hipSuccess;
