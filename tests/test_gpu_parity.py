@@ -400,7 +400,7 @@ def test_unpack_i8(fmt):
 @pytest.mark.parametrize("kblock", [256, 32])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (17, 130, 512), (200, 64, 1024), (128, 257, 2048),
                                    (300, 200, 1024), (513, 1300, 512), (256, 128, 1280),
-                                   (600, 300, 3072)])
+                                   (600, 300, 3072), (64, 1000, 2048), (48, 520, 1024)])
 def test_gemm_parity(kblock, M, N, K):
     xq = synth.integers([220, M, K], (M, K), -127, 127).astype(np.int8)
     wq = synth.integers([221, N, K], (N, K), -127, 127).astype(np.int8)
