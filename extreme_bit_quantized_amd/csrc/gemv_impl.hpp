@@ -726,7 +726,8 @@ constexpr int kTileCachePolicy = 2;  // nt
 // and the tail segment if (nseg % nwk) == wk.  lds: this wave's region.
 template <int FMT, int NB, bool WI>
 __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, int nwk, uint8_t* lds,
-                                          const int8_t* v8, float (&y)[NB], int32_t* Ibase) {
+                                          const int8_t* v8, float (&y)[NB], int32_t* Ibase, int sk = 0,
+                                          int sn = 1) {
   constexpr int CH = Seg<FMT>::CH;
   constexpr int SEGK = Seg<FMT>::K;
   constexpr int SPS = Seg<FMT>::SPS;
@@ -885,8 +886,11 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
         constexpr int SUB = decltype(scc)::value;
         // the block the scalar pipeline loads after this sub-chunk
         const int kb_after = SUB + 1 < NSUB ? seg * (SEGK / 32) + (SUB + 1) * 8 : nsg * (SEGK / 32);
-        sub_compute<FMT, NB, SUB, WI, KACT>(T, S, act[SUB], kp, AK, seg * (SEGK / 32) + SUB * 8, 8, kb_after, prev,
-                                            v8, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
+        // (sn > 1: this wave computes only sub-chunks SUB % sn == sk; formats
+        // without state carried between sub-chunks and without the scalar pipeline)
+        if (sn == 1 || SUB % sn == sk)
+          sub_compute<FMT, NB, SUB, WI, KACT>(T, S, act[SUB], kp, AK, seg * (SEGK / 32) + SUB * 8, 8, kb_after, prev,
+                                              v8, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
         if constexpr (!KACT) {
           // kept after the sub-chunk's compute: the new values take its registers
           __builtin_amdgcn_sched_barrier(0);
@@ -1013,7 +1017,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float ga
   float y[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) y[b] = 0.0f;
-  gemv_tile<FMT, NB, WI>(it, row0, wave, 4, lds + wave * Seg<FMT>::CH * 1024, v8, y, Iout);
+  // A row of one or two whole segments has fewer segments than waves: the
+  // waves of a segment then split its 256-weight sub-chunks.
+  constexpr bool SPLIT_OK = !WI && NB <= 2 && FMT != QFMT_INT2 && FMT != QFMT_TRELLIS2;
+  const int nseg = it.cols / Seg<FMT>::K;
+  if (SPLIT_OK && it.cols % Seg<FMT>::K == 0 && (nseg == 1 || nseg == 2))
+    gemv_tile<FMT, NB, WI>(it, row0, wave % nseg, nseg, lds + wave * Seg<FMT>::CH * 1024, v8, y, Iout, wave / nseg,
+                           4 / nseg);
+  else
+    gemv_tile<FMT, NB, WI>(it, row0, wave, 4, lds + wave * Seg<FMT>::CH * 1024, v8, y, Iout);
   wait_all();  // no tile DMA or scalar load may still be landing when the wave ends
   if (WI) return;
 #pragma unroll
