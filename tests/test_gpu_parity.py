@@ -19,7 +19,7 @@ import extreme_bit_quantized_amd as ebq  # noqa: E402
 
 ebq.load()
 ALL = [TERN, INT2, SIGN1, INT4, TRELLIS]
-SHAPES = [(1, 1024), (70, 1280), (200, 1024), (130, 5120), (64, 2304)]
+SHAPES = [(1, 1024), (70, 1280), (200, 1024), (130, 5120), (64, 2304), (37, 512), (90, 2048)]
 
 
 def _sync():
