@@ -340,6 +340,29 @@ def test_gemv_full_size_sampled(fmt, N, K, B):
     assert_close_terms(host(y)[:, rows], yr, absT, what="%s %dx%d B=%d" % (NAMES[fmt], N, K, B))
 
 
+@pytest.mark.parametrize("B", [2, 3, 4, 5, 6, 7])
+def test_grouped_every_batch_size(B):
+    """The grouped launch at every batch size between 1 and 8 (each batch size and
+    format has its own workgroup size), all five formats in one plan."""
+    specs = [(SIGN1, 200, 2048), (TERN, 130, 1280), (INT4, 70, 1024), (INT2, 90, 2560), (TRELLIS, 65, 1536)]
+    entries, refs = [], []
+    for i, (fmt, N, K) in enumerate(specs):
+        raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 400 + 10 * B + i, B)
+        q, pl, d, s = gpu_act_planes(x)
+        y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+        entries.append((pw, q, pl, d, s, y))
+        rq, rd, _ = oracle.act_quant(x)
+        refs.append(oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd))
+    plan = ebq.GroupedPlan(entries, B)
+    for rep in range(2):
+        for e in entries:
+            e[5].fill_(float("nan"))
+        plan.run()
+        _sync()
+        for (fmt, N, K), e, (yr, absT, _) in zip(specs, entries, refs):
+            assert_close_terms(host(e[5]), yr, absT, what="grouped %s B=%d rep %d" % (NAMES[fmt], B, rep))
+
+
 # ---------------------------------------------------------------------------------------------
 # trellis decode, unpack, GEMM
 # ---------------------------------------------------------------------------------------------
