@@ -101,8 +101,14 @@ double qref_f16_to_f64(uint16_t h) {
  * llama.cpp": decode via DP4A GEMV, batches via INT8 MMA, prefill via INT8
  * GEMM).  One fp32 scale per block of n values:
  *   amax = max |v|;  d = amax / 127 (fp32, IEEE division);
- *   id = amax == 0 ? 0 : 1 / d (fp32);  q = clamp(rint(v * id), -127, 127)
- * with rint rounding half to even.  -128 never occurs. */
+ *   r = 1 / d (fp32);  id = r if r is finite, else 0;
+ *   q = clamp(rint(v * id), -127, 127) with rint rounding half to even.
+ * r is infinite for a zero block (d = 0) and whenever d <= 2^-128, where the
+ * reciprocal overflows (amax below about 3.7e-37): such a block quantizes to
+ * q = 0, qsum = 0, and d keeps the value amax / 127.  -128 never occurs.
+ * Inputs are finite; v * id is then finite too (|v * id| <= 127 (1 + 2^-22)),
+ * and the NaN test below is never taken for them (it only keeps a non-finite
+ * input from reaching an undefined float-to-int conversion). */
 void qref_q8_block(const float* v, int n, int8_t* q, float* d, int32_t* qsum) {
   float amax = 0.0f;
   for (int i = 0; i < n; ++i) {
@@ -110,14 +116,16 @@ void qref_q8_block(const float* v, int n, int8_t* q, float* d, int32_t* qsum) {
     if (a > amax) amax = a;
   }
   float dd = amax / 127.0f;
-  float id = (amax == 0.0f) ? 0.0f : 1.0f / dd;
+  float r = 1.0f / dd;
+  float id = isfinite(r) ? r : 0.0f;
   int32_t s = 0;
   for (int i = 0; i < n; ++i) {
     float prod = v[i] * id;
-    float r = rintf(prod);
-    if (r > 127.0f) r = 127.0f;
-    if (r < -127.0f) r = -127.0f;
-    q[i] = (int8_t)r;
+    float t = rintf(prod);
+    if (t != t) t = 0.0f;
+    if (t > 127.0f) t = 127.0f;
+    if (t < -127.0f) t = -127.0f;
+    q[i] = (int8_t)t;
     s += q[i];
   }
   *d = dd;

@@ -23,7 +23,9 @@ def test_trellis_hash_byte_offset():
 
 def _q8_reference(v, am):
     dd = np.float32(am) / np.float32(127.0)
-    inv = np.float32(0.0) if am == 0 else np.float32(1.0) / dd
+    with np.errstate(divide="ignore", over="ignore"):
+        r = np.float32(1.0) / dd
+    inv = r if np.isfinite(r) else np.float32(0.0)   # 1/d overflows for d <= 2^-128: a zero block
     t = (v * inv).astype(np.float32)
     return np.clip(np.rint(t), -127, 127).astype(np.int64), t
 
@@ -32,14 +34,18 @@ def test_q8_magic_sum_rounding():
     """The low byte of fp32(1.5 * 2^23 + t), t = fp32(v * (1 / d)), is rint(t)
     (ties to even) in two's complement, and |rint(t)| <= 127 for every |v| <=
     amax, so the clamp never acts: checked on blocks with amax spread over many
-    binades, including v = +-amax, ties and values next to them."""
+    binades down to the smallest subnormal (blocks whose 1/d overflows have
+    id = 0 and every t = 0), including v = +-amax, ties and values next to them."""
     rng = np.random.default_rng(7)
-    for am in np.concatenate([[1e-30, 1e-7, 0.37, 1.0, 126.99, 127.0, 3.3e7],
+    tiny = [1.4e-45, 1e-44, 1e-42, 1e-40, 1e-38, 3.0e-37, 3.73e-37, 3.8e-37, 1e-36, 1e-35, 2.0 ** -118]
+    for am in np.concatenate([tiny, [1e-30, 1e-7, 0.37, 1.0, 126.99, 127.0, 3.3e7],
                               rng.uniform(1e-6, 1e6, 200)]).astype(np.float32):
         dd = np.float32(am) / np.float32(127.0)
-        inv = np.float32(1.0) / dd
+        with np.errstate(divide="ignore", over="ignore"):
+            inv = np.float32(1.0) / dd
+        step = inv if np.isfinite(inv) else np.float32(1.0)
         v = np.concatenate([rng.uniform(-am, am, 4000).astype(np.float32), [am, -am, 0.0],
-                            ((np.arange(-127, 128) + 0.5) / inv).astype(np.float32)]).astype(np.float32)
+                            ((np.arange(-127, 128) + 0.5) / step).astype(np.float32)]).astype(np.float32)
         v = v[np.abs(v) <= am]
         q, t = _q8_reference(v, am)
         assert np.abs(np.rint(t)).max() <= 127          # no clamp needed

@@ -114,6 +114,51 @@ def test_q8_hand_worked_ties(qref):
     assert list(q[:4]) == [int(v) for v in rows["q2"]] and d == float(rows["d2"][0])
 
 
+def _tiny_cases():
+    cases = {}
+    for r in _golden_lines("q8_tiny.txt"):
+        cases.setdefault(r[0], {})[r[1]] = r[2:]
+    return cases
+
+
+def test_q8_tiny_blocks_hand_worked(qref):
+    """Blocks whose amax is tiny (tests/golden/q8_tiny.txt): a reciprocal 1/d that
+    overflows makes a zero block, a subnormal d that does not is quantized
+    normally; the boundary pair E/F sits one fp32 step apart.  The golden lines
+    are re-derived here in exact rational arithmetic as well."""
+    import golden.q8_exact as qe
+
+    for name, c in _tiny_cases().items():
+        xb = [int(h, 16) for h in c["x"]]
+        x = np.zeros(32, np.uint32)
+        x[:len(xb)] = xb
+        q, d, s = qref.q8_block(x.view(np.float32))
+        want_q = [int(v) for v in c["q"]]
+        assert list(q[:len(want_q)]) == want_q and not q[len(want_q):].any(), name
+        assert np.float32(d).view(np.uint32) == int(c["d"][0], 16), name
+        assert s == int(c["qsum"][0]), name
+        eq, ed, es = qe.q8_exact([qe.from_bits(b) for b in xb])
+        assert eq == want_q and qe.f32_bits(ed) == int(c["d"][0], 16) and es == s, name
+
+
+def test_q8_matches_exact_arithmetic(qref):
+    """Random blocks with amax from the smallest subnormal up to 1e6 (dense
+    around the 2^-128 reciprocal-overflow boundary): the oracle's fp32 Q8 equals
+    the same definition carried out in exact rational arithmetic."""
+    import golden.q8_exact as qe
+
+    rng = np.random.default_rng(31)
+    exps = np.concatenate([np.arange(-149, -100), rng.integers(-100, 20, 40)])
+    for e in exps:
+        for rep in range(3):
+            mant = rng.integers(1, 1 << 24, 32).astype(np.float64)
+            v = (mant * 2.0 ** (int(e) - 23) * rng.choice([-1.0, 1.0], 32)).astype(np.float32)
+            v[rng.integers(0, 32, 4)] = 0.0
+            q, d, s = qref.q8_block(v)
+            eq, ed, es = qe.q8_exact([qe.from_bits(int(b)) for b in v.view(np.uint32)])
+            assert list(q) == eq and np.float32(d).view(np.uint32) == qe.f32_bits(ed) and s == es, (e, rep)
+
+
 def test_q8_properties(qref):
     x = synth.gauss([11], (64, 1024)) * synth.uniform([12], (64, 1), 0.01, 100.0)
     x[3, :32] = 0.0  # an all-zero block
@@ -187,6 +232,21 @@ def test_sign_quantizer(qref):
     assert (b == (w >= 0)).all() and b[0, 0] == 1
     m = np.abs(w.astype(np.float64)).reshape(4, -1, 128).mean(-1)
     assert (s == m.astype(np.float16).view(np.uint16)).all()
+
+
+def test_sign_quantizer_hand_worked_scales(qref):
+    """tests/golden/sign1_scales.txt: the fp16 scale (mean |w|, ties to even) and
+    the sign bits of hand-built blocks."""
+    for r in _golden_lines("sign1_scales.txt"):
+        vals = []
+        for run in r[1:-2]:
+            n, v = run.split("x")
+            vals += [float(v)] * int(n)
+        w = np.array([vals], np.float32)
+        assert w.shape == (1, 128), r[0]
+        b, s = qref.quantize(qref.SIGN1, w)
+        assert s[0, 0] == int(r[-2], 16), (r[0], hex(s[0, 0]))
+        assert int(b.sum()) == int(r[-1]), r[0]
 
 
 # ----------------------------------------------------------------------------------
