@@ -260,12 +260,17 @@ def qgemv_grouped_run(host_plan, dev_plan, stream=None):
 
 
 class GroupedPlan:
-    """A plan built on the host and copied to the device."""
+    """A plan built on the host and copied to the device.
+
+    The plan stores the device addresses of every entry's tensors; the plan
+    object keeps those tensors (and the PackedWeights) referenced for as long as
+    it lives, so none of them can be freed and reused while the plan may run."""
 
     def __init__(self, entries, B: int, device="cuda"):
         import torch
 
-        self.items = make_items(entries)
+        self._entries = [tuple(e) for e in entries]
+        self.items = make_items(self._entries)
         self.B = B
         nb = qgemv_grouped_plan_bytes(self.items, B)
         # 16-byte aligned host buffer

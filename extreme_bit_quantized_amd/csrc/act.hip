@@ -25,13 +25,21 @@ __device__ __forceinline__ int group_sum(int v, int width) {
   return v;
 }
 
+// Reciprocal of the Q8 step d: 1 / d when finite, else 0.  1 / d is +inf for a
+// zero block (d = 0) and whenever d <= 2^-128 (the reciprocal overflows); such
+// blocks quantize to q = 0 and qsum = 0, with d kept.
+__device__ __forceinline__ float q8_inv(float d) {
+  const float r = 1.0f / d;
+  return r < __builtin_inff() ? r : 0.0f;
+}
+
 // Q8 of four values held by this lane, whose block spans `width` lanes.
 // Writes the 4 int8 codes to q4 and, from the block's first lane, d and qsum.
 __device__ __forceinline__ void q8_lane4(f32x4 v, int width, bool first, uint32_t* q4, float* d, int32_t* qsum) {
   float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   am = group_max(am, width);
   const float dd = am / 127.0f;
-  const float id = am == 0.0f ? 0.0f : 1.0f / dd;
+  const float id = q8_inv(dd);
   const float e[4] = {v.x, v.y, v.z, v.w};
   uint32_t packed = 0;
   int s = 0;
@@ -114,7 +122,7 @@ hipError_t launch_act_planes(const int8_t* q, int B, int K, uint32_t* planes, hi
 // Batched Q8 per 32 + planes: job j owns threads [start[j], start[j + 1]) (one
 // per 16 values, starts multiples of 256, so a workgroup serves one job).  Lanes
 // 2k and 2k + 1 hold the two halves of 32-block k (DPP partners for the block's
-// max and sum); q = rint(v / d) comes from the low byte of the fp32 sum
+// max and sum); q = rint(v * (1 / d)) comes from the low byte of the fp32 sum
 // 1.5 * 2^23 + v * (1 / d) (unit ulp: nearest integer, ties to even; |q| <= 127,
 // so no clamp), and each lane writes plane words g (lo nibbles) and 4 + g (hi
 // nibbles) of its two 8-value groups g as k_act_planes does.
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(256) void k_act_quant_batch(const ActBatch b) {
   for (int k = 0; k < 16; ++k) am = fmaxf(am, fabsf(v[k]));
   am = fmaxf(am, xlane<1>(am));
   const float dd = am / 127.0f;
-  const float id = am == 0.0f ? 0.0f : 1.0f / dd;
+  const float id = q8_inv(dd);
   uint32_t pk[4];
   uint32_t bsum = 0;  // 16 x 0x4B400000 + the sum of the 16 codes, mod 2^32
 #pragma unroll
@@ -217,13 +225,13 @@ hipError_t launch_act_quant_batch(const qact_job_t* jobs, int n, hipStream_t s) 
 // (Every stage adds and subtracts the same pairs in the same order as the
 // definition, so the rounding is the same: a cross stage forms
 // fma(own, +-1, partner's), which is the partner's value plus or minus its
-// own, rounded once.)  The final 1/16 is a power of two, so it is applied to
-// amax and the reciprocal instead of every element: the products are the
-// same numbers (barring subnormal values).  Then Q8 per qblock over
-// WIDTH = qblock / 16 lanes (q from the low byte of 1.5 * 2^23 + v * (1 / d),
-// which rounds to the nearest integer with ties to even, |q| <= 127 without a
-// clamp) and one 16-byte store per lane.  Each lane's block advances by a
-// fixed quotient and remainder per turn of the grid (no division per block).
+// own, rounded once.)  Then every element is multiplied by 1/16, as the
+// definition does (the product rounds only where it is subnormal, and must then
+// round the same way), and Q8 per qblock over WIDTH = qblock / 16 lanes (q
+// from the low byte of 1.5 * 2^23 + v * (1 / d), which rounds to the nearest
+// integer with ties to even, |q| <= 127 without a clamp) and one 16-byte store
+// per lane.  Each lane's block advances by a fixed quotient and remainder per
+// turn of the grid (no division per block).
 template <int WIDTH>
 __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict__ x, int K, int nblocks,
                                                         const uint32_t* __restrict__ sign_bits,
@@ -279,6 +287,8 @@ __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict_
     cross(std::integral_constant<int, 2>{});
     cross(std::integral_constant<int, 4>{});
     cross(std::integral_constant<int, 8>{});
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] *= 0.0625f;
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(u[i]));
@@ -288,9 +298,8 @@ __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict_
       am = fmaxf(am, xlane<4>(am));
       am = fmaxf(am, xlane<8>(am));
     }
-    am *= 0.0625f;
     const float dd = am / 127.0f;
-    const float id = (am == 0.0f ? 0.0f : 1.0f / dd) * 0.0625f;
+    const float id = q8_inv(dd);
     uint32_t pk[4];
     uint32_t bsum = 0;  // sum of the 16 biased values: 16 * 0x4B400000 + sum of q, mod 2^32
 #pragma unroll

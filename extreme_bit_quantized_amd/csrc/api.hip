@@ -2,6 +2,9 @@
 // Every check runs before any HIP call, so rejected calls never touch the GPU.
 #include <algorithm>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
 #include "internal.hpp"
@@ -95,6 +98,25 @@ int64_t count_tiles(const qgemv_item_t* items, int32_t n) {
 }
 
 }  // namespace
+
+namespace qk {
+int resident_workgroups(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;  // (kernel, device) -> workgroups
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(kernel, dev);
+  const auto hit = cache.find(key);
+  if (hit != cache.end()) return hit->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  const int n = per_cu < 1 ? 0 : cus * per_cu;
+  cache[key] = n;
+  return n;
+}
+}  // namespace qk
 
 extern "C" {
 

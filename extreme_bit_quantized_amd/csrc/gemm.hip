@@ -565,23 +565,12 @@ hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* w
     const int tiles = n_tiles * m_tiles;
     // one run per resident workgroup (one per CU: the ring fills its LDS), at most
     // one per tile; a multiple of 8 so runs can be numbered XCD-major
-    static int cached_dev = -1, cached_slots = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (dev != cached_dev) {
-      int cus = 0, per_cu = 0;
-      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorInvalidDevice;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_gemm_i8_p256, PTHREADS, 0) != hipSuccess ||
-          per_cu < 1)
-        per_cu = 1;
-      cached_slots = cus * per_cu;
-      cached_dev = dev;
-    }
+    const int S = resident_workgroups((const void*)k_gemm_i8_p256, PTHREADS);
+    if (S <= 0) return hipErrorInvalidDevice;
     // Whole tiles, one workgroup each, unless the last round would leave more
     // than a quarter of the rounds' time idle: then runs of equal length, one per
     // slot (the idle tail of a short last round is cheaper than cutting tiles:
     // with few CUs busy the clock rises).
-    const int S = cached_slots;
     const int rounds = (tiles + S - 1) / S;
     const bool even_runs = tiles > S && 4 * ((int64_t)rounds * S - tiles) > (int64_t)rounds * S;
     const int G = even_runs ? (S >= 8 ? S & ~7 : S) : tiles;

@@ -12,29 +12,14 @@
 namespace qk {
 
 namespace {
-// Grid of a persistent grouped launch: every CU filled to the kernel's occupancy
-// (one workgroup per CU at the sizes chosen).  0 if a workgroup does not fit.
-// Cached per variant and device (one device per process in practice).
-int grouped_grid(const void* kernel, int variant, int threads) {  // variant = format 1..5
-  static int cached_dev[6] = {-1, -1, -1, -1, -1, -1}, cached_grid[6] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev == cached_dev[variant]) return cached_grid[variant];
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1) return 0;
-  cached_dev[variant] = dev;
-  cached_grid[variant] = cus * per_cu;
-  return cached_grid[variant];
-}
-
 template <int NB, int ONLY>
 hipError_t launch_grouped_variant(const PlanHeader& h, const void* plan, const V8Table& v8, float gain,
                                   hipStream_t s) {
   const int t0 = h.fmt_begin[ONLY], t1 = h.fmt_begin[ONLY + 1];
   if (t1 <= t0) return hipSuccess;
   constexpr int threads = 64 * grouped_wpg(NB, ONLY);
-  const int grid = grouped_grid((const void*)k_gemv_grouped<NB, ONLY>, ONLY, threads);
+  // every CU filled to the kernel's occupancy (one workgroup per CU at the sizes chosen)
+  const int grid = resident_workgroups((const void*)k_gemv_grouped<NB, ONLY>, threads);
   if (grid <= 0) return hipErrorInvalidDevice;
   hipLaunchKernelGGL((k_gemv_grouped<NB, ONLY>), dim3(grid), dim3(threads), 0, s, (const uint8_t*)plan, v8, gain);
   return hipGetLastError();

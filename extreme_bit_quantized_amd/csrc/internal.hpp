@@ -164,6 +164,13 @@ struct V16Table { uint16_t v[256]; };
 // Host-side codebook (built once, thread-safe): V16, V8 and the gain V16[255]/127.
 void trellis_tables(V16Table* v16, V8Table* v8, float* gain);
 
+// Workgroups of `threads` threads of `kernel` the current device holds at once
+// (compute units x resident workgroups per unit): the grid of a persistent
+// launch.  Queried once per (kernel, device) and cached under a lock, so
+// concurrent callers on any threads see a complete entry; 0 if a query fails
+// or no workgroup fits.
+int resident_workgroups(const void* kernel, int threads);
+
 // ---- launchers (each returns a hipError_t) --------------------------------------------
 hipError_t launch_act_quant(const float* x, int B, int K, int qblock, int8_t* q, float* d,
                             int32_t* qsum, hipStream_t s);

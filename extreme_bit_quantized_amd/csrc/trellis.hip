@@ -78,7 +78,7 @@ void trellis_tables(V16Table* v16, V8Table* v8, float* gain) {
 // of 0x9E37 st are those of 55 st, so bits 2..9 of 220 st are bits 0..7 of
 // 0x9E37 st, and bits 2..9 of st >> 5 are bits 0..7 of st >> 7); a multiply
 // takes only the window's low 24 bits, and bits above the state land outside
-// the mask.  q = rint(v / d) comes from the fp32 sum 1.5 * 2^23 + v * (1 / d):
+// the mask.  q = rint(v * (1 / d)) comes from the fp32 sum 1.5 * 2^23 + v * (1 / d):
 // that sum has a unit ulp, so it rounds v * (1 / d) to the nearest integer
 // with ties to even, and its low byte is q in two's complement.  No clamp:
 // |v| <= amax, so |v * (1 / d)| <= 127 (1 + 3 ulp) and q stays in [-127, 127].
@@ -136,7 +136,8 @@ __global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, V16Table v1
       am = fmaxf(am, xlane<8>(am));
     }
     const float dd = am / 127.0f;
-    const float id = am == 0.0f ? 0.0f : 1.0f / dd;
+    const float r = 1.0f / dd;                          // +inf when d = 0 or d <= 2^-128:
+    const float id = r < __builtin_inff() ? r : 0.0f;   // then a zero block, as Q8 defines
     uint32_t pk[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {

@@ -19,7 +19,10 @@
  *   - Return value: 0 on success or a negative QERR_* code.  All argument checks
  *     run on the host before any HIP call, so a rejected call has no effect on
  *     the GPU.  QERR_HIP means a launch failed.  No exception crosses the ABI.
- *   - Calls are reentrant and keep no state between calls.
+ *   - Calls are reentrant and thread-safe.  The only state kept between calls
+ *     is built once and then only read: the trellis codebook tables and, per
+ *     device and kernel, the number of workgroups a persistent launch uses
+ *     (an occupancy query); both are filled under a lock.
  *   - Codes are dense row-major: weight row n is `row_bytes` bytes at
  *     codes + n*row_bytes.  Scales are fp16 bit patterns in the tiled order
  *     described at qfmt_scales_bytes (convert with qweight_set_scales /
@@ -152,8 +155,10 @@ int qweight_pack(int32_t fmt, const int8_t* levels, int32_t rows, int32_t cols,
 
 /* ---- activation quantization (device) --------------------------------------------- */
 
-/* Q8 per block of `qblock` (32 or 256) values of x [B][K] fp32:
- *   amax = max|x|; d = amax / 127 (fp32, IEEE division); id = amax ? 1/d : 0;
+/* Q8 per block of `qblock` (32 or 256) values of x [B][K] fp32 (finite):
+ *   amax = max|x|; d = amax / 127 (fp32, IEEE division); r = 1/d (fp32);
+ *   id = r if r is finite, else 0 (a zero block, or d <= 2^-128 where the
+ *   reciprocal overflows: q = 0, qsum = 0, d kept);
  *   q = clamp(rint(x * id), -127, 127) (ties to even); qsum = sum q.
  * int8 activations are what the pages' int8 dot-product GEMV and int8 MMA /
  * GEMM paths consume ([P1] "把非标准格式塞进 llama.cpp，难在哪").
@@ -235,7 +240,10 @@ int qgemv_blockdots(const qweight_t* w, const int8_t* q, const uint32_t* planes,
  * Fusing many small single-token kernels was part of the 3x decode gain of the
  * pages' 1-bit kernel ([P5] §二).  Use: build a plan on the host, copy the
  * plan bytes to device memory, then run it as often as wanted.  The plan
- * stores the device pointers of every item; it stays valid while they do. */
+ * stores the device pointers of every item (codes, scales, seeds, q, planes,
+ * d, qsum, y): the caller keeps all of them allocated, at the same addresses,
+ * for as long as it may run the plan; running a plan whose buffers were freed
+ * reads and writes freed memory. */
 typedef struct qgemv_item {
   qweight_t w;
   const int8_t* q;          /* [B][w.cols] (device); may be NULL for INT2, SIGN1 */
@@ -264,10 +272,14 @@ int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* stream)
 
 /* ---- prefill: trellis decode to int8 and the int8 MFMA GEMM --------------------------- */
 
-/* Decode TRELLIS2 weights to int8 for the GEMM: per row the exact fp32 values
- * s * V16[h] (both fp16, so the product is exact), then Q8 per (row, oblock)
- * as in qact_quant_i8.  Output wq [rows][cols] int8, dw [rows][cols/oblock]
- * fp32 (device).  oblock 256 or 32. */
+/* Decode TRELLIS2 weights to int8 for the GEMM.  The codebook is computed at
+ * run time from the hash ([P1] "2.4bit 是个什么量级": trellis codes of 2 to 3
+ * bits per weight, codebook hashed on the fly), and the pages' prefill runs as
+ * an INT8 GEMM ([P1] "把非标准格式塞进 llama.cpp，难在哪"), so the exact fp32
+ * values s * V16[h] of each row (both fp16, so the product is exact) are
+ * re-quantized by Q8 per (row, oblock) as in qact_quant_i8.  Output wq
+ * [rows][cols] int8, dw [rows][cols/oblock] fp32 (device).  oblock 256 or 32;
+ * cols a multiple of 256. */
 int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw, void* stream);
 
 /* Unpack TERN_B3 / INT2 / SIGN1 / INT4 weights to int8 levels for the GEMM:

@@ -235,3 +235,37 @@ def test_grouped_plan_on_host(ebq):
         assert max(loads) - min(loads) <= max(fcosts)
     # too small a buffer is refused
     assert ebq.load().qgemv_grouped_plan(items, 4, 2, host.data_ptr(), nb - 16) == -6
+
+
+def test_grouped_plan_keeps_its_tensors(ebq):
+    """The plan stores raw device addresses, so the Python plan object holds every
+    tensor of every entry (and the PackedWeights) for its own lifetime: dropping
+    the caller's references frees nothing.  Host tensors stand in for device ones
+    (building a plan is host work; nothing runs)."""
+    import gc
+    import weakref
+
+    import torch
+
+    def aligned(n):
+        """n zero bytes on the host, 64-byte aligned."""
+        raw = torch.zeros(n + 64, dtype=torch.uint8)
+        off = (-raw.data_ptr()) % 64
+        return raw[off:off + n]
+
+    fmt, N, K = 3, 70, 1024
+    codes = aligned(N * ebq.qfmt_row_bytes(fmt, K)).view(N, -1)
+    scales = aligned(ebq.qfmt_scales_bytes(fmt, N, K)).view(torch.int16)
+    pw = ebq.PackedWeight(fmt, N, K, codes, scales)
+    planes = aligned(4 * 8 * K // 32).view(torch.int32)
+    d = aligned(4 * K // 32).view(torch.float32)
+    qs = aligned(4 * K // 32).view(torch.int32)
+    y = aligned(4 * N).view(torch.float32)
+    refs = [weakref.ref(t) for t in (codes, scales, planes, d, qs, y)] + [weakref.ref(pw)]
+    plan = ebq.GroupedPlan([(pw, None, planes, d, qs, y)], 1, device="cpu")
+    del codes, scales, pw, planes, d, qs, y
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    del plan
+    gc.collect()
+    assert all(r() is None for r in refs)

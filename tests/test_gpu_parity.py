@@ -1,6 +1,8 @@
 """GPU parity of every kernel against the CPU oracle, at sizes the oracle runs
 in seconds (several 64-row tiles, ragged row counts, K with and without a tail
 segment) and on edge cases.  All calls go through the C ABI."""
+import os
+
 import numpy as np
 import pytest
 
@@ -86,6 +88,54 @@ def test_act_quant_batch_bit_exact():
             assert (host(pl).view(np.uint32) == oracle.act_planes(rq)).all()
 
 
+def _tiny_rows(seed, B, K):
+    """Rows whose blocks have amax around the Q8 reciprocal-overflow boundary
+    (d <= 2^-128 gives a zero block) and subnormal values: per 32 values a
+    random binade from 2^-149 to 2^-100, plus the hand-worked blocks of
+    tests/golden/q8_tiny.txt at the start of row 0."""
+    rng = np.random.default_rng(synth.seed64(seed, B, K))
+    mant = rng.integers(1, 1 << 24, (B, K)).astype(np.float64)
+    e = np.repeat(rng.integers(-149, -99, (B, K // 32)), 32, axis=1)
+    x = (mant * 2.0 ** (e - 23) * rng.choice([-1.0, 1.0], (B, K))).astype(np.float32)
+    x[rng.random((B, K)) < 0.1] = 0.0
+    golden = os.path.join(os.path.dirname(__file__), "golden", "q8_tiny.txt")
+    blocks = {}
+    with open(golden) as f:
+        for line in f:
+            r = line.split()
+            if len(r) > 2 and not line.startswith("#") and r[1] == "x":
+                blocks[r[0]] = np.array([int(h, 16) for h in r[2:]], np.uint32).view(np.float32)
+    for i, v in enumerate(blocks.values()):
+        if 32 * (i + 1) <= K:
+            x[0, 32 * i:32 * (i + 1)] = 0.0
+            x[0, 32 * i:32 * i + len(v)] = v
+    return x
+
+
+@pytest.mark.parametrize("B,K,qblock", [(3, 1024, 32), (2, 5120, 256)])
+def test_act_quant_tiny_blocks_bit_exact(B, K, qblock):
+    """Q8 where 1/d overflows (zero blocks), where d is subnormal but 1/d is finite,
+    and on subnormal inputs: the per-launch kernel and the batched one."""
+    x = _tiny_rows(102, B, K)
+    q, d, s = gpu_act(x, qblock)
+    _sync()
+    rq, rd, rs = oracle.act_quant(x, qblock)
+    assert (host(q) == rq).all()
+    assert (host(d).view(np.uint32) == rd.view(np.uint32)).all()
+    assert (host(s) == rs).all()
+    if qblock == 32:
+        qb = torch.zeros((B, K), dtype=torch.int8, device="cuda")
+        pl = torch.zeros((B, K // 32, 8), dtype=torch.int32, device="cuda")
+        db = torch.zeros((B, K // 32), dtype=torch.float32, device="cuda")
+        sb = torch.zeros((B, K // 32), dtype=torch.int32, device="cuda")
+        ebq.qact_quant_batch([(dev(x), qb, pl, db, sb)])
+        _sync()
+        assert (host(qb) == rq).all()
+        assert (host(db).view(np.uint32) == rd.view(np.uint32)).all()
+        assert (host(sb) == rs).all()
+        assert (host(pl).view(np.uint32) == oracle.act_planes(rq)).all()
+
+
 def test_act_quant_empty_batch():
     x = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
     q = torch.zeros((0, 64), dtype=torch.int8, device="cuda")
@@ -104,6 +154,30 @@ def test_hadamard_quant_bit_exact(B, K, qblock):
     ebq.qact_hadamard_quant_i8(xt, dev(sb), qblock, q, d, s)
     _sync()
     rq, rd, rs = oracle.hadamard_quant(x, sb, qblock)
+    assert (host(q) == rq).all()
+    assert (host(d).view(np.uint32) == rd.view(np.uint32)).all()
+    assert (host(s) == rs).all()
+
+
+@pytest.mark.parametrize("qblock", [256, 32])
+def test_hadamard_quant_tiny_bit_exact(qblock):
+    """Rotation + Q8 on rows scaled into the subnormal range: after the 1/16 the
+    rotated values are subnormal (rounded by that multiply) and the blocks' amax
+    straddles the 2^-128 reciprocal-overflow boundary of d."""
+    K = 1024
+    scales = [2.0 ** -e for e in (110, 114, 116, 117, 118, 119, 120, 121, 122, 124, 126, 130, 135, 140, 149)]
+    x = synth.with_outliers(synth.gauss([113], (len(scales), K)), [114])
+    x = (x.astype(np.float64) * np.array(scales)[:, None]).astype(np.float32)
+    sb = synth.sign_bits([115, K], K)
+    q = torch.empty((len(scales), K), dtype=torch.int8, device="cuda")
+    d = torch.empty((len(scales), K // qblock), dtype=torch.float32, device="cuda")
+    s = torch.empty((len(scales), K // qblock), dtype=torch.int32, device="cuda")
+    ebq.qact_hadamard_quant_i8(dev(x), dev(sb), qblock, q, d, s)
+    _sync()
+    rq, rd, rs = oracle.hadamard_quant(x, sb, qblock)
+    nz = rq.reshape(len(scales), -1, qblock).any(-1)
+    assert ((rd > 0) & ~nz).any()                               # 1/d overflowed: zero blocks with d > 0
+    assert ((rd > 0) & (rd < 2.0 ** -126) & nz).any()           # subnormal d, quantized normally
     assert (host(q) == rq).all()
     assert (host(d).view(np.uint32) == rd.view(np.uint32)).all()
     assert (host(s) == rs).all()
@@ -211,6 +285,81 @@ def test_gemv_every_batch_size(B):
     rq, rd, _ = oracle.act_quant(x)
     yr, absT, _ = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd)
     assert_close_terms(host(y), yr, absT, what="B=%d" % B)
+
+
+@pytest.mark.parametrize("fmt,K", [(TERN, 1024), (TERN, 2048), (INT4, 256), (INT4, 512), (SIGN1, 1024),
+                                   (SIGN1, 2048), (INT2, 512), (INT2, 1024), (INT2, 2560), (TRELLIS, 512)])
+@pytest.mark.parametrize("B", [1, 2])
+def test_gemv_one_or_two_segment_rows(fmt, K, B):
+    """Rows of one or two whole segments, where the single-matrix launch has the
+    waves of a tile split a segment's sub-chunks between them (batch 1 and 2),
+    and the 2-bit scalar-operand pipeline at batch 2."""
+    N = 130
+    raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 165 + fmt + 3 * B, B)
+    q, pl, d, s = gpu_act_planes(x)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    ebq.qgemv(pw, q, pl, d, s, B, y)
+    _sync()
+    rq, rd, _ = oracle.act_quant(x)
+    yr, absT, _ = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd)
+    assert_close_terms(host(y), yr, absT, what="%s K=%d B=%d" % (NAMES[fmt], K, B))
+
+
+PARTIAL = [(INT2, 96), (INT2, 288), (INT4, 96), (INT4, 288), (SIGN1, 384), (TRELLIS, 320), (TERN, 768)]
+
+
+@pytest.mark.parametrize("fmt,K", PARTIAL)
+@pytest.mark.parametrize("B", [1, 2, 3])
+def test_gemv_partial_sub_chunk(fmt, K, B):
+    """K that ends inside a 256-weight sub-chunk (or a segment): the clamped
+    activation loads, the masked blocks past K and the bounded test-hook copy,
+    single matrix and grouped, and the block dots at batch 1."""
+    N = 70
+    raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 175 + fmt + 7 * B, B)
+    q, pl, d, s = gpu_act_planes(x)
+    rq, rd, _ = oracle.act_quant(x)
+    yr, absT, I = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd, want_I=True)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    ebq.qgemv(pw, q, pl, d, s, B, y)
+    yg = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    plan = ebq.GroupedPlan([(pw, q, pl, d, s, yg)], B)
+    plan.run()
+    _sync()
+    assert_close_terms(host(y), yr, absT, what="%s K=%d B=%d" % (NAMES[fmt], K, B))
+    assert_close_terms(host(yg), yr, absT, what="grouped %s K=%d B=%d" % (NAMES[fmt], K, B))
+    if B == 1:
+        o2 = torch.full((N, K // 32), -7, dtype=torch.int32, device="cuda")
+        ebq.qgemv_blockdots(pw, q[:1], pl[:1], s[:1], o2)
+        _sync()
+        assert (host(o2) == I[0]).all(), NAMES[fmt]
+
+
+def test_gemv_trellis_edge_cases():
+    """Trellis rows with all-0 and all-3 symbols, seeds 0 and 0xFFFF, a row with
+    zero scales, zero activations and every q = 127."""
+    N, K = 66, 1024
+    codes = synth.symbols([184], (N, K), 4)
+    codes[0] = 0
+    codes[1] = 3
+    seeds = synth.u16([185], N)
+    seeds[0] = 0
+    seeds[1] = 0xFFFF
+    scales = synth.uniform_f16([186], (N, K // 64), 0.01, 0.03)
+    scales[5] = 0
+    raw = {"codes": codes, "scales": scales, "seeds": seeds}
+    pw = gpu_weight(TRELLIS, raw, N, K)
+    rp, rs, rseeds = oracle_weight(TRELLIS, raw)
+    x = synth.gauss([187], (3, K))
+    x[1] = 0.0
+    x[2, :] = 127.0
+    q, pl, d, s = gpu_act_planes(x)
+    y = torch.empty((3, N), dtype=torch.float32, device="cuda")
+    ebq.qgemv(pw, q, pl, d, s, 3, y)
+    _sync()
+    rq, rd, _ = oracle.act_quant(x)
+    yr, absT, _ = oracle.gemv(TRELLIS, rp, rs, rseeds, K, rq, rd)
+    assert_close_terms(host(y), yr, absT, what="trellis edge")
+    assert not host(y)[1].any() and not host(y)[:, 5].any()
 
 
 def test_gemv_deterministic():
@@ -378,6 +527,29 @@ def test_trellis_decode_bit_exact(oblock, N, K):
     _sync()
     rp, rs, rseeds = oracle_weight(TRELLIS, raw)
     rwq, rdw = oracle.trellis_decode_i8(rp, rseeds, rs, K, oblock)
+    assert (host(wq) == rwq).all()
+    assert (host(dw).view(np.uint32) == rdw.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("oblock", [256, 32])
+def test_trellis_decode_zero_and_tiny_scales(oblock):
+    """Rows whose scales are zero (zero blocks: d = 0, q = 0) or the smallest
+    fp16 subnormal 2^-24, and seeds 0 and 0xFFFF."""
+    N, K = 6, 1024
+    raw = raw_weight(TRELLIS, N, K, 202)
+    raw["scales"][0] = 0
+    raw["scales"][1] = 1                                   # fp16 2^-24
+    raw["scales"][2, ::2] = 0
+    raw["seeds"][3] = 0
+    raw["seeds"][4] = 0xFFFF
+    pw = gpu_weight(TRELLIS, raw, N, K)
+    wq = torch.full((N, K), 77, dtype=torch.int8, device="cuda")
+    dw = torch.full((N, K // oblock), -1.0, dtype=torch.float32, device="cuda")
+    ebq.qtrellis_decode_i8(pw, oblock, wq, dw)
+    _sync()
+    rp, rs, rseeds = oracle_weight(TRELLIS, raw)
+    rwq, rdw = oracle.trellis_decode_i8(rp, rseeds, rs, K, oblock)
+    assert not rwq[0].any() and (rdw[0] == 0).all()
     assert (host(wq) == rwq).all()
     assert (host(dw).view(np.uint32) == rdw.view(np.uint32)).all()
 
