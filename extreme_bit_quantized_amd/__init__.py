@@ -19,7 +19,8 @@ QFMT_TERN_B3, QFMT_INT2, QFMT_SIGN1, QFMT_INT4, QFMT_TRELLIS2 = 1, 2, 3, 4, 5
 FORMAT_NAMES = {QFMT_TERN_B3: "tern_b3", QFMT_INT2: "int2", QFMT_SIGN1: "sign1", QFMT_INT4: "int4",
                 QFMT_TRELLIS2: "trellis2"}
 QERR = {0: "QERR_OK", -1: "QERR_INVALID_ARG", -2: "QERR_UNSUPPORTED_FMT", -3: "QERR_SHAPE",
-        -4: "QERR_ALIGNMENT", -5: "QERR_HIP", -6: "QERR_BUFFER"}
+        -4: "QERR_ALIGNMENT", -5: "QERR_HIP", -6: "QERR_BUFFER", -7: "QERR_TOO_LARGE"}
+QGEMV_STATIC_PLAN_BYTES = 1 << 20
 
 
 class QError(RuntimeError):
@@ -81,6 +82,7 @@ def load(path: str = LIB_PATH):
         "qgemv_grouped_plan_bytes": (i64, [ctypes.POINTER(qgemv_item_t), i32, i32]),
         "qgemv_grouped_plan": (ctypes.c_int, [ctypes.POINTER(qgemv_item_t), i32, i32, P, i64]),
         "qgemv_grouped_run": (ctypes.c_int, [P, P, P]),
+        "qgemv_grouped_run_static": (ctypes.c_int, [P, P]),
         "qtrellis_decode_i8": (ctypes.c_int, [W, i32, P, P, P]),
         "qweight_unpack_i8": (ctypes.c_int, [W, P, P, P]),
         "qgemm_i8": (ctypes.c_int, [P, P, i32, P, P, i32, i32, i32, P, P]),
@@ -259,6 +261,11 @@ def qgemv_grouped_run(host_plan, dev_plan, stream=None):
     _check(load().qgemv_grouped_run(_ptr(host_plan), _ptr(dev_plan), _stream(stream)), "qgemv_grouped_run")
 
 
+def qgemv_grouped_run_static(host_plan, stream=None):
+    """Run a host plan from the library's static device plan storage (no allocation)."""
+    _check(load().qgemv_grouped_run_static(_ptr(host_plan), _stream(stream)), "qgemv_grouped_run_static")
+
+
 class GroupedPlan:
     """A plan built on the host and copied to the device.
 
@@ -284,6 +291,10 @@ class GroupedPlan:
     def run(self, stream=None):
         qgemv_grouped_run(self.host, self.dev, stream)
 
+    def run_static(self, stream=None):
+        """The same launch from the library's static plan storage (allocates nothing)."""
+        qgemv_grouped_run_static(self.host, stream)
+
 
 def qtrellis_decode_i8(w: PackedWeight, oblock: int, wq, dw, stream=None):
     _check(load().qtrellis_decode_i8(ctypes.byref(w.desc), oblock, _ptr(wq), _ptr(dw), _stream(stream)),
@@ -305,3 +316,4 @@ def qgemm_i8(xq, dx, wq, dw, kblock: int, y, stream=None):
 def qcalib_mfma_i8(blocks: int, iters: int, clocks, sink, stream=None):
     """clocks: int64 tensor of 4 * blocks entries, sink: int32 tensor (both on the device)."""
     _check(load().qcalib_mfma_i8(blocks, iters, _ptr(clocks), _ptr(sink), _stream(stream)), "qcalib_mfma_i8")
+

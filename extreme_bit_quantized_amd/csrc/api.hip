@@ -97,6 +97,40 @@ int64_t count_tiles(const qgemv_item_t* items, int32_t n) {
   return t;
 }
 
+// Header of a plan built by qgemv_grouped_plan, or QERR_BUFFER.
+int read_plan_header(const void* host_plan, PlanHeader* h) {
+  std::memcpy(h, host_plan, sizeof(*h));
+  if (h->magic != kPlanMagic || h->version != kPlanVersion || h->B < 1 || h->B > 8 || h->n_items < 1 ||
+      h->n_tiles < 0 || h->n_workers != kPlanWorkers || h->total_bytes < (int64_t)sizeof(PlanHeader))
+    return QERR_BUFFER;
+  return QERR_OK;
+}
+
+// Plan storage of qgemv_grouped_run_static: a fixed device array, so that call
+// allocates nothing.  In host code `scratch` names a host-side stand-in, not a
+// device address; the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is used.
+constexpr int64_t kStaticPlanBytes = QGEMV_STATIC_PLAN_BYTES;
+__device__ __align__(256) uint8_t scratch[kStaticPlanBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (QERR_HIP if it cannot be had).
+int static_plan_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QERR_OK;
+}
+
 }  // namespace
 
 namespace qk {
@@ -129,6 +163,7 @@ const char* qstrerror(int err) {
     case QERR_ALIGNMENT: return "pointer or stride misaligned";
     case QERR_HIP: return "HIP launch or query failed";
     case QERR_BUFFER: return "caller buffer too small or corrupt";
+    case QERR_TOO_LARGE: return "plan larger than the library's static plan storage (QGEMV_STATIC_PLAN_BYTES)";
   }
   return "unknown error";
 }
@@ -366,12 +401,25 @@ int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* stream)
   if (!host_plan || !dev_plan) return QERR_INVALID_ARG;
   if (!aligned(host_plan, 16) || !aligned(dev_plan, 16)) return QERR_ALIGNMENT;
   PlanHeader h;
-  std::memcpy(&h, host_plan, sizeof(h));
-  if (h.magic != kPlanMagic || h.version != kPlanVersion || h.B < 1 || h.B > 8 || h.n_items < 1 || h.n_tiles < 0 ||
-      h.n_workers != kPlanWorkers)
-    return QERR_BUFFER;
+  if (read_plan_header(host_plan, &h)) return QERR_BUFFER;
   if (h.n_tiles == 0) return QERR_OK;
   return hip_rc(kGrouped[h.B](h, dev_plan, S(stream)));
+}
+
+int qgemv_grouped_run_static(const void* host_plan, void* stream) {
+  if (!host_plan) return QERR_INVALID_ARG;
+  if (!aligned(host_plan, 16)) return QERR_ALIGNMENT;
+  PlanHeader h;
+  if (read_plan_header(host_plan, &h)) return QERR_BUFFER;
+  if (h.total_bytes > kStaticPlanBytes) return QERR_TOO_LARGE;
+  if (h.n_tiles == 0) return QERR_OK;
+  void* dev_plan = nullptr;
+  const int rc = static_plan_address(&dev_plan);
+  if (rc) return rc;
+  const hipStream_t st = S(stream);
+  if (hipMemcpyAsync(dev_plan, host_plan, (size_t)h.total_bytes, hipMemcpyHostToDevice, st) != hipSuccess)
+    return QERR_HIP;
+  return hip_rc(kGrouped[h.B](h, dev_plan, st));
 }
 
 int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw, void* stream) {

@@ -46,6 +46,7 @@ extern "C" {
 #define QERR_ALIGNMENT (-4)       /* pointer or stride misaligned */
 #define QERR_HIP (-5)             /* a HIP launch or query failed */
 #define QERR_BUFFER (-6)          /* caller buffer too small, or not a plan */
+#define QERR_TOO_LARGE (-7)       /* exceeds a fixed limit of the library (static plan storage) */
 
 /* Human-readable text for a QERR_* code (static storage, never NULL). */
 const char* qstrerror(int err);
@@ -269,6 +270,23 @@ int qgemv_grouped_plan(const qgemv_item_t* items, int32_t n, int32_t B,
  * it: runs are deterministic (bit-identical) and independent of one another.
  * QERR_BUFFER if host_plan is not a plan (of this library's version). */
 int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* stream);
+
+/* Run a plan from the library's own static plan storage, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same results as qgemv_grouped_run
+ * with a device copy of the plan, bit for bit: the call copies host_plan (a
+ * plan written by qgemv_grouped_plan) into a fixed device array of
+ * QGEMV_STATIC_PLAN_BYTES bytes with hipMemcpyAsync on `stream`, then launches.
+ * It calls no hipMalloc, hipFree or other allocating routine.  host_plan is
+ * read by the stream at this call: keep it unchanged until the stream has
+ * passed the call.  Each GPU holds one such array for the life of the process,
+ * shared by every call on that GPU and holding the last call's plan; calls
+ * that overlap on one GPU (other streams or threads) race on it and must be
+ * ordered by the caller.  QERR_TOO_LARGE (before any HIP call) for a plan of
+ * more than QGEMV_STATIC_PLAN_BYTES bytes (qgemv_grouped_plan_bytes gives the
+ * size; the 448-matrix 64-layer 27B-shaped stack needs about 0.45 MiB). */
+#define QGEMV_STATIC_PLAN_BYTES (1 << 20)
+int qgemv_grouped_run_static(const void* host_plan, void* stream);
 
 /* ---- prefill: trellis decode to int8 and the int8 MFMA GEMM --------------------------- */
 

@@ -269,3 +269,29 @@ def test_grouped_plan_keeps_its_tensors(ebq):
     del plan
     gc.collect()
     assert all(r() is None for r in refs)
+
+
+def test_static_plan_size_limit(ebq):
+    """qgemv_grouped_run_static refuses a plan larger than its static storage
+    before any HIP call (so this runs without a GPU)."""
+    import torch
+
+    A = 1 << 20
+    rows = 64 * 140000                     # 140000 tiles of 8 bytes: more than 1 MiB of plan
+    d = _desc(ebq, fmt=3, rows=rows, cols=1024, codes=A, scales=A)
+    items = (ebq.qgemv_item_t * 1)()
+    items[0] = ebq.qgemv_item_t(d, A, A, A, A, A)
+    nb = ebq.qgemv_grouped_plan_bytes(items, 1)
+    assert nb > ebq.QGEMV_STATIC_PLAN_BYTES
+    raw = torch.zeros(nb + 16, dtype=torch.uint8)
+    off = (-raw.data_ptr()) % 16
+    host = raw[off:off + nb]
+    ebq.qgemv_grouped_plan(items, 1, host)
+    L = ebq.load()
+    assert L.qgemv_grouped_run_static(host.data_ptr(), None) == -7
+    assert L.qgemv_grouped_run_static(None, None) == -1
+    assert L.qgemv_grouped_run_static(host.data_ptr() + 4, None) == -4
+    junk = torch.zeros(256, dtype=torch.uint8)
+    o2 = (-junk.data_ptr()) % 16
+    assert L.qgemv_grouped_run_static(junk[o2:].data_ptr(), None) == -6
+    assert "static plan" in L.qstrerror(-7).decode()
