@@ -12,8 +12,14 @@ all 448 matrices.  Inputs are resident in HBM before timing starts.
 
 The same line carries:
   roofline      the grouped GEMV kernel's algorithmic bytes per launch over its
-                HIP-event duration, against 8 TB/s
-  cpu_baseline  the CPU oracle timed on one layer of the same stack
+                HIP-event duration, against 8 TB/s and against the measured
+                streaming-read ceiling (a 4 GiB read, qcalib_hbm_read)
+  settle_*      after --warmup, headline steps run back to back for --settle
+                seconds before timing (the first launches after the stack is
+                built run slower while clocks settle); sclk_mhz is the shader
+                clock just before and just after the timed region
+  cpu_baseline  the CPU oracle timed on one layer of the same stack (OpenMP and
+                one thread), plus bounded samples of the other workloads
   extra         the other workloads: mixed 4-bit/ternary stack at batch 1 and 8,
                 one 2-bit layer (8 copies cycled), the 1024x1024 ternary GEMV,
                 prefill (rotation, trellis decode, int8 MFMA GEMM), and the same
@@ -183,6 +189,40 @@ def time_kernel(fn, reps, warmup):
     return sum(ts) / len(ts), ts[len(ts) // 2]
 
 
+def settle(fn, seconds):
+    """Run fn back to back for at least `seconds` of wall time (after the
+    --warmup steps): the first launches after the stack is built run slower
+    while the part's clocks and power settle, so the timed region starts from
+    a steady state.  Returns (calls, seconds)."""
+    import torch
+
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(20):
+            fn()
+        n += 20
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            return n, dt
+
+
+REFCLK_MHZ = 100.0  # rate of the constant-rate counter s_memrealtime on this part
+
+
+def sclk_probe(ebq):
+    """Shader clock right now: one small matrix-core calibration launch (one
+    workgroup, ~1 M cycles), its wave cycle counter over the constant-rate
+    counter (s_memtime / s_memrealtime) x 100 MHz."""
+    import torch
+
+    clocks = torch.zeros(4, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ebq.qcalib_mfma_i8(1, 2000, clocks, sink)
+    c = clocks.cpu().numpy().astype(np.float64)
+    return round(float((c[1] - c[0]) / max(c[3] - c[2], 1.0) * REFCLK_MHZ), 1)
+
+
 # ---------------------------------------------------------------------------------------
 # parity spot checks against the oracle (rows sampled from the large workloads)
 # ---------------------------------------------------------------------------------------
@@ -213,55 +253,157 @@ def sampled_parity(ebq, stack, layer_ids, rows_per_matrix=16, seed=0):
 
 
 # ---------------------------------------------------------------------------------------
-# CPU baseline: the oracle on one layer of the headline stack
+# CPU baseline: the oracle on bounded samples of every workload
 # ---------------------------------------------------------------------------------------
 
-def cpu_baseline(ebq, stack):
-    import torch
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
 
+    return platform.processor() or "unknown"
+
+
+def _timed(fn, min_s, max_reps=10 ** 6):
+    """Run fn until at least min_s seconds have passed; (reps, seconds, last result)."""
+    reps, t0, out = 0, time.perf_counter(), None
+    while True:
+        out = fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s or reps >= max_reps:
+            return reps, dt, out
+
+
+def _oracle_layer(kind, layer, B, shapes=synth.LAYER_SHAPES, x_seed=2000):
+    """Oracle inputs of one layer of a stack: packed weights and Q8 activations."""
     import oracle
 
-    threads = os.cpu_count() or 1
-    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    threads = int(os.environ["OMP_NUM_THREADS"])
-    layer = 0
+    prep = []
+    for mi, (name, N, K) in enumerate(shapes):
+        fmt = layer_fmt(kind, name)
+        w = synth.gauss_torch([seed_of(kind), layer, mi], (N, K), 1.0 if kind == "sign1" else 0.02).cpu().numpy()
+        codes, sc = oracle.quantize(fmt, w)
+        del w
+        packed = oracle.pack(fmt, codes)
+        del codes
+        rq, rd, _ = oracle.act_quant(synth.gauss([seed_of(kind), x_seed, K, B], (B, K)), 32)
+        prep.append((fmt, packed, sc, K, rq, rd))
+    return prep
+
+
+def _run_layer(prep):
+    import oracle
+
+    return [oracle.gemv(fmt, p, s, None, K, rq, rd) for fmt, p, s, K, rq, rd in prep]
+
+
+def cpu_other_configs():
+    """The oracle on the other workloads, each a bounded sample (OpenMP threads)."""
+    import oracle
+
+    out = {}
+    # ternary 1024 x 1024, batch 1: the whole GEMV
+    N = K = 1024
+    packed = oracle.pack(TERN, synth.trits([1], (N, K)))
+    sc = synth.uniform_f16([1, 1], (N, K // 256), 0.01, 0.1)
+    rq, rd, _ = oracle.act_quant(synth.gauss([1, 2], (1, K)), 32)
+    reps, dt, _ = _timed(lambda: oracle.gemv(TERN, packed, sc, None, K, rq, rd), 0.5)
+    out["ternary_1024x1024"] = {"gemv_us": round(dt / reps * 1e6, 1), "sample": "whole GEMV, %d runs" % reps}
+    # one 2-bit layer (q/k/v fused), batch 1
+    prep = _oracle_layer("int2", 0, 1, synth.LAYER_SHAPES_FUSED)
+    nbytes = sum(p.nbytes + s.nbytes for _, p, s, _, _, _ in prep)
+    reps, dt, _ = _timed(lambda: _run_layer(prep), 1.0)
+    out["int2_one_layer"] = {"gbs": round(nbytes * reps / dt / 1e9, 4), "layer_ms": round(dt / reps * 1e3, 2),
+                             "sample": "one whole layer (%d bytes), %d runs" % (nbytes, reps)}
+    del prep
+    # mixed stack: one layer at 1, 8 and 64 tokens, x64 for the stack
+    for B in (1, 8, 64):
+        prep = _oracle_layer("mixed", 0, B)
+        reps, dt, _ = _timed(lambda: _run_layer(prep), 0.5 if B < 64 else 0.1, max_reps=50)
+        per_layer = dt / reps
+        out["mixed_B%d" % B] = {"layer_ms": round(per_layer * 1e3, 2), "step_ms_64_layers": round(per_layer * 64e3, 1),
+                                "tok_s": round(B / (per_layer * 64), 4),
+                                "sample": "layer 0 (7 matrices), %d runs; 64-layer step = 64 x the layer" % reps}
+        del prep
+    # prefill, 5120 -> 17408: rotation + Q8 and the GEMM on 16 of the 2048 tokens,
+    # the trellis decode of the whole matrix
+    M, Ms, Kin, Nout = 2048, 16, 5120, 17408
+    xs = synth.with_outliers(synth.gauss([5, 7, Kin], (Ms, Kin)), [5, 8, Kin])
+    sb = synth.sign_bits([5, 99, Kin], Kin)
+    packed = oracle.pack(TRELLIS, synth.rng(5, 2, Kin).integers(0, 4, size=(Nout, Kin), dtype=np.int8))
+    sc = synth.uniform_f16([5, 3, Kin], (Nout, Kin // 64), 0.01, 0.03)
+    seeds = synth.u16([5, 4, Kin], Nout)
+    t0 = time.perf_counter()
+    xq, dx, _ = oracle.hadamard_quant(xs, sb, 256)
+    t_rot = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    wq, dw = oracle.trellis_decode_i8(packed, seeds, sc, Kin, 256)
+    t_dec = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.gemm_i8(xq, dx, wq, dw, 256)
+    t_gemm = time.perf_counter() - t0
+    scale = M / Ms
+    total = (t_rot + t_gemm) * scale + t_dec
+    out["prefill_5120x17408"] = {
+        "gemm_gops": round(2.0 * Ms * Nout * Kin / t_gemm / 1e9, 2),
+        "rotate_quant_ms_16_tokens": round(t_rot * 1e3, 2),
+        "trellis_decode_ms": round(t_dec * 1e3, 1),
+        "gemm_ms_16_tokens": round(t_gemm * 1e3, 1),
+        "tok_s_this_matrix": round(M / total, 2),
+        "sample": "rotation + Q8 and GEMM on %d of %d tokens (x%d stated), decode of the whole matrix" % (Ms, M, scale),
+    }
+    return out
+
+
+def cpu_baseline(ebq, stack):
+    """The oracle on layer 0 of the headline stack (OpenMP over rows, the thread
+    count it actually uses, then single-threaded), checked against the GPU's
+    layer-0 outputs, plus bounded samples of the other workloads."""
+    import oracle
+
+    threads = oracle.threads()
     prep = []
     for mi, (name, N, K) in enumerate(stack.shapes):
         fmt = layer_fmt(stack.kind, name)
-        w = synth.gauss_torch([seed_of(stack.kind), layer, mi], (N, K), 1.0 if stack.kind == "sign1" else 0.02)
+        w = synth.gauss_torch([seed_of(stack.kind), 0, mi], (N, K), 1.0 if stack.kind == "sign1" else 0.02)
         w = w.cpu().numpy()
         codes, sc = oracle.quantize(fmt, w)
         del w
         packed = oracle.pack(fmt, codes)
         del codes
-        x = stack.x[K][layer * stack.B:(layer + 1) * stack.B].cpu().numpy()
-        rq, rd, _ = oracle.act_quant(x, 32)
+        rq, rd, _ = oracle.act_quant(stack.x[K][0:stack.B].cpu().numpy(), 32)
         prep.append((fmt, packed, sc, K, rq, rd))
     nbytes = sum(p.nbytes + s.nbytes for _, p, s, _, _, _ in prep)
-    # the layer's GEMVs, repeated until about 10 s of CPU work have been timed
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        outs = [oracle.gemv(fmt, p, s, None, K, rq, rd) for fmt, p, s, K, rq, rd in prep]
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0:
-            break
-    # full-layer parity of the GPU result against the oracle
+    nw = sum(p.shape[0] * K for _, p, _, K, _, _ in prep)
+    reps, dt, outs = _timed(lambda: _run_layer(prep), 8.0)
+    oracle.set_threads(1)
+    reps1, dt1, _ = _timed(lambda: _run_layer(prep), 2.0)
+    oracle.set_threads(threads)
     ok = True
-    for (yr, absT, _), y in zip(outs, stack.y[layer]):
+    for (yr, absT, _), y in zip(outs, stack.y[0]):
         yg = y.cpu().numpy().astype(np.float64)
         ok &= bool((np.abs(yg - yr) <= 1e-4 * absT).all())
+    del prep
     return {
         "value": round(nbytes * reps / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": "layer 0 of the 1-bit stack (7 matrices, %d weights, %d bytes) at batch 1, its 7 GEMVs run %d "
-                  "times (OpenMP over rows): %.2f s" % (sum(p.shape[0] * K for _, p, _, K, _, _ in prep), nbytes,
-                                                       reps, dt),
+                  "times on %d OpenMP threads: %.2f s" % (nw, nbytes, reps, threads, dt),
         "equiv_tok_s": round(reps / (dt * stack.layers), 6),
+        "single_thread_gbs": round(nbytes * reps1 / dt1 / 1e9, 4),
+        "single_thread_sample": "the same layer, %d runs on 1 thread: %.2f s" % (reps1, dt1),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
         "layer_parity": "ok" if ok else "FAIL",
+        "other_workloads": cpu_other_configs(),
     }
 
 
@@ -269,16 +411,22 @@ def cpu_baseline(ebq, stack):
 # secondary workloads
 # ---------------------------------------------------------------------------------------
 
-def bench_stack_grouped(ebq, stack, steps, warmup):
+def bench_stack_grouped(ebq, stack, steps, warmup, settle_s=0.0):
     plan = ebq.GroupedPlan(stack.entries(), stack.B)
 
     def step():
         stack.quantize_acts(ebq)
         plan.run()
 
-    t, _ = time_region(step, steps, warmup)
+    for _ in range(warmup):
+        step()
+    pre = settle(step, settle_s) if settle_s > 0 else (0, 0.0)
+    clk0 = sclk_probe(ebq)
+    t, _ = time_region(step, steps, 0)
+    clk1 = sclk_probe(ebq)
     tk, tk_med = time_kernel(plan.run, max(steps, 5), 2)
-    return plan, t, tk, tk_med
+    return plan, t, tk, tk_med, {"settle_steps": pre[0], "settle_s": round(pre[1], 3),
+                                 "sclk_mhz_before": clk0, "sclk_mhz_after": clk1}
 
 
 def bench_dependent_chain(ebq, stack, reps):
@@ -296,8 +444,12 @@ def bench_dependent_chain(ebq, stack, reps):
             for e in ents:
                 ebq.qgemv(e[0], e[1], e[2], e[3], e[4], stack.B, e[5])
     torch.cuda.synchronize()
+    for l in range(stack.layers):                       # the replays must write these afresh
+        for y in stack.y[l]:
+            y.fill_(float("nan"))
     t, _ = time_region(g.replay, reps, 2)
-    return t
+    ok, worst = sampled_parity(ebq, stack, [0, stack.layers - 1], rows_per_matrix=8, seed=5)
+    return t, ok, worst
 
 
 def bench_prefill(ebq, reps):
@@ -317,13 +469,13 @@ def bench_prefill(ebq, reps):
         dx = torch.empty((M, Kin // 256), dtype=torch.float32, device="cuda")
         sx = torch.empty((M, Kin // 256), dtype=torch.int32, device="cuda")
         rng = synth.rng(5, 2, Kin)
-        codes = torch.from_numpy(rng.integers(0, 4, size=(Nout, Kin), dtype=np.int8)).cuda()
+        codes_h = rng.integers(0, 4, size=(Nout, Kin), dtype=np.int8)
+        scales_h = synth.uniform_f16([5, 3, Kin], (Nout, Kin // 64), 0.01, 0.03)
+        seeds_h = synth.u16([5, 4, Kin], Nout)
         pw = ebq.PackedWeight.empty(TRELLIS, Nout, Kin)
-        ebq.qweight_pack(TRELLIS, codes, pw)
-        del codes
-        ebq.qweight_set_scales(pw, torch.from_numpy(
-            synth.uniform_f16([5, 3, Kin], (Nout, Kin // 64), 0.01, 0.03).view(np.int16)).cuda())
-        pw.seeds.copy_(torch.from_numpy(synth.u16([5, 4, Kin], Nout).view(np.int16)).cuda())
+        ebq.qweight_pack(TRELLIS, torch.from_numpy(codes_h).cuda(), pw)
+        ebq.qweight_set_scales(pw, torch.from_numpy(scales_h.view(np.int16)).cuda())
+        pw.seeds.copy_(torch.from_numpy(seeds_h.view(np.int16)).cuda())
         wq = torch.empty((Nout, Kin), dtype=torch.int8, device="cuda")
         dw = torch.empty((Nout, Kin // 256), dtype=torch.float32, device="cuda")
         y = torch.empty((M, Nout), dtype=torch.float32, device="cuda")
@@ -331,6 +483,20 @@ def bench_prefill(ebq, reps):
         t_dec, _ = time_kernel(lambda: ebq.qtrellis_decode_i8(pw, 256, wq, dw), reps, 2)
         t_gemm, _ = time_kernel(lambda: ebq.qgemm_i8(xq, dx, wq, dw, 256, y), reps, 2)
         ops = 2.0 * M * Nout * Kin
+        # parity of the chain (rotation + Q8, trellis decode, GEMM) on sampled tokens
+        # and output columns: the oracle redoes every step from the same draws
+        import oracle
+
+        prng = np.random.default_rng(Kin)
+        rows = np.sort(np.concatenate([[0, M - 1], prng.choice(np.arange(1, M - 1), 6, replace=False)]))
+        cols = np.sort(np.concatenate([[0, Nout - 1], prng.choice(np.arange(1, Nout - 1), 62, replace=False)]))
+        xs = x[torch.from_numpy(rows).cuda()].cpu().numpy()
+        rxq, rdx, _ = oracle.hadamard_quant(xs, sb[Kin].cpu().numpy().view(np.uint32), 256)
+        rwq, rdw = oracle.trellis_decode_i8(oracle.pack(TRELLIS, codes_h[cols]), seeds_h[cols], scales_h[cols], Kin, 256)
+        yr, absT = oracle.gemm_i8(rxq, rdx, rwq, rdw, 256)
+        err = np.abs(y.cpu().numpy()[np.ix_(rows, cols)].astype(np.float64) - yr)
+        pok = bool((err <= 1e-4 * absT).all())
+        del codes_h
         out[tag] = {
             "gemm_us": round(t_gemm * 1e6, 2),
             "gemm_tops": round(ops / t_gemm / 1e12, 1),
@@ -340,6 +506,10 @@ def bench_prefill(ebq, reps):
             "trellis_decode_us": round(t_dec * 1e6, 2),
             "trellis_decode_gbs": round((pw.nbytes + Nout * Kin + Nout * (Kin // 256) * 4) / t_dec / 1e9, 1),
             "prefill_tok_s_this_matrix": round(M / (t_rot + t_dec + t_gemm), 1),
+            "parity": "ok" if pok else "FAIL",
+            "parity_sample": "%d tokens x %d output columns, rotation + Q8, decode and GEMM redone by the oracle"
+                             % (len(rows), len(cols)),
+            "worst_err_over_sum_abs_terms": float((err / np.maximum(absT, 1e-300)).max()),
         }
         del x, xq, wq, y
     return out
@@ -465,8 +635,7 @@ def bench_mfma_ceiling(ebq):
         "tops": round(tops, 1),
         "frac_of_published": round(tops / INT8_PEAK_TOPS, 4),
         "kernel_us": round(t * 1e6, 1),
-        "shader_clock_mhz": round(cycles / t / 1e6, 1),
-        "reference_counter_mhz": round(ref / t / 1e6, 2),
+        "shader_clock_mhz": round(cycles / ref * REFCLK_MHZ, 1),
         "cycles_per_mfma_per_simd": round(cycles / (2 * iters * 16), 2),
     }
 
@@ -492,7 +661,15 @@ def bench_small_ternary(ebq, reps):
 
     t, _ = time_region(step, reps, 10)
     tk, _ = time_kernel(lambda: ebq.qgemv(pw, q, None, d, s, 1, y), reps, 10)
-    return {"step_us": round(t * 1e6, 2), "gemv_us": round(tk * 1e6, 2)}
+    import oracle
+
+    xh = x.cpu().numpy()
+    rq, rd, _ = oracle.act_quant(xh, 32)
+    sc = synth.uniform_f16([1, 1], (N, K // 256), 0.01, 0.1)
+    yr, absT, _ = oracle.gemv(TERN, oracle.pack(TERN, trits.cpu().numpy()), sc, None, K, rq, rd)
+    ok = bool((np.abs(y.cpu().numpy().astype(np.float64) - yr) <= 1e-4 * absT).all())
+    return {"step_us": round(t * 1e6, 2), "gemv_us": round(tk * 1e6, 2), "parity": "ok" if ok else "FAIL",
+            "parity_sample": "all 1024 outputs against the oracle"}
 
 
 def copy_calibration():
@@ -509,17 +686,19 @@ def copy_calibration():
     del a, b
 
 
-def bench_copy_ceiling(reps):
-    """Device-to-device copy of 2 GiB: the achievable read+write HBM rate."""
+def bench_hbm_read_ceiling(ebq, reps=5, nbytes=1 << 32):
+    """Streaming read of 4 GiB (qcalib_hbm_read): the achievable HBM read rate,
+    the ceiling for the weight-streaming GEMV (which reads and barely writes)."""
     import torch
 
-    n = 1 << 31
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a.fill_(1)
-    t, _ = time_kernel(lambda: b.copy_(a), reps, 2)
-    del a, b
-    return round(2 * n / t / 1e9, 1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t, t_med = time_kernel(lambda: ebq.qcalib_hbm_read(a, sink), reps, 2)
+    del a
+    torch.cuda.empty_cache()
+    return {"gbs": round(nbytes / t / 1e9, 1), "bytes": nbytes, "avg_us": round(t * 1e6, 1),
+            "frac_of_8tbs": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 # ---------------------------------------------------------------------------------------
@@ -595,6 +774,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle", type=float, default=1.5,
+                    help="seconds of headline steps run after --warmup and before timing (clocks settle)")
     ap.add_argument("--quick", action="store_true", help="headline only (no secondary workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--prefill-only", action="store_true",
@@ -627,9 +808,11 @@ def main():
     # ---- headline: 1-bit 64-layer stack, batch 1 ----
     log("building the 1-bit 64-layer stack")
     stack = Stack(ebq, "sign1", synth.N_LAYERS, 1)
-    plan, t_step, t_kern, t_kern_med = bench_stack_grouped(ebq, stack, args.steps, args.warmup)
-    log("step %.1f us, grouped kernel %.1f us" % (t_step * 1e6, t_kern * 1e6))
+    plan, t_step, t_kern, t_kern_med, cond = bench_stack_grouped(ebq, stack, args.steps, args.warmup, args.settle)
+    log("step %.1f us, grouped kernel %.1f us, %s" % (t_step * 1e6, t_kern * 1e6, cond))
     ok, worst = sampled_parity(ebq, stack, [0, 31, 63])
+    ceiling = bench_hbm_read_ceiling(ebq)
+    log("streaming-read ceiling %.1f GB/s" % ceiling["gbs"])
     step_bytes = stack.step_bytes()
     gemv_bytes = stack.gemv_bytes()
     value = step_bytes / t_step / 1e9
@@ -655,7 +838,12 @@ def main():
             "step_bytes": step_bytes,
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "pct_of_read_ceiling": round(100 * value / ceiling["gbs"], 2),
+        "hbm_read_ceiling": ceiling,
         "equiv_tok_s": round(1.0 / t_step, 1),
+        "settle_steps": cond["settle_steps"],
+        "settle_s": cond["settle_s"],
+        "sclk_mhz": {"before_timed": cond["sclk_mhz_before"], "after_timed": cond["sclk_mhz_after"]},
         "parity": {"sampled_rows": "ok" if ok else "FAIL", "worst_err_over_sum_abs_terms": worst},
         "roofline": {
             "kernel": "qk::k_gemv_grouped<1, QFMT_SIGN1>",
@@ -664,6 +852,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac_of_read_ceiling": round(achieved / ceiling["gbs"], 4),
             "traffic": measured_traffic(),
             "bytes_per_launch": gemv_bytes,
             "avg_launch_us": round(t_kern * 1e6, 2),
@@ -675,10 +864,12 @@ def main():
         try:
             reps = min(30, max(5, args.steps // 2))
             extra["dependent_chain_hipgraph"] = {}
-            t_chain = bench_dependent_chain(ebq, stack, reps)
+            t_chain, okc, wc = bench_dependent_chain(ebq, stack, reps)
             extra["dependent_chain_hipgraph"] = {
                 "gemv_us": round(t_chain * 1e6, 1),
                 "gbs": round(gemv_bytes / t_chain / 1e9, 1),
+                "parity": "ok" if okc else "FAIL",
+                "worst_err_over_sum_abs_terms": wc,
             }
             log("chain done")
         except Exception as e:  # report, do not hide
@@ -695,7 +886,7 @@ def main():
         for B in (1, 8):
             log("mixed stack B=%d" % B)
             ms = Stack(ebq, "mixed", synth.N_LAYERS, B)
-            plan, t, tk, _ = bench_stack_grouped(ebq, ms, reps, 2)
+            plan, t, tk, _, _ = bench_stack_grouped(ebq, ms, reps, 2, 0.3)
             okm, wm = sampled_parity(ebq, ms, [0, 63], rows_per_matrix=8)
             extra["mixed_int4_attn_ternary_ffn_B%d" % B] = {
                 "step_us": round(t * 1e6, 1),
@@ -714,7 +905,7 @@ def main():
         torch.cuda.empty_cache()
         log("2-bit layer x8 copies")
         l2 = Stack(ebq, "int2", 8, 1, shapes=synth.LAYER_SHAPES_FUSED, copies_of=lambda l: l)
-        plan, t, tk, _ = bench_stack_grouped(ebq, l2, reps, 2)
+        plan, t, tk, _, _ = bench_stack_grouped(ebq, l2, reps, 2, 0.3)
         ok2, _ = sampled_parity(ebq, l2, [0], rows_per_matrix=8)
         extra["int2_one_layer_8_copies"] = {
             "step_us_8_layers": round(t * 1e6, 1),
@@ -734,7 +925,6 @@ def main():
         for v in pre.values():
             v["mfma_frac_of_measured"] = round(v["gemm_tops"] / ceiling["tops"], 4)
         extra["prefill_2048_tokens"] = pre
-        extra["hbm_copy_ceiling_gbs"] = bench_copy_ceiling(5)
         res["extra"] = extra
     elif extra:
         res["extra"] = extra

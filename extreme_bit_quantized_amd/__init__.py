@@ -87,6 +87,7 @@ def load(path: str = LIB_PATH):
         "qweight_unpack_i8": (ctypes.c_int, [W, P, P, P]),
         "qgemm_i8": (ctypes.c_int, [P, P, i32, P, P, i32, i32, i32, P, P]),
         "qcalib_mfma_i8": (ctypes.c_int, [i32, i32, P, P, P]),
+        "qcalib_hbm_read": (ctypes.c_int, [P, i64, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -317,3 +318,9 @@ def qcalib_mfma_i8(blocks: int, iters: int, clocks, sink, stream=None):
     """clocks: int64 tensor of 4 * blocks entries, sink: int32 tensor (both on the device)."""
     _check(load().qcalib_mfma_i8(blocks, iters, _ptr(clocks), _ptr(sink), _stream(stream)), "qcalib_mfma_i8")
 
+
+def qcalib_hbm_read(buf, sink, nbytes: int | None = None, stream=None):
+    """buf: any device tensor (its first nbytes bytes are read, all by default),
+    sink: an int32 device tensor."""
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check(load().qcalib_hbm_read(_ptr(buf), n, _ptr(sink), _stream(stream)), "qcalib_hbm_read")

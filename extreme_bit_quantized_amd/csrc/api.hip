@@ -465,4 +465,13 @@ int qcalib_mfma_i8(int32_t blocks, int32_t iters, uint64_t* clocks, int32_t* sin
   return hip_rc(launch_mfma_peak(blocks, iters, clocks, sink, S(stream)));
 }
 
+int qcalib_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0) return QERR_INVALID_ARG;
+  if (bytes == 0) return QERR_OK;
+  if (!buf || !sink) return QERR_INVALID_ARG;
+  if (bytes % 16 != 0) return QERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return QERR_ALIGNMENT;
+  return hip_rc(launch_hbm_read(buf, bytes, sink, S(stream)));
+}
+
 }  // extern "C"

@@ -329,6 +329,17 @@ int qgemm_i8(const int8_t* xq, const float* dx, int32_t M, const int8_t* wq, con
  * rate is blocks x 4 x iters x 16 x 65536 ops over the elapsed time. */
 int qcalib_mfma_i8(int32_t blocks, int32_t iters, uint64_t* clocks, int32_t* sink, void* stream);
 
+/* Calibration for the GEMV's roofline (not part of the method): one streaming
+ * read of buf [bytes] (device, 16-byte aligned, bytes a multiple of 16), every
+ * byte read once with non-temporal 16-byte loads, four workgroups per compute
+ * unit each reading one contiguous span, nothing written except sink (device
+ * uint32), which is written
+ * only in a case that practically never occurs, to keep the loads live.  Time
+ * the call with events on the stream: bytes over the elapsed time is the
+ * streaming-read rate this device sustains, the ceiling of a bandwidth-bound
+ * decode GEMV ([P3] §1.2: bandwidth is the main bottleneck). */
+int qcalib_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,8 @@ def _L():
             P = ctypes.c_void_p
             i32, i64, u32, u16, d = ctypes.c_int, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint16, ctypes.c_double
             sig = {
+                "qref_threads": (i32, []),
+                "qref_set_threads": (None, [i32]),
                 "qref_scale_block": (i32, [i32]),
                 "qref_packed_row_bytes": (i64, [i32, i32]),
                 "qref_row_stride": (i64, [i32, i32]),
@@ -91,6 +93,17 @@ def _p(a):
 def _c(a, dtype):
     a = np.ascontiguousarray(a, dtype=dtype)
     return a
+
+
+# -- threads (timing records only) ------------------------------------------------
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return _L().qref_threads()
+
+
+def set_threads(n: int) -> None:
+    _L().qref_set_threads(int(n))
 
 
 # -- geometry -----------------------------------------------------------------

@@ -10,6 +10,27 @@
 #include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the parallel loops below use (OpenMP), for timing records. */
+int qref_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Set the thread count of the parallel loops (n >= 1). */
+void qref_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
 
 /* ------------------------------------------------------------------------ */
 /* Format geometry                                                           */

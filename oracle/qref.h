@@ -44,6 +44,10 @@ enum {
   QREF_TRELLIS2 = 5   /* 2-bit bit-shift trellis codes, scale per 64 */
 };
 
+/* OpenMP threads of the parallel loops (timing only; results do not depend on it). */
+int qref_threads(void);
+void qref_set_threads(int n);
+
 /* Scale block along K for a format (0 for an unknown format). */
 int qref_scale_block(int fmt);
 /* Packed bytes of one row of K weights, without padding (<0 on bad K). */

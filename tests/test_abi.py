@@ -182,6 +182,11 @@ def test_call_validation_without_gpu(ebq):
     assert L.qcalib_mfma_i8(2, 10, None, A, None) == -1
     assert L.qcalib_mfma_i8(2, 10, A + 4, A, None) == -4
     assert ebq.load().qstrerror(-4).decode().startswith("pointer")
+    assert L.qcalib_hbm_read(A, -16, A, None) == -1
+    assert L.qcalib_hbm_read(A, 0, A, None) == 0
+    assert L.qcalib_hbm_read(None, 16, A, None) == -1
+    assert L.qcalib_hbm_read(A, 24, A, None) == -3
+    assert L.qcalib_hbm_read(A + 8, 16, A, None) == -4
 
 
 def test_grouped_plan_on_host(ebq):
