@@ -22,7 +22,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemv.so")
 ARCH = "gfx950"
-MAX_B = 8
+MAX_B = 8          # DPP GEMV batch sizes (one object each)
+MAX_TG = 4         # matrix-core GEMV token groups of 16 (batches up to 64)
 
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC",
@@ -50,6 +51,9 @@ def _units():
         if name == "gemv_inst.hip":
             for b in range(1, MAX_B + 1):
                 units.append((src, os.path.join(BUILD, "gemv_b%d.o" % b), ["-DQGEMV_NB=%d" % b]))
+        elif name == "gemv_mfma_inst.hip":
+            for t in range(1, MAX_TG + 1):
+                units.append((src, os.path.join(BUILD, "gemv_mfma_tg%d.o" % t), ["-DQGEMV_TG=%d" % t]))
         else:
             units.append((src, os.path.join(BUILD, name[:-4] + ".o"), []))
     return units

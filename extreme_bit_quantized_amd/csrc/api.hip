@@ -88,6 +88,21 @@ const GemvLaunch kGemv[9] = {nullptr, launch_gemv_b1, launch_gemv_b2, launch_gem
 const GroupedLaunch kGrouped[9] = {nullptr, launch_grouped_b1, launch_grouped_b2, launch_grouped_b3,
                                    launch_grouped_b4, launch_grouped_b5, launch_grouped_b6, launch_grouped_b7,
                                    launch_grouped_b8};
+// Batches above kMaxDppBatch run on the matrix cores in groups of 16 tokens.
+constexpr int kMaxDppBatch = 8;
+constexpr int kMaxBatch = 64;
+using MfmaLaunch = hipError_t (*)(const GemvItem&, int, hipStream_t);
+const MfmaLaunch kGemvMfma[5] = {nullptr, launch_gemv_mfma_tg1, launch_gemv_mfma_tg2, launch_gemv_mfma_tg3,
+                                 launch_gemv_mfma_tg4};
+const GroupedLaunch kGroupedMfma[5] = {nullptr, launch_grouped_mfma_tg1, launch_grouped_mfma_tg2,
+                                       launch_grouped_mfma_tg3, launch_grouped_mfma_tg4};
+
+hipError_t launch_gemv_any(const GemvItem& it, int B, hipStream_t s) {
+  return B <= kMaxDppBatch ? kGemv[B](it, s) : kGemvMfma[(B + 15) / 16](it, B, s);
+}
+hipError_t launch_grouped_any(const PlanHeader& h, const void* plan, hipStream_t s) {
+  return h.B <= kMaxDppBatch ? kGrouped[h.B](h, plan, s) : kGroupedMfma[(h.B + 15) / 16](h, plan, s);
+}
 
 int64_t align16(int64_t x) { return (x + 15) / 16 * 16; }
 
@@ -100,7 +115,7 @@ int64_t count_tiles(const qgemv_item_t* items, int32_t n) {
 // Header of a plan built by qgemv_grouped_plan, or QERR_BUFFER.
 int read_plan_header(const void* host_plan, PlanHeader* h) {
   std::memcpy(h, host_plan, sizeof(*h));
-  if (h->magic != kPlanMagic || h->version != kPlanVersion || h->B < 1 || h->B > 8 || h->n_items < 1 ||
+  if (h->magic != kPlanMagic || h->version != kPlanVersion || h->B < 1 || h->B > kMaxBatch || h->n_items < 1 ||
       h->n_tiles < 0 || h->n_workers != kPlanWorkers || h->total_bytes < (int64_t)sizeof(PlanHeader))
     return QERR_BUFFER;
   return QERR_OK;
@@ -293,13 +308,13 @@ int qgemv(const qweight_t* w, const int8_t* q, const uint32_t* planes, const flo
           int32_t B, float* y, void* stream) {
   int rc = check_weight(w);
   if (rc) return rc;
-  if (B < 0 || B > 8) return QERR_INVALID_ARG;
+  if (B < 0 || B > kMaxBatch) return QERR_INVALID_ARG;
   if (B == 0 || w->rows == 0) return QERR_OK;
   rc = check_act(w->fmt, q, planes, d, qsum);
   if (rc) return rc;
   if (!y) return QERR_INVALID_ARG;
   if (!aligned(y, 4)) return QERR_ALIGNMENT;
-  return hip_rc(kGemv[B](make_item(w, q, planes, d, qsum, y), S(stream)));
+  return hip_rc(launch_gemv_any(make_item(w, q, planes, d, qsum, y), B, S(stream)));
 }
 
 int qgemv_blockdots(const qweight_t* w, const int8_t* q, const uint32_t* planes, const int32_t* qsum, int32_t* out,
@@ -316,7 +331,7 @@ int qgemv_blockdots(const qweight_t* w, const int8_t* q, const uint32_t* planes,
 }
 
 int64_t qgemv_grouped_plan_bytes(const qgemv_item_t* items, int32_t n, int32_t B) {
-  if (!items || n <= 0 || B < 1 || B > 8) return QERR_INVALID_ARG;
+  if (!items || n <= 0 || B < 1 || B > kMaxBatch) return QERR_INVALID_ARG;
   for (int32_t i = 0; i < n; ++i) {
     const int rc = check_item(items[i], B);
     if (rc) return rc;
@@ -403,7 +418,7 @@ int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* stream)
   PlanHeader h;
   if (read_plan_header(host_plan, &h)) return QERR_BUFFER;
   if (h.n_tiles == 0) return QERR_OK;
-  return hip_rc(kGrouped[h.B](h, dev_plan, S(stream)));
+  return hip_rc(launch_grouped_any(h, dev_plan, S(stream)));
 }
 
 int qgemv_grouped_run_static(const void* host_plan, void* stream) {
@@ -419,7 +434,7 @@ int qgemv_grouped_run_static(const void* host_plan, void* stream) {
   const hipStream_t st = S(stream);
   if (hipMemcpyAsync(dev_plan, host_plan, (size_t)h.total_bytes, hipMemcpyHostToDevice, st) != hipSuccess)
     return QERR_HIP;
-  return hip_rc(kGrouped[h.B](h, dev_plan, st));
+  return hip_rc(launch_grouped_any(h, dev_plan, st));
 }
 
 int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw, void* stream) {

@@ -200,6 +200,15 @@ QK_DECL_NB(6)
 QK_DECL_NB(7)
 QK_DECL_NB(8)
 #undef QK_DECL_NB
+// Matrix-core GEMV for batches of 16 TG - 15 .. 16 TG tokens (TG = 1..4).
+#define QK_DECL_TG(n)                                                                  \
+  hipError_t launch_gemv_mfma_tg##n(const GemvItem& it, int B, hipStream_t s);          \
+  hipError_t launch_grouped_mfma_tg##n(const PlanHeader& h, const void* plan, hipStream_t s);
+QK_DECL_TG(1)
+QK_DECL_TG(2)
+QK_DECL_TG(3)
+QK_DECL_TG(4)
+#undef QK_DECL_TG
 hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, float* dw, hipStream_t s);
 hipError_t launch_mfma_peak(int blocks, int iters, uint64_t* clocks, int32_t* sink, hipStream_t s);
 hipError_t launch_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);

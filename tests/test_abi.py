@@ -131,7 +131,8 @@ def test_call_validation_without_gpu(ebq):
     d = _desc(ebq)
     w = ctypes.byref(d)
     A = 1 << 20  # fake, aligned "device" addresses: every call below is rejected before launch
-    assert L.qgemv(w, A, A, A, A, 9, A, None) == -1
+    assert L.qgemv(w, A, A, A, A, 65, A, None) == -1
+    assert L.qgemv(w, A, A, A, A, -1, A, None) == -1
     assert L.qgemv(w, A, A, A, A, 0, A, None) == 0         # empty batch: no-op
     # 1-bit reads the activation planes (32-byte aligned); q is not needed
     assert L.qgemv(w, A, A + 16, A, A, 1, A, None) == -4
@@ -240,6 +241,10 @@ def test_grouped_plan_on_host(ebq):
         assert max(loads) - min(loads) <= max(fcosts)
     # too small a buffer is refused
     assert ebq.load().qgemv_grouped_plan(items, 4, 2, host.data_ptr(), nb - 16) == -6
+    # batches up to 64 (above 8 the launch runs on the matrix cores)
+    assert ebq.load().qgemv_grouped_plan_bytes(items, 4, 64) > 0
+    assert ebq.load().qgemv_grouped_plan_bytes(items, 4, 65) == -1
+    assert ebq.load().qgemv_grouped_plan_bytes(items, 4, 0) == -1
 
 
 def test_grouped_plan_keeps_its_tensors(ebq):

@@ -362,6 +362,121 @@ def test_gemv_trellis_edge_cases():
     assert not host(y)[1].any() and not host(y)[:, 5].any()
 
 
+# ---- 9 to 64 tokens: the matrix-core GEMV ------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("B", [9, 16, 33, 64])
+def test_gemv_mfma_parity(fmt, N, K, B):
+    """Batches above 8 run on the matrix cores (qgemv, single matrix, four waves
+    splitting K): every format and shape at 9, 16, 33 and 64 tokens."""
+    raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 700 + fmt + B, B)
+    q, pl, d, s = gpu_act_planes(x)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    ebq.qgemv(pw, q, pl, d, s, B, y)
+    _sync()
+    rq, rd, _ = oracle.act_quant(x)
+    yr, absT, _ = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd)
+    assert_close_terms(host(y), yr, absT, what="%s N=%d K=%d B=%d" % (NAMES[fmt], N, K, B))
+
+
+@pytest.mark.parametrize("B", [9, 10, 11, 12, 13, 14, 15, 16, 17, 31, 32, 47, 48, 49, 63, 64])
+def test_gemv_mfma_every_token_count(B):
+    """Every token count a 16-token group can end on, all five formats in one
+    grouped plan (run twice) and as single-matrix launches."""
+    specs = [(SIGN1, 200, 2048), (TERN, 130, 1280), (INT4, 70, 1024), (INT2, 90, 2560), (TRELLIS, 65, 1536)]
+    entries, refs, singles = [], [], []
+    for i, (fmt, N, K) in enumerate(specs):
+        raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 720 + 10 * B + i, B)
+        q, pl, d, s = gpu_act_planes(x)
+        y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+        ys = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+        ebq.qgemv(pw, q, pl, d, s, B, ys)
+        singles.append(ys)
+        entries.append((pw, q, pl, d, s, y))
+        rq, rd, _ = oracle.act_quant(x)
+        refs.append(oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd))
+    plan = ebq.GroupedPlan(entries, B)
+    for rep in range(2):
+        for e in entries:
+            e[5].fill_(float("nan"))
+        plan.run()
+        _sync()
+        for (fmt, N, K), e, ys, (yr, absT, _) in zip(specs, entries, singles, refs):
+            assert_close_terms(host(e[5]), yr, absT, what="grouped %s B=%d rep %d" % (NAMES[fmt], B, rep))
+            assert_close_terms(host(ys), yr, absT, what="single %s B=%d" % (NAMES[fmt], B))
+
+
+@pytest.mark.parametrize("fmt,K", PARTIAL)
+def test_gemv_mfma_partial_sub_chunk(fmt, K):
+    """K ending inside a 256-weight sub-chunk on the matrix-core path (blocks past
+    K are skipped), single and grouped, 20 tokens."""
+    B, N = 20, 70
+    raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 760 + fmt, B)
+    q, pl, d, s = gpu_act_planes(x)
+    rq, rd, _ = oracle.act_quant(x)
+    yr, absT, _ = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    ebq.qgemv(pw, q, pl, d, s, B, y)
+    yg = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    plan = ebq.GroupedPlan([(pw, q, pl, d, s, yg)], B)
+    plan.run()
+    _sync()
+    assert_close_terms(host(y), yr, absT, what="%s K=%d" % (NAMES[fmt], K))
+    assert_close_terms(host(yg), yr, absT, what="grouped %s K=%d" % (NAMES[fmt], K))
+
+
+@pytest.mark.parametrize("fmt", [TERN, INT2, SIGN1, INT4, TRELLIS])
+def test_gemv_mfma_edge_cases(fmt):
+    """All-max / all-min codes, a row of zero scales, zero activations for one
+    token, every q = 127 for another, at 24 tokens; exact zeros where every term
+    is zero."""
+    N, K, B = 66, 1024, 24
+    if fmt == TRELLIS:
+        codes = synth.symbols([770], (N, K), 4)
+        codes[0] = 0
+        codes[1] = 3
+        seeds = synth.u16([771], N)
+        seeds[0], seeds[1] = 0, 0xFFFF
+        scales = synth.uniform_f16([772], (N, K // 64), 0.01, 0.03)
+        raw = {"codes": codes, "scales": scales, "seeds": seeds}
+    else:
+        lo, hi = {TERN: (-1, 1), INT2: (0, 3), SIGN1: (0, 1), INT4: (0, 15)}[fmt]
+        codes = np.zeros((N, K), np.int8)
+        codes[0::3] = hi
+        codes[1::3] = lo
+        codes[2::3] = synth.symbols([773, fmt], (N // 3, K), hi - lo + 1) + lo
+        scales = synth.uniform_f16([774, fmt], (N, K // oracle.scale_block(fmt)), 0.01, 0.1)
+        raw = {"codes": codes, "scales": scales}
+    raw["scales"][5] = 0
+    pw = gpu_weight(fmt, raw, N, K)
+    rp, rs, rseeds = oracle_weight(fmt, raw)
+    x = synth.gauss([775, fmt], (B, K))
+    x[1] = 0.0
+    x[2, :] = 127.0
+    x[23, :] = -127.0
+    q, pl, d, s = gpu_act_planes(x)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    ebq.qgemv(pw, q, pl, d, s, B, y)
+    _sync()
+    rq, rd, _ = oracle.act_quant(x)
+    yr, absT, _ = oracle.gemv(fmt, rp, rs, rseeds, K, rq, rd)
+    assert_close_terms(host(y), yr, absT, what=NAMES[fmt])
+    assert not host(y)[1].any() and not host(y)[:, 5].any()
+
+
+def test_gemv_mfma_deterministic():
+    fmt, N, K, B = TERN, 300, 5120, 40
+    raw, pw, _, x = _prep(fmt, N, K, 780, B)
+    q, pl, d, s = gpu_act_planes(x)
+    y1 = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y1)
+    ebq.qgemv(pw, q, pl, d, s, B, y1)
+    ebq.qgemv(pw, q, pl, d, s, B, y2)
+    _sync()
+    assert (host(y1).view(np.uint32) == host(y2).view(np.uint32)).all()
+
+
 def test_gemv_deterministic():
     fmt, N, K = TERN, 300, 5120
     raw, pw, _, x = _prep(fmt, N, K, 170)
@@ -453,10 +568,10 @@ def test_grouped_parity_and_reuse(B):
 
 @pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408)])
-@pytest.mark.parametrize("B", [1, 8])
+@pytest.mark.parametrize("B", [1, 8, 16, 64])
 def test_gemv_full_size_sampled(fmt, N, K, B):
     """Every format at the 27B FFN shapes (gate / up 17408 x 5120, down
-    5120 x 17408), batch 1 and 8, run as a grouped plan (the launch the stack
+    5120 x 17408), batch 1, 8, 16 and 64, run as a grouped plan (the launch the stack
     benchmarks time), checked against the oracle on sampled rows: the first
     and last tiles and 62 rows between.  Quantization and packing are per row,
     so the oracle builds only the sampled rows from the same draws."""
