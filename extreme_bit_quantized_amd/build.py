@@ -22,7 +22,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemv.so")
 ARCH = "gfx950"
-MAX_B = 8          # DPP GEMV batch sizes (one object each)
+MAX_B = 6          # lane-per-row dot4 GEMV batch sizes (one object each)
 MAX_TG = 4         # matrix-core GEMV token groups of 16 (batches up to 64)
 
 FLAGS = [

@@ -83,13 +83,16 @@ int check_item(const qgemv_item_t& it, int32_t B) {
 
 using GemvLaunch = hipError_t (*)(const GemvItem&, hipStream_t);
 using GroupedLaunch = hipError_t (*)(const PlanHeader&, const void*, hipStream_t);
-const GemvLaunch kGemv[9] = {nullptr, launch_gemv_b1, launch_gemv_b2, launch_gemv_b3, launch_gemv_b4,
-                             launch_gemv_b5, launch_gemv_b6, launch_gemv_b7, launch_gemv_b8};
-const GroupedLaunch kGrouped[9] = {nullptr, launch_grouped_b1, launch_grouped_b2, launch_grouped_b3,
-                                   launch_grouped_b4, launch_grouped_b5, launch_grouped_b6, launch_grouped_b7,
-                                   launch_grouped_b8};
+const GemvLaunch kGemv[7] = {nullptr, launch_gemv_b1, launch_gemv_b2, launch_gemv_b3, launch_gemv_b4,
+                             launch_gemv_b5, launch_gemv_b6};
+const GroupedLaunch kGrouped[7] = {nullptr, launch_grouped_b1, launch_grouped_b2, launch_grouped_b3,
+                                   launch_grouped_b4, launch_grouped_b5, launch_grouped_b6};
 // Batches above kMaxDppBatch run on the matrix cores in groups of 16 tokens.
-constexpr int kMaxDppBatch = 8;
+// Measured on 64-layer stacks: the lane-per-row dot4 kernels win up to 6 tokens
+// in every format (2.16 ms against 2.34 ms for the 4-bit/ternary stack at 5
+// tokens), the matrix cores from 7 (2.25 ms against 2.58 ms for the 1-bit stack
+// at 8, 2.46 against 3.09 for the 2-bit one).
+constexpr int kMaxDppBatch = 6;
 constexpr int kMaxBatch = 64;
 using MfmaLaunch = hipError_t (*)(const GemvItem&, int, hipStream_t);
 const MfmaLaunch kGemvMfma[5] = {nullptr, launch_gemv_mfma_tg1, launch_gemv_mfma_tg2, launch_gemv_mfma_tg3,

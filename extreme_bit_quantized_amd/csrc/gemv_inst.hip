@@ -1,5 +1,5 @@
 // gemv_inst.hip — instantiates the GEMV kernels for one batch size.  Built once
-// per batch size B = 1..8 with -DQGEMV_NB=B (separate objects, parallel build).
+// per batch size B = 1..6 with -DQGEMV_NB=B (separate objects, parallel build).
 #include "gemv_impl.hpp"
 
 #ifndef QGEMV_NB

@@ -197,8 +197,6 @@ QK_DECL_NB(3)
 QK_DECL_NB(4)
 QK_DECL_NB(5)
 QK_DECL_NB(6)
-QK_DECL_NB(7)
-QK_DECL_NB(8)
 #undef QK_DECL_NB
 // Matrix-core GEMV for batches of 16 TG - 15 .. 16 TG tokens (TG = 1..4).
 #define QK_DECL_TG(n)                                                                  \

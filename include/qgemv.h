@@ -226,7 +226,13 @@ int qact_hadamard_quant_i8(const float* x, int32_t B, int32_t K, const uint32_t*
  * planes [B][K/32][8] (32-byte aligned, qact_planes of q).  INT2 and SIGN1
  * read planes and may get q = NULL; the other formats read q and may get
  * planes = NULL.
- * Output y [B][rows] fp32 (device), overwritten.  1 <= B <= 8.
+ * Output y [B][rows] fp32 (device), overwritten.  1 <= B <= 64
+ * (QERR_INVALID_ARG otherwise).  Up to 6 tokens each lane decodes one row and
+ * takes 4-way int8 dot products per token; from 7 tokens the decoded 32-weight
+ * blocks go, as int8 operands, to the int8 matrix cores in groups of 16 tokens
+ * (large batches on INT8 MMA, [P1] "把非标准格式塞进 llama.cpp，难在哪"), each
+ * block's integer dot scaled in fp32 as above.  Both read the weights once per
+ * call whatever B is.
  * Accuracy: I exact; |y - y_exact| <= 1e-4 * sum|T| (fp32 accumulation). */
 int qgemv(const qweight_t* w, const int8_t* q, const uint32_t* planes, const float* d,
           const int32_t* qsum, int32_t B, float* y, void* stream);
@@ -254,7 +260,9 @@ typedef struct qgemv_item {
   float* y;             /* [B][w.rows] (device), must not overlap another item's y */
 } qgemv_item_t;
 
-/* Bytes of the plan for these items (host); <0 on invalid items. */
+/* Bytes of the plan for these items (host); <0 on invalid items.  Every item
+ * has B tokens, 1 <= B <= 64, and runs on the same kernels as qgemv would run
+ * it at that B. */
 int64_t qgemv_grouped_plan_bytes(const qgemv_item_t* items, int32_t n, int32_t B);
 /* Validate the items and write the plan to host_plan [plan_bytes] (host).
  * The work is cut into 64-row tiles; inside each format they are dealt,

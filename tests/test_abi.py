@@ -241,7 +241,7 @@ def test_grouped_plan_on_host(ebq):
         assert max(loads) - min(loads) <= max(fcosts)
     # too small a buffer is refused
     assert ebq.load().qgemv_grouped_plan(items, 4, 2, host.data_ptr(), nb - 16) == -6
-    # batches up to 64 (above 8 the launch runs on the matrix cores)
+    # batches up to 64 (above 6 the launch runs on the matrix cores)
     assert ebq.load().qgemv_grouped_plan_bytes(items, 4, 64) > 0
     assert ebq.load().qgemv_grouped_plan_bytes(items, 4, 65) == -1
     assert ebq.load().qgemv_grouped_plan_bytes(items, 4, 0) == -1

@@ -236,7 +236,7 @@ def test_pack_levels_bit_exact(fmt):
 
 
 # ---------------------------------------------------------------------------------------------
-# GEMV: exact block dots, fp32 outputs within tolerance, batches 1..8
+# GEMV: exact block dots, fp32 outputs within tolerance, batches 1..64
 # ---------------------------------------------------------------------------------------------
 
 def _prep(fmt, N, K, seed, B=1):
@@ -262,7 +262,7 @@ def test_blockdots_bit_exact(fmt, N, K):
 
 @pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("N,K", SHAPES)
-@pytest.mark.parametrize("B", [1, 3, 8])
+@pytest.mark.parametrize("B", [1, 3, 6])
 def test_gemv_parity(fmt, N, K, B):
     raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 150 + fmt + B, B)
     q, pl, d, s = gpu_act_planes(x)
@@ -366,10 +366,10 @@ def test_gemv_trellis_edge_cases():
 
 @pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("N,K", SHAPES)
-@pytest.mark.parametrize("B", [9, 16, 33, 64])
+@pytest.mark.parametrize("B", [7, 9, 16, 33, 64])
 def test_gemv_mfma_parity(fmt, N, K, B):
-    """Batches above 8 run on the matrix cores (qgemv, single matrix, four waves
-    splitting K): every format and shape at 9, 16, 33 and 64 tokens."""
+    """Batches above 6 run on the matrix cores (qgemv, single matrix, four waves
+    splitting K): every format and shape at 7, 9, 16, 33 and 64 tokens."""
     raw, pw, (rp, rs, rseeds), x = _prep(fmt, N, K, 700 + fmt + B, B)
     q, pl, d, s = gpu_act_planes(x)
     y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
@@ -380,7 +380,7 @@ def test_gemv_mfma_parity(fmt, N, K, B):
     assert_close_terms(host(y), yr, absT, what="%s N=%d K=%d B=%d" % (NAMES[fmt], N, K, B))
 
 
-@pytest.mark.parametrize("B", [9, 10, 11, 12, 13, 14, 15, 16, 17, 31, 32, 47, 48, 49, 63, 64])
+@pytest.mark.parametrize("B", [7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 31, 32, 47, 48, 49, 63, 64])
 def test_gemv_mfma_every_token_count(B):
     """Every token count a 16-token group can end on, all five formats in one
     grouped plan (run twice) and as single-matrix launches."""
