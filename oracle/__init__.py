@@ -73,6 +73,9 @@ def _L():
                 "qref_trellis_states": (None, [P, P, i32, i32, P]),
                 "qref_trellis_decode_f32": (None, [P, P, P, i32, i32, P]),
                 "qref_trellis_decode_i8": (None, [P, P, P, i32, i32, i32, P, P]),
+                "qref_viterbi": (i32, [i32, P, P, P, i32, P, P]),
+                "qref_trellis_rms_scale": (u16, [P]),
+                "qref_trellis_encode": (i32, [P, i32, i32, P, P, P, P, P]),
                 "qref_gemv": (i32, [i32, P, P, P, i32, i32, P, P, i32, P, P, P]),
                 "qref_fwht256": (None, [P]),
                 "qref_hadamard_quant": (None, [P, i32, i32, P, i32, P, P, P]),
@@ -248,6 +251,41 @@ def trellis_decode_i8(packed, seeds, scales, K: int, oblock: int = 256):
     dw = np.empty((N, K // oblock), np.float32)
     _L().qref_trellis_decode_i8(_p(packed), _p(seeds), _p(scales), N, K, oblock, _p(wq), _p(dw))
     return wq, dw
+
+
+def viterbi(L: int, val, w, sc):
+    """Viterbi over an L-bit bit-shift trellis: (state path uint32 [K], fp32 cost)."""
+    val = _c(val, np.float32)
+    w = _c(w, np.float32)
+    sc = _c(sc, np.float32)
+    K = w.shape[0]
+    assert val.shape[0] == 1 << L and sc.shape[0] == K
+    st = np.empty(K, np.uint32)
+    cost = ctypes.c_float()
+    rc = _L().qref_viterbi(L, _p(val), _p(w), _p(sc), K, _p(st), ctypes.byref(cost))
+    assert rc == 0, rc
+    return st, np.float32(cost.value)
+
+
+def trellis_rms_scale(w64) -> int:
+    w64 = _c(w64, np.float32)
+    assert w64.shape == (64,)
+    return int(_L().qref_trellis_rms_scale(_p(w64)))
+
+
+def trellis_encode(w, scales_in=None):
+    """Trellis encoder: w [N][K] fp32 -> (packed, seeds, scales row-major, cost [N] fp32)."""
+    w = _c(np.atleast_2d(w), np.float32)
+    N, K = w.shape
+    packed = np.zeros((N, row_stride(TRELLIS2, K)), np.uint8)
+    seeds = np.empty(N, np.uint16)
+    scales = np.empty((N, K // 64), np.uint16)
+    cost = np.empty(N, np.float32)
+    si = None if scales_in is None else _c(np.atleast_2d(scales_in), np.uint16)
+    rc = _L().qref_trellis_encode(_p(w), N, K, None if si is None else _p(si), _p(packed), _p(seeds),
+                                  _p(scales), _p(cost))
+    assert rc == 0, rc
+    return packed, seeds, scales, cost
 
 
 # -- GEMV / rotation / GEMM ---------------------------------------------------------

@@ -514,6 +514,130 @@ void qref_trellis_decode_i8(const uint8_t* packed, const uint16_t* seeds, const 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Trellis encoder: Viterbi over the bit-shift trellis                        */
+/* ------------------------------------------------------------------------ */
+
+/* Coding a row "jointly, a group of weights at a time" over the trellis
+ * ([P2] "12 GB 装下 27B，靠的是什么取舍", after QTIP) means choosing the
+ * symbol sequence whose decoded values are closest to the weights.  Closest
+ * in squared error is a shortest path through the trellis: the Viterbi
+ * algorithm, here in its textbook form over every state.
+ *
+ * States are L-bit words (2 <= L <= 16); a step shifts a 2-bit symbol c in:
+ * st_i = ((st_{i-1} << 2) | c) mod 2^L, so state s has the 4 predecessors
+ * (s >> 2) | (a << (L-2)), a = 0..3.  Any first state is allowed (the
+ * seed is free).  The value of state s at step i is sc[i] * val[s].
+ * Arithmetic, all fp32, each operation rounded once:
+ *   d = w[i] - sc[i] * val[s]      (one fused rounding: fmaf(-sc, val, w))
+ *   C_0[s] = d * d                 (fmaf(d, d, 0))
+ *   C_i[s] = d * d + min_a C_{i-1}[(s >> 2) | (a << (L-2))]   (fmaf)
+ * Decisions on ties: the smallest a; the last state is the smallest s of
+ * minimum cost.  Writes the state path st[0..K-1] and the minimum cost. */
+int qref_viterbi(int L, const float* val, const float* w, const float* sc, int K, uint32_t* st,
+                 float* cost) {
+  if (L < 2 || L > 16 || K < 1) return -1;
+  const uint32_t S = 1u << L, top = (uint32_t)(L - 2);
+  float* prev = (float*)malloc(sizeof(float) * S);
+  float* cur = (float*)malloc(sizeof(float) * S);
+  uint8_t* dec = (uint8_t*)malloc((size_t)K * S);
+  if (!prev || !cur || !dec) {
+    free(prev); free(cur); free(dec);
+    return -2;
+  }
+  for (int i = 0; i < K; ++i) {
+    for (uint32_t s = 0; s < S; ++s) {
+      float m = 0.0f;
+      uint8_t best = 0;
+      if (i > 0) {
+        m = prev[s >> 2];
+        for (uint32_t a = 1; a < 4; ++a) {
+          float c = prev[(s >> 2) | (a << top)];
+          if (c < m) {
+            m = c;
+            best = (uint8_t)a;
+          }
+        }
+      }
+      dec[(size_t)i * S + s] = best;
+      float d = fmaf(-sc[i], val[s], w[i]);
+      cur[s] = fmaf(d, d, m);
+    }
+    float* t = prev;
+    prev = cur;
+    cur = t;
+  }
+  uint32_t last = 0;
+  for (uint32_t s = 1; s < S; ++s)
+    if (prev[s] < prev[last]) last = s;
+  *cost = prev[last];
+  st[K - 1] = last;
+  for (int i = K - 1; i > 0; --i) {
+    uint32_t s = st[i];
+    st[i - 1] = (s >> 2) | ((uint32_t)dec[(size_t)i * S + s] << top);
+  }
+  free(prev); free(cur); free(dec);
+  return 0;
+}
+
+/* Per-64 scale of the encoder when none is given: the block's root mean
+ * square, so that the scaled values have unit power like the N(0,1)
+ * codebook.  fp32: acc = fmaf(w_k, w_k, acc) for k = 0..63 in order, then
+ * sqrtf(acc * (1/64)) (the factor is a power of two), stored as fp16 (round
+ * to nearest even). */
+uint16_t qref_trellis_rms_scale(const float* w64) {
+  float acc = 0.0f;
+  for (int k = 0; k < 64; ++k) acc = fmaf(w64[k], w64[k], acc);
+  return qref_f64_to_f16((double)sqrtf(acc * 0.015625f));
+}
+
+/* Encode rows w [N][K] (K a multiple of 64) into the trellis format: scales
+ * [N][K/64] fp16 (from scales_in when it is not NULL, else the RMS rule
+ * above), then the Viterbi path of each row over the 2^16-state trellis with
+ * val[s] = V16[hash(s)] and sc = the block's scale.  The symbols are the low
+ * 2 bits of the path's states, packed as qref_pack does; the seed is
+ * st_0 >> 2 (its top 2 bits are shifted out by the first symbol, so they are
+ * written as 0).  cost [N] = the Viterbi minimum (the fp32 squared error of
+ * the row's reconstruction as the recursion accumulates it). */
+int qref_trellis_encode(const float* w, int N, int K, const uint16_t* scales_in, uint8_t* packed,
+                        uint16_t* seeds, uint16_t* scales, float* cost) {
+  if (N < 1 || K < 64 || K % 64) return -1;
+  uint16_t v16[256];
+  qref_codebook_v16(v16);
+  float* val = (float*)malloc(sizeof(float) * 65536);
+  int8_t* codes = (int8_t*)malloc((size_t)N * K);
+  if (!val || !codes) {
+    free(val); free(codes);
+    return -2;
+  }
+  for (uint32_t s = 0; s < 65536; ++s) val[s] = (float)qref_f16_to_f64(v16[qref_trellis_hash(s)]);
+  const int nb = K / 64;
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+  for (int n = 0; n < N; ++n) {
+    const float* row = w + (size_t)n * K;
+    float* sc = (float*)malloc(sizeof(float) * K);
+    uint32_t* st = (uint32_t*)malloc(sizeof(uint32_t) * K);
+    if (!sc || !st) {
+      free(sc); free(st);
+      err |= 1;
+      continue;
+    }
+    for (int b = 0; b < nb; ++b) {
+      uint16_t h = scales_in ? scales_in[(size_t)n * nb + b] : qref_trellis_rms_scale(row + 64 * b);
+      scales[(size_t)n * nb + b] = h;
+      for (int k = 0; k < 64; ++k) sc[64 * b + k] = (float)qref_f16_to_f64(h);
+    }
+    if (qref_viterbi(16, val, row, sc, K, st, cost + n)) err |= 1;
+    for (int i = 0; i < K; ++i) codes[(size_t)n * K + i] = (int8_t)(st[i] & 3u);
+    seeds[n] = (uint16_t)(st[0] >> 2);
+    free(sc); free(st);
+  }
+  if (!err) qref_pack(QREF_TRELLIS2, codes, N, K, packed);
+  free(val); free(codes);
+  return err ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* GEMV                                                                       */
 /* ------------------------------------------------------------------------ */
 

@@ -97,6 +97,19 @@ void qref_trellis_decode_f32(const uint8_t* packed, const uint16_t* seeds, const
 void qref_trellis_decode_i8(const uint8_t* packed, const uint16_t* seeds, const uint16_t* scales,
                             int N, int K, int oblock, int8_t* wq, float* dw);
 
+/* Viterbi over an L-bit bit-shift trellis (2 bits per step): the state path
+ * st [K] minimising the squared error to w with state values sc[i]*val[s],
+ * in fp32 (see qref.c for the exact operations and tie rules).  0 or <0. */
+int qref_viterbi(int L, const float* val, const float* w, const float* sc, int K, uint32_t* st,
+                 float* cost);
+/* RMS scale of one 64-block for the encoder, as fp16 bits. */
+uint16_t qref_trellis_rms_scale(const float* w64);
+/* Trellis encoder: w [N][K] fp32 -> packed [N][stride], seeds [N], scales
+ * [N][K/64] fp16 (row-major; scales_in overrides the RMS rule when not
+ * NULL), cost [N] fp32.  0 or <0. */
+int qref_trellis_encode(const float* w, int N, int K, const uint16_t* scales_in, uint8_t* packed,
+                        uint16_t* seeds, uint16_t* scales, float* cost);
+
 /* GEMV over packed weights and Q8 activations (per-32 activation blocks).
  *   packed [N][stride], scales fp16 [N][K/block], seeds [N] (TRELLIS2 only)
  *   q [B][K], d [B][K/32]
