@@ -84,6 +84,8 @@ def load(path: str = LIB_PATH):
         "qgemv_grouped_run": (ctypes.c_int, [P, P, P]),
         "qgemv_grouped_run_static": (ctypes.c_int, [P, P]),
         "qtrellis_decode_i8": (ctypes.c_int, [W, i32, P, P, P]),
+        "qtrellis_encode_workspace_bytes": (i64, [i32, i32, i32]),
+        "qtrellis_encode": (ctypes.c_int, [P, i32, i32, P, P, i64, P, P, P, i32, P, i64, P]),
         "qweight_unpack_i8": (ctypes.c_int, [W, P, P, P]),
         "qgemm_i8": (ctypes.c_int, [P, P, i32, P, P, i32, i32, i32, P, P]),
         "qcalib_mfma_i8": (ctypes.c_int, [i32, i32, P, P, P]),
@@ -300,6 +302,23 @@ class GroupedPlan:
 def qtrellis_decode_i8(w: PackedWeight, oblock: int, wq, dw, stream=None):
     _check(load().qtrellis_decode_i8(ctypes.byref(w.desc), oblock, _ptr(wq), _ptr(dw), _stream(stream)),
            "qtrellis_decode_i8")
+
+
+def qtrellis_encode_workspace_bytes(rows: int, cols: int, rows_per_pass: int) -> int:
+    n = load().qtrellis_encode_workspace_bytes(rows, cols, rows_per_pass)
+    _check(n if n < 0 else 0, "qtrellis_encode_workspace_bytes")
+    return n
+
+
+def qtrellis_encode(w, out: PackedWeight, workspace, rows_per_pass: int, scales_in=None, cost=None, stream=None):
+    """w: fp32 [rows][cols] (device); out: an empty TRELLIS2 PackedWeight of the same
+    shape; workspace: a device tensor of at least qtrellis_encode_workspace_bytes."""
+    rows, cols = w.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().qtrellis_encode(_ptr(w), rows, cols, _ptr(scales_in), _ptr(out.codes), out.row_bytes,
+                                  _ptr(out.seeds), _ptr(out.scales), _ptr(cost), rows_per_pass, _ptr(workspace),
+                                  ws_bytes, _stream(stream)), "qtrellis_encode")
+    return out
 
 
 def qweight_unpack_i8(w: PackedWeight, wq, dw, stream=None):

@@ -94,6 +94,8 @@ const GroupedLaunch kGrouped[7] = {nullptr, launch_grouped_b1, launch_grouped_b2
 // at 8, 2.46 against 3.09 for the 2-bit one).
 constexpr int kMaxDppBatch = 6;
 constexpr int kMaxBatch = 64;
+// Longest row the encoder takes (its choices use 4 KB per row and weight).
+constexpr int32_t kMaxEncodeCols = 1 << 20;
 using MfmaLaunch = hipError_t (*)(const GemvItem&, int, hipStream_t);
 const MfmaLaunch kGemvMfma[5] = {nullptr, launch_gemv_mfma_tg1, launch_gemv_mfma_tg2, launch_gemv_mfma_tg3,
                                  launch_gemv_mfma_tg4};
@@ -451,6 +453,29 @@ int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw
   if (!aligned(wq, 4) || !aligned(dw, 4)) return QERR_ALIGNMENT;
   const GemvItem it = make_item(w, nullptr, nullptr, nullptr, nullptr, nullptr);
   return hip_rc(launch_trellis_decode(it, oblock, wq, dw, S(stream)));
+}
+
+int64_t qtrellis_encode_workspace_bytes(int32_t rows, int32_t cols, int32_t rows_per_pass) {
+  if (rows < 1 || cols < 1 || rows_per_pass < 1) return QERR_INVALID_ARG;
+  if (cols < 64 || cols % 64 != 0 || cols > kMaxEncodeCols) return QERR_SHAPE;
+  return encode_workspace_bytes(rows, cols, rows_per_pass < rows ? rows_per_pass : rows);
+}
+
+int qtrellis_encode(const float* w, int32_t rows, int32_t cols, const uint16_t* scales_in, void* codes,
+                    int64_t row_bytes, uint16_t* seeds, uint16_t* scales, float* cost, int32_t rows_per_pass,
+                    void* workspace, int64_t workspace_bytes, void* stream) {
+  if (rows < 0 || cols < 0 || rows_per_pass < 1) return QERR_INVALID_ARG;
+  if (rows == 0) return QERR_OK;
+  if (cols < 64 || cols % 64 != 0 || cols > kMaxEncodeCols) return QERR_SHAPE;
+  if (!w || !codes || !seeds || !scales || !workspace) return QERR_INVALID_ARG;
+  if (row_bytes < packed_row_bytes(QFMT_TRELLIS2, cols) || row_bytes % 16 != 0) return QERR_SHAPE;
+  if (!aligned(w, 4) || !aligned(codes, 16) || !aligned(seeds, 2) || !aligned(scales, 16) ||
+      !aligned(scales_in, 2) || !aligned(cost, 4) || !aligned(workspace, 256))
+    return QERR_ALIGNMENT;
+  const int32_t per = rows_per_pass < rows ? rows_per_pass : rows;
+  if (workspace_bytes < encode_workspace_bytes(rows, cols, per)) return QERR_BUFFER;
+  return hip_rc(launch_trellis_encode(w, rows, cols, scales_in, (uint8_t*)codes, row_bytes, seeds, scales, cost,
+                                      per, workspace, S(stream)));
 }
 
 int qweight_unpack_i8(const qweight_t* w, int8_t* wq, float* dw, void* stream) {

@@ -208,6 +208,11 @@ QK_DECL_TG(3)
 QK_DECL_TG(4)
 #undef QK_DECL_TG
 hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, float* dw, hipStream_t s);
+// Trellis encoder (encode.hip): workspace bytes and the launch sequence.
+int64_t encode_workspace_bytes(int rows, int cols, int rows_per_pass);
+hipError_t launch_trellis_encode(const float* w, int rows, int cols, const uint16_t* scales_in, uint8_t* codes,
+                                 int64_t row_bytes, uint16_t* seeds, uint16_t* scales, float* cost,
+                                 int rows_per_pass, void* ws, hipStream_t s);
 hipError_t launch_mfma_peak(int blocks, int iters, uint64_t* clocks, int32_t* sink, hipStream_t s);
 hipError_t launch_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* wq, const float* dw,

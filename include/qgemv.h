@@ -296,6 +296,37 @@ int qgemv_grouped_run(const void* host_plan, const void* dev_plan, void* stream)
 #define QGEMV_STATIC_PLAN_BYTES (1 << 20)
 int qgemv_grouped_run_static(const void* host_plan, void* stream);
 
+/* ---- trellis encoder ----------------------------------------------------------------- */
+
+/* Encode fp32 weights into TRELLIS2: per row, the symbol path through the
+ * 2^16-state bit-shift trellis whose decoded values are closest to the row in
+ * squared error, found by the Viterbi algorithm (the format codes each row
+ * jointly over a trellis, [P2] "12 GB 装下 27B，靠的是什么取舍", after QTIP;
+ * its codebook is hashed at run time, [P1] "2.4bit 是个什么量级").
+ *   Scales: s [rows][cols/64] fp16 = scales_in when it is not NULL (device,
+ *   row-major), else fp16(sqrt(acc / 64)) with acc = fma(w_k, w_k, acc) over
+ *   the block's 64 weights in order (fp32, round to nearest even).  Blocks
+ *   whose root mean square exceeds the fp16 range get an infinite scale.
+ *   Path: states st_i = ((st_{i-1} << 2) | c_i) & 0xFFFF, any first state;
+ *   fp32 recursion d = fma(-s, V16[hash(st)], w_i) (s * V16 is exact),
+ *   C_i[st] = fma(d, d, min over the 4 predecessors of C_{i-1}), C_{-1} = 0;
+ *   on equal costs the predecessor with the smaller top 2 bits, and the
+ *   smallest last state.  seed = st_0 >> 2 (top 2 bits 0).
+ * Inputs: w [rows][cols] fp32 (device, finite), cols a multiple of 64, at most
+ * 2^20.  Outputs (device): codes [rows][row_bytes] (16-byte aligned, padding
+ * zeroed), seeds [rows], scales (tiled, qfmt_scales_bytes(QFMT_TRELLIS2, rows,
+ * cols) bytes, 16-byte aligned), and cost [rows] fp32 = the recursion's
+ * minimum (the row's squared reconstruction error; may be NULL).  Bit-exact:
+ * the same fp32 operations in the same order, so the codes are unique.
+ * Rows are encoded rows_per_pass at a time (one compute unit each); the
+ * caller's workspace (device, 256-byte aligned) holds the scales and each
+ * pass's choices, 4 KB per row and weight:
+ * qtrellis_encode_workspace_bytes gives its size (QERR_BUFFER if smaller). */
+int64_t qtrellis_encode_workspace_bytes(int32_t rows, int32_t cols, int32_t rows_per_pass);
+int qtrellis_encode(const float* w, int32_t rows, int32_t cols, const uint16_t* scales_in, void* codes,
+                    int64_t row_bytes, uint16_t* seeds, uint16_t* scales, float* cost, int32_t rows_per_pass,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
 /* ---- prefill: trellis decode to int8 and the int8 MFMA GEMM --------------------------- */
 
 /* Decode TRELLIS2 weights to int8 for the GEMM.  The codebook is computed at

@@ -305,3 +305,33 @@ def test_static_plan_size_limit(ebq):
     o2 = (-junk.data_ptr()) % 16
     assert L.qgemv_grouped_run_static(junk[o2:].data_ptr(), None) == -6
     assert "static plan" in L.qstrerror(-7).decode()
+
+
+def test_trellis_encode_validation_without_gpu(ebq):
+    """The encoder's argument checks run on the host before any HIP call."""
+    L = ebq.load()
+    A = 1 << 20
+    need = L.qtrellis_encode_workspace_bytes(4, 256, 2)
+    # scales of all rows, (state, cost) per pass row, 4 KB of choices per pass row and step
+    assert need == 2048 // 2048 * 256 + 256 + 2 * 255 * 4096
+    assert L.qtrellis_encode_workspace_bytes(4, 256, 9) == L.qtrellis_encode_workspace_bytes(4, 256, 4)
+    assert L.qtrellis_encode_workspace_bytes(4, 96, 2) == -3
+    assert L.qtrellis_encode_workspace_bytes(0, 256, 2) == -1
+    assert L.qtrellis_encode_workspace_bytes(4, 256, 0) == -1
+
+    def enc(w=A, rows=4, cols=256, si=None, codes=A, rb=64, seeds=A, sc=A, cost=None, per=2, ws=A, wsb=need):
+        return L.qtrellis_encode(w, rows, cols, si, codes, rb, seeds, sc, cost, per, ws, wsb, None)
+
+    assert enc(rows=0) == 0
+    assert enc(rows=-1) == -1
+    assert enc(per=0) == -1
+    assert enc(cols=96) == -3
+    assert enc(cols=32) == -3
+    assert enc(cols=(1 << 20) + 64) == -3
+    assert enc(rb=48) == -3             # below the 64 packed bytes of 256 symbols
+    assert enc(rb=72) == -3             # not a multiple of 16
+    assert enc(w=None) == -1 and enc(codes=None) == -1 and enc(seeds=None) == -1
+    assert enc(sc=None) == -1 and enc(ws=None) == -1
+    assert enc(w=A + 2) == -4 and enc(codes=A + 8) == -4 and enc(seeds=A + 1) == -4
+    assert enc(sc=A + 8) == -4 and enc(si=A + 1) == -4 and enc(cost=A + 2) == -4 and enc(ws=A + 128) == -4
+    assert enc(wsb=need - 1) == -6
