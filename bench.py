@@ -56,6 +56,8 @@ METRIC = "weight-stream HBM GB/s (% of peak) + equiv. tok/s, 27B-shaped batch-1 
 def layer_fmt(kind: str, name: str) -> int:
     if kind == "sign1":
         return SIGN1
+    if kind == "trellis":
+        return TRELLIS
     if kind == "int2":
         return INT2
     if kind == "mixed":
@@ -64,15 +66,31 @@ def layer_fmt(kind: str, name: str) -> int:
 
 
 def seed_of(kind: str) -> int:
-    return {"int2": 2, "sign1": 3, "mixed": 4}[kind]
+    return {"int2": 2, "sign1": 3, "mixed": 4, "trellis": 5}[kind]
+
+
+def trellis_draws(layer, mi, N, K):
+    """Synthetic trellis-coded matrix, drawn on the device: uniform 2-bit symbols
+    (as bytes), uniform 16-bit seeds, fp16 scales U[0.01, 0.03] per 64 (row-major)."""
+    return (synth.bytes_torch([5, layer, mi, 1], (N, K // 4)), synth.u16_torch([5, layer, mi, 2], (N,)),
+            synth.uniform_f16_torch([5, layer, mi, 3], (N, K // 64), 0.01, 0.03))
 
 
 def build_matrix(ebq, kind, layer, mi, name, N, K):
     """Quantize N(0, sigma) draws for one matrix on the GPU with the library's
-    quantizer.  1-bit draws are N(0,1) (sign + mean|w|), the others N(0,0.02)."""
+    quantizer.  1-bit draws are N(0,1) (sign + mean|w|), the others N(0,0.02).
+    Trellis matrices are random codes, seeds and scales (trellis_draws)."""
     import torch
 
     fmt = layer_fmt(kind, name)
+    if fmt == TRELLIS:
+        codes, seeds, sc = trellis_draws(layer, mi, N, K)
+        pw = ebq.PackedWeight.empty(fmt, N, K)
+        pw.codes.copy_(codes)
+        pw.seeds.copy_(seeds)
+        ebq.qweight_set_scales(pw, sc)
+        del codes, seeds, sc
+        return pw
     sigma = 1.0 if kind == "sign1" else 0.02
     w = synth.gauss_torch([seed_of(kind), layer, mi], (N, K), sigma)
     pw = ebq.PackedWeight.empty(fmt, N, K)
@@ -228,6 +246,8 @@ def sclk_probe(ebq):
 # ---------------------------------------------------------------------------------------
 
 def sampled_parity(ebq, stack, layer_ids, rows_per_matrix=16, seed=0):
+    import torch
+
     import oracle
 
     rng = np.random.default_rng(seed)
@@ -236,13 +256,23 @@ def sampled_parity(ebq, stack, layer_ids, rows_per_matrix=16, seed=0):
         for mi, (name, N, K) in enumerate(stack.shapes):
             fmt = layer_fmt(stack.kind, name)
             rows = np.sort(rng.choice(N, size=min(rows_per_matrix, N), replace=False))
-            sigma = 1.0 if stack.kind == "sign1" else 0.02
-            w = synth.gauss_torch([seed_of(stack.kind), l, mi], (N, K), sigma)[rows].cpu().numpy()
-            codes, sc = oracle.quantize(fmt, w)
-            packed = oracle.pack(fmt, codes)
+            seeds = None
+            if fmt == TRELLIS:
+                # the sampled rows of the same device draws
+                ct, st, sct = trellis_draws(l, mi, N, K)
+                idx = torch.from_numpy(rows).cuda()
+                packed = ct[idx].cpu().numpy()
+                seeds = st[idx].cpu().numpy().view(np.uint16)
+                sc = sct[idx].cpu().numpy().view(np.uint16)
+                del ct, st, sct
+            else:
+                sigma = 1.0 if stack.kind == "sign1" else 0.02
+                w = synth.gauss_torch([seed_of(stack.kind), l, mi], (N, K), sigma)[rows].cpu().numpy()
+                codes, sc = oracle.quantize(fmt, w)
+                packed = oracle.pack(fmt, codes)
             x = stack.x[K][l * stack.B:(l + 1) * stack.B].cpu().numpy()
             rq, rd, _ = oracle.act_quant(x, 32)
-            yr, absT, _ = oracle.gemv(fmt, packed, sc, None, K, rq, rd)
+            yr, absT, _ = oracle.gemv(fmt, packed, sc, seeds, K, rq, rd)
             yg = stack.y[l][mi].cpu().numpy()[:, rows].astype(np.float64)
             err = np.abs(yg - yr)
             ratio = float((err / np.maximum(absT, 1e-300)).max())
@@ -513,6 +543,47 @@ def bench_prefill(ebq, reps):
         }
         del x, xq, wq, y
     return out
+
+
+def bench_trellis_encoder(ebq, reps, N=512, K=5120, per=256, sample=(0, 511)):
+    """Trellis encoder (Viterbi over the 2^16-state trellis) on N(0, 0.02) rows of
+    the 5120 input width, rows_per_pass = 256 (one row per compute unit).
+    Parity: codes, seeds, scales and costs of the sampled rows bit-exact against
+    the oracle.  Roofline: VALU issue (the recursion is plain fp32 arithmetic)."""
+    import torch
+
+    import oracle
+
+    w_h = synth.gauss([5, 900, N, K], (N, K), 0.02)
+    w = torch.from_numpy(w_h).cuda()
+    out = ebq.PackedWeight.empty(TRELLIS, N, K)
+    ws = torch.empty(ebq.qtrellis_encode_workspace_bytes(N, K, per), dtype=torch.uint8, device="cuda")
+    cost = torch.empty(N, dtype=torch.float32, device="cuda")
+    t, _ = time_region(lambda: ebq.qtrellis_encode(w, out, ws, per, cost=cost), reps, 1)
+    codes, seeds = out.codes.cpu().numpy(), out.seeds.cpu().numpy().view(np.uint16)
+    sc = torch.empty((N, K // 64), dtype=torch.int16, device="cuda")
+    ebq.qweight_get_scales(out, sc)
+    sc = sc.cpu().numpy().view(np.uint16)
+    cost_h = cost.cpu().numpy()
+    rows = list(sample)
+    rp, rs, rsc, rc = oracle.trellis_encode(w_h[rows])
+    ok = bool((codes[rows] == rp).all() and (seeds[rows] == rs).all() and (sc[rows] == rsc).all()
+              and (cost_h[rows].view(np.uint32) == rc.view(np.uint32)).all())
+    state_steps = float(N) * K * 65536
+    nmse = float(cost_h.astype(np.float64).sum() / (w_h.astype(np.float64) ** 2).sum())
+    del w, out, ws, cost
+    torch.cuda.empty_cache()
+    return {
+        "rows": N, "cols": K, "rows_per_pass": per,
+        "ms": round(t * 1e3, 3),
+        "rows_per_s": round(N / t, 1),
+        "weights_per_s": round(N * K / t, 1),
+        "state_steps_per_s": round(state_steps / t, 1),
+        "nmse": round(nmse, 5),
+        "nmse_bounds": "above 0.0625 (Gaussian rate-distortion at 2 bits), below 0.1175 (4-level Lloyd-Max)",
+        "parity": "ok" if ok else "FAIL",
+        "parity_sample": "rows %s: codes, seeds, scales and cost bit-exact against the oracle" % (rows,),
+    }
 
 
 def bench_mfma_ceiling(ebq):
@@ -822,6 +893,27 @@ def main():
         }
         del plan, l2
         torch.cuda.empty_cache()
+        log("trellis 64-layer stack B=1")
+        ts = Stack(ebq, "trellis", synth.N_LAYERS, 1)
+        plan, t, tk, _, cond = bench_stack_grouped(ebq, ts, reps, 2, 0.3)
+        okt, wt = sampled_parity(ebq, ts, [0, 63], rows_per_matrix=8)
+        extra["trellis2_64layer_stack_B1"] = {
+            "step_us": round(t * 1e6, 1),
+            "gemv_us": round(tk * 1e6, 1),
+            "gbs": round(ts.step_bytes() / t / 1e9, 1),
+            "gemv_gbs": round(ts.gemv_bytes() / tk / 1e9, 1),
+            "frac_of_8tbs": round(ts.gemv_bytes() / tk / 8e12, 4),
+            "equiv_tok_s": round(1 / t, 1),
+            "weight_bytes": ts.weight_bytes(),
+            "sclk_mhz": cond.get("sclk_mhz_after"),
+            "parity": "ok" if okt else "FAIL",
+            "parity_sample": "8 rows of every matrix of layers 0 and 63",
+            "worst_err_over_sum_abs_terms": wt,
+        }
+        del plan, ts
+        torch.cuda.empty_cache()
+        log("trellis encoder")
+        extra["trellis_encoder_512x5120"] = bench_trellis_encoder(ebq, 3)
         log("ternary 1024x1024")
         extra["ternary_1024x1024_latency"] = bench_small_ternary(ebq, 50)
         log("prefill")

@@ -115,3 +115,35 @@ def gauss_torch(seed, shape, sigma: float = 1.0, device: str = "cuda"):
     if sigma != 1.0:
         x.mul_(sigma)
     return x
+
+
+def _torch_gen(seed, device):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed64(*seed))
+    return g
+
+
+def bytes_torch(seed, shape, device: str = "cuda"):
+    """Uniform random bytes (uint8) drawn on the device."""
+    import torch
+
+    return torch.randint(0, 256, shape, generator=_torch_gen(seed, device), device=device, dtype=torch.uint8)
+
+
+def u16_torch(seed, shape, device: str = "cuda"):
+    """Uniform 16-bit words drawn on the device, stored as int16 bit patterns."""
+    import torch
+
+    x = torch.randint(0, 1 << 16, shape, generator=_torch_gen(seed, device), device=device, dtype=torch.int32)
+    return x.to(torch.int16)
+
+
+def uniform_f16_torch(seed, shape, lo: float, hi: float, device: str = "cuda"):
+    """U[lo, hi) fp32 draws on the device stored as fp16 bit patterns (int16),
+    rounded to nearest even."""
+    import torch
+
+    x = torch.rand(shape, generator=_torch_gen(seed, device), device=device, dtype=torch.float32)
+    return (x * (hi - lo) + lo).to(torch.float16).view(torch.int16)
