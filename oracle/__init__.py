@@ -76,6 +76,10 @@ def _L():
                 "qref_viterbi": (i32, [i32, P, P, P, i32, P, P]),
                 "qref_trellis_rms_scale": (u16, [P]),
                 "qref_trellis_encode": (i32, [P, i32, i32, P, P, P, P, P]),
+                "qref_kv_row_bytes": (i64, [i32, i32]),
+                "qref_kv_quant": (i32, [i32, P, i64, i32, P, P]),
+                "qref_kv_dequant": (i32, [i32, P, P, i64, i32, P]),
+                "qref_attn_decode": (i32, [i32, P, i32, i32, i32, i32, i64, P, P, P, P, P, P]),
                 "qref_gemv": (i32, [i32, P, P, P, i32, i32, P, P, i32, P, P, P]),
                 "qref_fwht256": (None, [P]),
                 "qref_hadamard_quant": (None, [P, i32, i32, P, i32, P, P, P]),
@@ -286,6 +290,54 @@ def trellis_encode(w, scales_in=None):
                                   _p(scales), _p(cost))
     assert rc == 0, rc
     return packed, seeds, scales, cost
+
+
+# -- KV cache and decode attention ---------------------------------------------------
+
+KV_Q4, KV_Q8 = 4, 8
+
+
+def kv_row_bytes(fmt: int, D: int) -> int:
+    return int(_L().qref_kv_row_bytes(fmt, D))
+
+
+def kv_quant(fmt: int, x):
+    """x [..., D] fp32 -> (codes uint8 [..., row bytes], scales fp16 bits [..., D/32])."""
+    x = _c(x, np.float32)
+    D = x.shape[-1]
+    rows = int(np.prod(x.shape[:-1]))
+    codes = np.empty(x.shape[:-1] + (kv_row_bytes(fmt, D),), np.uint8)
+    scales = np.empty(x.shape[:-1] + (D // 32,), np.uint16)
+    rc = _L().qref_kv_quant(fmt, _p(x), rows, D, _p(codes), _p(scales))
+    assert rc == 0, rc
+    return codes, scales
+
+
+def kv_dequant(fmt: int, codes, scales, D: int):
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint16)
+    rows = int(np.prod(codes.shape[:-1]))
+    x = np.empty(codes.shape[:-1] + (D,), np.float64)
+    rc = _L().qref_kv_dequant(fmt, _p(codes), _p(scales), rows, D, _p(x))
+    assert rc == 0, rc
+    return x
+
+
+def attn_decode(fmt: int, q, kc, ks, vc, vs, T: int):
+    """q [n_kv * G][D] fp32; kc, vc [n_kv][t_cap][row bytes]; ks, vs [n_kv][t_cap][D/32].
+    Returns (out fp64 [n_kv * G][D], bound fp64 [n_kv * G][D])."""
+    q = _c(q, np.float32)
+    kc, vc = _c(kc, np.uint8), _c(vc, np.uint8)
+    ks, vs = _c(ks, np.uint16), _c(vs, np.uint16)
+    n_kv, t_cap = kc.shape[0], kc.shape[1]
+    D = q.shape[1]
+    G = q.shape[0] // n_kv
+    out = np.empty(q.shape, np.float64)
+    bound = np.empty(q.shape, np.float64)
+    rc = _L().qref_attn_decode(fmt, _p(q), n_kv, G, D, T, t_cap, _p(kc), _p(ks), _p(vc), _p(vs), _p(out),
+                               _p(bound))
+    assert rc == 0, rc
+    return out, bound
 
 
 # -- GEMV / rotation / GEMM ---------------------------------------------------------

@@ -638,6 +638,153 @@ int qref_trellis_encode(const float* w, int N, int K, const uint16_t* scales_in,
 }
 
 /* ------------------------------------------------------------------------ */
+/* KV cache in Q8 / Q4 and decode attention over it                           */
+/* ------------------------------------------------------------------------ */
+
+/* The KV cache grows with the context and is kept in 4 or 8 bits ([P1]
+ * "12G 的账本要这么算": KV at Q4 or Q8 decides how long a context fits).
+ * Each row of D values (one token of one KV head) is cut into 32-value
+ * blocks with one fp16 scale each:
+ *   Q8: d = amax / 127, r = 1 / d, id = r if finite else 0,
+ *       c = clamp(rint(x * id), -127, 127), stored as int8;
+ *   Q4: d = amax / 7, id likewise, c = clamp(rint(x * id), -7, 7), stored
+ *       as the nibble c + 8 (byte j of a block: value 2j low, 2j+1 high).
+ * All fp32, ties to even; the stored scale is fp16(d) (round to nearest
+ * even), and the cached value is c * fp16(d). */
+int64_t qref_kv_row_bytes(int fmt, int D) {
+  if (D < 32 || D % 32) return -1;
+  if (fmt == QREF_KV_Q8) return D;
+  if (fmt == QREF_KV_Q4) return D / 2;
+  return -1;
+}
+
+int qref_kv_quant(int fmt, const float* x, int64_t rows, int D, uint8_t* codes, uint16_t* scales) {
+  const int64_t rb = qref_kv_row_bytes(fmt, D);
+  if (rb < 0) return -1;
+  const float top = fmt == QREF_KV_Q8 ? 127.0f : 7.0f;
+  const int nb = D / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int b = 0; b < nb; ++b) {
+      const float* v = x + r * D + 32 * b;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i)
+        if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+      const float d = amax / top;
+      const float inv = 1.0f / d;
+      const float id = isfinite(inv) ? inv : 0.0f;
+      scales[r * nb + b] = qref_f64_to_f16((double)d);
+      for (int i = 0; i < 32; ++i) {
+        float t = rintf(v[i] * id);
+        if (t > top) t = top;
+        if (t < -top) t = -top;
+        const int c = (int)t;
+        if (fmt == QREF_KV_Q8) {
+          codes[r * rb + 32 * b + i] = (uint8_t)(int8_t)c;
+        } else {
+          uint8_t* by = codes + r * rb + 16 * b + i / 2;
+          if (i % 2 == 0) *by = (uint8_t)(c + 8);
+          else *by = (uint8_t)(*by | ((c + 8) << 4));
+        }
+      }
+    }
+  return 0;
+}
+
+/* Cached values in fp64 (exact: a small integer times an fp16 scale). */
+int qref_kv_dequant(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t rows, int D, double* x) {
+  const int64_t rb = qref_kv_row_bytes(fmt, D);
+  if (rb < 0) return -1;
+  const int nb = D / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int i = 0; i < D; ++i) {
+      const double d = qref_f16_to_f64(scales[r * nb + i / 32]);
+      int c;
+      if (fmt == QREF_KV_Q8) {
+        c = (int8_t)codes[r * rb + i];
+      } else {
+        const uint8_t by = codes[r * rb + i / 2];
+        c = (int)((i % 2 == 0) ? (by & 15) : (by >> 4)) - 8;
+      }
+      x[r * D + i] = c * d;
+    }
+  return 0;
+}
+
+/* Decode attention of one new token with grouped KV heads ([P1]
+ * "把非标准格式塞进 llama.cpp，难在哪": the KV heads serve query heads in
+ * groups of 6).  Query row i = h * G + g (KV head h, member g) attends over
+ * the T cached tokens of KV head h:
+ *   s_t = (q_i . k_t) / sqrt(D),  p_t = exp(s_t - max s),
+ *   out_i = sum_t p_t v_t / sum_t p_t,
+ * with k_t, v_t the cached (dequantized) values; all in fp64.  Cache layout
+ * codes [n_kv][t_cap][row bytes], scales [n_kv][t_cap][D/32].
+ * bound (may be NULL) gets, per output, an error allowance for an fp32
+ * computation of the same sums in any order (with u = 2^-24):
+ *   sum_t p_t (e_t + 4u + u |s_t - max s|) (|v_t| + |out|) / sum p
+ *   + 2 (T + D) u sum_t p_t |v_t| / sum p,   e_t = 2 D u sum_d |q_d k_td| / sqrt(D),
+ * the score, exponential and summation errors (e_t bounds a D-term fp32 dot
+ * product with a factor 2 of slack). */
+int qref_attn_decode(int fmt, const float* q, int n_kv, int G, int D, int T, int64_t t_cap, const uint8_t* kc,
+                     const uint16_t* ks, const uint8_t* vc, const uint16_t* vs, double* out, double* bound) {
+  const int64_t rb = qref_kv_row_bytes(fmt, D);
+  if (rb < 0 || n_kv < 1 || G < 1 || T < 1 || t_cap < T) return -1;
+  const int nb = D / 32;
+  const double u = ldexp(1.0, -24), isd = 1.0 / sqrt((double)D);
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+  for (int h = 0; h < n_kv; ++h) {
+    double* K = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* V = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* s = (double*)malloc(sizeof(double) * (size_t)T);
+    double* e = (double*)malloc(sizeof(double) * (size_t)T);
+    if (!K || !V || !s || !e) {
+      free(K); free(V); free(s); free(e);
+      err |= 1;
+      continue;
+    }
+    qref_kv_dequant(fmt, kc + (size_t)h * t_cap * rb, ks + (size_t)h * t_cap * nb, T, D, K);
+    qref_kv_dequant(fmt, vc + (size_t)h * t_cap * rb, vs + (size_t)h * t_cap * nb, T, D, V);
+    for (int g = 0; g < G; ++g) {
+      const float* qi = q + ((size_t)h * G + g) * D;
+      double m = -INFINITY;
+      for (int t = 0; t < T; ++t) {
+        double acc = 0.0, aabs = 0.0;
+        for (int d = 0; d < D; ++d) {
+          acc += (double)qi[d] * K[(size_t)t * D + d];
+          aabs += fabs((double)qi[d] * K[(size_t)t * D + d]);
+        }
+        s[t] = acc * isd;
+        e[t] = 2.0 * D * u * aabs * isd;
+        if (s[t] > m) m = s[t];
+      }
+      double L = 0.0;
+      for (int t = 0; t < T; ++t) L += exp(s[t] - m);
+      double* o = out + ((size_t)h * G + g) * D;
+      double* bo = bound ? bound + ((size_t)h * G + g) * D : NULL;
+      for (int d = 0; d < D; ++d) {
+        double acc = 0.0, aabs = 0.0;
+        for (int t = 0; t < T; ++t) {
+          const double p = exp(s[t] - m);
+          acc += p * V[(size_t)t * D + d];
+          aabs += p * fabs(V[(size_t)t * D + d]);
+        }
+        o[d] = acc / L;
+        if (bo) {
+          double b = 0.0;
+          for (int t = 0; t < T; ++t) {
+            const double p = exp(s[t] - m);
+            b += p * (e[t] + 4.0 * u + u * fabs(s[t] - m)) * (fabs(V[(size_t)t * D + d]) + fabs(o[d]));
+          }
+          bo[d] = b / L + 2.0 * (T + D) * u * aabs / L;
+        }
+      }
+    }
+    free(K); free(V); free(s); free(e);
+  }
+  return err ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* GEMV                                                                       */
 /* ------------------------------------------------------------------------ */
 

@@ -44,6 +44,12 @@ enum {
   QREF_TRELLIS2 = 5   /* 2-bit bit-shift trellis codes, scale per 64 */
 };
 
+/* KV cache formats (values are part of the cache descriptor). */
+enum {
+  QREF_KV_Q4 = 4,     /* 4-bit, fp16 scale per 32 */
+  QREF_KV_Q8 = 8      /* 8-bit, fp16 scale per 32 */
+};
+
 /* OpenMP threads of the parallel loops (timing only; results do not depend on it). */
 int qref_threads(void);
 void qref_set_threads(int n);
@@ -109,6 +115,18 @@ uint16_t qref_trellis_rms_scale(const float* w64);
  * NULL), cost [N] fp32.  0 or <0. */
 int qref_trellis_encode(const float* w, int N, int K, const uint16_t* scales_in, uint8_t* packed,
                         uint16_t* seeds, uint16_t* scales, float* cost);
+
+/* KV cache: bytes per row of D values, quantization of rows x [rows][D] fp32
+ * to codes [rows][row bytes] + fp16 scales [rows][D/32], and the cached values
+ * back in fp64.  0 or <0. */
+int64_t qref_kv_row_bytes(int fmt, int D);
+int qref_kv_quant(int fmt, const float* x, int64_t rows, int D, uint8_t* codes, uint16_t* scales);
+int qref_kv_dequant(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t rows, int D, double* x);
+/* Decode attention over the cached KV heads, G query rows per KV head:
+ * q [n_kv * G][D] fp32 -> out [n_kv * G][D] fp64, bound (may be NULL) the
+ * per-output fp32 error allowance (see qref.c).  0 or <0. */
+int qref_attn_decode(int fmt, const float* q, int n_kv, int G, int D, int T, int64_t t_cap, const uint8_t* kc,
+                     const uint16_t* ks, const uint8_t* vc, const uint16_t* vs, double* out, double* bound);
 
 /* GEMV over packed weights and Q8 activations (per-32 activation blocks).
  *   packed [N][stride], scales fp16 [N][K/block], seeds [N] (TRELLIS2 only)
