@@ -586,6 +586,59 @@ def bench_trellis_encoder(ebq, reps, N=512, K=5120, per=256, sample=(0, 511)):
     }
 
 
+def bench_decode_attention(ebq, reps, T=65536, n_kv=4, group=6):
+    """Decode attention of one token over a 64K-token KV cache in Q8 and in Q4,
+    the 27B-shaped grouping (4 KV heads, 6 query heads each, head dim 256):
+    the six query heads of a KV head packed into one workgroup (each cached
+    byte read once per group) against one query head per workgroup (read six
+    times).  Bytes: the cache (codes + fp16 scales of K and V), q, out and the
+    per-chunk partial sums written and read back.  Parity against the oracle
+    on one KV head's group (within its fp32 allowance)."""
+    import torch
+
+    import oracle
+
+    D = 256
+    out = {}
+    for fmt, name in ((ebq.QKV_Q8, "q8"), (ebq.QKV_Q4, "q4")):
+        rb = ebq.qkv_row_bytes(fmt)
+        kc = torch.empty((n_kv, T, rb), dtype=torch.uint8, device="cuda")
+        vc = torch.empty_like(kc)
+        ks = torch.empty((n_kv, T, D // 32), dtype=torch.int16, device="cuda")
+        vs = torch.empty_like(ks)
+        for i, (c, s_) in enumerate(((kc, ks), (vc, vs))):
+            x = synth.gauss_torch([7, 100 + i, fmt], (n_kv, T, D))
+            ebq.qkv_quant(fmt, x, c, s_)
+            del x
+        q = synth.gauss_torch([7, 200], (n_kv * group, D))
+        o = torch.empty_like(q)
+        ws = torch.empty(ebq.qattn_decode_workspace_bytes(n_kv, group, T), dtype=torch.uint8, device="cuda")
+        cache = 2 * n_kv * T * (rb + D // 32 * 2)
+        part = ebq.qattn_decode_workspace_bytes(n_kv, group, T)
+        alg = cache + 2 * q.numel() * 4 + 2 * part
+        res = {}
+        for hpb, tag in ((group, "packed"), (1, "one_head_per_block")):
+            t, _ = time_region(lambda: ebq.qattn_decode(fmt, q, kc, ks, vc, vs, T, o, ws, heads_per_block=hpb),
+                               reps, 3)
+            res[tag] = {"us": round(t * 1e6, 2), "gbs": round(alg / t / 1e9, 1),
+                        "frac_of_8tbs": round(alg / t / 8e12, 4)}
+        h = 1
+        want, bound = oracle.attn_decode(fmt, q[h * group:(h + 1) * group].cpu().numpy(), kc[h:h + 1].cpu().numpy(),
+                                         ks[h:h + 1].cpu().numpy().view(np.uint16), vc[h:h + 1].cpu().numpy(),
+                                         vs[h:h + 1].cpu().numpy().view(np.uint16), T)
+        ebq.qattn_decode(fmt, q, kc, ks, vc, vs, T, o, ws)
+        got = o[h * group:(h + 1) * group].cpu().numpy().astype(np.float64)
+        ok = bool((np.abs(got - want) <= bound).all())
+        res.update({"cache_bytes": cache, "algorithmic_bytes": alg,
+                    "packing_speedup": round(res["one_head_per_block"]["us"] / res["packed"]["us"], 3),
+                    "parity": "ok" if ok else "FAIL",
+                    "parity_sample": "KV head 1's six query rows against the oracle, within its fp32 allowance"})
+        out[name] = res
+        del kc, vc, ks, vs, q, o, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_mfma_ceiling(ebq):
     """The dense int8 matrix-core rate this part sustains: MFMA 32x32x32 i8 only,
     two waves per SIMD on every CU, and the shader clock it ran at (the waves'
@@ -914,6 +967,8 @@ def main():
         torch.cuda.empty_cache()
         log("trellis encoder")
         extra["trellis_encoder_512x5120"] = bench_trellis_encoder(ebq, 3)
+        log("decode attention 64K")
+        extra["decode_attention_64k_gqa6"] = bench_decode_attention(ebq, 20)
         log("ternary 1024x1024")
         extra["ternary_1024x1024_latency"] = bench_small_ternary(ebq, 50)
         log("prefill")

@@ -85,6 +85,10 @@ def load(path: str = LIB_PATH):
         "qgemv_grouped_run_static": (ctypes.c_int, [P, P]),
         "qtrellis_decode_i8": (ctypes.c_int, [W, i32, P, P, P]),
         "qtrellis_encode_workspace_bytes": (i64, [i32, i32, i32]),
+        "qkv_row_bytes": (i64, [i32]),
+        "qkv_quant": (ctypes.c_int, [i32, P, i64, P, P, P]),
+        "qattn_decode_workspace_bytes": (i64, [i32, i32, i32]),
+        "qattn_decode": (ctypes.c_int, [i32, P, i32, i32, i32, i32, i64, P, P, P, P, P, P, i64, P]),
         "qtrellis_encode": (ctypes.c_int, [P, i32, i32, P, P, i64, P, P, P, i32, P, i64, P]),
         "qweight_unpack_i8": (ctypes.c_int, [W, P, P, P]),
         "qgemm_i8": (ctypes.c_int, [P, P, i32, P, P, i32, i32, i32, P, P]),
@@ -318,6 +322,39 @@ def qtrellis_encode(w, out: PackedWeight, workspace, rows_per_pass: int, scales_
     _check(load().qtrellis_encode(_ptr(w), rows, cols, _ptr(scales_in), _ptr(out.codes), out.row_bytes,
                                   _ptr(out.seeds), _ptr(out.scales), _ptr(cost), rows_per_pass, _ptr(workspace),
                                   ws_bytes, _stream(stream)), "qtrellis_encode")
+    return out
+
+
+QKV_Q4, QKV_Q8, QATTN_HEAD_DIM = 4, 8, 256
+
+
+def qkv_row_bytes(fmt: int) -> int:
+    n = load().qkv_row_bytes(fmt)
+    _check(n if n < 0 else 0, "qkv_row_bytes")
+    return n
+
+
+def qkv_quant(fmt: int, x, codes, scales, stream=None):
+    """x: fp32 [..., 256] (device) -> codes uint8 [..., row bytes], scales int16 [..., 8]."""
+    rows = x.numel() // QATTN_HEAD_DIM
+    _check(load().qkv_quant(fmt, _ptr(x), rows, _ptr(codes), _ptr(scales), _stream(stream)), "qkv_quant")
+
+
+def qattn_decode_workspace_bytes(n_kv: int, group: int, T: int) -> int:
+    n = load().qattn_decode_workspace_bytes(n_kv, group, T)
+    _check(n if n < 0 else 0, "qattn_decode_workspace_bytes")
+    return n
+
+
+def qattn_decode(fmt: int, q, kcodes, kscales, vcodes, vscales, T: int, out, workspace, heads_per_block=None,
+                 stream=None):
+    """q [n_kv * group][256] fp32; caches [n_kv][t_cap][...] (device tensors)."""
+    n_kv, t_cap = kcodes.shape[0], kcodes.shape[1]
+    group = q.shape[0] // n_kv
+    hpb = group if heads_per_block is None else heads_per_block
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().qattn_decode(fmt, _ptr(q), n_kv, group, hpb, T, t_cap, _ptr(kcodes), _ptr(kscales), _ptr(vcodes),
+                               _ptr(vscales), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)), "qattn_decode")
     return out
 
 

@@ -14,7 +14,15 @@ using namespace qk;
 namespace {
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
-inline hipStream_t S(void* s) { return (hipStream_t)s; }
+// The caller's stream for a launch.  Launch failures are read back with
+// hipGetLastError right after each launch, and HIP keeps the last error of any
+// earlier runtime call on the thread (the caller's own, or another library's)
+// until it is read, so a stale one is cleared here first rather than reported
+// as this call's failure.
+inline hipStream_t S(void* s) {
+  (void)hipGetLastError();
+  return (hipStream_t)s;
+}
 inline int hip_rc(hipError_t e) { return e == hipSuccess ? QERR_OK : QERR_HIP; }
 
 int check_weight(const qweight_t* w) {
@@ -453,6 +461,43 @@ int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw
   if (!aligned(wq, 4) || !aligned(dw, 4)) return QERR_ALIGNMENT;
   const GemvItem it = make_item(w, nullptr, nullptr, nullptr, nullptr, nullptr);
   return hip_rc(launch_trellis_decode(it, oblock, wq, dw, S(stream)));
+}
+
+int64_t qkv_row_bytes(int32_t fmt) {
+  if (fmt == QKV_Q8) return QATTN_HEAD_DIM;
+  if (fmt == QKV_Q4) return QATTN_HEAD_DIM / 2;
+  return QERR_UNSUPPORTED_FMT;
+}
+
+int qkv_quant(int32_t fmt, const float* x, int64_t rows, void* codes, uint16_t* scales, void* stream) {
+  if (fmt != QKV_Q8 && fmt != QKV_Q4) return QERR_UNSUPPORTED_FMT;
+  if (rows < 0) return QERR_INVALID_ARG;
+  if (rows == 0) return QERR_OK;
+  if (!x || !codes || !scales) return QERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return QERR_ALIGNMENT;
+  if (rows >= ((int64_t)1 << 40) / QATTN_HEAD_DIM) return QERR_SHAPE;
+  return hip_rc(launch_kv_quant(fmt, x, rows, (uint8_t*)codes, scales, S(stream)));
+}
+
+int64_t qattn_decode_workspace_bytes(int32_t n_kv, int32_t group, int32_t T) {
+  if (n_kv < 1 || group < 1 || group > 8 || T < 1) return QERR_INVALID_ARG;
+  return attn_workspace_bytes(n_kv, group, T);
+}
+
+int qattn_decode(int32_t fmt, const float* q, int32_t n_kv, int32_t group, int32_t heads_per_block, int32_t T,
+                 int64_t t_cap, const void* kcodes, const uint16_t* kscales, const void* vcodes,
+                 const uint16_t* vscales, float* out, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (fmt != QKV_Q8 && fmt != QKV_Q4) return QERR_UNSUPPORTED_FMT;
+  if (n_kv < 1 || group < 1 || group > 8 || (heads_per_block != 1 && heads_per_block != group))
+    return QERR_INVALID_ARG;
+  if (T < 1 || t_cap < T || n_kv > 65535 / group) return QERR_SHAPE;
+  if (!q || !kcodes || !kscales || !vcodes || !vscales || !out || !workspace) return QERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kcodes, 16) || !aligned(vcodes, 16) || !aligned(kscales, 2) ||
+      !aligned(vscales, 2) || !aligned(out, 4) || !aligned(workspace, 16))
+    return QERR_ALIGNMENT;
+  if (workspace_bytes < attn_workspace_bytes(n_kv, group, T)) return QERR_BUFFER;
+  return hip_rc(launch_attn_decode(fmt, q, n_kv, group, heads_per_block, T, t_cap, kcodes, kscales, vcodes, vscales,
+                                   out, workspace, S(stream)));
 }
 
 int64_t qtrellis_encode_workspace_bytes(int32_t rows, int32_t cols, int32_t rows_per_pass) {

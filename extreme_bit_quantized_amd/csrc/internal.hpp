@@ -208,6 +208,12 @@ QK_DECL_TG(3)
 QK_DECL_TG(4)
 #undef QK_DECL_TG
 hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, float* dw, hipStream_t s);
+// KV cache and decode attention (attn.hip).
+int64_t attn_workspace_bytes(int n_kv, int group, int T);
+hipError_t launch_kv_quant(int fmt, const float* x, int64_t rows, uint8_t* codes, uint16_t* scales, hipStream_t s);
+hipError_t launch_attn_decode(int fmt, const float* q, int n_kv, int group, int heads_per_block, int T,
+                              int64_t t_cap, const void* kc, const uint16_t* ks, const void* vc,
+                              const uint16_t* vs, float* out, void* ws, hipStream_t s);
 // Trellis encoder (encode.hip): workspace bytes and the launch sequence.
 int64_t encode_workspace_bytes(int rows, int cols, int rows_per_pass);
 hipError_t launch_trellis_encode(const float* w, int rows, int cols, const uint16_t* scales_in, uint8_t* codes,

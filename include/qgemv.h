@@ -327,6 +327,51 @@ int qtrellis_encode(const float* w, int32_t rows, int32_t cols, const uint16_t* 
                     int64_t row_bytes, uint16_t* seeds, uint16_t* scales, float* cost, int32_t rows_per_pass,
                     void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ---- KV cache and decode attention ------------------------------------------------------- */
+
+/* KV cache formats: the cache grows with the context, and holding it in 4 or
+ * 8 bits decides how long a context fits ([P1] "12G 的账本要这么算").  Rows of
+ * D = QATTN_HEAD_DIM values (one token of one KV head) in 32-value blocks
+ * with an fp16 scale each:
+ *   QKV_Q8: d = amax / 127, codes c = clamp(rint(x * id), -127, 127) int8;
+ *   QKV_Q4: d = amax / 7,   codes c = clamp(rint(x * id), -7, 7) stored as the
+ *           nibble c + 8 (byte j of a block: value 2j low, value 2j + 1 high);
+ * fp32 with r = 1 / d, id = r if finite else 0, ties to even; the stored scale
+ * is fp16(d) (round to nearest even) and the cached value c * fp16(d). */
+#define QKV_Q4 4
+#define QKV_Q8 8
+#define QATTN_HEAD_DIM 256
+
+/* Bytes of one cached row of QATTN_HEAD_DIM values: 256 (Q8) or 128 (Q4);
+ * <0 for an unknown format. */
+int64_t qkv_row_bytes(int32_t fmt);
+/* Quantize rows x [rows][QATTN_HEAD_DIM] fp32 (device, 16-byte aligned, finite)
+ * into codes [rows][qkv_row_bytes] (16-byte aligned) and fp16 scales
+ * [rows][QATTN_HEAD_DIM / 32] (device).  Bit-exact to the rule above. */
+int qkv_quant(int32_t fmt, const float* x, int64_t rows, void* codes, uint16_t* scales, void* stream);
+
+/* Decode attention of one new token over a cached context, with the query
+ * heads grouped per KV head (grouped-query attention, 6 query heads per KV
+ * head in the pages' model, [P1] "把非标准格式塞进 llama.cpp，难在哪"):
+ * query row i = h * group + g attends over tokens 0 .. T-1 of KV head h,
+ *   s_t = (q_i . k_t) / sqrt(QATTN_HEAD_DIM),  p_t = exp(s_t - max s),
+ *   out_i = sum_t p_t v_t / sum_t p_t,
+ * k_t, v_t the cached values, fp32 arithmetic.  heads_per_block query rows of
+ * a KV head share each read of the cache: group (the pages' packing of the six
+ * heads into one block) or 1 (each row reads the cache on its own, for
+ * comparison).  Inputs (device): q [n_kv * group][QATTN_HEAD_DIM] fp32;
+ * kcodes, vcodes [n_kv][t_cap][qkv_row_bytes] (16-byte aligned); kscales,
+ * vscales [n_kv][t_cap][QATTN_HEAD_DIM / 32] fp16.  Output out
+ * [n_kv * group][QATTN_HEAD_DIM] fp32.  1 <= group <= 8, 1 <= T <= t_cap.
+ * Workspace (device, 16-byte aligned) of qattn_decode_workspace_bytes: the
+ * per-chunk partial sums (256 tokens a chunk).  Accuracy: each output within
+ * the fp32 error allowance of the same sums in any order (score dot products,
+ * exponentials, sums over tokens); deterministic. */
+int64_t qattn_decode_workspace_bytes(int32_t n_kv, int32_t group, int32_t T);
+int qattn_decode(int32_t fmt, const float* q, int32_t n_kv, int32_t group, int32_t heads_per_block, int32_t T,
+                 int64_t t_cap, const void* kcodes, const uint16_t* kscales, const void* vcodes,
+                 const uint16_t* vscales, float* out, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* ---- prefill: trellis decode to int8 and the int8 MFMA GEMM --------------------------- */
 
 /* Decode TRELLIS2 weights to int8 for the GEMM.  The codebook is computed at

@@ -718,12 +718,17 @@ int qref_kv_dequant(int fmt, const uint8_t* codes, const uint16_t* scales, int64
  *   out_i = sum_t p_t v_t / sum_t p_t,
  * with k_t, v_t the cached (dequantized) values; all in fp64.  Cache layout
  * codes [n_kv][t_cap][row bytes], scales [n_kv][t_cap][D/32].
- * bound (may be NULL) gets, per output, an error allowance for an fp32
- * computation of the same sums in any order (with u = 2^-24):
+ * bound (may be NULL) gets, per output, an error allowance (first order, a
+ * factor 2 of slack) for an fp32 computation that sums each score over its
+ * 32-value blocks and then over the D/32 blocks, and sums over tokens in
+ * chunks of at most 256 tokens whose results are then summed in turn
+ * (flash-decoding order), with u = 2^-24:
  *   sum_t p_t (e_t + 4u + u |s_t - max s|) (|v_t| + |out|) / sum p
- *   + 2 (T + D) u sum_t p_t |v_t| / sum p,   e_t = 2 D u sum_d |q_d k_td| / sqrt(D),
- * the score, exponential and summation errors (e_t bounds a D-term fp32 dot
- * product with a factor 2 of slack). */
+ *   + 2 (256 + ceil(T / 256) + D / 32) u sum_t p_t |v_t| / sum p,
+ *   e_t = 2 (32 + D / 32 + 8) u sum_d |q_d k_td| / sqrt(D):
+ * the score error e_t moves the token's weight by that relative amount, the
+ * exponential and the max subtraction add 4u + u |s_t - max s|, and the
+ * token sums add the last term. */
 int qref_attn_decode(int fmt, const float* q, int n_kv, int G, int D, int T, int64_t t_cap, const uint8_t* kc,
                      const uint16_t* ks, const uint8_t* vc, const uint16_t* vs, double* out, double* bound) {
   const int64_t rb = qref_kv_row_bytes(fmt, D);
@@ -737,8 +742,11 @@ int qref_attn_decode(int fmt, const float* q, int n_kv, int G, int D, int T, int
     double* V = (double*)malloc(sizeof(double) * (size_t)T * D);
     double* s = (double*)malloc(sizeof(double) * (size_t)T);
     double* e = (double*)malloc(sizeof(double) * (size_t)T);
-    if (!K || !V || !s || !e) {
-      free(K); free(V); free(s); free(e);
+    double* acc_v = (double*)malloc(sizeof(double) * 3 * (size_t)D);
+    double* abs_v = acc_v ? acc_v + D : NULL;
+    double* err_v = acc_v ? acc_v + 2 * D : NULL;
+    if (!K || !V || !s || !e || !acc_v) {
+      free(K); free(V); free(s); free(e); free(acc_v);
       err |= 1;
       continue;
     }
@@ -754,32 +762,32 @@ int qref_attn_decode(int fmt, const float* q, int n_kv, int G, int D, int T, int
           aabs += fabs((double)qi[d] * K[(size_t)t * D + d]);
         }
         s[t] = acc * isd;
-        e[t] = 2.0 * D * u * aabs * isd;
+        e[t] = 2.0 * (32 + D / 32 + 8) * u * aabs * isd;
         if (s[t] > m) m = s[t];
       }
       double L = 0.0;
-      for (int t = 0; t < T; ++t) L += exp(s[t] - m);
+      for (int t = 0; t < T; ++t) {
+        e[t] += 4.0 * u + u * fabs(s[t] - m);  /* the token's relative weight error */
+        s[t] = exp(s[t] - m);                   /* from here on s holds p */
+        L += s[t];
+      }
       double* o = out + ((size_t)h * G + g) * D;
       double* bo = bound ? bound + ((size_t)h * G + g) * D : NULL;
-      for (int d = 0; d < D; ++d) {
-        double acc = 0.0, aabs = 0.0;
-        for (int t = 0; t < T; ++t) {
-          const double p = exp(s[t] - m);
-          acc += p * V[(size_t)t * D + d];
-          aabs += p * fabs(V[(size_t)t * D + d]);
+      for (int d = 0; d < D; ++d) acc_v[d] = abs_v[d] = err_v[d] = 0.0;
+      for (int t = 0; t < T; ++t)
+        for (int d = 0; d < D; ++d) {
+          acc_v[d] += s[t] * V[(size_t)t * D + d];
+          abs_v[d] += s[t] * fabs(V[(size_t)t * D + d]);
         }
-        o[d] = acc / L;
-        if (bo) {
-          double b = 0.0;
-          for (int t = 0; t < T; ++t) {
-            const double p = exp(s[t] - m);
-            b += p * (e[t] + 4.0 * u + u * fabs(s[t] - m)) * (fabs(V[(size_t)t * D + d]) + fabs(o[d]));
-          }
-          bo[d] = b / L + 2.0 * (T + D) * u * aabs / L;
-        }
+      for (int d = 0; d < D; ++d) o[d] = acc_v[d] / L;
+      if (bo) {
+        for (int t = 0; t < T; ++t)
+          for (int d = 0; d < D; ++d) err_v[d] += s[t] * e[t] * (fabs(V[(size_t)t * D + d]) + fabs(o[d]));
+        const double chain = 256.0 + (double)((T + 255) / 256) + D / 32;
+        for (int d = 0; d < D; ++d) bo[d] = err_v[d] / L + 2.0 * chain * u * abs_v[d] / L;
       }
     }
-    free(K); free(V); free(s); free(e);
+    free(K); free(V); free(s); free(e); free(acc_v);
   }
   return err ? -2 : 0;
 }

@@ -335,3 +335,30 @@ def test_trellis_encode_validation_without_gpu(ebq):
     assert enc(w=A + 2) == -4 and enc(codes=A + 8) == -4 and enc(seeds=A + 1) == -4
     assert enc(sc=A + 8) == -4 and enc(si=A + 1) == -4 and enc(cost=A + 2) == -4 and enc(ws=A + 128) == -4
     assert enc(wsb=need - 1) == -6
+
+
+def test_attention_validation_without_gpu(ebq):
+    L = ebq.load()
+    A = 1 << 20
+    assert L.qkv_row_bytes(8) == 256 and L.qkv_row_bytes(4) == 128 and L.qkv_row_bytes(5) == -2
+    assert L.qkv_quant(5, A, 4, A, A, None) == -2
+    assert L.qkv_quant(8, A, 0, A, A, None) == 0
+    assert L.qkv_quant(8, A, -1, A, A, None) == -1
+    assert L.qkv_quant(8, None, 4, A, A, None) == -1
+    assert L.qkv_quant(8, A + 4, 4, A, A, None) == -4
+    assert L.qkv_quant(4, A, 4, A + 8, A, None) == -4
+    # partial sums of 256-token chunks: [rows][chunks][256 values + max + sum] fp32
+    assert L.qattn_decode_workspace_bytes(4, 6, 65536) == 24 * 256 * 258 * 4
+    assert L.qattn_decode_workspace_bytes(4, 9, 100) == -1
+    need = L.qattn_decode_workspace_bytes(2, 6, 300)
+
+    def att(fmt=8, q=A, n_kv=2, group=6, hpb=6, T=300, t_cap=512, kc=A, ks=A, vc=A, vs=A, out=A, ws=A, wsb=need):
+        return L.qattn_decode(fmt, q, n_kv, group, hpb, T, t_cap, kc, ks, vc, vs, out, ws, wsb, None)
+
+    assert att(fmt=5) == -2
+    assert att(group=0) == -1 and att(group=9, hpb=9) == -1
+    assert att(hpb=3) == -1 and att(hpb=1, T=0) == -3
+    assert att(T=0) == -3 and att(t_cap=299) == -3
+    assert att(q=None) == -1 and att(kc=None) == -1 and att(vs=None) == -1 and att(ws=None) == -1
+    assert att(q=A + 4) == -4 and att(kc=A + 8) == -4 and att(ks=A + 1) == -4 and att(out=A + 2) == -4
+    assert att(wsb=need - 1) == -6
