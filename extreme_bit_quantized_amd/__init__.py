@@ -27,6 +27,8 @@ class QError(RuntimeError):
     def __init__(self, code: int, func: str):
         self.code = code
         msg = _lib.qstrerror(code).decode() if _lib is not None else "?"
+        if code == -5 and _lib is not None:
+            msg += ": " + _lib.qhip_error_name().decode()
         super().__init__("%s failed: %s (%s)" % (func, QERR.get(code, code), msg))
 
 
@@ -56,6 +58,11 @@ def load(path: str = LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
+    # torch first: it carries its own copy of the HIP runtime under the same
+    # soname as the system one the library links against.  Loaded in this order
+    # the library binds to torch's copy and both share one runtime; loaded the
+    # other way round, the library's launches failed with hipErrorNoDevice.
+    import torch  # noqa: F401
     if not os.path.exists(path):
         raise ImportError("libqgemv.so is not built at %s; run `python -m extreme_bit_quantized_amd.build`" % path)
     lib = ctypes.CDLL(path)
@@ -63,6 +70,7 @@ def load(path: str = LIB_PATH):
     W = ctypes.POINTER(qweight_t)
     sig = {
         "qstrerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "qhip_error_name": (ctypes.c_char_p, []),
         "qfmt_scale_block": (i32, [i32]),
         "qfmt_packed_row_bytes": (i64, [i32, i32]),
         "qfmt_row_bytes": (i64, [i32, i32]),

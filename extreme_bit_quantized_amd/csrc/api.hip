@@ -23,7 +23,14 @@ inline hipStream_t S(void* s) {
   (void)hipGetLastError();
   return (hipStream_t)s;
 }
-inline int hip_rc(hipError_t e) { return e == hipSuccess ? QERR_OK : QERR_HIP; }
+// The HIP error behind the calling thread's last QERR_HIP (qhip_error_name).
+thread_local hipError_t t_last_hip = hipSuccess;
+
+inline int hip_rc(hipError_t e) {
+  if (e == hipSuccess) return QERR_OK;
+  t_last_hip = e;
+  return QERR_HIP;
+}
 
 int check_weight(const qweight_t* w) {
   if (!w) return QERR_INVALID_ARG;
@@ -181,6 +188,8 @@ int resident_workgroups(const void* kernel, int threads) {
 }  // namespace qk
 
 extern "C" {
+
+const char* qhip_error_name(void) { return hipGetErrorName(t_last_hip); }
 
 const char* qstrerror(int err) {
   switch (err) {

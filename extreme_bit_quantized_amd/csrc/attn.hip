@@ -16,14 +16,17 @@
 //
 // Chunk kernel (256 threads, chunk of C = 256 tokens, D = 256):
 //   1. q rows times 1/16 (= 1/sqrt(D), exact) into LDS;
-//   2. scores: thread = token; per 32-block the fp32 dot of q with the codes,
-//      times the block scale, summed over the blocks;
+//   2. scores on the matrix cores (v_mfma_f32_16x16x32_f16, 16 rows x 16 tokens
+//      x one 32-value block): the codes are exact in fp16, each q row is scaled
+//      by a power of two and split into fp16 high and low halves (two MFMAs,
+//      about 22 bits of q); each block's result times the token's block scale,
+//      summed over the blocks in fp32, the row scale taken off;
 //   3. softmax statistics of the chunk: m = max s, p = exp(s - m), l = sum p;
 //   4. p V: thread = 4 dimensions, wave = 64 tokens; per token and row the
 //      weight p * (scale of the lane's block) times the codes; the four
 //      waves' sums added in LDS.
 // The merge kernel: M = max over chunks of m, out = sum_c exp(m_c - M) O_c /
-// sum_c exp(m_c - M) l_c.
+// sum_c exp(m_c - M) l_c, each row's chunks split over 16 waves.
 #include <hip/hip_fp16.h>
 
 #include "internal.hpp"
@@ -112,6 +115,44 @@ struct KvGeo {
   static constexpr int row_bytes = FMT == QKV_Q8 ? kD : kD / 2;
 };
 
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+// Two codes as exact fp16 values: the halves 0x6400 | u (= 1024 + u, u the
+// unsigned code byte) minus 1024 + the code offset (packed fp16 add; every
+// value is an integer below 2048, so all of it is exact).
+__device__ __forceinline__ uint32_t halves_minus(uint32_t magic_pair, float off) {
+  const h2_t v = __builtin_bit_cast(h2_t, magic_pair) - (h2_t){(_Float16)(1024.0f + off), (_Float16)(1024.0f + off)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// The 8 codes of a lane's share of a 32-value block as an fp16 MFMA operand.
+// Q8: 8 bytes (w0, w1), code c as the byte c + 128; Q4: 4 bytes (w0), low nibble
+// first, code c as the nibble c + 8.
+template <int FMT>
+__device__ __forceinline__ h8_t codes_f16(uint32_t w0, uint32_t w1) {
+  uint32_t o[4];
+  if constexpr (FMT == QKV_Q8) {
+    const uint32_t a = w0 ^ 0x80808080u, b = w1 ^ 0x80808080u;
+    o[0] = halves_minus(__builtin_amdgcn_perm(0x64646464u, a, 0x04010400u), 128.0f);
+    o[1] = halves_minus(__builtin_amdgcn_perm(0x64646464u, a, 0x04030402u), 128.0f);
+    o[2] = halves_minus(__builtin_amdgcn_perm(0x64646464u, b, 0x04010400u), 128.0f);
+    o[3] = halves_minus(__builtin_amdgcn_perm(0x64646464u, b, 0x04030402u), 128.0f);
+  } else {
+    const uint32_t lo = w0 & 0x0F0F0F0Fu, hi = (w0 >> 4) & 0x0F0F0F0Fu;  // values 2j, 2j + 1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // bytes: value 2j, 0x64, value 2j + 1, 0x64
+      const uint32_t pair = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u + 0x00010001u * j) | 0x64006400u;
+      o[j] = halves_minus(pair, 8.0f);
+    }
+  }
+  h8_t r;
+  __builtin_memcpy(&r, o, 16);
+  return r;
+}
+
 // One (KV head, chunk of tokens) for G query rows.  Grid (chunks, row groups);
 // row group y covers query rows y G .. y G + G - 1 of KV head y G / group.
 // part: [row group][chunk][G][kD + 2] floats (O, then m and l).
@@ -121,9 +162,18 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
                                                     const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
                                                     float* __restrict__ part) {
   constexpr int RB = KvGeo<FMT>::row_bytes;
-  __shared__ __attribute__((aligned(16))) float qs[G][kD];
+  // LDS: the q rows, their MFMA operands and the scores live only until the
+  // softmax, so the waves' p V sums reuse that space at the end.
+  constexpr int QS_BYTES = G * kD * 4, QA_BYTES = (kD / 32) * 2 * 64 * 16, SC_BYTES = G * kChunk * 4;
+  constexpr int RED_BYTES = 4 * G * kD * 4;
+  constexpr int PH1 = QS_BYTES + QA_BYTES + SC_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t ubuf[PH1 > RED_BYTES ? PH1 : RED_BYTES];
+  float(&qs)[G][kD] = *reinterpret_cast<float(*)[G][kD]>(ubuf);
+  uint4(&qa)[kD / 32][2][64] = *reinterpret_cast<uint4(*)[kD / 32][2][64]>(ubuf + QS_BYTES);
+  float(&Sc)[G][kChunk] = *reinterpret_cast<float(*)[G][kChunk]>(ubuf + QS_BYTES + QA_BYTES);
+  float(&red)[4][G][kD] = *reinterpret_cast<float(*)[4][G][kD]>(ubuf);
+  __shared__ float rsc[G][2];                                  // row scale 2^e and 2^-e
   __shared__ __attribute__((aligned(16))) float P[kChunk][8];  // weights of each token, rows padded to 8
-  __shared__ float red[4][G][kD];
   __shared__ float stat[2][4][G];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -137,46 +187,89 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   for (int g = 0; g < G; ++g) qs[g][tid] = q[(int64_t)(row0 + g) * kD + tid] * 0.0625f;
   __syncthreads();
 
-  // ---- scores: thread = token ----
-  float s[G];
+  // ---- scores on the matrix cores ----
+  // Row scales: 2^(15 - E) with max |q row| in [2^(E-1), 2^E), so the scaled row
+  // peaks in [2^14, 2^15): its fp16 high halves stay finite and its fp16 low
+  // halves (the rest) stay normal down to 2^-17 of the peak.
 #pragma unroll
-  for (int g = 0; g < G; ++g) s[g] = -__builtin_inff();
-  if (tid < nt) {
-    const int64_t t = (int64_t)h * t_cap + t0 + tid;
-    const uint8_t* krow = kc + t * RB;
-    const uint16_t* srow = ks + t * (kD / 32);
+  for (int g = 0; g < G; ++g) {
+    float v = fabsf(qs[g][tid]);
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = 0.0f;
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (lane == 0) stat[0][wv][g] = v;
+  }
+  __syncthreads();
+  if (tid < G) {
+    const float mxq = fmaxf(fmaxf(stat[0][0][tid], stat[0][1][tid]), fmaxf(stat[0][2][tid], stat[0][3][tid]));
+    int e = 0;
+    if (mxq > 0.0f) (void)frexpf(mxq, &e);
+    rsc[tid][0] = ldexpf(1.0f, 15 - e);
+    rsc[tid][1] = ldexpf(1.0f, e - 15);
+  }
+  __syncthreads();
+  // A operands (lane: row lane % 16, values 8 (lane / 16) .. + 7 of each block),
+  // q = hi + lo in fp16 after the row scale, rows G .. 15 zero; built once into
+  // LDS, each thread two (block, lane) slots.
+  for (int slot = tid; slot < (kD / 32) * 64; slot += 256) {
+    const int b = slot >> 6, ln = slot & 63, r = ln & 15, jq = ln >> 4;
+    h8_t hi8, lo8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = r < G ? qs[r < G ? r : 0][32 * b + 8 * jq + j] * rsc[r < G ? r : 0][0] : 0.0f;
+      const _Float16 hi = (_Float16)x;
+      hi8[j] = hi;
+      lo8[j] = (_Float16)(x - (float)hi);
+    }
+    qa[b][0][ln] = __builtin_bit_cast(uint4, hi8);
+    qa[b][1][ln] = __builtin_bit_cast(uint4, lo8);
+  }
+  __syncthreads();
+  {
+    const int r = lane & 15, jq = lane >> 4;
+    // wave wv: four 16-token tiles; lane: token lane % 16 of the tile, values
+    // 8 (lane / 16) .. + 7 of each block (the B operand)
 #pragma unroll 1
-    for (int b = 0; b < kD / 32; ++b) {
-      constexpr int WORDS = FMT == QKV_Q8 ? 8 : 4;
-      uint32_t w[WORDS];
-      if constexpr (FMT == QKV_Q8) {
-        const uint4 a = *(const uint4*)(krow + 32 * b), c = *(const uint4*)(krow + 32 * b + 16);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
-      } else {
-        const uint4 a = *(const uint4*)(krow + 16 * b);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    for (int tt = 0; tt < 4; ++tt) {
+      const int kl = 64 * wv + 16 * tt + r;
+      const bool valid = kl < nt;
+      const int64_t t = (int64_t)h * t_cap + t0 + (valid ? kl : 0);
+      uint4 scv = make_uint4(0u, 0u, 0u, 0u);
+      if (valid) scv = *(const uint4*)(ks + t * (kD / 32));
+      const uint32_t sw[4] = {scv.x, scv.y, scv.z, scv.w};
+      f4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int b = 0; b < kD / 32; ++b) {
+        uint32_t w0 = 0u, w1 = 0u;
+        if (valid) {
+          if constexpr (FMT == QKV_Q8) {
+            const uint2 v = *(const uint2*)(kc + t * RB + 32 * b + 8 * jq);
+            w0 = v.x;
+            w1 = v.y;
+          } else {
+            w0 = *(const uint32_t*)(kc + t * RB + 16 * b + 4 * jq);
+          }
+        }
+        const h8_t kb = codes_f16<FMT>(w0, w1);
+        const h8_t qhi = __builtin_bit_cast(h8_t, qa[b][0][lane]), qlo = __builtin_bit_cast(h8_t, qa[b][1][lane]);
+        f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi, kb, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo, kb, c, 0, 0, 0);
+        const float sc = h2f((uint16_t)(sw[b >> 1] >> (16 * (b & 1))));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[i] = __builtin_fmaf(sc, c[i], sacc[i]);
       }
-      const float sc = h2f(srow[b]);
-      float acc[G];
+      // C lane: token lane % 16, rows 4 (lane / 16) + i
 #pragma unroll
-      for (int g = 0; g < G; ++g) acc[g] = 0.0f;
-      constexpr int PER = FMT == QKV_Q8 ? 4 : 8;
-#pragma unroll
-      for (int k = 0; k < WORDS; ++k) {
-        float f[8];
-        codes_f32<FMT>(w[k], f);
-#pragma unroll
-        for (int j = 0; j < PER; ++j)
-#pragma unroll
-          for (int g = 0; g < G; ++g) acc[g] = __builtin_fmaf(qs[g][32 * b + PER * k + j], f[j], acc[g]);
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * jq + i;
+        if (row < G) Sc[row][kl] = sacc[i] * rsc[row][1];
       }
-#pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = __builtin_fmaf(sc, acc[g], s[g]);
     }
   }
+  __syncthreads();
+  float s[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = tid < nt ? Sc[g][tid] : -__builtin_inff();
 
   // ---- softmax statistics of the chunk ----
   float m[G], l[G];
@@ -213,7 +306,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const int tn = nt - tb < 64 ? (nt - tb > 0 ? nt - tb : 0) : 64;
   const int blk = lane >> 3;  // the lane's 32-block
   const int64_t tbase = (int64_t)h * t_cap + t0 + tb;
-#pragma unroll 2
+#pragma unroll 8
   for (int k = 0; k < tn; ++k) {
     const int64_t t = tbase + k;
     uint32_t w;
@@ -235,7 +328,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[wv][g][4 * lane + j] = o[g][j];
+    for (int j = 0; j < 4; ++j) red[wv][g][4 * lane + j] = o[g][j];  // over qs / qa / Sc, read before a barrier
   __syncthreads();
   float* pout = part + ((int64_t)y * gridDim.x + chunk) * G * (kD + 2);
 #pragma unroll
@@ -248,36 +341,52 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   }
 }
 
-// Merge the chunks of each query row: thread = dimension.
-__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part, int G, int nchunk,
-                                                    float* __restrict__ out) {
-  __shared__ float e[1024];
-  __shared__ float mx[4];
+// Merge the chunks of each query row.  Grid (rows, kD / 64): a workgroup takes
+// 64 dimensions of one row; its 16 waves take every 16th chunk (lane =
+// dimension), then the waves' sums are added in LDS.  M = max over chunks of m,
+// out = sum_c exp(m_c - M) O_c / sum_c exp(m_c - M) l_c.
+constexpr int kMergeWaves = 16;
+
+__global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(const float* __restrict__ part, int G, int nchunk,
+                                                                 float* __restrict__ out) {
+  __shared__ float mx[kMergeWaves];
+  __shared__ float accs[kMergeWaves][64];
+  __shared__ float ls[kMergeWaves];
   const int row = blockIdx.x;  // query row = y G + g
   const int y = row / G, g = row % G;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int d = blockIdx.y * 64 + lane;
   const float* base = part + (int64_t)y * nchunk * G * (kD + 2) + g * (kD + 2);
   const int64_t cstride = (int64_t)G * (kD + 2);
   float M = -__builtin_inff();
-  for (int c = tid; c < nchunk; c += 256) M = fmaxf(M, base[c * cstride + kD]);
+  for (int c = threadIdx.x; c < nchunk; c += 64 * kMergeWaves) M = fmaxf(M, base[c * cstride + kD]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if ((tid & 63) == 0) mx[tid >> 6] = M;
+  if (lane == 0) mx[wv] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+  M = mx[0];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, mx[w]);
   float L = 0.0f, acc = 0.0f;
-  for (int c0 = 0; c0 < nchunk; c0 += 1024) {
-    const int n = nchunk - c0 < 1024 ? nchunk - c0 : 1024;
-    __syncthreads();
-    for (int c = tid; c < n; c += 256) e[c] = expf(base[(c0 + c) * cstride + kD] - M);
-    __syncthreads();
-    for (int c = 0; c < n; ++c) {
-      const float f = e[c];
-      L = __builtin_fmaf(f, base[(c0 + c) * cstride + kD + 1], L);
-      acc = __builtin_fmaf(f, base[(c0 + c) * cstride + tid], acc);
-    }
+#pragma unroll 4
+  for (int c = wv; c < nchunk; c += kMergeWaves) {
+    const float* pc = base + c * cstride;
+    const float f = expf(pc[kD] - M);
+    L = __builtin_fmaf(f, pc[kD + 1], L);
+    acc = __builtin_fmaf(f, pc[d], acc);
   }
-  out[(int64_t)row * kD + tid] = acc / L;
+  accs[wv][lane] = acc;
+  if (lane == 0) ls[wv] = L;
+  __syncthreads();
+  if (wv == 0) {
+    float a = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+      a += accs[w][lane];
+      l += ls[w];
+    }
+    out[(int64_t)row * kD + d] = a / l;
+  }
 }
 
 template <int FMT, int G>
@@ -331,7 +440,8 @@ hipError_t launch_attn_decode(int fmt, const float* q, int n_kv, int group, int 
                            : launch_chunks_g<QKV_Q4>(heads_per_block, q, n_kv, group, T, t_cap, kc, ks, vc, vs, part, s);
   if (e != hipSuccess) return e;
   const int nchunk = (T + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(k_attn_merge, dim3(n_kv * group), dim3(256), 0, s, part, heads_per_block, nchunk, out);
+  hipLaunchKernelGGL(k_attn_merge, dim3(n_kv * group, kD / 64), dim3(64 * kMergeWaves), 0, s, part, heads_per_block,
+                     nchunk, out);
   return hipGetLastError();
 }
 

@@ -50,6 +50,9 @@ extern "C" {
 
 /* Human-readable text for a QERR_* code (static storage, never NULL). */
 const char* qstrerror(int err);
+/* Name of the HIP error behind the calling thread's most recent QERR_HIP
+ * ("hipSuccess" if there was none); static storage, never NULL. */
+const char* qhip_error_name(void);
 
 /* ---- weight formats ----------------------------------------------------------- *
  * Level counts: 4 bits hold 16 levels, 2 bits 4, 1 bit only the sign ([P1]
