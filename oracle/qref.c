@@ -531,17 +531,26 @@ void qref_trellis_decode_i8(const uint8_t* packed, const uint16_t* seeds, const 
  *   d = w[i] - sc[i] * val[s]      (one fused rounding: fmaf(-sc, val, w))
  *   C_0[s] = d * d                 (fmaf(d, d, 0))
  *   C_i[s] = d * d + min_a C_{i-1}[(s >> 2) | (a << (L-2))]   (fmaf)
- * Decisions on ties: the smallest a; the last state is the smallest s of
- * minimum cost.  Writes the state path st[0..K-1] and the minimum cost. */
+ * The predecessor taken by each state: within each pair {a, a + 2} (a = 0, 1)
+ * the one of smaller cost C_{i-1}, on equal costs the one whose own incoming
+ * minimum was smaller, then the smaller a; between the two pair winners the
+ * one of smaller cost, on equal costs the winner of the pair {0, 2}.  (Where
+ * the two states of a pair have the same value, as in the trellis below whose
+ * hash ignores bit 15, a pair's order is that of the incoming minima, which
+ * lets an implementation decide a pair before it adds the branch term.)  The
+ * last state is the smallest s of minimum cost.  Writes the state path
+ * st[0..K-1] and the minimum cost. */
 int qref_viterbi(int L, const float* val, const float* w, const float* sc, int K, uint32_t* st,
                  float* cost) {
   if (L < 2 || L > 16 || K < 1) return -1;
   const uint32_t S = 1u << L, top = (uint32_t)(L - 2);
   float* prev = (float*)malloc(sizeof(float) * S);
   float* cur = (float*)malloc(sizeof(float) * S);
+  float* inprev = (float*)malloc(sizeof(float) * S);  /* incoming minimum of each state */
+  float* incur = (float*)malloc(sizeof(float) * S);
   uint8_t* dec = (uint8_t*)malloc((size_t)K * S);
-  if (!prev || !cur || !dec) {
-    free(prev); free(cur); free(dec);
+  if (!prev || !cur || !inprev || !incur || !dec) {
+    free(prev); free(cur); free(inprev); free(incur); free(dec);
     return -2;
   }
   for (int i = 0; i < K; ++i) {
@@ -549,22 +558,28 @@ int qref_viterbi(int L, const float* val, const float* w, const float* sc, int K
       float m = 0.0f;
       uint8_t best = 0;
       if (i > 0) {
-        m = prev[s >> 2];
-        for (uint32_t a = 1; a < 4; ++a) {
-          float c = prev[(s >> 2) | (a << top)];
-          if (c < m) {
-            m = c;
-            best = (uint8_t)a;
-          }
+        uint32_t p[4];
+        for (uint32_t a = 0; a < 4; ++a) p[a] = (s >> 2) | (a << top);
+        uint32_t win[2];
+        for (uint32_t a = 0; a < 2; ++a) {
+          const uint32_t x = p[a], y = p[a + 2];
+          const int take_y = prev[y] < prev[x] || (prev[y] == prev[x] && inprev[y] < inprev[x]);
+          win[a] = take_y ? a + 2 : a;
         }
+        best = (uint8_t)(prev[p[win[1]]] < prev[p[win[0]]] ? win[1] : win[0]);
+        m = prev[p[best]];
       }
       dec[(size_t)i * S + s] = best;
+      incur[s] = m;
       float d = fmaf(-sc[i], val[s], w[i]);
       cur[s] = fmaf(d, d, m);
     }
     float* t = prev;
     prev = cur;
     cur = t;
+    t = inprev;
+    inprev = incur;
+    incur = t;
   }
   uint32_t last = 0;
   for (uint32_t s = 1; s < S; ++s)
@@ -575,7 +590,7 @@ int qref_viterbi(int L, const float* val, const float* w, const float* sc, int K
     uint32_t s = st[i];
     st[i - 1] = (s >> 2) | ((uint32_t)dec[(size_t)i * S + s] << top);
   }
-  free(prev); free(cur); free(dec);
+  free(prev); free(cur); free(inprev); free(incur); free(dec);
   return 0;
 }
 

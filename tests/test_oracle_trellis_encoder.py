@@ -185,3 +185,58 @@ def test_encoder_gaussian_distortion_between_bounds():
 def test_encoder_zero_rows():
     packed, seeds, scales, cost = oracle.trellis_encode(np.zeros((2, 128), np.float32))
     assert (packed == 0).all() and (seeds == 0).all() and (scales == 0).all() and (cost == 0).all()
+
+
+def _viterbi_rule_reference(L, val, w, sc):
+    """The documented recursion and tie rules written out again in Python with
+    exact rational fused operations (each rounded once to fp32)."""
+    S, top, K = 1 << L, L - 2, len(w)
+    f32 = lambda x: round_f32(Fraction(float(np.float32(x))))  # noqa: E731
+    C = [None] * S
+    IN = [Fraction(0)] * S
+    dec = []
+    for i in range(K):
+        nC, nIN, di = [None] * S, [None] * S, [0] * S
+        for s in range(S):
+            if i == 0:
+                m, best = Fraction(0), 0
+            else:
+                p = [(s >> 2) | (a << top) for a in range(4)]
+                win = []
+                for a in range(2):
+                    x, y = p[a], p[a + 2]
+                    take_y = C[y] < C[x] or (C[y] == C[x] and IN[y] < IN[x])
+                    win.append(a + 2 if take_y else a)
+                best = win[1] if C[p[win[1]]] < C[p[win[0]]] else win[0]
+                m = C[p[best]]
+            di[s] = best
+            nIN[s] = m
+            d = round_f32(f32(w[i]) - f32(sc[i]) * f32(val[s]))
+            nC[s] = round_f32(d * d + m)
+        C, IN = nC, nIN
+        dec.append(di)
+    last = min(range(S), key=lambda s: (C[s], s))
+    st = [last]
+    for i in range(K - 1, 0, -1):
+        s = st[-1]
+        st.append((s >> 2) | (dec[i][s] << top))
+    return st[::-1], C[last]
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_viterbi_tie_rules_against_a_written_out_reference(seed):
+    """Cases built to tie: the values ignore the top state bit (as the trellis
+    hash ignores bit 15), few distinct values, and a large step that rounds
+    different incoming costs to the same cost.  The path must be the one the
+    documented rules pick."""
+    rng = np.random.default_rng(seed)
+    L = 4
+    base = rng.integers(-2, 3, 8).astype(np.float32) * np.float32(0.5)
+    val = np.concatenate([base, base])          # val[s] = val[s ^ 8]
+    w = rng.integers(-3, 4, 5).astype(np.float32) * np.float32(0.25)
+    w[2] = np.float32(3000.0)                    # d^2 ~ 1e7: costs that differ a little round together
+    sc = np.ones(5, np.float32)
+    st, cost = oracle.viterbi(L, val, w, sc)
+    want, wcost = _viterbi_rule_reference(L, val, w, sc)
+    assert [int(x) for x in st] == want
+    assert Fraction(float(cost)) == wcost
