@@ -545,9 +545,11 @@ def bench_prefill(ebq, reps):
     return out
 
 
-def bench_trellis_encoder(ebq, reps, N=512, K=5120, per=256, sample=(0, 511)):
+def bench_trellis_encoder(ebq, reps, N=512, K=5120, per=512, sample=(0, 511)):
     """Trellis encoder (Viterbi over the 2^16-state trellis) on N(0, 0.02) rows of
-    the 5120 input width, rows_per_pass = 256 (one row per compute unit).
+    the 5120 input width in one pass of 512 rows (two rows per compute unit; the
+    backtrack's time per pass does not grow with the rows, so larger passes
+    spread it thinner; the workspace holds 20 MB of choices per row).
     Parity: codes, seeds, scales and costs of the sampled rows bit-exact against
     the oracle.  Roofline: VALU issue (the recursion is plain fp32 arithmetic)."""
     import torch

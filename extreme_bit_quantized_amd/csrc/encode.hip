@@ -10,8 +10,10 @@
 // s64 * V16[hash(s)].  The recursion, fp32 with each operation rounded once:
 //   d = fma(-s64, V16[hash(s)], w_i)                       (s64 * V16 is exact)
 //   C_i[s] = fma(d, d, min_a C_{i-1}[(s >> 2) + 16384 a])   (C_{-1} = 0)
-// with the smallest a on ties, and the last state the smallest s of minimum
-// cost.  Any first state is allowed; the seed is st_0 >> 2.
+// with the predecessor chosen pairwise: within {a, a + 2} by cost, then by its
+// own incoming minimum, then the smaller a; between the two pair winners by
+// cost, then the pair {0, 2}; the last state is the smallest s of minimum cost.
+// Any first state is allowed; the seed is st_0 >> 2.
 //
 // GPU form.  The 4 states 4j .. 4j+3 share one predecessor set, so only
 //   M_i[j] = min_a C_i[j + 16384 a],   j = 0 .. 16383,
@@ -20,9 +22,11 @@
 //   C_i[j + 16384 a] = fma(d, d, M_{i-1}[(j >> 2) + 4096 a]).
 // One workgroup of 1024 threads per row holds M double-buffered in LDS
 // (128 KB); thread t owns j = 16 t .. 16 t + 15, so it reads M_{i-1} at
-// 4 t .. 4 t + 3 (+ 4096 a) as four 16-byte loads, keeps the 64 values V16[hash]
-// of its states in registers, writes its 16 new M as four 16-byte stores and
-// its 16 choices as one 32-bit word: 4 KB of choices per row and step, coalesced.
+// 4 t .. 4 t + 3 (+ 4096 a) as four 16-byte loads, keeps the 32 distinct values
+// V16[hash] of its 64 states in registers, decides each pair of states with
+// equal values on their incoming minima (one compare) before adding the branch
+// term, writes its 16 new M as four 16-byte stores and its 16 choices as one
+// 32-bit word: 4 KB of choices per row and step, coalesced.
 // The backtrack then walks each row's choices from the end, one lane per row.
 #include <type_traits>
 
@@ -87,12 +91,13 @@ __global__ __launch_bounds__(kEncThreads) void k_enc_forward(const float* __rest
   if (t < 64) wbuf[0][t] = wr[t];
   __syncthreads();
 
-  // values of this thread's 64 states s = 16 t + u + 16384 a
-  float v[16][4];
+  // values of this thread's 64 states s = 16 t + u + 16384 a; the hash ignores
+  // bit 15, so a and a + 2 share one (kept once, index a & 1)
+  float v[16][2];
 #pragma unroll
   for (int u = 0; u < 16; ++u)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < 2; ++a) {
       const uint32_t s = 16u * t + u + 16384u * a;
       v[u][a] = v32[((s * 0x9E37u) ^ (s >> 7)) & 0xFFu];
     }
@@ -125,39 +130,47 @@ __global__ __launch_bounds__(kEncThreads) void k_enc_forward(const float* __rest
     uint32_t word = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float nm[4];
+      float m[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int u = 4 * q + r;
-        float c[4];
+      for (int a = 0; a < 4; ++a) m[a] = q == 0 ? mp[a].x : q == 1 ? mp[a].y : q == 2 ? mp[a].z : mp[a].w;
+      if constexpr (LAST) {
+        // every state's cost, for the smallest state of minimum cost
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const float m = q == 0 ? mp[a].x : q == 1 ? mp[a].y : q == 2 ? mp[a].z : mp[a].w;
-          const float d = __builtin_fmaf(-sb, v[u][a], wi);
-          c[a] = __builtin_fmaf(d, d, m);
-        }
-        float best = c[0];
-        uint32_t ba = 0;
+        for (int r = 0; r < 4; ++r) {
+          const int u = 4 * q + r;
 #pragma unroll
-        for (int a = 1; a < 4; ++a) {
-          const bool lt = c[a] < best;
-          best = lt ? c[a] : best;
-          ba = lt ? (uint32_t)a : ba;
-        }
-        nm[r] = best;
-        if constexpr (LAST) {
-          const uint32_t st = 16u * t + u + 16384u * ba;
-          if (u == 0) {
-            lc = best;
-            ls = st;
-          } else {
-            take_min(lc, ls, best, st);
+          for (int a = 0; a < 4; ++a) {
+            const float d = __builtin_fmaf(-sb, v[u][a & 1], wi);
+            const float c = __builtin_fmaf(d, d, m[a]);
+            const uint32_t st = 16u * t + u + 16384u * a;
+            if (u == 0 && a == 0) {
+              lc = c;
+              ls = st;
+            } else {
+              take_min(lc, ls, c, st);
+            }
           }
-        } else {
-          word |= ba << (2 * u);
         }
+      } else {
+        // States j and j + 32768 differ only in bit 15, which the hash ignores:
+        // equal branch terms, so each pair {a, a + 2} is decided by the incoming
+        // minima (the smaller, a on equality) before the branch term is added;
+        // then the two pair winners by cost (the pair {0, 2} on equality).
+        const bool t0 = m[2] < m[0], t1 = m[3] < m[1];
+        const float mm0 = t0 ? m[2] : m[0], mm1 = t1 ? m[3] : m[1];
+        const uint32_t w0 = t0 ? 2u : 0u, w1 = t1 ? 3u : 1u;
+        float nm[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int u = 4 * q + r;
+          const float d0 = __builtin_fmaf(-sb, v[u][0], wi), d1 = __builtin_fmaf(-sb, v[u][1], wi);
+          const float c0 = __builtin_fmaf(d0, d0, mm0), c1 = __builtin_fmaf(d1, d1, mm1);
+          const bool lt = c1 < c0;
+          nm[r] = lt ? c1 : c0;
+          word |= (lt ? w1 : w0) << (2 * u);
+        }
+        *(float4*)(mo + 4 * q) = make_float4(nm[0], nm[1], nm[2], nm[3]);
       }
-      if constexpr (!LAST) *(float4*)(mo + 4 * q) = make_float4(nm[0], nm[1], nm[2], nm[3]);
     }
     if constexpr (!LAST) drow[(int64_t)i * kEncThreads] = word;
   };
@@ -190,6 +203,8 @@ __global__ __launch_bounds__(kEncThreads) void k_enc_forward(const float* __rest
 // Backtrack, one lane per row: from the last state, s_{i-1} = (s_i >> 2) +
 // 16384 A_{i-1}[s_i >> 2]; symbols c_i = s_i & 3 packed four to a byte, first
 // symbol in the top bits; seed = s_0 >> 2; padding bytes of the row zeroed.
+// Each step waits for the word the previous step chose (a dependent load per
+// weight): the kernel's time does not depend on how many rows a pass holds.
 __global__ __launch_bounds__(64) void k_enc_backtrack(int cols, int row0, int nrows,
                                                       const uint32_t* __restrict__ dec,
                                                       const uint2* __restrict__ fin, uint8_t* __restrict__ codes,
