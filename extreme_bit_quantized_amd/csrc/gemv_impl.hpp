@@ -590,10 +590,120 @@ __device__ __forceinline__ void sub_tern(const uint32_t (&T)[52], const uint32_t
   for (int b = 0; b < NB; ++b) y[b] = __builtin_fmaf(s, acc[b], y[b]);
 }
 
-// Trellis: `prev` holds the last 16 bits of seed||bytes before the sub-chunk.
+// ---- trellis codebook lookups ---------------------------------------------------------------------
+// The int8 codebook sits in LDS once per lane of a half-wave, in two
+// pre-shifted forms: entry h of copy c = lane % 32 is the dword v << 24 at
+// byte h * 256 + 4 c and the dword v << 16 at byte h * 256 + 128 + 4 c
+// (v = the entry's byte).  The 32 lanes of a half-wave then read 32 different
+// banks whatever their hashes (one shared 256-byte table costs about 1.7x as
+// much per read: two of its dwords share each of the 32 banks), and reads of
+// different widths and offsets return v alone in byte 0, 1, 2 or 3:
+//   u8 at +3: v;  u16 at +2: v << 8;  b32 at +128: v << 16;  b32 at +0: v << 24.
+// The table starts at LDS address 0, so a lookup's address register is the
+// address itself.
+constexpr int kTrellisTableBytes = 65536;
+
+// Lookup state of one wave: the table and 16 standing address registers, each
+// holding 4 (lane % 32) in byte 0 and zeros in bytes 2 and 3.  A lookup only
+// rewrites byte 1 with the hash, so the address costs two instructions.
+struct TrellisCtx {
+  const uint8_t* tbl;
+  uint32_t ad[16];
+};
+
+__device__ __forceinline__ void trellis_ctx_init(TrellisCtx& c, const uint8_t* tbl) {
+  c.tbl = tbl;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c.ad[i] = (threadIdx.x & 31u) << 2;
+}
+
+// Fills the replicated table from the 256 codebook entries (every thread of
+// the workgroup takes part; a barrier must follow before any lookup).
+__device__ __forceinline__ void trellis_table_fill(uint8_t* tbl, const V8Table& v8t) {
+  for (int i = threadIdx.x; i < 256 * 32; i += blockDim.x) {
+    const int h = i >> 5, c = i & 31;
+    const uint32_t v = (uint8_t)v8t.v[h];
+    *(uint32_t*)(tbl + h * 256 + c * 4) = v << 24;
+    *(uint32_t*)(tbl + h * 256 + 128 + c * 4) = v << 16;
+  }
+}
+
+// h = ((st * 0x9E37) ^ (st >> 7)) & 0xFF of the 16-bit states of the four
+// weights of one code byte, written into byte 1 of their address registers
+// ad[0..3]: the low byte of st * 0x9E37 depends only on lo8 = st & 0xFF, and
+// (st >> 7) & 0xFF is mid8 = bits 7..14 of st.  Weight k's lo8 is byte M of
+// lo[k] and its mid8 byte M of mid[k] (SDWA byte selects; each multiply writes
+// the low 8 bits of lo8 * 0x9E37 into byte 1, each XOR folds mid8 in, both
+// leaving the other bytes as they are).  A VALU read of a register right after
+// a partial (SDWA dst_sel) write of it sees the unmerged result on this part,
+// so the four multiplies come first, then the XORs, then one wait state before
+// anything reads the addresses.
+template <int M>
+__device__ __forceinline__ void trellis_addr4(uint32_t& a0, uint32_t& a1, uint32_t& a2, uint32_t& a3,
+                                              const uint32_t (&lo)[4], const uint32_t (&mid)[4], uint32_t mul) {
+#define QK_TR_MUL(D, L, B) \
+  "v_mul_u32_u24_sdwa " D ", " L ", %12 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_" #B " src1_sel:DWORD\n\t"
+#define QK_TR_XOR(D, X, B) \
+  "v_xor_b32_sdwa " D ", " D ", " X " dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:BYTE_" #B "\n\t"
+#define QK_TR_ADDR4(B)                                                                                  \
+  asm(QK_TR_MUL("%0", "%4", B) QK_TR_MUL("%1", "%5", B) QK_TR_MUL("%2", "%6", B) QK_TR_MUL("%3", "%7", B) \
+      QK_TR_XOR("%0", "%8", B) QK_TR_XOR("%1", "%9", B) QK_TR_XOR("%2", "%10", B) QK_TR_XOR("%3", "%11", B) \
+      "s_nop 0"                                                                                          \
+      : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)                                                           \
+      : "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3]), "v"(mid[0]), "v"(mid[1]), "v"(mid[2]), "v"(mid[3]), "s"(mul))
+  if constexpr (M == 0) QK_TR_ADDR4(0);
+  else if constexpr (M == 1) QK_TR_ADDR4(1);
+  else if constexpr (M == 2) QK_TR_ADDR4(2);
+  else QK_TR_ADDR4(3);
+#undef QK_TR_ADDR4
+#undef QK_TR_XOR
+#undef QK_TR_MUL
+}
+
+typedef const uint8_t __attribute__((address_space(3))) l_u8;
+typedef const uint16_t __attribute__((address_space(3))) l_u16;
+typedef const uint32_t __attribute__((address_space(3))) l_u32;
+
+// Codebook values of the 16 weights of one code word W (4 code bytes, first
+// byte in stream order in the low byte), as 4 dwords of int8 lined up with the
+// activation dwords: p[O + g] holds weights 4g .. 4g + 3.  `be` holds the
+// previous code bytes big-endian in its low 16 bits and is left holding W's.
+// With BE = W byte-reversed, (be : BE) >> s exposes the stream shifted by s
+// bits: weight 4g + j has the 16-bit state ((B[g-2] B[g-1] B[g]) >> (6 - 2j)),
+// whose lo8 is byte 3 - g of the stream shifted by 6 - 2j and whose mid8 is
+// byte 3 - g of the stream shifted by 13 - 2j.
+template <int O>
+__device__ __forceinline__ void trellis_word(TrellisCtx& c, uint32_t W, uint32_t& be, uint32_t (&p)[8], uint32_t mul) {
+  const uint32_t BE = __builtin_amdgcn_perm(W, W, 0x00010203u);
+  uint32_t lo[4], mid[4];
+  lo[0] = BE;
+#pragma unroll
+  for (int k = 1; k < 4; ++k) lo[k] = __builtin_amdgcn_alignbit(be, BE, 2 * k);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) mid[k] = __builtin_amdgcn_alignbit(be, BE, 2 * k + 7);
+  l_u8* t = (l_u8*)c.tbl;
+  static_for(std::make_integer_sequence<int, 4>{}, [&](auto gc) {
+    constexpr int g = decltype(gc)::value, m = 3 - g;
+    trellis_addr4<m>(c.ad[4 * g], c.ad[4 * g + 1], c.ad[4 * g + 2], c.ad[4 * g + 3], lo, mid, mul);
+    // weight 4g + j uses shift 2k = 6 - 2j; each read lands its value alone in
+    // byte j (written out: the compiler would narrow the ORs to 16 bits and mask)
+    const uint32_t r0 = t[c.ad[4 * g + 3] + 3];
+    const uint32_t r1 = *(l_u16*)(t + c.ad[4 * g + 2] + 2);
+    const uint32_t r2 = *(l_u32*)(t + c.ad[4 * g + 1] + 128);
+    const uint32_t r3 = *(l_u32*)(t + c.ad[4 * g + 0]);
+    uint32_t w;
+    asm("v_or3_b32 %0, %1, %2, %3\n\tv_or_b32 %0, %0, %4" : "=&v"(w) : "v"(r0), "v"(r1), "v"(r2), "v"(r3));
+    p[O + g] = w;
+  });
+  be = BE;
+}
+
+// Trellis: `prev` holds the last 16 bits of seed||bytes before the sub-chunk
+// (big-endian, higher bits ignored).
 template <int NB, int SUB, bool WI>
 __device__ __forceinline__ void sub_trellis(const uint32_t (&T)[32], const uint32_t (&S)[4], const ActSub (&AS)[NB],
-                                            uint32_t& prev, const int8_t* v8, float (&y)[NB], int32_t* Iout) {
+                                            uint32_t& prev, TrellisCtx& tc, float (&y)[NB], int32_t* Iout) {
+  const uint32_t mul = sgpr_const(0x9E37u);
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {  // 64-weight scale blocks
     float acc[NB];
@@ -603,23 +713,8 @@ __device__ __forceinline__ void sub_trellis(const uint32_t (&T)[32], const uint3
     for (int h2 = 0; h2 < 2; ++h2) {
       const int kb = sb * 2 + h2;
       uint32_t p[8];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint32_t W = T[SUB * 16 + kb * 2 + w];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const uint32_t w24 = (prev << 8) | ((W >> (8 * q4)) & 0xFFu);
-          uint32_t L = 0;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t st = (w24 >> (6 - 2 * jj)) & 0xFFFFu;
-            const uint32_t h = ((st * 0x9E37u) ^ (st >> 7)) & 0xFFu;
-            L |= ((uint32_t)(uint8_t)v8[h]) << (8 * jj);
-          }
-          prev = w24 & 0xFFFFu;
-          p[w * 4 + q4] = L;
-        }
-      }
+      trellis_word<0>(tc, T[SUB * 16 + kb * 2], prev, p, mul);
+      trellis_word<4>(tc, T[SUB * 16 + kb * 2 + 1], prev, p, mul);
       blk_any<NB, WI, 2>(kb, acc, AS, p, Iout, SUB * 8 + kb);
     }
     const int si = SUB * 4 + sb;
@@ -681,13 +776,13 @@ __device__ __forceinline__ void load_act_all(ActSub (&dst)[NB], const ActG& AG, 
 template <int FMT, int NB, int SUB, bool WI, bool PIPE = false>
 __device__ __forceinline__ void sub_compute(const uint32_t (&T)[Seg<FMT>::CH * 4], const uint32_t (&S)[Seg<FMT>::SPS / 2],
                                             const ActSub (&AS)[NB], KPipe<NB>& kp, const ActK& AK, int kb0, int kbv,
-                                            int kb_after, uint32_t& prev, const int8_t* v8, float (&y)[NB],
+                                            int kb_after, uint32_t& prev, TrellisCtx& tc, float (&y)[NB],
                                             int32_t* Iseg) {
   if constexpr (FMT == QFMT_SIGN1) sub_sign1<NB, SUB, WI, PIPE>(T, S, AS, kp, AK, kb0, kbv, kb_after, y, Iseg);
   else if constexpr (FMT == QFMT_INT2) sub_int2<NB, SUB, WI, PIPE>(T, S, AS, kp, AK, kb0, kbv, kb_after, y, Iseg);
   else if constexpr (FMT == QFMT_INT4) sub_int4<NB, WI>(T, S, AS, y, Iseg);
   else if constexpr (FMT == QFMT_TERN_B3) sub_tern<NB, SUB, WI>(T, S, AS, y, Iseg);
-  else sub_trellis<NB, SUB, WI>(T, S, AS, prev, v8, y, Iseg);
+  else sub_trellis<NB, SUB, WI>(T, S, AS, prev, tc, y, Iseg);
 }
 
 // Result scale applied once per row after accumulation.
@@ -726,7 +821,7 @@ constexpr int kTileCachePolicy = 2;  // nt
 // and the tail segment if (nseg % nwk) == wk.  lds: this wave's region.
 template <int FMT, int NB, bool WI>
 __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, int nwk, uint8_t* lds,
-                                          const int8_t* v8, float (&y)[NB], int32_t* Ibase, int sk = 0,
+                                          const uint8_t* v8, float (&y)[NB], int32_t* Ibase, int sk = 0,
                                           int sn = 1) {
   constexpr int CH = Seg<FMT>::CH;
   constexpr int SEGK = Seg<FMT>::K;
@@ -756,6 +851,8 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
   AK.qs = gptr<k_i32*>(it.qsum);
   AK.kbs = K >> 5;
   KPipe<NB> kp;
+  TrellisCtx tc;
+  if constexpr (FMT == QFMT_TRELLIS2) trellis_ctx_init(tc, v8);
 
   // This lane's scales for segment sg: slot `lane` of the tile's group sg (rows
   // past the end read zero padding).
@@ -890,7 +987,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
         // without state carried between sub-chunks and without the scalar pipeline)
         if (sn == 1 || SUB % sn == sk)
           sub_compute<FMT, NB, SUB, WI, KACT>(T, S, act[SUB], kp, AK, seg * (SEGK / 32) + SUB * 8, 8, kb_after, prev,
-                                              v8, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
+                                              tc, y, Irow ? Irow + seg * (SEGK / 32) : nullptr);
         if constexpr (!KACT) {
           // kept after the sub-chunk's compute: the new values take its registers
           __builtin_amdgcn_sched_barrier(0);
@@ -946,7 +1043,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
         const int nkb = (SUB + 1 < NSUB) ? seg * (SEGK / 32) + (SUB + 1) * 8
                                          : (more_seg ? nx : seg) * (SEGK / 32);
         load_act_all<FMT, NB, false>(nxt, AG, nkb, 8);
-        sub_compute<FMT, NB, SUB, WI>(T, S, cur, kp, AK, seg * (SEGK / 32) + SUB * 8, 8, 0, prev, v8, y,
+        sub_compute<FMT, NB, SUB, WI>(T, S, cur, kp, AK, seg * (SEGK / 32) + SUB * 8, 8, 0, prev, tc, y,
                                       Irow ? Irow + seg * (SEGK / 32) : nullptr);
 #pragma unroll
         for (int b = 0; b < NB; ++b) cur[b] = nxt[b];
@@ -983,7 +1080,7 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
 #pragma unroll
         for (int b = 0; b < NB; ++b) yt[b] = 0.0f;
         // the test hook must not write past the row's last block: bounded copy
-        sub_compute<FMT, NB, SUB, WI>(T, St, at, kp, AK, kb0 + SUB * 8, kbv, 0, prev, v8, yt,
+        sub_compute<FMT, NB, SUB, WI>(T, St, at, kp, AK, kb0 + SUB * 8, kbv, 0, prev, tc, yt,
                                       WI && Irow ? Ib : nullptr);
         if (WI && Irow) {
 #pragma unroll
@@ -1004,13 +1101,17 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
 // order, so results are deterministic.
 template <int FMT, int NB, bool WI>
 __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float gain, int32_t* Iout) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * Seg<FMT>::CH * 1024];
-  __shared__ float red[4][NB][64];
-  __shared__ int8_t v8[256];
+  // One LDS array, so that the trellis table is at address 0: [table][tiles][partial sums]
+  constexpr int TBL = FMT == QFMT_TRELLIS2 ? kTrellisTableBytes : 0;
+  constexpr int TILES = 4 * Seg<FMT>::CH * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TBL + TILES + 4 * NB * 64 * 4];
+  uint8_t* const v8 = smem;
+  uint8_t* const lds = smem + TBL;
+  float (*const red)[NB][64] = (float (*)[NB][64])(smem + TBL + TILES);
   // wave-uniform: lets the compiler keep everything derived from it in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if constexpr (FMT == QFMT_TRELLIS2) {
-    v8[threadIdx.x] = v8t.v[threadIdx.x];
+    trellis_table_fill(v8, v8t);
     __syncthreads();
   }
   const int row0 = blockIdx.x * 64;
@@ -1043,12 +1144,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvItem it, V8Table v8t, float ga
 
 // Waves per workgroup of the grouped kernel for batch NB and format FMT: every
 // wave a CU holds at the kernel's register count (at most 16), so one
-// workgroup fills a CU; the ternary tile (13 KB of LDS per wave) allows 12.
+// workgroup fills a CU; the ternary tile (13 KB of LDS per wave) allows 12,
+// the trellis tiles beside the 64 KB lookup table 11.
 // The kernel's launch bound follows from it, and the build fails if that bound
 // forces register spills.
 constexpr int grouped_wpg(int nb, int fmt) {
-  constexpr int t[8][5] = {{12, 16, 16, 16, 16}, {8, 16, 12, 16, 12}, {12, 16, 16, 16, 12}, {12, 12, 16, 12, 12},
-                           {8, 12, 12, 12, 12},  {8, 12, 12, 12, 8},  {8, 8, 12, 12, 8},   {8, 8, 8, 8, 8}};
+  constexpr int t[8][5] = {{12, 16, 16, 16, 11}, {8, 16, 12, 16, 11}, {12, 16, 16, 16, 11}, {12, 12, 16, 12, 11},
+                           {8, 12, 12, 12, 11},  {8, 12, 12, 12, 8},  {8, 8, 12, 12, 8},   {8, 8, 8, 8, 8}};
   return t[nb - 1][fmt - 1];
 }
 
@@ -1068,18 +1170,19 @@ __global__ __launch_bounds__(64 * grouped_wpg(NB, ONLY)) void k_gemv_grouped(con
   static_assert(ONLY >= 1 && ONLY <= 5, "one format per launch");
   constexpr int P = grouped_wpg(NB, ONLY);
   constexpr int WAVE_LDS = Seg<ONLY>::CH * 1024;
-  static_assert(P * WAVE_LDS + 256 + 4 <= 160 * 1024, "LDS per workgroup");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[P * WAVE_LDS];
-  __shared__ int8_t v8[256];
-  __shared__ int next_k;
+  // One LDS array, so that the trellis table is at address 0: [table][tiles][tile counter]
+  constexpr int TBL = ONLY == QFMT_TRELLIS2 ? kTrellisTableBytes : 0;
+  static_assert(TBL + P * WAVE_LDS + 16 <= 160 * 1024, "LDS per workgroup");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TBL + P * WAVE_LDS + 16];
+  uint8_t* const v8 = smem;
+  uint8_t* const lds = smem + TBL;
+  int& next_k = *(int*)(smem + TBL + P * WAVE_LDS);
   const PlanHeader* hp = (const PlanHeader*)plan;
   const GemvItem* items = (const GemvItem*)(plan + hp->items_off);
   const GemvTile* tiles = (const GemvTile*)(plan + hp->tiles_off);
   const int nwk = hp->n_workers;
   const int32_t* wb = (const int32_t*)(plan + hp->workers_off) + ONLY * (nwk + 1);
-  if constexpr (ONLY == QFMT_TRELLIS2) {
-    if (threadIdx.x < 256) v8[threadIdx.x] = v8t.v[threadIdx.x];
-  }
+  if constexpr (ONLY == QFMT_TRELLIS2) trellis_table_fill(v8, v8t);
   if (threadIdx.x == 0) next_k = 0;
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
