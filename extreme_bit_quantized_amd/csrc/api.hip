@@ -501,8 +501,8 @@ int qattn_decode(int32_t fmt, const float* q, int32_t n_kv, int32_t group, int32
     return QERR_INVALID_ARG;
   if (T < 1 || t_cap < T || n_kv > 65535 / group) return QERR_SHAPE;
   if (!q || !kcodes || !kscales || !vcodes || !vscales || !out || !workspace) return QERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(kcodes, 16) || !aligned(vcodes, 16) || !aligned(kscales, 2) ||
-      !aligned(vscales, 2) || !aligned(out, 4) || !aligned(workspace, 16))
+  if (!aligned(q, 16) || !aligned(kcodes, 16) || !aligned(vcodes, 16) || !aligned(kscales, 16) ||
+      !aligned(vscales, 16) || !aligned(out, 4) || !aligned(workspace, 16))
     return QERR_ALIGNMENT;
   if (workspace_bytes < attn_workspace_bytes(n_kv, group, T)) return QERR_BUFFER;
   return hip_rc(launch_attn_decode(fmt, q, n_kv, group, heads_per_block, T, t_cap, kcodes, kscales, vcodes, vscales,

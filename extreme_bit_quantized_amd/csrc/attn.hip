@@ -157,7 +157,7 @@ __device__ __forceinline__ h8_t codes_f16(uint32_t w0, uint32_t w1) {
 // row group y covers query rows y G .. y G + G - 1 of KV head y G / group.
 // part: [row group][chunk][G][kD + 2] floats (O, then m and l).
 template <int FMT, int G>
-__global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q, int group, int T, int64_t t_cap,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_attn_chunk(const float* __restrict__ q, int group, int T, int64_t t_cap,
                                                     const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
                                                     const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
                                                     float* __restrict__ part) {
@@ -183,6 +183,19 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const int t0 = chunk * kChunk;
   const int nt = T - t0 < kChunk ? T - t0 : kChunk;
 
+  // Scales issued first, so their latency overlaps the q set-up: this thread's
+  // token of the chunk for the V scales (staged through LDS for the p V pass),
+  // and the K scales of the lane's token in each of its wave's four tiles.
+  const int r16 = lane & 15, jq = lane >> 4;
+  uint4 vsr = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < nt) vsr = *(const uint4*)(vs + ((int64_t)h * t_cap + t0 + tid) * (kD / 32));
+  uint4 ksr[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int kl = 64 * wv + 16 * tt + r16;
+    ksr[tt] = make_uint4(0u, 0u, 0u, 0u);
+    if (kl < nt) ksr[tt] = *(const uint4*)(ks + ((int64_t)h * t_cap + t0 + kl) * (kD / 32));
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) qs[g][tid] = q[(int64_t)(row0 + g) * kD + tid] * 0.0625f;
   __syncthreads();
@@ -225,48 +238,62 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   }
   __syncthreads();
   {
-    const int r = lane & 15, jq = lane >> 4;
-    // wave wv: four 16-token tiles; lane: token lane % 16 of the tile, values
-    // 8 (lane / 16) .. + 7 of each block (the B operand)
+    // wave wv: four 16-token tiles, two at a time (16 code loads in flight per
+    // lane); lane: token lane % 16 of the tile, values 8 (lane / 16) .. + 7 of
+    // each block (the B operand)
 #pragma unroll 1
-    for (int tt = 0; tt < 4; ++tt) {
-      const int kl = 64 * wv + 16 * tt + r;
-      const bool valid = kl < nt;
-      const int64_t t = (int64_t)h * t_cap + t0 + (valid ? kl : 0);
-      uint4 scv = make_uint4(0u, 0u, 0u, 0u);
-      if (valid) scv = *(const uint4*)(ks + t * (kD / 32));
-      const uint32_t sw[4] = {scv.x, scv.y, scv.z, scv.w};
-      f4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int tp = 0; tp < 2; ++tp) {
+      uint32_t kw[2][8][2];
+      // tokens past the end read token 0 of the chunk (no branch per load);
+      // their scores are dropped below
 #pragma unroll
-      for (int b = 0; b < kD / 32; ++b) {
-        uint32_t w0 = 0u, w1 = 0u;
-        if (valid) {
+      for (int i = 0; i < 2; ++i) {
+        const int kl = 64 * wv + 16 * (2 * tp + i) + r16;
+        const int64_t t = (int64_t)h * t_cap + t0 + (kl < nt ? kl : 0);
+#pragma unroll
+        for (int b = 0; b < kD / 32; ++b) {
           if constexpr (FMT == QKV_Q8) {
             const uint2 v = *(const uint2*)(kc + t * RB + 32 * b + 8 * jq);
-            w0 = v.x;
-            w1 = v.y;
+            kw[i][b][0] = v.x;
+            kw[i][b][1] = v.y;
           } else {
-            w0 = *(const uint32_t*)(kc + t * RB + 16 * b + 4 * jq);
+            kw[i][b][0] = *(const uint32_t*)(kc + t * RB + 16 * b + 4 * jq);
+            kw[i][b][1] = 0u;
           }
         }
-        const h8_t kb = codes_f16<FMT>(w0, w1);
-        const h8_t qhi = __builtin_bit_cast(h8_t, qa[b][0][lane]), qlo = __builtin_bit_cast(h8_t, qa[b][1][lane]);
-        f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi, kb, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo, kb, c, 0, 0, 0);
-        const float sc = h2f((uint16_t)(sw[b >> 1] >> (16 * (b & 1))));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[i] = __builtin_fmaf(sc, c[i], sacc[i]);
       }
-      // C lane: token lane % 16, rows 4 (lane / 16) + i
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * jq + i;
-        if (row < G) Sc[row][kl] = sacc[i] * rsc[row][1];
+      for (int i = 0; i < 2; ++i) {
+        const int tt = 2 * tp + i;
+        const int kl = 64 * wv + 16 * tt + r16;
+        const uint4 kq = tp == 0 ? ksr[i] : ksr[2 + i];  // (no run-time index into the array)
+        const uint32_t sw[4] = {kq.x, kq.y, kq.z, kq.w};
+        f4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int b = 0; b < kD / 32; ++b) {
+          const h8_t kb = codes_f16<FMT>(kw[i][b][0], kw[i][b][1]);
+          const h8_t qhi = __builtin_bit_cast(h8_t, qa[b][0][lane]), qlo = __builtin_bit_cast(h8_t, qa[b][1][lane]);
+          f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi, kb, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo, kb, c, 0, 0, 0);
+          const float sc = h2f((uint16_t)(sw[b >> 1] >> (16 * (b & 1))));
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) sacc[i4] = __builtin_fmaf(sc, c[i4], sacc[i4]);
+        }
+        // C lane: token lane % 16, rows 4 (lane / 16) + i
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int row = 4 * jq + i4;
+          if (row < G) Sc[row][kl] = sacc[i4] * rsc[row][1];
+        }
       }
     }
   }
   __syncthreads();
+  // V scales of the chunk's tokens (zero past the end) over the q operands,
+  // which the scores no longer need
+  uint16_t(&vsc)[kChunk][kD / 32] = *reinterpret_cast<uint16_t(*)[kChunk][kD / 32]>(ubuf + QS_BYTES);
+  *(uint4*)&vsc[tid][0] = vsr;
   float s[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) s[g] = tid < nt ? Sc[g][tid] : -__builtin_inff();
@@ -306,25 +333,37 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const float* __restrict__ q,
   const int tn = nt - tb < 64 ? (nt - tb > 0 ? nt - tb : 0) : 64;
   const int blk = lane >> 3;  // the lane's 32-block
   const int64_t tbase = (int64_t)h * t_cap + t0 + tb;
-#pragma unroll 8
-  for (int k = 0; k < tn; ++k) {
-    const int64_t t = tbase + k;
-    uint32_t w;
-    if constexpr (FMT == QKV_Q8) w = *(const uint32_t*)(vc + t * RB + 4 * lane);
-    else w = *(const uint16_t*)(vc + t * RB + 2 * lane);
-    const float sc = h2f(vs[t * (kD / 32) + blk]);
-    float f[8];
-    codes_f32<FMT>(w, f);
-    const float4 pa = *(const float4*)&P[tb + k][0];
-    const float4 pb = *(const float4*)&P[tb + k][4];
-    const float pp[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+  // 16 tokens' codes in flight per lane; tokens past the end read the chunk's
+  // last token (no branch per load) and add 0: their p and scale are 0 and
+  // every code is finite
+  const int64_t tlast = (int64_t)h * t_cap + t0 + nt - 1;
+#pragma unroll 1
+  for (int k0 = 0; k0 < 64; k0 += 16) {
+    uint32_t w[16];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float wgt = pp[g] * sc;
+    for (int i = 0; i < 16; ++i) {
+      const int64_t t = k0 + i < tn ? tbase + k0 + i : tlast;
+      if constexpr (FMT == QKV_Q8) w[i] = *(const uint32_t*)(vc + t * RB + 4 * lane);
+      else w[i] = *(const uint16_t*)(vc + t * RB + 2 * lane);
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[g][j] = __builtin_fmaf(wgt, f[j], o[g][j]);
+    for (int i = 0; i < 16; ++i) {
+      const int k = k0 + i;
+      const float sc = h2f(vsc[tb + k][blk]);
+      float f[8];
+      codes_f32<FMT>(w[i], f);
+      const float4 pa = *(const float4*)&P[tb + k][0];
+      const float4 pb = *(const float4*)&P[tb + k][4];
+      const float pp[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float wgt = pp[g] * sc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[g][j] = __builtin_fmaf(wgt, f[j], o[g][j]);
+      }
     }
   }
+  __syncthreads();  // every wave's scale reads are done before the sums overwrite them
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll

@@ -364,7 +364,8 @@ int qkv_quant(int32_t fmt, const float* x, int64_t rows, void* codes, uint16_t* 
  * heads into one block) or 1 (each row reads the cache on its own, for
  * comparison).  Inputs (device): q [n_kv * group][QATTN_HEAD_DIM] fp32;
  * kcodes, vcodes [n_kv][t_cap][qkv_row_bytes] (16-byte aligned); kscales,
- * vscales [n_kv][t_cap][QATTN_HEAD_DIM / 32] fp16.  Output out
+ * vscales [n_kv][t_cap][QATTN_HEAD_DIM / 32] fp16 (16-byte aligned: each
+ * token's scales are read as one 16-byte row).  Output out
  * [n_kv * group][QATTN_HEAD_DIM] fp32.  1 <= group <= 8, 1 <= T <= t_cap.
  * Workspace (device, 16-byte aligned) of qattn_decode_workspace_bytes: the
  * per-chunk partial sums (256 tokens a chunk).  Accuracy: each output within

@@ -361,4 +361,5 @@ def test_attention_validation_without_gpu(ebq):
     assert att(T=0) == -3 and att(t_cap=299) == -3
     assert att(q=None) == -1 and att(kc=None) == -1 and att(vs=None) == -1 and att(ws=None) == -1
     assert att(q=A + 4) == -4 and att(kc=A + 8) == -4 and att(ks=A + 1) == -4 and att(out=A + 2) == -4
+    assert att(ks=A + 2) == -4 and att(vs=A + 8) == -4  # scale rows are read 16 bytes at a time
     assert att(wsb=need - 1) == -6
