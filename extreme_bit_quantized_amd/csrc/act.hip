@@ -219,19 +219,83 @@ hipError_t launch_act_quant_batch(const qact_job_t* jobs, int n, hipStream_t s) 
 }
 
 
-// One 256-block per 16 lanes, four per wave, in a grid-stride loop: lane t of
-// a quarter holds elements 16t .. 16t+15, so stages h = 1, 2, 4, 8 run inside
-// the lane and h = 16, 32, 64, 128 pair lanes t ^ 1, t ^ 2, t ^ 4, t ^ 8.
-// (Every stage adds and subtracts the same pairs in the same order as the
-// definition, so the rounding is the same: a cross stage forms
-// fma(own, +-1, partner's), which is the partner's value plus or minus its
-// own, rounded once.)  Then every element is multiplied by 1/16, as the
-// definition does (the product rounds only where it is subnormal, and must then
-// round the same way), and Q8 per qblock over WIDTH = qblock / 16 lanes (q
-// from the low byte of 1.5 * 2^23 + v * (1 / d), which rounds to the nearest
-// integer with ties to even, |q| <= 127 without a clamp) and one 16-byte store
-// per lane.  Each lane's block advances by a fixed quotient and remainder per
-// turn of the grid (no division per block).
+// The rotation of one 256-block by its 16-lane group: lane t holds elements
+// 16t .. 16t+15 (xk = the lane's 16 inputs, k0 their first feature index), so
+// stages h = 1, 2, 4, 8 run inside the lane and h = 16, 32, 64, 128 pair lanes
+// t ^ 1, t ^ 2, t ^ 4, t ^ 8.  (Every stage adds and subtracts the same pairs
+// in the same order as the definition, so the rounding is the same: a cross
+// stage forms fma(own, +-1, partner's), which is the partner's value plus or
+// minus its own, rounded once.)  Then every element is multiplied by 1/16, as
+// the definition does (the product rounds only where it is subnormal, and must
+// then round the same way).  Lanes whose group has no block (ok false) compute
+// on zeros: the cross-lane steps need the whole wave.
+__device__ __forceinline__ void rotate256(const float* __restrict__ xk, const uint32_t* __restrict__ sign_bits,
+                                          int k0, int t, bool ok, float u[16]) {
+  if (ok) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 v = *(const f32x4*)(xk + 4 * c);
+      u[4 * c] = v.x;
+      u[4 * c + 1] = v.y;
+      u[4 * c + 2] = v.z;
+      u[4 * c + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = 0.0f;
+  }
+  const uint32_t sw = ok ? sign_bits[k0 >> 5] >> (k0 & 31) : 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)  // sign bit i of the word onto element i
+    u[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, u[i]) ^ ((sw << (31 - i)) & 0x80000000u));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i & h) == 0) {
+        const float a = u[i], b = u[i + h];
+        u[i] = a + b;
+        u[i + h] = a - b;
+      }
+  // lower element: u_i + u_{i+h}; upper element: u_i - u_{i+h} (u_i the lower partner's)
+  auto cross = [&](auto m_c) {
+    constexpr int m = decltype(m_c)::value;
+    const float sg = (t & m) != 0 ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = __builtin_fmaf(u[i], sg, xlane<m>(u[i]));
+  };
+  cross(std::integral_constant<int, 1>{});
+  cross(std::integral_constant<int, 2>{});
+  cross(std::integral_constant<int, 4>{});
+  cross(std::integral_constant<int, 8>{});
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u[i] *= 0.0625f;
+}
+
+// Q8 codes of 16 values (u * id rounded through the 1.5 * 2^23 sum: its low
+// byte is q in two's complement, ties to even, |q| <= 127 without a clamp when
+// |u| <= amax) packed into four words; returns the sum of the 16 codes.
+__device__ __forceinline__ int q8_pack16(const float u[16], float id, uint32_t pk[4]) {
+  uint32_t bsum = 0;  // 16 * 0x4B400000 + sum of q, mod 2^32
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b[j] = __builtin_bit_cast(uint32_t, u[4 * w + j] * id + 12582912.0f);
+      bsum += b[j];
+    }
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // q0 | q1 << 8
+    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);  // q2 | q3 << 8
+    pk[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+  return (int)(bsum - 16u * 0x4B400000u);
+}
+
+// One 256-block per 16 lanes, four per wave, in a grid-stride loop: the
+// rotation (rotate256), then Q8 per qblock over WIDTH = qblock / 16 lanes and
+// one 16-byte store per lane.  Each lane's block advances by a fixed quotient
+// and remainder per turn of the grid (no division per block).
 template <int WIDTH>
 __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict__ x, int K, int nblocks,
                                                         const uint32_t* __restrict__ sign_bits,
@@ -249,46 +313,7 @@ __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict_
     const bool ok = blk < nblocks;  // the whole 16-lane group agrees
     const int64_t off = (int64_t)tok * K + kb * 256 + 16 * t;
     float u[16];
-    if (ok) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 v = *(const f32x4*)(x + off + 4 * c);
-        u[4 * c] = v.x;
-        u[4 * c + 1] = v.y;
-        u[4 * c + 2] = v.z;
-        u[4 * c + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) u[i] = 0.0f;
-    }
-    const int k0 = kb * 256 + 16 * t;
-    const uint32_t sw = ok ? sign_bits[k0 >> 5] >> (k0 & 31) : 0u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)  // sign bit i of the word onto element i
-      u[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, u[i]) ^ ((sw << (31 - i)) & 0x80000000u));
-#pragma unroll
-    for (int h = 1; h < 16; h <<= 1)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if ((i & h) == 0) {
-          const float a = u[i], b = u[i + h];
-          u[i] = a + b;
-          u[i + h] = a - b;
-        }
-    // lower element: u_i + u_{i+h}; upper element: u_i - u_{i+h} (u_i the lower partner's)
-    auto cross = [&](auto m_c) {
-      constexpr int m = decltype(m_c)::value;
-      const float sg = (t & m) != 0 ? -1.0f : 1.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) u[i] = __builtin_fmaf(u[i], sg, xlane<m>(u[i]));
-    };
-    cross(std::integral_constant<int, 1>{});
-    cross(std::integral_constant<int, 2>{});
-    cross(std::integral_constant<int, 4>{});
-    cross(std::integral_constant<int, 8>{});
-#pragma unroll
-    for (int i = 0; i < 16; ++i) u[i] *= 0.0625f;
+    rotate256(x + off, sign_bits, kb * 256 + 16 * t, t, ok, u);
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(u[i]));
@@ -301,20 +326,7 @@ __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict_
     const float dd = am / 127.0f;
     const float id = q8_inv(dd);
     uint32_t pk[4];
-    uint32_t bsum = 0;  // sum of the 16 biased values: 16 * 0x4B400000 + sum of q, mod 2^32
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t b[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        b[j] = __builtin_bit_cast(uint32_t, u[4 * w + j] * id + 12582912.0f);
-        bsum += b[j];
-      }
-      const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // q0 | q1 << 8
-      const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);  // q2 | q3 << 8
-      pk[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    }
-    int sum = (int)(bsum - 16u * 0x4B400000u);
+    int sum = q8_pack16(u, id, pk);
     sum += xlane_i<1>(sum);
     if constexpr (WIDTH > 2) {
       sum += xlane_i<2>(sum);
@@ -345,8 +357,78 @@ __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict_
   }
 }
 
+
+// Q8 with one scale per token row (qblock = K): one workgroup per row, its 16
+// groups of 16 lanes rotating blocks g, g + 16, ... (up to NB each, kept in
+// registers); the row's amax and code sum are reduced over the group's lanes,
+// the wave and then the workgroup (LDS).
+template <int NB>
+__global__ __launch_bounds__(256) void k_hadamard_quant_row(const float* __restrict__ x, int K,
+                                                            const uint32_t* __restrict__ sign_bits,
+                                                            int8_t* __restrict__ q, float* __restrict__ d,
+                                                            int32_t* __restrict__ qsum) {
+  __shared__ float s_am[4];
+  __shared__ int s_sum[4];
+  const int tok = blockIdx.x;
+  const int lane = threadIdx.x & 63, t = lane & 15, g = threadIdx.x >> 4, wave = threadIdx.x >> 6;
+  const int nkb = K / 256;
+  const float* const xr = x + (int64_t)tok * K;
+  float u[NB][16];
+  float am = 0.0f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int kb = g + 16 * b;
+    const bool ok = kb < nkb;  // the whole 16-lane group agrees
+    rotate256(xr + kb * 256 + 16 * t, sign_bits, kb * 256 + 16 * t, t, ok, u[b]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(u[b][i]));
+  }
+  for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+  if (lane == 0) s_am[wave] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(s_am[0], s_am[1]), fmaxf(s_am[2], s_am[3]));
+  const float dd = am / 127.0f;
+  const float id = q8_inv(dd);
+  const bool vec = ((uintptr_t)q & 15) == 0;
+  int sum = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int kb = g + 16 * b;
+    uint32_t pk[4];
+    const int sb = q8_pack16(u[b], id, pk);
+    if (kb < nkb) {
+      sum += sb;
+      int8_t* o = q + (int64_t)tok * K + kb * 256 + 16 * t;
+      if (vec) {
+        *(uint4*)o = uint4{pk[0], pk[1], pk[2], pk[3]};
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ((uint32_t*)o)[w] = pk[w];
+      }
+    }
+  }
+  for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m);
+  if (lane == 0) s_sum[wave] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    d[tok] = dd;
+    qsum[tok] = s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
+  }
+}
+
 hipError_t launch_hadamard_quant(const float* x, int B, int K, const uint32_t* sign_bits, int qblock, int8_t* q,
                                  float* d, int32_t* qsum, hipStream_t s) {
+  if (qblock == K && qblock != 32 && qblock != 256) {  // one scale per row
+    const int nb = (K / 256 + 15) / 16;  // blocks per 16-lane group
+    const dim3 grid(B), block(256);
+    if (nb <= 1) hipLaunchKernelGGL(k_hadamard_quant_row<1>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
+    else if (nb <= 2) hipLaunchKernelGGL(k_hadamard_quant_row<2>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
+    else if (nb <= 4) hipLaunchKernelGGL(k_hadamard_quant_row<4>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
+    else if (nb <= 6) hipLaunchKernelGGL(k_hadamard_quant_row<6>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
+    else if (nb <= 8) hipLaunchKernelGGL(k_hadamard_quant_row<8>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   const int64_t nblocks = (int64_t)B * (K / 256);
   if (nblocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int grid = (int)std::min<int64_t>((nblocks + 15) / 16, 8192);

@@ -316,9 +316,10 @@ int qact_quant_batch(const qact_job_t* jobs, int32_t n, void* stream) {
 int qact_hadamard_quant_i8(const float* x, int32_t B, int32_t K, const uint32_t* sign_bits, int32_t qblock,
                            int8_t* q, float* d, int32_t* qsum, void* stream) {
   if (B < 0 || K < 0) return QERR_INVALID_ARG;
-  if (qblock != 32 && qblock != 256) return QERR_INVALID_ARG;
+  if (qblock != 32 && qblock != 256 && qblock != K) return QERR_INVALID_ARG;
   if (B == 0) return QERR_OK;
   if (K == 0 || K % 256 != 0) return QERR_SHAPE;
+  if (qblock == K && K > 32768) return QERR_SHAPE;  // one scale per row: the row fits one workgroup
   if (!x || !q || !d || !qsum || !sign_bits) return QERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(q, 4) || !aligned(d, 4) || !aligned(qsum, 4) || !aligned(sign_bits, 4))
     return QERR_ALIGNMENT;
@@ -463,8 +464,9 @@ int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw
   int rc = check_weight(w);
   if (rc) return rc;
   if (w->fmt != QFMT_TRELLIS2) return QERR_UNSUPPORTED_FMT;
-  if (oblock != 32 && oblock != 256) return QERR_INVALID_ARG;
+  if (oblock != 32 && oblock != 256 && oblock != w->cols) return QERR_INVALID_ARG;
   if (w->cols % 256 != 0) return QERR_SHAPE;
+  if (oblock == w->cols && w->cols > 32768) return QERR_SHAPE;  // one scale per row: the row fits one workgroup
   if (w->rows == 0) return QERR_OK;
   if (!wq || !dw) return QERR_INVALID_ARG;
   if (!aligned(wq, 4) || !aligned(dw, 4)) return QERR_ALIGNMENT;
@@ -545,7 +547,7 @@ int qweight_unpack_i8(const qweight_t* w, int8_t* wq, float* dw, void* stream) {
 int qgemm_i8(const int8_t* xq, const float* dx, int32_t M, const int8_t* wq, const float* dw, int32_t N, int32_t K,
              int32_t kblock, float* y, void* stream) {
   if (M < 0 || N < 0 || K < 0) return QERR_INVALID_ARG;
-  if (kblock != 32 && kblock != 256) return QERR_INVALID_ARG;
+  if (kblock != 32 && kblock != 256 && kblock != K) return QERR_INVALID_ARG;
   if (M == 0 || N == 0) return QERR_OK;
   if (K == 0 || K % kblock != 0 || K % 64 != 0) return QERR_SHAPE;
   if (!xq || !dx || !wq || !dw || !y) return QERR_INVALID_ARG;

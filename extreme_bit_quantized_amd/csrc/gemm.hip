@@ -558,6 +558,24 @@ void k_gemm_i8_p256(const int8_t* __restrict__ xq, const float* __restrict__ dx,
 
 hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* wq, const float* dw, int N, int K,
                        int kblock, float* y, hipStream_t s) {
+  // One scale per row of each operand (kblock = K): the plain int8 kernel.  The
+  // wave tile is 128 x 128 unless narrower tiles take fewer rounds of
+  // workgroups over the compute units for the same work (rounds x tile width).
+  if (kblock == K && kblock != 32 && kblock != 256) {
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return hipErrorInvalidDevice;
+    const int mt = (M + 255) / 256;
+    int best = 128;
+    int64_t best_cost = INT64_MAX;
+    for (const int wc : {128, 80, 64}) {
+      const int64_t tiles = (int64_t)mt * ((N + 2 * wc - 1) / (2 * wc));
+      const int64_t cost = (tiles + cus - 1) / cus * wc;
+      if (cost < best_cost) best_cost = cost, best = wc;
+    }
+    return launch_gemm_rs(xq, dx, M, wq, dw, N, K, best, y, s);
+  }
   // 256-blocks, K a multiple of 1024 (scales in 16-byte groups of four blocks):
   // the pipelined kernel.
   if (kblock == 256 && K % 1024 == 0) {

@@ -65,23 +65,73 @@ void trellis_tables(V16Table* v16, V8Table* v8, float* gain) {
   if (gain) *gain = t.gain;
 }
 
-// One wave per (row, 1024 weights): lane l decodes code bytes 4l .. 4l+3 of the
-// unit (16 weights), one 16-lane quarter per 256-block, with one 4-byte load;
-// the two bytes before its first byte come from the previous lane (lane 0:
-// from memory, or the seed at the row start).  Then Q8 per oblock (WIDTH
-// lanes: 16 for 256, 2 for 32) and one 16-byte store per lane.  Waves walk
-// the units in a grid-stride loop (the unit's row and position advance by a
-// fixed quotient and remainder, no division per unit), so the codebook is
-// copied to LDS once per workgroup, as fp32 (exact for fp16 values).
+// Decode of one 1024-weight unit ub of row `row` by a whole wave: lane l takes
+// code bytes 4l .. 4l+3 of the unit (16 weights, one 16-lane quarter per
+// 256-block) with one 4-byte load; the two bytes before its first byte come
+// from the previous lane (lane 0: from memory, or the seed at the row start).
 // Per weight: the state st is the 16-bit window ending at its symbol, and
 // 4 h = ((220 st) ^ (st >> 5)) & 0x3FC is the table byte offset (the low 8 bits
 // of 0x9E37 st are those of 55 st, so bits 2..9 of 220 st are bits 0..7 of
 // 0x9E37 st, and bits 2..9 of st >> 5 are bits 0..7 of st >> 7); a multiply
 // takes only the window's low 24 bits, and bits above the state land outside
-// the mask.  q = rint(v * (1 / d)) comes from the fp32 sum 1.5 * 2^23 + v * (1 / d):
-// that sum has a unit ulp, so it rounds v * (1 / d) to the nearest integer
-// with ties to even, and its low byte is q in two's complement.  No clamp:
-// |v| <= amax, so |v * (1 / d)| <= 127 (1 + 3 ulp) and q stays in [-127, 127].
+// the mask.  v = s * V16[h] exactly (both fp16).  Returns whether the lane's
+// 256-block exists (its v are zeros otherwise).
+__device__ __forceinline__ bool decode_unit(const GemvItem& it, int row, int ub, int lane, uint32_t lds_base,
+                                            float v[16]) {
+  const int nblk = it.cols / 256;
+  const bool ok = ub * 4 + (lane >> 4) < nblk;  // this lane's 256-block exists
+  const uint8_t* rp = it.codes + (int64_t)row * it.row_bytes;
+  const int g0 = ub * 256 + 4 * lane;  // first code byte of the lane
+  const uint32_t cur = ok ? *(const uint32_t*)(rp + g0) : 0u;
+  uint32_t prev = __shfl_up(cur, 1);
+  if (lane == 0) {
+    const uint32_t seed = it.seeds[row];
+    // bytes -1 and -2 of a row are the seed's low and high byte
+    prev = ub == 0 ? ((seed & 0xFFu) << 24) | (((seed >> 8) & 0xFFu) << 16) : *(const uint32_t*)(rp + g0 - 4);
+  }
+  const uint64_t x = ((uint64_t)cur << 32) | prev;
+  const float s = ok ? __half2float(__ushort_as_half(it.scales[scale_index(QFMT_TRELLIS2, it.cols, row, g0 / 16)]))
+                     : 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // bytes g-2, g-1, g (g = g0 + k) as the big-endian window g-2 | g-1 | g
+    const uint32_t y3 = (uint32_t)(x >> (16 + 8 * k));
+    const uint32_t w24 = ((y3 & 0xFFu) << 16) | (y3 & 0xFF00u) | ((y3 >> 16) & 0xFFu);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = w24 >> (6 - 2 * j);      // st in the low 16 bits
+      const uint32_t off = ((a * 220u) ^ (a >> 5)) & 0x3FCu;  // 4 h
+      const float val = *(const __attribute__((address_space(3))) float*)(uintptr_t)(lds_base + off);
+      v[4 * k + j] = s * val;  // exact: 11-bit x 11-bit significands
+    }
+  }
+  return ok;
+}
+
+// Q8 codes of 16 values through the 1.5 * 2^23 sum (its low byte is
+// rint(v * (1 / d)) in two's complement, ties to even; no clamp: |v| <= amax,
+// so |v * (1 / d)| <= 127 (1 + 3 ulp) and q stays in [-127, 127]), packed.
+__device__ __forceinline__ float q8_inv(float d) {  // 1 / d, or 0 where it overflows (a zero block)
+  const float r = 1.0f / d;  // +inf when d = 0 or d <= 2^-128
+  return r < __builtin_inff() ? r : 0.0f;
+}
+__device__ __forceinline__ void q8_pack16(const float v[16], float id, uint32_t pk[4]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = __builtin_bit_cast(uint32_t, v[4 * w + j] * id + 12582912.0f);
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // q0 | q1 << 8
+    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);  // q2 | q3 << 8
+    pk[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+}
+
+// One wave per (row, 1024 weights) (decode_unit), then Q8 per oblock (WIDTH
+// lanes: 16 for 256, 2 for 32) and one 16-byte store per lane.  Waves walk the
+// units in a grid-stride loop (the unit's row and position advance by a fixed
+// quotient and remainder, no division per unit), so the codebook is copied to
+// LDS once per workgroup, as fp32 (exact for fp16 values).
 template <int WIDTH>
 __global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, V16Table v16t, int8_t* __restrict__ wq,
                                                         float* __restrict__ dw, int upr, int step_rows,
@@ -99,33 +149,9 @@ __global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, V16Table v1
   const int u0 = blockIdx.x * 4 + wave;
   int row = u0 / upr, ub = u0 - row * upr;
   for (; row < it.rows;) {
-    const bool ok = ub * 4 + (lane >> 4) < nblk;  // this lane's 256-block exists
-    const uint8_t* rp = it.codes + (int64_t)row * it.row_bytes;
-    const int g0 = ub * 256 + 4 * lane;  // first code byte of the lane
-    const uint32_t cur = ok ? *(const uint32_t*)(rp + g0) : 0u;
-    uint32_t prev = __shfl_up(cur, 1);
-    if (lane == 0) {
-      const uint32_t seed = it.seeds[row];
-      // bytes -1 and -2 of a row are the seed's low and high byte
-      prev = ub == 0 ? ((seed & 0xFFu) << 24) | (((seed >> 8) & 0xFFu) << 16) : *(const uint32_t*)(rp + g0 - 4);
-    }
-    const uint64_t x = ((uint64_t)cur << 32) | prev;
-    const float s = ok ? __half2float(__ushort_as_half(it.scales[scale_index(QFMT_TRELLIS2, it.cols, row, g0 / 16)]))
-                       : 0.0f;
     float v[16];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // bytes g-2, g-1, g (g = g0 + k) as the big-endian window g-2 | g-1 | g
-      const uint32_t y3 = (uint32_t)(x >> (16 + 8 * k));
-      const uint32_t w24 = ((y3 & 0xFFu) << 16) | (y3 & 0xFF00u) | ((y3 >> 16) & 0xFFu);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t a = w24 >> (6 - 2 * j);      // st in the low 16 bits
-        const uint32_t off = ((a * 220u) ^ (a >> 5)) & 0x3FCu;  // 4 h
-        const float val = *(const __attribute__((address_space(3))) float*)(uintptr_t)(lds_base + off);
-        v[4 * k + j] = s * val;  // exact: 11-bit x 11-bit significands
-      }
-    }
+    const bool ok = decode_unit(it, row, ub, lane, lds_base, v);
+    const int g0 = ub * 256 + 4 * lane;  // first code byte of the lane
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
@@ -136,18 +162,9 @@ __global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, V16Table v1
       am = fmaxf(am, xlane<8>(am));
     }
     const float dd = am / 127.0f;
-    const float r = 1.0f / dd;                          // +inf when d = 0 or d <= 2^-128:
-    const float id = r < __builtin_inff() ? r : 0.0f;   // then a zero block, as Q8 defines
+    const float id = q8_inv(dd);
     uint32_t pk[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t b[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = __builtin_bit_cast(uint32_t, v[4 * w + j] * id + 12582912.0f);
-      const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // q0 | q1 << 8
-      const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);  // q2 | q3 << 8
-      pk[w] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    }
+    q8_pack16(v, id, pk);
     if (ok) {
       int8_t* o = wq + (int64_t)row * it.cols + 4 * (int64_t)g0;
       if (vec) {
@@ -167,10 +184,69 @@ __global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, V16Table v1
   }
 }
 
+
+// Q8 with one scale per weight row (oblock = cols): one workgroup per row, its
+// four waves decoding units w, w + 4, ... (up to NB each, kept in registers);
+// the row's amax is reduced over the wave and then the workgroup (LDS).
+template <int NB>
+__global__ __launch_bounds__(256) void k_trellis_decode_row(GemvItem it, V16Table v16t, int8_t* __restrict__ wq,
+                                                            float* __restrict__ dw) {
+  __shared__ float v32[256];
+  __shared__ float s_am[4];
+  v32[threadIdx.x] = __half2float(__ushort_as_half(v16t.v[threadIdx.x]));
+  __syncthreads();
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)v32;
+  float v[NB][16];
+  bool ok[NB];
+  float am = 0.0f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    ok[b] = decode_unit(it, row, wave + 4 * b, lane, lds_base, v[b]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[b][i]));
+  }
+  for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+  if (lane == 0) s_am[wave] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(s_am[0], s_am[1]), fmaxf(s_am[2], s_am[3]));
+  const float dd = am / 127.0f;
+  const float id = q8_inv(dd);
+  const bool vec = ((uintptr_t)wq & 15) == 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    uint32_t pk[4];
+    q8_pack16(v[b], id, pk);
+    if (ok[b]) {
+      int8_t* o = wq + (int64_t)row * it.cols + 4 * (int64_t)((wave + 4 * b) * 256 + 4 * lane);
+      if (vec) {
+        *(uint4*)o = uint4{pk[0], pk[1], pk[2], pk[3]};
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ((uint32_t*)o)[w] = pk[w];
+      }
+    }
+  }
+  if (threadIdx.x == 0) dw[row] = dd;
+}
+
 hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, float* dw, hipStream_t s) {
   V16Table v16;
   trellis_tables(&v16, nullptr, nullptr);
   const int upr = (it.cols / 256 + 3) / 4;  // 1024-weight units per row
+  if (oblock == it.cols && oblock != 32 && oblock != 256) {  // one scale per row
+    const int nb = (upr + 3) / 4;                            // units per wave
+    const dim3 grid(it.rows), block(256);
+    if (nb <= 1) hipLaunchKernelGGL(k_trellis_decode_row<1>, grid, block, 0, s, it, v16, wq, dw);
+    else if (nb <= 2) hipLaunchKernelGGL(k_trellis_decode_row<2>, grid, block, 0, s, it, v16, wq, dw);
+    else if (nb <= 4) hipLaunchKernelGGL(k_trellis_decode_row<4>, grid, block, 0, s, it, v16, wq, dw);
+    else if (nb <= 6) hipLaunchKernelGGL(k_trellis_decode_row<6>, grid, block, 0, s, it, v16, wq, dw);
+    else if (nb <= 8) hipLaunchKernelGGL(k_trellis_decode_row<8>, grid, block, 0, s, it, v16, wq, dw);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   const int64_t units = (int64_t)it.rows * upr;
   const int grid = (int)std::min<int64_t>((units + 3) / 4, 8192);
   const int stride = grid * 4;  // units per turn of the grid

@@ -208,8 +208,9 @@ int qact_quant_batch(const qact_job_t* jobs, int32_t n, void* stream);
  * 256-block, u = sigma * x with sigma_k = -1 where bit k%32 of sign_bits[k/32]
  * is set; stages h = 1, 2, ..., 128 map (u_i, u_{i+h}) to (u_i + u_{i+h},
  * u_i - u_{i+h}) for (i & h) == 0 (Sylvester order); times 1/16; then Q8 per
- * qblock (32 or 256) as in qact_quant_i8.  fp32, bit-exact.
- * K multiple of 256; sign_bits [K/32] (device). */
+ * qblock (32, 256, or K: one scale per token row, K <= 32768, else
+ * QERR_SHAPE) as in qact_quant_i8; d and qsum [B][K/qblock].  fp32,
+ * bit-exact.  K multiple of 256; sign_bits [K/32] (device). */
 int qact_hadamard_quant_i8(const float* x, int32_t B, int32_t K, const uint32_t* sign_bits,
                            int32_t qblock, int8_t* q, float* d, int32_t* qsum, void* stream);
 
@@ -384,8 +385,9 @@ int qattn_decode(int32_t fmt, const float* q, int32_t n_kv, int32_t group, int32
  * an INT8 GEMM ([P1] "把非标准格式塞进 llama.cpp，难在哪"), so the exact fp32
  * values s * V16[h] of each row (both fp16, so the product is exact) are
  * re-quantized by Q8 per (row, oblock) as in qact_quant_i8.  Output wq
- * [rows][cols] int8, dw [rows][cols/oblock] fp32 (device).  oblock 256 or 32;
- * cols a multiple of 256. */
+ * [rows][cols] int8, dw [rows][cols/oblock] fp32 (device).  oblock 256, 32,
+ * or cols (one scale per row, cols <= 32768, else QERR_SHAPE); cols a
+ * multiple of 256. */
 int qtrellis_decode_i8(const qweight_t* w, int32_t oblock, int8_t* wq, float* dw, void* stream);
 
 /* Unpack TERN_B3 / INT2 / SIGN1 / INT4 weights to int8 levels for the GEMM:
@@ -399,8 +401,11 @@ int qweight_unpack_i8(const qweight_t* w, int8_t* wq, float* dw, void* stream);
  *   y[m][n] = sum_kb dx[m][kb] * dw[n][kb] * I[m][n][kb],
  *   I = exact int32 dot of xq[m] and wq[n] over K-block kb (size kblock).
  * xq [M][K] int8, dx [M][K/kblock], wq [N][K] int8, dw [N][K/kblock],
- * y [M][N] fp32 (all device; xq, wq 16-byte aligned).  kblock 256 or 32;
- * K a multiple of kblock and of 64. */
+ * y [M][N] fp32 (all device; xq, wq 16-byte aligned).  kblock 256, 32, or K:
+ * one scale per row of each operand (dx [M][1], dw [N][1]: per-token
+ * activations and per-output-row weights, the scaling an INT8 GEMM library
+ * applies to its int32 result), y = dx[m] dw[n] I with I over the whole row.
+ * K a multiple of kblock and of 64; QERR_INVALID_ARG for any other kblock. */
 int qgemm_i8(const int8_t* xq, const float* dx, int32_t M, const int8_t* wq, const float* dw,
              int32_t N, int32_t K, int32_t kblock, float* y, void* stream);
 

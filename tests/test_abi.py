@@ -160,7 +160,21 @@ def test_call_validation_without_gpu(ebq):
     assert L.qgemm_i8(A, A, 16, A, A, 16, 96, 32, A, None) == -3
     assert L.qgemm_i8(A, A, 16, A, A, 16, 256, 64, A, None) == -1
     assert L.qgemm_i8(A, A, 0, A, A, 16, 256, 256, A, None) == 0
+    # one scale per row: kblock = K (any multiple of 64); other block sizes rejected
+    assert L.qgemm_i8(A, A, 16, A, A, 16, 192, 96, A, None) == -1
+    assert L.qgemm_i8(A, A, 16, A, A, 16, 160, 160, A, None) == -3     # K % 64
+    assert L.qgemm_i8(A + 4, A, 16, A, A, 16, 192, 192, A, None) == -4
+    assert L.qgemm_i8(A, A, 0, A, A, 16, 192, 192, A, None) == 0
+    # rotation + Q8 per token row: qblock = K, at most 32768
+    assert L.qact_hadamard_quant_i8(A, 1, 1024, A, 512, A, A, A, None) == -1
+    assert L.qact_hadamard_quant_i8(A, 1, 33024, A, 33024, A, A, A, None) == -3
+    assert L.qact_hadamard_quant_i8(A, 0, 5120, A, 5120, A, A, A, None) == 0
     assert L.qtrellis_decode_i8(w, 256, A, A, None) == -2   # not a trellis matrix
+    tr = ctypes.byref(_desc(ebq, fmt=5, cols=5120, seeds=12288))
+    assert L.qtrellis_decode_i8(tr, 512, A, A, None) == -1  # block neither 32, 256 nor the row
+    assert L.qtrellis_decode_i8(tr, 5120, A + 2, A, None) == -4
+    big = ctypes.byref(_desc(ebq, fmt=5, cols=33024, seeds=12288))
+    assert L.qtrellis_decode_i8(big, 33024, A, A, None) == -3  # one scale per row: at most 32768
     assert L.qweight_quantize(5, A, 4, 256, A, 64, A, None) == -2
     assert L.qweight_pack(2, A, 4, 48, A, 16, None) == -3
     assert L.qgemv_grouped_run(None, A, None) == -1

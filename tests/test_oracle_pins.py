@@ -645,7 +645,7 @@ def test_gemv_zero_activation(qref):
 # GEMM
 # ----------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kblock", [256, 32])
+@pytest.mark.parametrize("kblock", [256, 32, 512])
 def test_gemm_brute_force(qref, kblock):
     M, N, K = 13, 9, 512
     xq = synth.integers([40], (M, K), -127, 127)
@@ -659,3 +659,53 @@ def test_gemm_brute_force(qref, kblock):
     T = dx.astype(np.float64)[:, None, :] * dw.astype(np.float64)[None, :, :] * Ib
     assert np.abs(y - T.sum(-1)).max() <= 1e-12 * a.max()
     assert np.allclose(a, np.abs(T).sum(-1), rtol=1e-14, atol=0)
+
+
+def test_per_row_scales(qref):
+    """One scale per row (the block is the whole row): the rotation + Q8 per token
+    and the trellis decode + Q8 per weight row follow the Q8 rule with amax over
+    the row (the amax element maps to +-127, reconstruction within half a step
+    of the rotated / decoded values, Sigma q), pinned against the rotation and the
+    decoded values themselves (each pinned above); the GEMM is the exact integer
+    matmul times the outer product of the scales."""
+    import scipy.linalg
+
+    B, K = 5, 1280
+    x = synth.with_outliers(synth.gauss([50], (B, K)), [51])
+    sb = synth.sign_bits([52, K], K)
+    q, d, s = qref.hadamard_quant(x, sb, K)
+    assert q.shape == (B, K) and d.shape == (B, 1) and s.shape == (B, 1)
+    sign = 1.0 - 2.0 * ((sb[np.arange(K) // 32] >> (np.arange(K) % 32)) & 1)
+    H = scipy.linalg.hadamard(256).astype(np.float64)
+    rot = ((x.astype(np.float64) * sign).reshape(B, -1, 256) @ H.T / 16.0).reshape(B, K)
+    am = np.abs(rot).max(1)
+    assert np.allclose(d[:, 0], am / 127.0, rtol=1e-6)
+    qi = q.astype(np.int64)
+    assert (np.abs(qi) <= 127).all() and (np.abs(qi).max(1) == 127).all()
+    assert (np.abs(rot - qi * d) <= d * 0.5 + am[:, None] * 1e-5).all()
+    assert (qi.sum(1) == s[:, 0]).all()
+    # trellis decode with one scale per row, against the exact decoded values
+    N = 4
+    codes = synth.symbols([53], (N, K), 4)
+    sc = synth.uniform_f16([54], (N, K // 64), 0.01, 0.03)
+    seeds = synth.u16([55], N)
+    p = qref.pack(qref.TRELLIS2, codes)
+    w = qref.trellis_decode_f32(p, seeds, sc, K).astype(np.float64)
+    wq, dw = qref.trellis_decode_i8(p, seeds, sc, K, K)
+    assert dw.shape == (N, 1)
+    amw = np.abs(w).max(1)
+    assert (dw[:, 0] == (amw.astype(np.float32) / np.float32(127.0))).all()
+    wi = wq.astype(np.int64)
+    assert (np.abs(wi).max(1) == 127).all()
+    assert (np.abs(w - wi * dw) <= dw * 0.5 * (1 + 1e-5)).all()
+    # GEMM, kblock = K: y = dx dw (xq . wq), the sum of absolute terms |y|
+    M, Nn, Kk = 7, 6, 320
+    xq = synth.integers([56], (M, Kk), -127, 127).astype(np.int8)
+    wq2 = synth.integers([57], (Nn, Kk), -127, 127).astype(np.int8)
+    dx = synth.uniform([58], (M, 1), 0.001, 0.1)
+    dw2 = synth.uniform([59], (Nn, 1), 0.001, 0.1)
+    y, a = qref.gemm_i8(xq, dx, wq2, dw2, Kk)
+    I = xq.astype(np.int64) @ wq2.astype(np.int64).T
+    ref = dx.astype(np.float64) * dw2.astype(np.float64).T * I
+    assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+    assert np.allclose(a, np.abs(ref), rtol=1e-14, atol=0)
