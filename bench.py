@@ -370,13 +370,13 @@ def cpu_other_configs():
     sc = synth.uniform_f16([5, 3, Kin], (Nout, Kin // 64), 0.01, 0.03)
     seeds = synth.u16([5, 4, Kin], Nout)
     t0 = time.perf_counter()
-    xq, dx, _ = oracle.hadamard_quant(xs, sb, 256)
+    xq, dx, _ = oracle.hadamard_quant(xs, sb, Kin)
     t_rot = time.perf_counter() - t0
     t0 = time.perf_counter()
-    wq, dw = oracle.trellis_decode_i8(packed, seeds, sc, Kin, 256)
+    wq, dw = oracle.trellis_decode_i8(packed, seeds, sc, Kin, Kin)
     t_dec = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.gemm_i8(xq, dx, wq, dw, 256)
+    oracle.gemm_i8(xq, dx, wq, dw, Kin)
     t_gemm = time.perf_counter() - t0
     scale = M / Ms
     total = (t_rot + t_gemm) * scale + t_dec
@@ -386,7 +386,8 @@ def cpu_other_configs():
         "trellis_decode_ms": round(t_dec * 1e3, 1),
         "gemm_ms_16_tokens": round(t_gemm * 1e3, 1),
         "tok_s_this_matrix": round(M / total, 2),
-        "sample": "rotation + Q8 and GEMM on %d of %d tokens (x%d stated), decode of the whole matrix" % (Ms, M, scale),
+        "sample": "one scale per row: rotation + Q8 and GEMM on %d of %d tokens (x%d stated), decode of the "
+                  "whole matrix" % (Ms, M, scale),
     }
     return out
 
@@ -483,7 +484,13 @@ def bench_dependent_chain(ebq, stack, reps):
 
 
 def bench_prefill(ebq, reps):
+    """The prefill chain per FFN shape at 2048 tokens, in both scale readings: one
+    scale per row of each operand (per-token activations after the rotation,
+    per-output-row weights: the int8 GEMM's own scaling; the headline GEMM
+    figures) and one scale pair per 256-block (the rotation block)."""
     import torch
+
+    import oracle
 
     M = 2048
     out = {}
@@ -495,9 +502,6 @@ def bench_prefill(ebq, reps):
         g.manual_seed(synth.seed64(5, 1, Kin))
         mask = torch.rand((M, Kin), generator=g, device="cuda") < 0.001
         x[mask] *= 20.0
-        xq = torch.empty((M, Kin), dtype=torch.int8, device="cuda")
-        dx = torch.empty((M, Kin // 256), dtype=torch.float32, device="cuda")
-        sx = torch.empty((M, Kin // 256), dtype=torch.int32, device="cuda")
         rng = synth.rng(5, 2, Kin)
         codes_h = rng.integers(0, 4, size=(Nout, Kin), dtype=np.int8)
         scales_h = synth.uniform_f16([5, 3, Kin], (Nout, Kin // 64), 0.01, 0.03)
@@ -506,42 +510,51 @@ def bench_prefill(ebq, reps):
         ebq.qweight_pack(TRELLIS, torch.from_numpy(codes_h).cuda(), pw)
         ebq.qweight_set_scales(pw, torch.from_numpy(scales_h.view(np.int16)).cuda())
         pw.seeds.copy_(torch.from_numpy(seeds_h.view(np.int16)).cuda())
+        xq = torch.empty((M, Kin), dtype=torch.int8, device="cuda")
         wq = torch.empty((Nout, Kin), dtype=torch.int8, device="cuda")
-        dw = torch.empty((Nout, Kin // 256), dtype=torch.float32, device="cuda")
         y = torch.empty((M, Nout), dtype=torch.float32, device="cuda")
-        t_rot, _ = time_kernel(lambda: ebq.qact_hadamard_quant_i8(x, sb[Kin], 256, xq, dx, sx), reps, 2)
-        t_dec, _ = time_kernel(lambda: ebq.qtrellis_decode_i8(pw, 256, wq, dw), reps, 2)
-        t_gemm, _ = time_kernel(lambda: ebq.qgemm_i8(xq, dx, wq, dw, 256, y), reps, 2)
         ops = 2.0 * M * Nout * Kin
-        # parity of the chain (rotation + Q8, trellis decode, GEMM) on sampled tokens
-        # and output columns: the oracle redoes every step from the same draws
-        import oracle
-
+        # parity of each chain (rotation + Q8, trellis decode, GEMM) on sampled
+        # tokens and output columns: the oracle redoes every step from the same draws
         prng = np.random.default_rng(Kin)
         rows = np.sort(np.concatenate([[0, M - 1], prng.choice(np.arange(1, M - 1), 6, replace=False)]))
         cols = np.sort(np.concatenate([[0, Nout - 1], prng.choice(np.arange(1, Nout - 1), 62, replace=False)]))
         xs = x[torch.from_numpy(rows).cuda()].cpu().numpy()
-        rxq, rdx, _ = oracle.hadamard_quant(xs, sb[Kin].cpu().numpy().view(np.uint32), 256)
-        rwq, rdw = oracle.trellis_decode_i8(oracle.pack(TRELLIS, codes_h[cols]), seeds_h[cols], scales_h[cols], Kin, 256)
-        yr, absT = oracle.gemm_i8(rxq, rdx, rwq, rdw, 256)
-        err = np.abs(y.cpu().numpy()[np.ix_(rows, cols)].astype(np.float64) - yr)
-        pok = bool((err <= 1e-4 * absT).all())
-        del codes_h
-        out[tag] = {
-            "gemm_us": round(t_gemm * 1e6, 2),
-            "gemm_tops": round(ops / t_gemm / 1e12, 1),
-            "mfma_frac": round(ops / t_gemm / 1e12 / INT8_PEAK_TOPS, 4),
-            "rotate_quant_us": round(t_rot * 1e6, 2),
-            "rotate_quant_gbs": round((M * Kin * 4 + M * Kin + M * (Kin // 256) * 8) / t_rot / 1e9, 1),
-            "trellis_decode_us": round(t_dec * 1e6, 2),
-            "trellis_decode_gbs": round((pw.nbytes + Nout * Kin + Nout * (Kin // 256) * 4) / t_dec / 1e9, 1),
-            "prefill_tok_s_this_matrix": round(M / (t_rot + t_dec + t_gemm), 1),
-            "parity": "ok" if pok else "FAIL",
-            "parity_sample": "%d tokens x %d output columns, rotation + Q8, decode and GEMM redone by the oracle"
-                             % (len(rows), len(cols)),
-            "worst_err_over_sum_abs_terms": float((err / np.maximum(absT, 1e-300)).max()),
-        }
-        del x, xq, wq, y
+        rsub = oracle.pack(TRELLIS, codes_h[cols])
+        res = {}
+        for blk_name, blk in (("per_row", Kin), ("per_256", 256)):
+            nb = Kin // blk
+            dx = torch.empty((M, nb), dtype=torch.float32, device="cuda")
+            sx = torch.empty((M, nb), dtype=torch.int32, device="cuda")
+            dw = torch.empty((Nout, nb), dtype=torch.float32, device="cuda")
+            t_rot, _ = time_kernel(lambda: ebq.qact_hadamard_quant_i8(x, sb[Kin], blk, xq, dx, sx), reps, 2)
+            t_dec, _ = time_kernel(lambda: ebq.qtrellis_decode_i8(pw, blk, wq, dw), reps, 2)
+            t_gemm, _ = time_kernel(lambda: ebq.qgemm_i8(xq, dx, wq, dw, blk, y), reps, 2)
+            rxq, rdx, _ = oracle.hadamard_quant(xs, sb[Kin].cpu().numpy().view(np.uint32), blk)
+            rwq, rdw = oracle.trellis_decode_i8(rsub, seeds_h[cols], scales_h[cols], Kin, blk)
+            yr, absT = oracle.gemm_i8(rxq, rdx, rwq, rdw, blk)
+            err = np.abs(y.cpu().numpy()[np.ix_(rows, cols)].astype(np.float64) - yr)
+            res[blk_name] = {
+                "scales": "one per row of each operand (dx [M][1], dw [N][1])" if blk == Kin
+                          else "one pair per 256-block (dx [M][K/256], dw [N][K/256])",
+                "gemm_kernel": "qk::k_gemm_i8_rs" if blk == Kin else "qk::k_gemm_i8_p256",
+                "gemm_us": round(t_gemm * 1e6, 2),
+                "gemm_tops": round(ops / t_gemm / 1e12, 1),
+                "mfma_frac": round(ops / t_gemm / 1e12 / INT8_PEAK_TOPS, 4),
+                "rotate_quant_us": round(t_rot * 1e6, 2),
+                "rotate_quant_gbs": round((M * Kin * 4 + M * Kin + M * nb * 8) / t_rot / 1e9, 1),
+                "trellis_decode_us": round(t_dec * 1e6, 2),
+                "trellis_decode_gbs": round((pw.nbytes + Nout * Kin + Nout * nb * 4) / t_dec / 1e9, 1),
+                "chain_us": round((t_rot + t_dec + t_gemm) * 1e6, 2),
+                "parity": "ok" if bool((err <= 1e-4 * absT).all()) else "FAIL",
+                "parity_sample": "%d tokens x %d output columns, rotation + Q8, decode and GEMM redone by the oracle"
+                                 % (len(rows), len(cols)),
+                "worst_err_over_sum_abs_terms": float((err / np.maximum(absT, 1e-300)).max()),
+            }
+            del dx, sx, dw
+        out[tag] = dict(res["per_row"])
+        out[tag]["per_256_block"] = res["per_256"]
+        del codes_h, x, xq, wq, y
     return out
 
 

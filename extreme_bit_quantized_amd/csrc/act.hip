@@ -358,26 +358,27 @@ __global__ __launch_bounds__(256) void k_hadamard_quant(const float* __restrict_
 }
 
 
-// Q8 with one scale per token row (qblock = K): one workgroup per row, its 16
-// groups of 16 lanes rotating blocks g, g + 16, ... (up to NB each, kept in
-// registers); the row's amax and code sum are reduced over the group's lanes,
-// the wave and then the workgroup (LDS).
+// Q8 with one scale per token row (qblock = K): one workgroup per row, of as
+// many waves as it takes for its G = blockDim / 16 groups of 16 lanes to rotate
+// all blocks g, g + G, ... (NB each at most, kept in registers); the row's amax
+// and code sum are reduced over the wave and then the workgroup (LDS).
 template <int NB>
-__global__ __launch_bounds__(256) void k_hadamard_quant_row(const float* __restrict__ x, int K,
-                                                            const uint32_t* __restrict__ sign_bits,
-                                                            int8_t* __restrict__ q, float* __restrict__ d,
-                                                            int32_t* __restrict__ qsum) {
-  __shared__ float s_am[4];
-  __shared__ int s_sum[4];
+__global__ __launch_bounds__(1024) void k_hadamard_quant_row(const float* __restrict__ x, int K,
+                                                             const uint32_t* __restrict__ sign_bits,
+                                                             int8_t* __restrict__ q, float* __restrict__ d,
+                                                             int32_t* __restrict__ qsum) {
+  __shared__ float s_am[16];
+  __shared__ int s_sum[16];
   const int tok = blockIdx.x;
   const int lane = threadIdx.x & 63, t = lane & 15, g = threadIdx.x >> 4, wave = threadIdx.x >> 6;
+  const int G = blockDim.x >> 4, nw = blockDim.x >> 6;
   const int nkb = K / 256;
   const float* const xr = x + (int64_t)tok * K;
   float u[NB][16];
   float am = 0.0f;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int kb = g + 16 * b;
+    const int kb = g + G * b;
     const bool ok = kb < nkb;  // the whole 16-lane group agrees
     rotate256(xr + kb * 256 + 16 * t, sign_bits, kb * 256 + 16 * t, t, ok, u[b]);
 #pragma unroll
@@ -386,14 +387,15 @@ __global__ __launch_bounds__(256) void k_hadamard_quant_row(const float* __restr
   for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
   if (lane == 0) s_am[wave] = am;
   __syncthreads();
-  am = fmaxf(fmaxf(s_am[0], s_am[1]), fmaxf(s_am[2], s_am[3]));
+  am = s_am[0];
+  for (int w = 1; w < nw; ++w) am = fmaxf(am, s_am[w]);
   const float dd = am / 127.0f;
   const float id = q8_inv(dd);
   const bool vec = ((uintptr_t)q & 15) == 0;
   int sum = 0;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int kb = g + 16 * b;
+    const int kb = g + G * b;
     uint32_t pk[4];
     const int sb = q8_pack16(u[b], id, pk);
     if (kb < nkb) {
@@ -411,21 +413,22 @@ __global__ __launch_bounds__(256) void k_hadamard_quant_row(const float* __restr
   if (lane == 0) s_sum[wave] = sum;
   __syncthreads();
   if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int w = 0; w < nw; ++w) tot += s_sum[w];
     d[tok] = dd;
-    qsum[tok] = s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
+    qsum[tok] = tot;
   }
 }
 
 hipError_t launch_hadamard_quant(const float* x, int B, int K, const uint32_t* sign_bits, int qblock, int8_t* q,
                                  float* d, int32_t* qsum, hipStream_t s) {
   if (qblock == K && qblock != 32 && qblock != 256) {  // one scale per row
-    const int nb = (K / 256 + 15) / 16;  // blocks per 16-lane group
-    const dim3 grid(B), block(256);
-    if (nb <= 1) hipLaunchKernelGGL(k_hadamard_quant_row<1>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
-    else if (nb <= 2) hipLaunchKernelGGL(k_hadamard_quant_row<2>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
-    else if (nb <= 4) hipLaunchKernelGGL(k_hadamard_quant_row<4>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
-    else if (nb <= 6) hipLaunchKernelGGL(k_hadamard_quant_row<6>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
-    else if (nb <= 8) hipLaunchKernelGGL(k_hadamard_quant_row<8>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
+    const int nkb = K / 256;
+    const int nb = (nkb + 63) / 64;                      // blocks per 16-lane group (<= 64 groups)
+    const int threads = ((nkb + nb - 1) / nb * 16 + 63) / 64 * 64;
+    const dim3 grid(B), block(threads);
+    if (nb == 1) hipLaunchKernelGGL(k_hadamard_quant_row<1>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
+    else if (nb == 2) hipLaunchKernelGGL(k_hadamard_quant_row<2>, grid, block, 0, s, x, K, sign_bits, q, d, qsum);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }

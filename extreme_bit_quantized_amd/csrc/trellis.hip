@@ -75,7 +75,8 @@ void trellis_tables(V16Table* v16, V8Table* v8, float* gain) {
 // 0x9E37 st, and bits 2..9 of st >> 5 are bits 0..7 of st >> 7); a multiply
 // takes only the window's low 24 bits, and bits above the state land outside
 // the mask.  v = s * V16[h] exactly (both fp16).  Returns whether the lane's
-// 256-block exists (its v are zeros otherwise).
+// 256-block exists (its v are zeros otherwise); a unit wholly past the row's
+// end (the per-row kernel's spare waves) reads no memory.
 __device__ __forceinline__ bool decode_unit(const GemvItem& it, int row, int ub, int lane, uint32_t lds_base,
                                             float v[16]) {
   const int nblk = it.cols / 256;
@@ -84,7 +85,7 @@ __device__ __forceinline__ bool decode_unit(const GemvItem& it, int row, int ub,
   const int g0 = ub * 256 + 4 * lane;  // first code byte of the lane
   const uint32_t cur = ok ? *(const uint32_t*)(rp + g0) : 0u;
   uint32_t prev = __shfl_up(cur, 1);
-  if (lane == 0) {
+  if (lane == 0 && ub * 4 < nblk) {  // (a unit past the row's end reads nothing)
     const uint32_t seed = it.seeds[row];
     // bytes -1 and -2 of a row are the seed's low and high byte
     prev = ub == 0 ? ((seed & 0xFFu) << 24) | (((seed >> 8) & 0xFFu) << 16) : *(const uint32_t*)(rp + g0 - 4);
@@ -185,51 +186,58 @@ __global__ __launch_bounds__(256) void k_trellis_decode(GemvItem it, V16Table v1
 }
 
 
-// Q8 with one scale per weight row (oblock = cols): one workgroup per row, its
-// four waves decoding units w, w + 4, ... (up to NB each, kept in registers);
-// the row's amax is reduced over the wave and then the workgroup (LDS).
+// Q8 with one scale per weight row (oblock = cols): a workgroup of W waves
+// takes rows blockIdx.x, blockIdx.x + gridDim.x, ... (one codebook copy for all
+// of them); the W waves decode a row's units w, w + W, ... (NB each at most,
+// kept in registers), and the row's amax is reduced over each wave and then
+// over the W waves (LDS, double-buffered by row parity so one barrier per row
+// suffices).
 template <int NB>
-__global__ __launch_bounds__(256) void k_trellis_decode_row(GemvItem it, V16Table v16t, int8_t* __restrict__ wq,
-                                                            float* __restrict__ dw) {
+__global__ __launch_bounds__(1024) void k_trellis_decode_row(GemvItem it, V16Table v16t, int8_t* __restrict__ wq,
+                                                             float* __restrict__ dw) {
   __shared__ float v32[256];
-  __shared__ float s_am[4];
-  v32[threadIdx.x] = __half2float(__ushort_as_half(v16t.v[threadIdx.x]));
+  __shared__ float s_am[2][16];
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) v32[i] = __half2float(__ushort_as_half(v16t.v[i]));
   __syncthreads();
-  const int row = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)v32;
-  float v[NB][16];
-  bool ok[NB];
-  float am = 0.0f;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    ok[b] = decode_unit(it, row, wave + 4 * b, lane, lds_base, v[b]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[b][i]));
-  }
-  for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
-  if (lane == 0) s_am[wave] = am;
-  __syncthreads();
-  am = fmaxf(fmaxf(s_am[0], s_am[1]), fmaxf(s_am[2], s_am[3]));
-  const float dd = am / 127.0f;
-  const float id = q8_inv(dd);
   const bool vec = ((uintptr_t)wq & 15) == 0;
+  int par = 0;
+  for (int row = blockIdx.x; row < it.rows; row += gridDim.x, par ^= 1) {
+    float v[NB][16];
+    bool ok[NB];
+    float am = 0.0f;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    uint32_t pk[4];
-    q8_pack16(v[b], id, pk);
-    if (ok[b]) {
-      int8_t* o = wq + (int64_t)row * it.cols + 4 * (int64_t)((wave + 4 * b) * 256 + 4 * lane);
-      if (vec) {
-        *(uint4*)o = uint4{pk[0], pk[1], pk[2], pk[3]};
-      } else {
+    for (int b = 0; b < NB; ++b) {
+      ok[b] = decode_unit(it, row, w + W * b, lane, lds_base, v[b]);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) ((uint32_t*)o)[w] = pk[w];
+      for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[b][i]));
+    }
+    for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+    if (lane == 0) s_am[par][w] = am;
+    __syncthreads();  // (the other parity's slots were last read before this barrier's previous pass)
+    am = s_am[par][0];
+    for (int k = 1; k < W; ++k) am = fmaxf(am, s_am[par][k]);
+    const float dd = am / 127.0f;
+    const float id = q8_inv(dd);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      uint32_t pk[4];
+      q8_pack16(v[b], id, pk);
+      if (ok[b]) {
+        int8_t* o = wq + (int64_t)row * it.cols + 4 * (int64_t)((w + W * b) * 256 + 4 * lane);
+        if (vec) {
+          *(uint4*)o = uint4{pk[0], pk[1], pk[2], pk[3]};
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) ((uint32_t*)o)[k] = pk[k];
+        }
       }
     }
+    if (w == 0 && lane == 0) dw[row] = dd;
   }
-  if (threadIdx.x == 0) dw[row] = dd;
 }
 
 hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, float* dw, hipStream_t s) {
@@ -237,13 +245,11 @@ hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, flo
   trellis_tables(&v16, nullptr, nullptr);
   const int upr = (it.cols / 256 + 3) / 4;  // 1024-weight units per row
   if (oblock == it.cols && oblock != 32 && oblock != 256) {  // one scale per row
-    const int nb = (upr + 3) / 4;                            // units per wave
-    const dim3 grid(it.rows), block(256);
-    if (nb <= 1) hipLaunchKernelGGL(k_trellis_decode_row<1>, grid, block, 0, s, it, v16, wq, dw);
-    else if (nb <= 2) hipLaunchKernelGGL(k_trellis_decode_row<2>, grid, block, 0, s, it, v16, wq, dw);
-    else if (nb <= 4) hipLaunchKernelGGL(k_trellis_decode_row<4>, grid, block, 0, s, it, v16, wq, dw);
-    else if (nb <= 6) hipLaunchKernelGGL(k_trellis_decode_row<6>, grid, block, 0, s, it, v16, wq, dw);
-    else if (nb <= 8) hipLaunchKernelGGL(k_trellis_decode_row<8>, grid, block, 0, s, it, v16, wq, dw);
+    const int nb = (upr + 15) / 16;                          // units per wave (<= 16 waves per row)
+    const int W = (upr + nb - 1) / nb;                       // waves per row
+    const dim3 grid(std::min(it.rows, 2048)), block(64 * W);
+    if (nb == 1) hipLaunchKernelGGL(k_trellis_decode_row<1>, grid, block, 0, s, it, v16, wq, dw);
+    else if (nb == 2) hipLaunchKernelGGL(k_trellis_decode_row<2>, grid, block, 0, s, it, v16, wq, dw);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }
