@@ -569,7 +569,7 @@ hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* w
     const int mt = (M + 255) / 256;
     int best = 128;
     int64_t best_cost = INT64_MAX;
-    for (const int wc : {128, 80, 64}) {
+    for (const int wc : {128, 96, 80, 64}) {
       const int64_t tiles = (int64_t)mt * ((N + 2 * wc - 1) / (2 * wc));
       const int64_t cost = (tiles + cus - 1) / cus * wc;
       if (cost < best_cost) best_cost = cost, best = wc;

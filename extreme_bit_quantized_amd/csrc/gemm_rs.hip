@@ -275,6 +275,7 @@ hipError_t launch_rs_wc(const int8_t* xq, const float* dx, int M, const int8_t* 
                         int wc, float* y, hipStream_t s) {
   switch (wc) {
     case 128: return launch_rs<128, SK>(xq, dx, M, wq, dw, N, K, y, s);
+    case 96: return launch_rs<96, SK>(xq, dx, M, wq, dw, N, K, y, s);
     case 80: return launch_rs<80, SK>(xq, dx, M, wq, dw, N, K, y, s);
     case 64: return launch_rs<64, SK>(xq, dx, M, wq, dw, N, K, y, s);
   }

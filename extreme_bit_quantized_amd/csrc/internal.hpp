@@ -223,7 +223,7 @@ hipError_t launch_mfma_peak(int blocks, int iters, uint64_t* clocks, int32_t* si
 hipError_t launch_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_gemm(const int8_t* xq, const float* dx, int M, const int8_t* wq, const float* dw,
                        int N, int K, int kblock, float* y, hipStream_t s);
-// One scale per row of each operand (gemm_rs.hip); wc = 128, 80 or 64, the
+// One scale per row of each operand (gemm_rs.hip); wc = 128, 96, 80 or 64, the
 // N extent of a wave's tile.
 hipError_t launch_gemm_rs(const int8_t* xq, const float* dx, int M, const int8_t* wq, const float* dw,
                           int N, int K, int wc, float* y, hipStream_t s);

@@ -47,9 +47,9 @@ def _check_sampled(y, xq, dx, wq, dw, K, nrows, ncols, seed, what):
 
 
 # Shapes by path (256 compute units): small shapes take the 128 x 64 wave tile,
-# 2048 x 5120 the 128 x 80 one, 2048 x 8192 the 128 x 128 one; K a multiple of
-# 128 runs 128-byte stages, an odd multiple of 64 the 64-byte ones (odd stage
-# count included).
+# 2048 x 5120 the 128 x 80 one, 2048 x 17408 the 128 x 96 one, 2048 x 8192 the
+# 128 x 128 one; K a multiple of 128 runs 128-byte stages, an odd multiple of 64
+# the 64-byte ones (odd stage count included).
 @pytest.mark.parametrize("M,N,K", [(64, 96, 64), (300, 520, 192), (513, 700, 640), (700, 333, 1280),
                                    (257, 2000, 3072), (1, 17, 128), (255, 129, 1088)])
 def test_gemm_rowscale_whole(M, N, K):
@@ -64,7 +64,7 @@ def test_gemm_rowscale_whole(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(2048, 5120, 1088), (2048, 8192, 640), (2048, 8192, 576),
                                    (2048, 17408, 5120), (2048, 5120, 17408)])
 def test_gemm_rowscale_large_sampled(M, N, K):
-    """The wave-tile widths 80 and 128 and both stage sizes at full width, and the
+    """The wave-tile widths 80, 96 and 128 and both stage sizes at full width, and the
     two prefill GEMMs at their benchmark shapes: every output written, sampled
     rows and columns (both edges) against the oracle."""
     xq, dx, wq, dw = _rand_gemm(M, N, K, 301)
