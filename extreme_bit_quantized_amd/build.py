@@ -73,6 +73,77 @@ def _scratch_users(remarks: str):
     return users
 
 
+# MFMAs written as inline asm are opaque to the compiler: it inserts no wait
+# states after them, so a read of an MFMA's result (or a write to its
+# destination) that the compiler schedules right behind it sees the old value.
+# Sources with such MFMAs have their device assembly checked: every access to
+# an MFMA destination register by another instruction must come at least
+# MFMA_WAIT_STATES wait states (instructions; s_nop n counts n + 1) after it.
+# Straight-line approximation: a label does not reset the count.
+MFMA_WAIT_STATES = 18
+_ASM_MFMA = re.compile(r'"\s*v_mfma|"v_mfma_\w+ %|QG_MF\(')
+_REG = re.compile(r"\b([av])(?:\[(\d+):(\d+)\]|(\d+)\b)")
+
+
+def _regs(text):
+    out = set()
+    for m in _REG.finditer(text):
+        if m.group(4) is not None:
+            out.add((m.group(1), int(m.group(4))))
+        else:
+            out.update((m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1))
+    return out
+
+
+def mfma_result_hazards(asm: str, wait_states: int = MFMA_WAIT_STATES):
+    """(function, distance, instruction) for each access to an MFMA destination
+    register fewer than wait_states wait states after that MFMA (another MFMA
+    accumulating into exactly that destination is the hardware's own chain)."""
+    found, fn, pending, n = [], None, {}, 0
+    for line in asm.splitlines():
+        t = line.split(";")[0].strip()
+        if re.match(r"^[A-Za-z_.$][\w.$]*:$", t):
+            if not t.startswith("."):
+                fn, pending, n = t[:-1], {}, 0
+            continue
+        if not t or t.startswith("."):
+            continue
+        op = t.split()[0]
+        if op == "s_nop":
+            n += int(t.split()[1], 0) + 1
+            continue
+        n += 1
+        args = t[len(op):]
+        mfma = op.startswith("v_mfma")
+        parts = [x.strip() for x in args.split(",")]
+        used = _regs(",".join(parts[1:3])) if mfma else _regs(args)
+        near = [n - pending[r] for r in used if r in pending and n - pending[r] < wait_states]
+        if near:
+            found.append((fn, min(near), t))
+        if mfma:
+            for r in _regs(parts[0]):
+                pending[r] = n
+        else:
+            for r in used:
+                pending.pop(r, None)
+    return found
+
+
+def _check_asm_mfma(hipcc, src, extra):
+    with open(src) as f:
+        if not _ASM_MFMA.search(f.read()):
+            return
+    out = os.path.join(BUILD, os.path.basename(src)[:-4] + "".join(extra).replace("=", "") + ".s")
+    cmd = [hipcc] + FLAGS + extra + ["--cuda-device-only", "-S", src, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc -S failed for %s:\n%s" % (os.path.basename(src), r.stderr))
+    with open(out) as f:
+        bad = mfma_result_hazards(f.read())
+    if bad:
+        raise RuntimeError("%s: MFMA results accessed too early: %s" % (os.path.basename(src), bad[:4]))
+
+
 def _compile(hipcc, src, obj, extra):
     cmd = [hipcc] + FLAGS + extra + ["-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -97,6 +168,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     jobs = jobs or min(len(units), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         futs = [ex.submit(_compile, hipcc, s, o, e) for s, o, e in units]
+        futs += [ex.submit(_check_asm_mfma, hipcc, s, e) for s, _, e in units]
         for f in futs:
             msg = f.result()
             if verbose and msg.strip():

@@ -48,10 +48,14 @@ def _check_sampled(y, xq, dx, wq, dw, K, nrows, ncols, seed, what):
 
 # Shapes by path (256 compute units): small shapes take the 128 x 64 wave tile,
 # 2048 x 5120 the 128 x 80 one, 2048 x 17408 the 128 x 96 one, 2048 x 8192 the
-# 128 x 128 one; K a multiple of 128 runs 128-byte stages, an odd multiple of 64
-# the 64-byte ones (odd stage count included).
+# 128 x 128 one; K a multiple of 128 runs 128-byte stages (1, 2, 3, 5 and more
+# stages: each takes its own path through the last two stages), an odd multiple
+# of 64 the 64-byte ones (odd stage count included).  A first output register
+# of each wave tile read before its last MFMA had written it (in the kernel's
+# final K-step) once broke 1, 3 and 5 stages here while 2 passed.
 @pytest.mark.parametrize("M,N,K", [(64, 96, 64), (300, 520, 192), (513, 700, 640), (700, 333, 1280),
-                                   (257, 2000, 3072), (1, 17, 128), (255, 129, 1088)])
+                                   (257, 2000, 3072), (1, 17, 128), (255, 129, 1088), (256, 128, 128),
+                                   (256, 128, 256), (256, 128, 384), (512, 512, 1280)])
 def test_gemm_rowscale_whole(M, N, K):
     xq, dx, wq, dw = _rand_gemm(M, N, K, 300)
     y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
