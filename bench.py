@@ -537,7 +537,7 @@ def bench_prefill(ebq, reps):
             res[blk_name] = {
                 "scales": "one per row of each operand (dx [M][1], dw [N][1])" if blk == Kin
                           else "one pair per 256-block (dx [M][K/256], dw [N][K/256])",
-                "gemm_kernel": "qk::k_gemm_i8_rs" if blk == Kin else "qk::k_gemm_i8_p256",
+                "gemm_kernel": "qk::k_gemm_i8_rs128" if blk == Kin else "qk::k_gemm_i8_p256",
                 "gemm_us": round(t_gemm * 1e6, 2),
                 "gemm_tops": round(ops / t_gemm / 1e12, 1),
                 "mfma_frac": round(ops / t_gemm / 1e12 / INT8_PEAK_TOPS, 4),
