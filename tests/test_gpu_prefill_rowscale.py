@@ -78,6 +78,68 @@ def test_gemm_rowscale_large_sampled(M, N, K):
     _check_sampled(y, xq, dx, wq, dw, K, 24, 70, 302, "gemm per-row %dx%dx%d" % (M, N, K))
 
 
+def _tile_rows(M, seed, per_tile=3):
+    """per_tile rows from every 256-row tile (its first and last valid row among them)."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for m0 in range(0, M, 256):
+        m1 = min(M, m0 + 256)
+        rows += [m0, m1 - 1] + list(rng.integers(m0, m1, per_tile - 2))
+    return np.unique(np.array(rows))
+
+
+def _check_rows_all_cols(y, xq, dx, wq, dw, K, rows, what):
+    yh = host(y)
+    assert np.isfinite(yh).all(), what + ": an output was not written"
+    yr, absT = oracle.gemm_i8(host(xq)[rows], host(dx)[rows], host(wq), host(dw), K)
+    assert_close_terms(yh[rows], yr, absT, what=what)
+
+
+# More tiles than compute units in rounds that do not come out whole (wave tile
+# 80 or 96 on 256 units), ragged M and N, K of 1, 2, 3 and 5 stages: every tile
+# checked (three rows of each 256-row tile, every column).
+@pytest.mark.parametrize("M,N,K", [(1000, 17408, 128), (1000, 17408, 256), (777, 17408, 384),
+                                   (1500, 15000, 640), (2048, 12000, 640), (2048, 17408, 384),
+                                   (2048, 13000, 256)])
+def test_gemm_rowscale_many_tiles(M, N, K):
+    xq, dx, wq, dw = _rand_gemm(M, N, K, 303)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ebq.qgemm_i8(xq, dx, wq, dw, K, y)
+    _sync()
+    _check_rows_all_cols(y, xq, dx, wq, dw, K, _tile_rows(M, 304), "gemm %dx%dx%d" % (M, N, K))
+
+
+def test_gemm_rowscale_prefill_shape_every_tile_and_repeatable():
+    """The 2048 x 17408 x 5120 prefill GEMM (728 tiles, 40 stages each): every
+    tile checked, and a second run bit-identical."""
+    M, N, K = 2048, 17408, 5120
+    xq, dx, wq, dw = _rand_gemm(M, N, K, 305)
+    outs = []
+    for _ in range(2):
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        ebq.qgemm_i8(xq, dx, wq, dw, K, y)
+        _sync()
+        outs.append(y)
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    _check_rows_all_cols(outs[0], xq, dx, wq, dw, K, _tile_rows(M, 306, 2), "gemm prefill up")
+
+
+def test_gemm_rowscale_concurrent_streams():
+    """Two GEMMs in flight at once on two streams, three times over: both right."""
+    shapes = [(2048, 17408, 640), (1500, 15000, 384)]
+    ins = [_rand_gemm(M, N, K, 307 + i) for i, (M, N, K) in enumerate(shapes)]
+    ys = [torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") for (M, N, K) in shapes]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    _sync()
+    for rep in range(3):
+        for (M, N, K), (xq, dx, wq, dw), y, st in zip(shapes, ins, ys, streams):
+            with torch.cuda.stream(st):
+                ebq.qgemm_i8(xq, dx, wq, dw, K, y, stream=st.cuda_stream)
+    _sync()
+    for i, ((M, N, K), (xq, dx, wq, dw), y) in enumerate(zip(shapes, ins, ys)):
+        _check_rows_all_cols(y, xq, dx, wq, dw, K, _tile_rows(M, 308 + i, 2), "gemm concurrent %d" % i)
+
+
 def test_gemm_rowscale_repeatable_and_extremes():
     """Operands at the int8 extremes (every product 127 * 127 or -127 * 127:
     |I| = 16129 K, the largest sum) and zero scales: exact results, and two runs
