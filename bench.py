@@ -816,6 +816,8 @@ def main():
                     help="seconds of headline steps run after --warmup and before timing (clocks settle)")
     ap.add_argument("--quick", action="store_true", help="headline only (no secondary workloads, no CPU baseline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--mixed-only", action="store_true",
+                    help="only the mixed 4-bit/ternary stack at batch 1 (--steps launches), for counter runs")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill pieces (--steps launches each) and the 1 GiB copy, for counter runs")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -837,6 +839,15 @@ def main():
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
     torch.cuda.init()
     log("device", torch.cuda.get_device_name(0))
+    if args.mixed_only:
+        ms = Stack(ebq, "mixed", synth.N_LAYERS, 1)
+        plan, t, tk, _, cond = bench_stack_grouped(ebq, ms, max(2, args.steps), args.warmup, args.settle)
+        okm, wm = sampled_parity(ebq, ms, [0, 63], rows_per_matrix=8)
+        print(json.dumps({"mixed_int4_attn_ternary_ffn_B1": {
+            "step_us": round(t * 1e6, 1), "gemv_us": round(tk * 1e6, 1),
+            "gemv_weight_gbs": round(ms.weight_bytes() / tk / 1e9, 1), "sclk_mhz": cond.get("sclk_mhz_after"),
+            "parity": "ok" if okm else "FAIL"}}), flush=True)
+        return
     if args.prefill_only:
         pre = bench_prefill(ebq, max(2, args.steps))
         copy_calibration()

@@ -52,7 +52,9 @@ hipError_t QK_CAT(launch_grouped_b, QGEMV_NB)(const PlanHeader& h, const void* p
   if (h.fmt_mask & (1 << QFMT_TRELLIS2)) trellis_tables(&v16, &v8, &gain);
   // one launch per format present, in stream order
   hipError_t e = hipSuccess;
-  if (e == hipSuccess) e = launch_grouped_variant<NB, QFMT_TERN_B3>(h, plan, v8, gain, s);
+  // ternary at one token: the matrix-core kernel of gemv_tern1.hip
+  if (e == hipSuccess)
+    e = NB == 1 ? launch_grouped_tern1(h, plan, s) : launch_grouped_variant<NB, QFMT_TERN_B3>(h, plan, v8, gain, s);
   if (e == hipSuccess) e = launch_grouped_variant<NB, QFMT_INT2>(h, plan, v8, gain, s);
   if (e == hipSuccess) e = launch_grouped_variant<NB, QFMT_SIGN1>(h, plan, v8, gain, s);
   if (e == hipSuccess) e = launch_grouped_variant<NB, QFMT_INT4>(h, plan, v8, gain, s);

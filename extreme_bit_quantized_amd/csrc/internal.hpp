@@ -207,6 +207,8 @@ QK_DECL_TG(2)
 QK_DECL_TG(3)
 QK_DECL_TG(4)
 #undef QK_DECL_TG
+// One token, the plan's ternary tiles, dot products on the matrix cores (gemv_tern1.hip).
+hipError_t launch_grouped_tern1(const PlanHeader& h, const void* plan, hipStream_t s);
 hipError_t launch_trellis_decode(const GemvItem& it, int oblock, int8_t* wq, float* dw, hipStream_t s);
 // KV cache and decode attention (attn.hip).
 int64_t attn_workspace_bytes(int n_kv, int group, int T);

@@ -566,6 +566,57 @@ def test_grouped_parity_and_reuse(B):
                 assert (a.view(np.uint32) == b.view(np.uint32)).all()
 
 
+def test_grouped_ternary_one_token_matrix_cores():
+    """The one-token ternary grouped launch (telescoped digits on the matrix
+    cores): row counts around the 16-row groups and 64-row tiles, K of only a
+    tail (256, 768), of whole 1024-weight segments and of segments plus a
+    tail; codes all +1, all -1, all 0 and random in one matrix; activations
+    with saturated blocks (every q = +-127) and zero blocks; a 4-bit matrix in
+    the same plan; three runs, bit-identical."""
+    specs = [(1, 256), (15, 768), (16, 1024), (17, 1280), (63, 3072), (64, 5120), (65, 6912), (130, 2560)]
+    entries, refs = [], []
+    for i, (N, K) in enumerate(specs):
+        codes = synth.symbols([610, i], (N, K), 3).astype(np.int8) - 1
+        codes[0::7] = 1
+        codes[1::7] = -1
+        codes[2::7] = 0
+        scales = synth.uniform_f16([611, i], (N, K // 256), 0.01, 0.1)
+        raw = {"codes": codes, "scales": scales}
+        pw = gpu_weight(TERN, raw, N, K)
+        rp, rs, _ = oracle_weight(TERN, raw)
+        x = synth.gauss([612, i], (1, K))
+        x[0, 32:64] = 50.0                                  # a block of q = +127
+        x[0, 64:96] = -50.0                                 # a block of q = -127
+        x[0, 96:128] = 0.0                                  # a zero block
+        x[0, K - 32:] = np.where(np.arange(32) % 2 == 0, 9.0, -9.0)  # alternating saturated block
+        q, pl, d, s = gpu_act_planes(x)
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda")
+        entries.append((pw, q, pl, d, s, y))
+        rq, rd, _ = oracle.act_quant(x)
+        refs.append((TERN, N, K) + oracle.gemv(TERN, rp, rs, None, K, rq, rd)[:2])
+    raw, pw, (rp, rs, rseeds), x = _prep(INT4, 70, 2048, 613)
+    q, pl, d, s = gpu_act_planes(x)
+    y = torch.full((1, 70), float("nan"), dtype=torch.float32, device="cuda")
+    entries.append((pw, q, pl, d, s, y))
+    rq, rd, _ = oracle.act_quant(x)
+    refs.append((INT4, 70, 2048) + oracle.gemv(INT4, rp, rs, rseeds, 2048, rq, rd)[:2])
+    plan = ebq.GroupedPlan(entries, 1)
+    first = None
+    for rep in range(3):
+        for e in entries:
+            e[5].fill_(float("nan"))
+        plan.run()
+        _sync()
+        outs = [host(e[5]).copy() for e in entries]
+        for (fmt, N, K, yr, absT), o in zip(refs, outs):
+            assert_close_terms(o, yr, absT, what="grouped %s %dx%d rep %d" % (NAMES[fmt], N, K, rep))
+        if first is None:
+            first = outs
+        else:
+            for a, b in zip(first, outs):
+                assert (a.view(np.uint32) == b.view(np.uint32)).all()
+
+
 @pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408)])
 @pytest.mark.parametrize("B", [1, 8, 16, 64])
