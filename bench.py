@@ -946,8 +946,9 @@ def main():
                 "gemv_us": round(tk * 1e6, 1),
                 "per_token_us": round(t * 1e6 / B, 1),
                 "step_cost_vs_B1": round(t / t_b1, 3),
-                "kernels": "dot4, lane per row" if B <= 6 else "int8 matrix cores, %d group(s) of 16 tokens"
-                           % ((B + 15) // 16),
+                "kernels": ("4-bit: dot4, lane per row; ternary: sparse int8 matrix cores, telescoped digits"
+                            if B == 1 else "dot4, lane per row") if B <= 6
+                           else "int8 matrix cores, %d group(s) of 16 tokens" % ((B + 15) // 16),
                 "gbs": round(ms.step_bytes() / t / 1e9, 1),
                 "gemv_weight_gbs": round(ms.weight_bytes() / tk / 1e9, 1),
                 "equiv_tok_s": round(B / t, 1),

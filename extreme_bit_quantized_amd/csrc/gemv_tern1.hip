@@ -16,15 +16,16 @@
 //    so h_j (j = 1..4: at most 80, a signed byte) is needed, not d_j, and
 //    h_j of two bytes is ONE multiply: x in two 16-bit lanes times 3^j puts
 //    h_j in byte 1 of each lane (3^4 255 < 2^16, no carry between lanes).
-//    The last digit, whose h_5 would reach 242, is taken directly: d_4 =
-//    floor(3 (3^4 x mod 256) / 256), i.e. (Y_4 & 0x00FF00FF) * 3.  The low byte
-//    of every 16-bit lane is junk and meets a zero activation.
+//    The last of five digits, whose h_5 would reach 242, is taken directly:
+//    d_4 = floor(3 (3^4 x mod 256) / 256), i.e. (Y_4 & 0x00FF00FF) * 3.  The low
+//    byte of every 16-bit lane is junk and meets a zero activation: the A
+//    operand is 2:4 sparse, which the sparse MFMA skips.
 // 2. The matrix core does the dot products, the telescoping and the
-//    separation into 32-blocks at once: v_mfma_i32_16x16x64_i8 with the
-//    weights as B (64 k x 16 rows) and the activations as A (16 A-rows x 64 k),
+//    separation into 32-blocks at once: v_smfmac_i32_16x16x128_i8 with the
+//    weights as B (128 k x 16 rows) and the activations as A (16 A-rows x 128 k, 2:4 sparse),
 //    A-row 2b + c holding, for the k-bytes of activation block b, the
 //    coefficient of the "+a_{j-1}" term (c = 0) or of the "-3 a_j" term (c = 1)
-//    and zeros elsewhere.  After the eight MFMAs of a 256-weight sub-chunk the
+//    and zeros elsewhere.  After the four MFMAs of a 256-weight sub-chunk the
 //    accumulator holds, per weight row, 16 sums from which the exact block
 //    dots I_b = C[2b] - 3 C[2b+1] - qsum_b follow (the accumulator starts at
 //    -qsum_b: digits are trit + 1), so the fp32 epilogue runs once per
@@ -33,9 +34,9 @@
 // Work unit: a wave owns a 64-row tile, four groups G of 16 rows.  Lane l
 // provides, for row 16 G + l % 16 and k-quarter q = l / 16 of each sub-chunk,
 // the B operand: code words 3q, 3q+1, 3q+2 (ten dwords each: h_1..h_4 and the
-// last digit of bytes 0,2 and of bytes 1,3) and two dwords of word 12 (whose
-// four digits are split between the four quarters), 32 dwords = eight MFMAs'
-// worth.  As A operand the same lane is A-row l % 16 of quarter q: the
+// last digit of bytes 0,2 and of bytes 1,3) and h_{q+1} of word 12 (four
+// digits: h_1..h_4 telescope it whole, one h per quarter), 32 dwords = four
+// sparse MFMAs' worth.  As A operand the same lane is A-row l % 16 of quarter q: the
 // activation dwords its quarter's codes meet, masked to its block and
 // coefficient.  Codes of a 1024-weight segment come into LDS by DMA in whole
 // 128-byte lines (as in the other GEMV kernels), together with the segment's
@@ -87,8 +88,9 @@ constexpr int t1_off(int i) { return 15 * ((i & 3) >> 1) + (i & 1) + 4 * (i >> 2
 // keeps its activation dword: it lies in block b and the coefficient exists.
 // Slot pair kappa % 5 = 0..2 carries h_1..h_3 (both terms), 3 carries h_4 (no
 // "-3 a_4" term: the last digit is taken directly), 4 the last digit (first
-// term only); in word 12 quarter qB holds h_{qB+1} (qB <= 2; h_3 has no second
-// term) or the last digit (qB = 3).
+// term only); in word 12 (four digits, so h_1..h_4 are all at most 80 and no
+// digit is taken directly) quarter qB holds h_{qB+1}, whose second term exists
+// for qB <= 2.
 constexpr uint64_t t1_mask(int i) {
   uint64_t m = 0;
   for (int l = 0; l < 64; ++l) {
@@ -96,7 +98,7 @@ constexpr uint64_t t1_mask(int i) {
     const T1Slot sl = t1_slot(i, j);
     bool on;
     if (sl.kappa < 15) on = ((15 * sl.qB + c + sl.kappa) >> 3) == b && !(c == 1 && sl.kappa % 5 >= 3);
-    else on = b == 7 && !(c == 1 && sl.qB >= 2);
+    else on = b == 7 && !(c == 1 && sl.qB == 3);
     if (on) m |= 1ull << l;
   }
   return m;
@@ -108,14 +110,12 @@ __device__ __forceinline__ uint32_t t1_keep(uint32_t v, uint64_t mask) {
   asm("v_cndmask_b32 %0, 0, %1, %2" : "=v"(r) : "v"(v), "s"(mask));
   return r;
 }
-// b where the lane's bit of `mask` is set, else a.
-__device__ __forceinline__ uint32_t t1_pick(uint32_t a, uint32_t b, uint64_t mask) {
-  uint32_t r;
-  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
-  return r;
-}
 
 __device__ __forceinline__ uint32_t mu24(uint32_t a, uint32_t b) { return __umul24(a, b); }
+
+// Activation dword [a0, a1, a2, a3] as [a0, a2, a1, a3]: the nonzero bytes
+// of [0, a0, 0, a2] and of [0, a1, 0, a3] in compressed A order.
+__device__ __forceinline__ uint32_t t1_aperm(uint32_t v) { return __builtin_amdgcn_perm(0u, v, 0x03010200u); }
 
 // Ten B dwords of code word W: [Y1l Y1h Y2l Y2h Y3l Y3h Y4l Y4h Dl Dh], Yj =
 // 3^j x (x = bytes 0,2 of W in 16-bit lanes for "l", bytes 1,3 for "h"; h_j in
@@ -138,9 +138,9 @@ __device__ __forceinline__ void t1_word(uint32_t W, uint32_t* b) {
 
 // One 256-weight sub-chunk of the tile.  w[G][0..3]: code words 3q, 3q+1, 3q+2
 // and 12 of row 16 G + l % 16; ar[16]: the activation dwords of the lane's
-// compressed A dwords (t1_slot); d0, d1, qs0, qs1: d and qsum of blocks 2q and 2q+1; sw[G]: the
+// compressed A dwords (t1_slot), bytes in the order 0, 2, 1, 3 (t1_aperm); d0, d1, qs0, qs1: d and qsum of blocks 2q and 2q+1; sw[G]: the
 // weight scale of row 16 G + l % 16; acc[G] += sw[G] (d0 I_2q + d1 I_2q+1).
-// z1/zm/z3: the lane's word-12 multiplier, its "last digit" lane mask (q = 3).
+// z1: the lane's word-12 multiplier 3^(q+1).
 __device__ __forceinline__ void t1_sub(const uint32_t (&w)[4][4], const uint32_t (&ar)[16], float d0, float d1,
                                        int qs0, int qs1, const float (&sw)[4], uint32_t z1, float (&acc)[4]) {
   // Compressed A: the nonzero bytes of [0, a_p0, 0, a_p2] (against an "l" B
@@ -152,7 +152,7 @@ __device__ __forceinline__ void t1_sub(const uint32_t (&w)[4][4], const uint32_t
 #define T1_KEEP(k)                                                          \
   {                                                                         \
     constexpr uint64_t mk = t1_mask(k);                                     \
-    A[k] = __builtin_amdgcn_perm(0u, t1_keep(ar[k], mk), 0x03010200u);      \
+    A[k] = t1_keep(ar[k], mk);                                              \
   }
     T1_KEEP(0) T1_KEEP(1) T1_KEEP(2) T1_KEEP(3) T1_KEEP(4) T1_KEEP(5) T1_KEEP(6) T1_KEEP(7)
     T1_KEEP(8) T1_KEEP(9) T1_KEEP(10) T1_KEEP(11) T1_KEEP(12) T1_KEEP(13) T1_KEEP(14) T1_KEEP(15)
@@ -165,12 +165,10 @@ __device__ __forceinline__ void t1_sub(const uint32_t (&w)[4][4], const uint32_t
 #pragma unroll
     for (int mm = 0; mm < 3; ++mm) t1_word(w[G][mm], Bd + 10 * mm);
     {
-      // word 12: quarter q < 3 holds h_{q+1} (3^(q+1) x), quarter 3 the last digit
+      // word 12: quarter q holds h_{q+1} = 3^(q+1) x
       const uint32_t W = w[G][3];
-      const uint32_t xl = W & m, xh = __builtin_amdgcn_perm(0u, W, 0x0C030C01u);
-      const uint32_t yl = mu24(xl, z1), yh = mu24(xh, z1);
-      Bd[30] = t1_pick(yl, mu24(yl & m, 3u), 0xFFFF000000000000ull);
-      Bd[31] = t1_pick(yh, mu24(yh & m, 3u), 0xFFFF000000000000ull);
+      Bd[30] = mu24(W & m, z1);
+      Bd[31] = mu24(__builtin_amdgcn_perm(0u, W, 0x0C030C01u), z1);
     }
     t1_v4i c = {-qs0, 0, -qs1, 0};
 #pragma unroll
@@ -202,8 +200,8 @@ __device__ __forceinline__ void t1_tile(const GemvItem& it, int row0, uint8_t* m
       gptr<const int32_t __attribute__((address_space(1)))*>(it.qsum);
   const int nsb = K >> 8;
   g_u16* stile = gptr<g_u16*>(it.scales) + (int64_t)(row0 >> 6) * ((nsb + 3) / 4) * 256;
-  // word-12 multiplier of this lane's quarter: 3, 9, 27 (h_1..h_3), 27 (then the last digit)
-  const uint32_t z1 = q == 0 ? 3u : q == 1 ? 9u : 27u;
+  // word-12 multiplier of this lane's quarter: 3^(q+1) (h_1..h_4)
+  const uint32_t z1 = q == 0 ? 3u : q == 1 ? 9u : q == 2 ? 27u : 81u;
   // activation dwords of the lane's compressed A (t1_slot): base + t1_off(i),
   // except i = 13 and 15, which in lane groups 2 and 3 are word-12 dwords
   const int abase = 30 * (q & 1) + 2 * (q >> 1) + c;
@@ -276,6 +274,14 @@ __device__ __forceinline__ void t1_tile(const GemvItem& it, int row0, uint8_t* m
         cw[G][s][3] = rp[13 * s + 12];
       }
     }
+    {
+      // this segment's activations into compressed-A byte order, in place; a
+      // wave's LDS accesses complete in order, so the reads below see it
+      u32x4* ap = (u32x4*)(actb + (seg & 1) * T1_ACT + 16 * lane);
+      u32x4 v = *ap;
+      v = u32x4{t1_aperm(v.x), t1_aperm(v.y), t1_aperm(v.z), t1_aperm(v.w)};
+      *ap = v;
+    }
     float sw[4][4];
 #pragma unroll
     for (int G = 0; G < 4; ++G)
@@ -326,7 +332,7 @@ __device__ __forceinline__ void t1_tile(const GemvItem& it, int row0, uint8_t* m
     g_u32* ag = (g_u32*)(qa + (int64_t)sc * 256);
     uint32_t ar[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ar[i] = ag[i == 13 ? sp13 : i == 15 ? sp15 : abase + t1_off(i)];
+    for (int i = 0; i < 16; ++i) ar[i] = t1_aperm(ag[i == 13 ? sp13 : i == 15 ? sp15 : abase + t1_off(i)]);
     const int kb = 8 * sc + 2 * q;
     const float d0 = dg[kb], d1 = dg[kb + 1];
     const int qs0 = sg[kb], qs1 = sg[kb + 1];
