@@ -813,7 +813,12 @@ __device__ __forceinline__ void wait_all() {
 }
 
 // Cache policy of the weight-tile loads: non-temporal (weights stream through
-// once per call; the activations and scales they would evict are reused).
+// once per call; the activations and scales they would evict are reused) where
+// a row segment is whole 128-byte lines.  A ternary segment (208 bytes) is
+// not: the line at each boundary belongs to two consecutive segments, and
+// non-temporal loads fetched it from memory twice (1.5x the weight bytes);
+// ordinary loads find it in L2 for most boundaries.
+template <int FMT> struct TileCachePolicy { static constexpr int v = FMT == QFMT_TERN_B3 ? 0 : 2; };
 constexpr int kTileCachePolicy = 2;  // nt
 
 // ---- one 64-row tile ----------------------------------------------------------------------------------
@@ -905,8 +910,14 @@ __device__ __forceinline__ void gemv_tile(const GemvItem& it, int row0, int wk, 
     for (int i = 0; i < CH; ++i) {
       if constexpr (NOFF == CH) asm volatile("" : "+v"(goff[i < NOFF ? i : 0]));
       const uint32_t off = NOFF == CH ? goff[i < NOFF ? i : 0] : tile_off(i);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tseg + (off & keep)),
-                                       (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0, kTileCachePolicy);
+      if constexpr (TileCachePolicy<FMT>::v == 0)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tseg + (off & keep)),
+                                         (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0,
+                                         0);
+      else
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tseg + (off & keep)),
+                                         (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0,
+                                         kTileCachePolicy);
     }
   };
 

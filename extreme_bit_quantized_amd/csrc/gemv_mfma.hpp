@@ -272,9 +272,14 @@ __device__ __forceinline__ void mfma_tile(const GemvItem& it, int B, int t0, int
       const int r = f / CH, pos = f % CH;
       const int c = CH == 8 ? (pos ^ ((r >> 1) & 7)) : pos;
       const uint32_t off = (uint32_t)(min(r, nvalid - 1) * rb + c * 16);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + (int64_t)sg * SEGB + off),
-                                       (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0,
-                                       kTileCachePolicy);
+      if constexpr (TileCachePolicy<FMT>::v == 0)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + (int64_t)sg * SEGB + off),
+                                         (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0,
+                                         0);
+      else
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + (int64_t)sg * SEGB + off),
+                                         (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0,
+                                         kTileCachePolicy);
     }
     __builtin_amdgcn_sched_barrier(0);
   };

@@ -63,6 +63,9 @@ constexpr int T1_ACT = 1024;                     // int8 activations of one segm
 constexpr int T1_DQ = 256;                       // d[32] then qsum[32] of its blocks
 constexpr int T1_WAVE_LDS = T1_CODE + 2 * T1_ACT + 2 * T1_DQ;
 static_assert(T1_WAVES * T1_WAVE_LDS + 16 <= 160 * 1024, "LDS per workgroup");
+// Cache policy of the code-tile loads: ordinary, not non-temporal (a 208-byte
+// segment shares a line with the next one; TileCachePolicy).
+constexpr int T1_TILE_POLICY = TileCachePolicy<QFMT_TERN_B3>::v;
 
 // Operand layout of v_smfmac_i32_16x16x128_i8 (checked against a host
 // product): B lane l = column l % 16, its eight dwords k-groups 4 j + d and
@@ -234,7 +237,7 @@ __device__ __forceinline__ void t1_tile(const GemvItem& it, int row0, uint8_t* m
       const uint32_t off = toff[i];
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tseg + off),
                                        (__attribute__((address_space(3))) void*)(codes + i * 1024), 16, 0,
-                                       kTileCachePolicy);
+                                       T1_TILE_POLICY);
     }
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(qa + (int64_t)sgi * T1_SEGK +
                                                                                       (uint32_t)(16 * ln)),
