@@ -39,7 +39,7 @@ def test_static_plan_matches_device_plan():
     ebq.load()
     big = [(SIGN1, 300, 5120), (TERN, 200, 2048), (INT4, 130, 1280), (INT2, 90, 2560), (TRELLIS, 70, 1536),
            (SIGN1, 65, 17408)]
-    small = [(INT4, 65, 1024), (SIGN1, 1, 1024)]
+    small = [(INT4, 65, 1024), (SIGN1, 1, 1024), (TERN, 70, 1280)]  # one token: the matrix-core ternary kernel
     for call, (B, specs, seed) in enumerate(((3, big, 600), (1, small, 620))):
         plan, entries, refs = _plan(specs, B, seed)
         assert plan.host.numel() <= ebq.QGEMV_STATIC_PLAN_BYTES
