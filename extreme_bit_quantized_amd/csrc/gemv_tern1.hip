@@ -4,8 +4,9 @@
 // At batch 1 the lane-per-row ternary kernel (gemv_impl.hpp) is bound by its
 // vector instructions, not by HBM: pulling the five base-3 digits out of each
 // byte costs five instructions per four weights (two multiplies by 3, two
-// masks, one byte gather) and the dot products one more.  This kernel needs
-// about 0.7 per weight, from two observations.
+// masks, one byte gather) and the dot products one more.  This kernel spends
+// about 0.7 per weight on the digits and about 1.06 in all (counters), from
+// two observations.
 //
 // 1. Telescoped digits.  A byte x holds the base-3 fraction of its 5 trits
 //    (ceil(256 b / 243)); with h_j = floor(3^j x / 256) the j-th digit is
@@ -38,10 +39,11 @@
 // digits: h_1..h_4 telescope it whole, one h per quarter), 32 dwords = four
 // sparse MFMAs' worth.  As A operand the same lane is A-row l % 16 of quarter q: the
 // activation dwords its quarter's codes meet, masked to its block and
-// coefficient.  Codes of a 1024-weight segment come into LDS by DMA in whole
-// 128-byte lines (as in the other GEMV kernels), together with the segment's
-// activations, d and qsum (double-buffered), and are read lane = (row, quarter)
-// straight from there: no transpose.  The wave's four lane groups end with
+// coefficient.  Codes of a 1024-weight segment (208 bytes per row) come into
+// LDS by DMA, 1 KB per instruction, together with the segment's activations, d
+// and qsum (double-buffered), and are read lane = (row, quarter) straight from
+// there: no transpose.  Ordinary (not non-temporal) loads: a segment shares its
+// boundary lines with its neighbours, whose second fetch then mostly hits L2.  The wave's four lane groups end with
 // partial sums of the same rows (different blocks), added by lane exchange.
 //
 // Sources: [P3] §1.2 (ternary weights: add, subtract or skip, bandwidth-bound);
